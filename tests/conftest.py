@@ -1,0 +1,25 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line(
+        "markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line(
+        "markers", "slow: full-size workloads (minutes of oracle time)")
+
+
+@pytest.fixture(scope="session")
+def gpu():
+    """The HIP binding, on a machine with a GPU.  Fails loudly otherwise."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("a GPU test ran on a machine without a GPU")
+    import sparse_kv_cache_rope_amd as fasa
+    return fasa

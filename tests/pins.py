@@ -1,0 +1,376 @@
+"""Pins: checks that tie the oracle to something other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with a
+closed form, a brute-force enumeration, a library routine or a hand-built
+example.  They look the oracle's functions up through the module attributes at
+call time, so ``test_oracle_mutations.py`` can plant a mistake in the oracle
+and check that some pin catches it.
+
+Passages ("FASA: Frequency-aware Sparse Attention"): gist.science/pt,
+"Resumo Tecnico" section 2 -- "A Descoberta" (RoPE's 2-D frequency chunks),
+TIP "Previsao Online" (sum of dominant-FC contributions), FAC bullets (select
+T_t, full attention over it, absolute positions kept); the decode setting is
+section 1.  The benchmark spec's own pins: with every FC dominant TIP equals the
+full q.k; with B >= n, FAC equals dense attention; TIP is the sum of per-FC
+rotated 2-D dot products; brute force on tiny contexts.
+"""
+
+import cmath
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ----------------------------------------------------------------- RoPE ----
+
+def pin_rope_identity_at_zero():
+    x = _rng(1).standard_normal((3, 64))
+    y = oracle.rope.rope_rotate(x, 0, 1e4)
+    assert np.array_equal(y, x), "RoPE at position 0 must be the identity"
+
+
+def pin_rope_norm_per_fc():
+    x = _rng(2).standard_normal((5, 128))
+    y = oracle.rope.rope_rotate(x, np.array([0, 1, 77, 4096, 131071]), 5e5)
+    nx = x[:, :64] ** 2 + x[:, 64:] ** 2
+    ny = y[:, :64] ** 2 + y[:, 64:] ** 2
+    assert np.allclose(nx, ny, rtol=1e-12, atol=1e-12), "FC norms must be kept"
+
+
+def pin_rope_relative_shift():
+    r = _rng(3)
+    q, k = r.standard_normal(64), r.standard_normal(64)
+    for (m, n, s) in [(5, 2, 100), (300, 17, 4096), (1, 0, 99999)]:
+        a = oracle.rope.rope_rotate(q, m, 1e4) @ oracle.rope.rope_rotate(k, n, 1e4)
+        b = oracle.rope.rope_rotate(q, m + s, 1e4) @ oracle.rope.rope_rotate(k, n + s, 1e4)
+        assert abs(a - b) <= 1e-9 * (1 + abs(a)), "q.k must depend on m - n only"
+
+
+def pin_rope_literal_angles():
+    """Hand-built case: angles are powers of ten by construction."""
+    with open(os.path.join(GOLDEN, "rope_d8_theta1e4.json")) as f:
+        g = json.load(f)
+    d, half = g["head_dim"], g["head_dim"] // 2
+    ang = g["angles_rad"]
+    for c in range(half):
+        e = np.zeros(d)
+        e[c] = 1.0
+        y = oracle.rope.rope_rotate(e, g["position"], g["theta"])
+        want = np.zeros(d)
+        want[c], want[c + half] = math.cos(ang[c]), math.sin(ang[c])
+        assert np.allclose(y, want, rtol=0, atol=1e-13), f"e_{c} rotated wrongly"
+        e = np.zeros(d)
+        e[c + half] = 1.0
+        y = oracle.rope.rope_rotate(e, g["position"], g["theta"])
+        want = np.zeros(d)
+        want[c], want[c + half] = -math.sin(ang[c]), math.cos(ang[c])
+        assert np.allclose(y, want, rtol=0, atol=1e-13), f"e_{c+half} rotated wrongly"
+
+
+def pin_rope_complex_form():
+    """(x_c + i x_{c+C}) * exp(i m theta^(-2c/d)), scalar complex arithmetic."""
+    x = _rng(4).standard_normal(64)
+    m, theta = 123, 1e4
+    y = oracle.rope.rope_rotate(x, m, theta)
+    for c in range(32):
+        z = complex(x[c], x[c + 32]) * cmath.exp(1j * m * math.pow(theta, -2 * c / 64))
+        assert abs(z.real - y[c]) < 1e-12 and abs(z.imag - y[c + 32]) < 1e-12
+
+
+def pin_round_to_dtype():
+    rd = oracle.rope.round_to_dtype
+    # bf16: 8 significant bits.  Representable values stay put.
+    exact = np.array([1.0, -1.5, 2.0 ** -126, 2.0 ** -133, 0.0, 1.0 + 2 ** -7,
+                      2.0 ** 127, -(2 - 2 ** -7) * 2.0 ** 127])
+    assert np.array_equal(rd(exact, "bf16"), exact)
+    # Midpoints go to the even neighbour; just above a midpoint goes up.
+    cases = [(1 + 2 ** -8, 1.0), (1 + 3 * 2 ** -8, 1 + 2 ** -6),
+             (1 + 2 ** -8 + 2 ** -30, 1 + 2 ** -7), (-(1 + 2 ** -8), -1.0),
+             (2.0 ** -134, 0.0), (3 * 2.0 ** -134, 2.0 ** -132),
+             (255.5, 256.0), (254.5, 254.0)]
+    for x, want in cases:
+        assert rd(np.array([x]), "bf16")[0] == want, (x, want)
+    # Against torch's fp32 -> bf16 conversion on fp32 inputs (no double rounding).
+    x = (_rng(5).standard_normal(20000) * 10.0 ** _rng(6).uniform(-30, 30, 20000))
+    x = x.astype(np.float32)
+    t = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(rd(x.astype(np.float64), "bf16"), t)
+    # fp32: ties to even at 24 bits.
+    assert rd(np.array([1 + 2 ** -24]), "f32")[0] == 1.0
+    assert rd(np.array([1 + 3 * 2 ** -24]), "f32")[0] == 1 + 2 ** -22
+
+
+# ------------------------------------------------------------------ TIP ----
+
+def pin_tip_all_fcs_is_full_dot():
+    r = _rng(7)
+    q, k = r.standard_normal(128), r.standard_normal((50, 128))
+    qr = oracle.rope.rope_rotate(q, 49, 5e5)
+    kr = oracle.rope.rope_rotate(k, np.arange(50), 5e5)
+    s = oracle.tip.tip_scores(qr, kr, np.arange(64))
+    full = np.array([float(np.dot(qr, kr[j])) for j in range(50)])
+    assert np.allclose(s, full, rtol=1e-12, atol=1e-12), "all-FC TIP must equal q.k"
+
+
+def pin_tip_relative_complex():
+    """TIP from pre-RoPE values: sum_c Re[z_q conj(z_k) exp(i (m_q - m_k) w_c)]."""
+    r = _rng(8)
+    d, half, theta = 64, 32, 1e4
+    q, k = r.standard_normal(d), r.standard_normal((20, d))
+    dom = np.array([0, 3, 17, 31])
+    mq = 40
+    qr = oracle.rope.rope_rotate(q, mq, theta)
+    kr = oracle.rope.rope_rotate(k, np.arange(20), theta)
+    s = oracle.tip.tip_scores(qr, kr, dom)
+    for j in range(20):
+        want = 0.0
+        for c in dom:
+            zq, zk = complex(q[c], q[c + half]), complex(k[j, c], k[j, c + half])
+            w = math.pow(theta, -2 * c / d)
+            want += (zq * zk.conjugate() * cmath.exp(1j * (mq - j) * w)).real
+        assert abs(s[j] - want) < 1e-10, (j, s[j], want)
+
+
+def pin_tip_single_fc():
+    r = _rng(9)
+    q, k = r.standard_normal(128), r.standard_normal((7, 128))
+    for c in (0, 5, 63):
+        s = oracle.tip.tip_scores(q, k, np.array([c]))
+        want = q[c] * k[:, c] + q[c + 64] * k[:, c + 64]
+        assert np.allclose(s, want, rtol=1e-14, atol=1e-14)
+
+
+def pin_tip_linear_in_q():
+    r = _rng(10)
+    q1, q2, k = r.standard_normal(64), r.standard_normal(64), r.standard_normal((9, 64))
+    dom = np.array([1, 2, 30])
+    lhs = oracle.tip.tip_scores(2.5 * q1 - 0.75 * q2, k, dom)
+    rhs = 2.5 * oracle.tip.tip_scores(q1, k, dom) - 0.75 * oracle.tip.tip_scores(q2, k, dom)
+    assert np.allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------ selection ----
+
+def _brute_force_topb(s, budget):
+    """Max-sum subset of size min(B, n); among equal sums the lexicographically
+    smallest ascending tuple (= ties to the lower position)."""
+    n = len(s)
+    take = min(budget, n)
+    best, best_key = None, None
+    for comb in itertools.combinations(range(n), take):
+        key = (-sum(s[j] for j in comb), comb)
+        if best_key is None or key < best_key:
+            best, best_key = comb, key
+    return list(best) + [-1] * (budget - take)
+
+
+def pin_select_brute_force():
+    r = _rng(11)
+    for trial in range(60):
+        n = int(r.integers(1, 11))
+        budget = int(r.integers(1, 5))
+        # Small integer scores force many ties.
+        s = r.integers(-3, 4, size=n).astype(np.float64)
+        got = oracle.select.select_topb(s, budget).tolist()
+        assert got == _brute_force_topb(s.tolist(), budget), (s, budget, got)
+
+
+def pin_select_vs_stable_argsort():
+    r = _rng(12)
+    s = np.round(r.standard_normal(3000), 2)  # many ties
+    for budget in (1, 17, 256, 2999, 3000):
+        got = oracle.select.select_topb(s, budget)
+        want = np.sort(np.argsort(-s, kind="stable")[:budget])
+        assert np.array_equal(got, want)
+
+
+def pin_select_hand_example():
+    with open(os.path.join(GOLDEN, "select_ties.json")) as f:
+        g = json.load(f)
+    # Worked by hand from the ranking 0, 2, 4, 3, 1, 5 (see the fixture).
+    expect = {1: [0], 2: [0, 2], 3: [0, 2, 4], 4: [0, 2, 3, 4],
+              8: [0, 1, 2, 3, 4, 5, -1, -1]}
+    for budget in g["budgets"]:
+        got = oracle.select.select_topb(np.array(g["scores"]), budget).tolist()
+        assert got == expect[budget], (budget, got)
+
+
+def pin_select_budget_ge_n():
+    s = _rng(13).standard_normal(10)
+    got = oracle.select.select_topb(s, 16)
+    assert got.tolist() == list(range(10)) + [-1] * 6
+
+
+# ------------------------------------------------------------------ FAC ----
+
+def _sdpa(q, k, v):
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, None, None, :],
+        torch.from_numpy(k)[None, None], torch.from_numpy(v)[None, None])
+    return out[0, 0, 0].numpy()
+
+
+def pin_fac_dense_when_budget_covers_all():
+    r = _rng(14)
+    q, k, v = r.standard_normal(128), r.standard_normal((40, 128)), r.standard_normal((40, 128))
+    got = oracle.fac.attend_subset(q, k, v, np.arange(40))
+    assert np.allclose(got, _sdpa(q, k, v), rtol=1e-12, atol=1e-12)
+
+
+def pin_fac_single_token():
+    r = _rng(15)
+    q, k, v = r.standard_normal(64), r.standard_normal((12, 64)), r.standard_normal((12, 64))
+    got = oracle.fac.attend_subset(q, k, v, np.array([7, -1, -1]))
+    assert np.allclose(got, v[7], rtol=0, atol=1e-15)
+
+
+def pin_fac_constant_values():
+    r = _rng(16)
+    q, k = r.standard_normal(64), r.standard_normal((12, 64))
+    v = np.tile(r.standard_normal(64), (12, 1))
+    got = oracle.fac.attend_subset(q, k, v, np.array([1, 4, 9]))
+    assert np.allclose(got, v[0], rtol=1e-14, atol=1e-14)
+
+
+def pin_fac_zero_query_is_mean():
+    r = _rng(17)
+    k, v = r.standard_normal((12, 64)), r.standard_normal((12, 64))
+    sub = np.array([0, 3, 5, 11])
+    got = oracle.fac.attend_subset(np.zeros(64), k, v, sub)
+    assert np.allclose(got, v[sub].mean(axis=0), rtol=1e-13, atol=1e-13)
+
+
+def pin_fac_permutation_invariant():
+    r = _rng(18)
+    q, k, v = r.standard_normal(64), r.standard_normal((30, 64)), r.standard_normal((30, 64))
+    sub = np.array([2, 8, 9, 20, 29])
+    a = oracle.fac.attend_subset(q, k, v, sub)
+    b = oracle.fac.attend_subset(q, k, v, sub[::-1].copy())
+    assert np.allclose(a, b, rtol=1e-14, atol=1e-14)
+
+
+def pin_fac_scale_closed_form():
+    """q.k_A = sqrt(d) ln 3, q.k_B = 0  =>  weights 3/4 and 1/4."""
+    d = 64
+    q = np.zeros(d)
+    q[0] = 1.0
+    k = np.zeros((2, d))
+    k[0, 0] = math.sqrt(d) * math.log(3.0)
+    v = np.zeros((2, d))
+    v[0, 0], v[1, 1] = 1.0, 1.0
+    got = oracle.fac.attend_subset(q, k, v, np.array([0, 1]))
+    assert abs(got[0] - 0.75) < 1e-14 and abs(got[1] - 0.25) < 1e-14, got[:2]
+
+
+def pin_fac_ignores_unselected():
+    r = _rng(19)
+    q, k, v = r.standard_normal(64), r.standard_normal((10, 64)), r.standard_normal((10, 64))
+    sub = np.array([1, 6])
+    a = oracle.fac.attend_subset(q, k, v, sub)
+    k2, v2 = k.copy(), v.copy()
+    k2[[0, 2, 3]] *= 50.0
+    v2[[0, 2, 3]] += 7.0
+    b = oracle.fac.attend_subset(q, k2, v2, sub)
+    assert np.allclose(a, b, rtol=0, atol=0)
+
+
+# --------------------------------------------------------------- decode ----
+
+def _state(n_q, n_kv, d, theta, dtype, dom, cap, batch=1):
+    return oracle.decode.OracleState(batch, n_q, n_kv, d, theta, dtype, dom, cap)
+
+
+def pin_decode_dense_equivalence():
+    """All FCs dominant and B >= n: the step is dense attention with RoPE."""
+    r = _rng(20)
+    d, n, theta = 64, 33, 1e4
+    dom = np.tile(np.arange(32), (2, 1))
+    st = _state(2, 1, d, theta, "f32", dom, 64)
+    k = r.standard_normal((1, n - 1, d)).astype(np.float32).astype(np.float64)
+    v = r.standard_normal((1, n - 1, d))
+    st.append(0, k, v)
+    q = r.standard_normal((1, 2, d))
+    kn, vn = r.standard_normal((1, 1, d)), r.standard_normal((1, 1, d))
+    res = st.step(q, kn, vn, budget=64)
+    kall = np.concatenate([k[0], kn[0]], axis=0)
+    vall = np.concatenate([v[0], vn[0]], axis=0)
+    # Independent rotation: complex phasors, query at the last position n-1.
+    def rot(x, m):
+        z = x[:32] + 1j * x[32:]
+        z = z * np.exp(1j * m * theta ** (-2.0 * np.arange(32) / d))
+        return np.concatenate([z.real, z.imag])
+    kr = np.stack([rot(kall[j], j) for j in range(n)])
+    for h in range(2):
+        want = _sdpa(rot(q[0, h], n - 1), kr, vall)
+        # The oracle rounds K to fp32 once; allow for that rounding only.
+        assert np.allclose(res["out"][0, h], want, rtol=1e-6, atol=1e-6), h
+        assert res["idx"][0, h].tolist()[:n] == list(range(n))
+
+
+def pin_decode_query_position():
+    """Equal pre-RoPE q and k rows at every position: the score of the token at
+    the query's own position is exactly |k|^2, the Cauchy-Schwarz maximum."""
+    r = _rng(21)
+    d, n, theta = 64, 20, 1e4
+    x = r.standard_normal(d)
+    dom = np.arange(32)[None, :]
+    st = _state(1, 1, d, theta, "f32", dom, 32)
+    st.append(0, np.tile(x, (1, n - 1, 1)), np.zeros((1, n - 1, d)))
+    st.append(0, x[None, None, :], np.zeros((1, 1, d)))
+    qr = st.query_rot(0, x[None, :])
+    s = st.head_scores(0, 0, qr[0])
+    assert abs(s[n - 1] - float(x @ x)) < 1e-5 * float(x @ x)
+    assert np.argmax(s) == n - 1
+
+
+def pin_decode_append_consistency():
+    """Bulk append and one-row appends give the same cache, and each row is
+    its own position's rotation rounded to the dtype."""
+    r = _rng(22)
+    d, n = 128, 40
+    dom = np.tile(np.arange(8), (4, 1))
+    k, v = r.standard_normal((2, n, d)), r.standard_normal((2, n, d))
+    a = _state(4, 2, d, 5e5, "bf16", dom, 64)
+    a.append(0, k, v)
+    b = _state(4, 2, d, 5e5, "bf16", dom, 64)
+    for j in range(n):
+        b.append(0, k[:, j:j + 1], v[:, j:j + 1])
+    assert np.array_equal(a.K, b.K) and np.array_equal(a.V, b.V)
+    j = 31
+    want = oracle.rope.round_to_dtype(oracle.rope.rope_rotate(k[1, j], j, 5e5), "bf16")
+    assert np.array_equal(a.K[0, 1, j], want)
+
+
+def pin_loops_agree():
+    """NumPy steps against the scalar-loop restatements."""
+    r = _rng(23)
+    d, n = 32, 25
+    q, k, v = r.standard_normal(d), r.standard_normal((n, d)), r.standard_normal((n, d))
+    kr = oracle.rope.rope_rotate(k, np.arange(n), 1e4)
+    for j in (0, 9, 24):
+        assert np.allclose(kr[j], oracle.loops.rope_loop(list(k[j]), j, 1e4), atol=1e-13)
+    dom = [2, 5, 11]
+    s = oracle.tip.tip_scores(q, kr, np.array(dom))
+    assert np.allclose(s, oracle.loops.tip_loop(list(q), kr.tolist(), dom), atol=1e-12)
+    for budget in (1, 4, 25, 30):
+        assert oracle.select.select_topb(s, budget).tolist() == \
+            oracle.loops.topb_loop(list(s), budget)
+    sub = oracle.select.select_topb(s, 6)
+    assert np.allclose(oracle.fac.attend_subset(q, kr, v, sub),
+                       oracle.loops.attend_loop(list(q), kr.tolist(), v.tolist(), list(sub)),
+                       atol=1e-13)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
