@@ -1,0 +1,210 @@
+/*
+ * fasa.h -- C ABI of the FASA decode hot path on MI355X (gfx950).
+ *
+ * FASA ("FASA: Frequency-aware Sparse Attention") scores every cached token
+ * with only the dominant RoPE frequency chunks (FCs) of each query head (TIP),
+ * keeps the top-B tokens per head (the critical set T_t) and runs full
+ * attention over those tokens only (FAC).  Passages: gist.science/pt,
+ * "Resumo Tecnico" section 2 ("A Descoberta"; TIP "Calibracao Offline" and
+ * "Previsao Online"; FAC bullets) and "Variantes de Implementacao" (FASA-C keeps
+ * the cache on the GPU and reads a sparse subset of it).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Shapes are row-major.  b = batch, Hq = query heads, Hkv = KV heads,
+ *   G = Hq / Hkv, d = head_dim (64 or 128), C = d / 2 FCs, cap = capacity.
+ *   Query head h reads KV head h / G.
+ * - FC c is the dimension pair (c, c + C) (rotate-half); its frequency is
+ *   theta^(-2c/d); the angle at absolute position m is m * theta^(-2c/d),
+ *   formed in fp64.
+ * - Element type ("dtype") of q, k_new, v_new, the K/V caches and the sidecar:
+ *   FASA_F32 = float, FASA_BF16 = bfloat16 (raw 16-bit patterns).
+ *   Accumulation is fp32; outputs and scores are float.
+ * - K cache, V cache: [b][Hkv][cap][d] dtype.  Slot j holds absolute position
+ *   j.  K holds RoPE(k, j) rounded once (nearest-even) to dtype; V holds v.
+ * - Sidecar: the K columns of each KV head's union U_g of its query heads'
+ *   dominant FCs, packed FC-major so TIP reads them with coalesced loads:
+ *   [b][P][cap] pairs, P = sum_g |U_g|, plane fasa_sidecar_layout() gives the
+ *   FC of each plane; a pair is (K[.., c], K[.., c + C]) (bf16: low half is
+ *   column c; f32: two floats).  It is bit-identical to those K columns.
+ * - seq_lens: device int32 [b].  Its meaning is stated per call.
+ * - max_seq_len: host-side upper bound on every sequence length the call
+ *   will see on the device (sizes the launch grid); must be <= cap.
+ * - Every device pointer is caller-owned (allocate with hipMalloc or a
+ *   framework); the library owns only the context and its small constant
+ *   tables.  All calls are asynchronous on `stream`, never synchronise, never
+ *   allocate (except fasa_create / fasa_check).
+ * - Workspace: fasa_workspace_bytes() bytes of device memory, zero-filled
+ *   before its first use (fasa_workspace_init does it); every call leaves it in
+ *   that state again.  Calls that share one workspace must be ordered on one
+ *   stream; calls on different workspaces may overlap.
+ * - Errors: a call that finds a bad argument on the host returns a negative
+ *   status and enqueues nothing; fasa_last_error() describes it.  Bad values
+ *   only the device can see (a sequence length beyond max_seq_len or cap, an
+ *   index >= its sequence length) set a sticky flag in the workspace; the
+ *   affected rows produce zeros / -1 and fasa_check() reports the flag.
+ */
+#ifndef FASA_H
+#define FASA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fasa_ctx fasa_ctx;
+
+typedef enum {
+  FASA_OK = 0,
+  FASA_ERR_INVALID_ARG = -1,  /* bad shape, null pointer, out-of-range value */
+  FASA_ERR_CAPACITY = -2,     /* max_seq_len / budget / rows beyond the ctx limits */
+  FASA_ERR_UNSUPPORTED = -3,  /* valid but not built: d, G or dtype */
+  FASA_ERR_HIP = -4,          /* a HIP runtime call failed */
+  FASA_ERR_DEVICE_FLAG = -5   /* fasa_check found the device error flag set */
+} fasa_status;
+
+typedef enum { FASA_F32 = 0, FASA_BF16 = 1 } fasa_dtype;
+
+/* fasa_decode_step flag: add 1 to every seq_lens[b] after the step. */
+#define FASA_ADVANCE_SEQ_LENS 1u
+
+/* Device error-flag bits (fasa_check's *flags). */
+#define FASA_DEVFLAG_SEQ_LEN 1u   /* a sequence length outside [1, max_seq_len] or > cap */
+#define FASA_DEVFLAG_INDEX 2u     /* an index >= its sequence length */
+#define FASA_DEVFLAG_APPEND 4u    /* an append beyond cap */
+
+/*
+ * Create a context for one attention layer's shapes.
+ * dom_fc: host int32 [n_q_heads][n_dom], the offline-calibrated dominant FC
+ *   indices I_dom of each query head (gist.science/pt, "Resumo Tecnico"
+ *   section 2, TIP "Calibracao Offline"), each in [0, C), distinct per head.
+ *   Copied; the caller keeps ownership.
+ * Limits: head_dim 64 or 128; G in {1, 2, 4, 8}; capacity a positive multiple
+ *   of 64; 1 <= n_dom <= C; 1 <= max_budget <= capacity.
+ * Allocates the constant tables on the current HIP device (the device every
+ * later call must run on).  *out is NULL on failure.
+ */
+fasa_status fasa_create(fasa_ctx** out, int batch, int n_q_heads, int n_kv_heads,
+                        int head_dim, int capacity, double rope_theta,
+                        fasa_dtype dtype, const int32_t* dom_fc, int n_dom,
+                        int max_budget);
+void fasa_destroy(fasa_ctx* ctx);
+
+/* Sizes in bytes of one K (or V) cache, the sidecar and the workspace. */
+size_t fasa_kv_cache_bytes(const fasa_ctx* ctx);
+size_t fasa_sidecar_bytes(const fasa_ctx* ctx);
+size_t fasa_workspace_bytes(const fasa_ctx* ctx);
+
+/*
+ * Sidecar layout.  plane_offset: host int32 [Hkv + 1] (planes of KV head g
+ * are plane_offset[g] .. plane_offset[g+1]-1); plane_fc: host int32 [P], the
+ * FC held by each plane (ascending within a KV head).  Either may be NULL.
+ * Returns P (>= 0) or a negative status.
+ */
+int fasa_sidecar_layout(const fasa_ctx* ctx, int32_t* plane_offset, int32_t* plane_fc);
+
+/* Zero-fill a workspace (a fill kernel on `stream`, no memset node). */
+fasa_status fasa_workspace_init(fasa_ctx* ctx, void* workspace, hipStream_t stream);
+
+/*
+ * Append n_new tokens per sequence (prefill, or a decode step's new token).
+ * Rotates each key at its absolute position (start_pos[b] + t) with RoPE in
+ * fp64, rounds once to dtype, writes the K row, the V row (copied) and the
+ * sidecar pairs.  Source: gist.science/pt, "Resumo Tecnico" section 2, FAC
+ * third bullet (absolute positions are kept) and "A Descoberta" (FCs);
+ * section 1 (the cache grows per generated token).
+ * k_new, v_new: device [b][Hkv][n_new][d] dtype, pre-RoPE.
+ * start_pos: device int32 [b], first position written; rows past cap are
+ *   skipped and raise FASA_DEVFLAG_APPEND.
+ * n_new: >= 0 (0 is a no-op).  workspace: only its error flag is used.
+ */
+fasa_status fasa_append_kv(fasa_ctx* ctx, void* k_cache, void* v_cache, void* sidecar,
+                           const void* k_new, const void* v_new,
+                           const int32_t* start_pos, int n_new, void* workspace,
+                           hipStream_t stream);
+
+/*
+ * TIP scores (gist.science/pt, "Resumo Tecnico" section 2, TIP "Previsao
+ * Online"): for every query head h and cached token j < n_b,
+ *   scores[b][h][j] = sum_{c in I_dom(h)} q~_c K[j][c] + q~_{c+C} K[j][c+C],
+ * with q~ = RoPE(q, n_b - 1) kept in fp32.  Read from the sidecar only.
+ * q: device [b][Hq][d] dtype, pre-RoPE.  seq_lens[b] = n_b, tokens scored
+ * (the query's position is n_b - 1).  scores: device float [b][Hq][cap];
+ * entries j >= n_b are not written.
+ */
+fasa_status fasa_tip_scores(fasa_ctx* ctx, const void* sidecar, const void* q,
+                            const int32_t* seq_lens, int max_seq_len, float* scores,
+                            void* workspace, hipStream_t stream);
+
+/*
+ * Top-B selection of the critical set T_t (gist.science/pt, "Resumo Tecnico"
+ * section 2, FAC first bullet): per (b, h), the min(budget, n_b) positions
+ * with the highest scores[b][h][0 .. n_b), equal scores going to the lower
+ * position, written ascending to idx[b][h][0 ..] and padded with -1 up to
+ * budget.  Exact (radix select on order-preserving keys of the fp32 scores).
+ * scores: device float [b][Hq][cap]; seq_lens[b] = n_b; 1 <= budget <=
+ * max_budget; idx: device int32 [b][Hq][budget].
+ */
+fasa_status fasa_topk(fasa_ctx* ctx, const float* scores, const int32_t* seq_lens,
+                      int max_seq_len, int budget, int32_t* idx, void* workspace,
+                      hipStream_t stream);
+
+/*
+ * FAC (gist.science/pt, "Resumo Tecnico" section 2, FAC second and third
+ * bullets): per (b, h), attention of q~ = RoPE(q, n_b - 1) over the rows
+ * idx[b][h][0 .. min(budget, n_b)) of the caches only:
+ *   out = sum_j softmax_j(q~ . K[j] / sqrt(d)) V[j], softmax over those rows.
+ * Entries < 0 are skipped; an entry >= n_b is skipped and raises
+ * FASA_DEVFLAG_INDEX.  A head with no row gets zeros.
+ * q: device [b][Hq][d] dtype, pre-RoPE; seq_lens[b] = n_b; idx: device int32
+ * [b][Hq][budget]; out: device float [b][Hq][d].
+ */
+fasa_status fasa_sparse_attn(fasa_ctx* ctx, const void* k_cache, const void* v_cache,
+                             const void* q, const int32_t* seq_lens, const int32_t* idx,
+                             int budget, float* out, void* workspace, hipStream_t stream);
+
+/*
+ * One whole decode step (gist.science/pt, "Resumo Tecnico" sections 1-2):
+ * append the new token at position seq_lens[b] (as fasa_append_kv), then
+ * with n_b = seq_lens[b] + 1 run TIP, top-B and FAC as the three calls
+ * above, the query at position n_b - 1.
+ * seq_lens: device int32 [b], tokens cached BEFORE this step; incremented on
+ *   the device after the step when flags has FASA_ADVANCE_SEQ_LENS.
+ * max_seq_len >= every n_b of this step.  q: [b][Hq][d]; k_new, v_new:
+ * [b][Hkv][d] (pre-RoPE, dtype).  out: float [b][Hq][d].  idx_out: int32
+ * [b][Hq][budget] or NULL.
+ */
+fasa_status fasa_decode_step(fasa_ctx* ctx, void* k_cache, void* v_cache, void* sidecar,
+                             const void* q, const void* k_new, const void* v_new,
+                             int32_t* seq_lens, int max_seq_len, int budget, float* out,
+                             int32_t* idx_out, void* workspace, unsigned flags,
+                             hipStream_t stream);
+
+/*
+ * Dense full-KV decode attention over all n_b cached tokens (the comparator
+ * the pages measure FASA against: full KV, gist.science/pt, "Resumo Tecnico"
+ * section 4).  seq_lens[b] = n_b; out: float [b][Hq][d].
+ */
+fasa_status fasa_dense_attn(fasa_ctx* ctx, const void* k_cache, const void* v_cache,
+                            const void* q, const int32_t* seq_lens, int max_seq_len,
+                            float* out, void* workspace, hipStream_t stream);
+
+/*
+ * Synchronise `stream`, read and clear the workspace's device error flag.
+ * *flags (may be NULL) receives the FASA_DEVFLAG_* bits.  Returns
+ * FASA_ERR_DEVICE_FLAG when any bit was set.
+ */
+fasa_status fasa_check(fasa_ctx* ctx, void* workspace, hipStream_t stream, uint32_t* flags);
+
+const char* fasa_status_string(fasa_status status);
+/* Detail of the last host-side error on the calling thread ("" if none). */
+const char* fasa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FASA_H */

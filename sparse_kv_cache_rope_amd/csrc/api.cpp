@@ -1,0 +1,426 @@
+// C ABI of libfasa: argument checks, context tables, workspace layout and the
+// launch order of each call.  Declarations and semantics: include/fasa.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "device_common.hpp"
+#include "fasa_internal.hpp"
+
+using namespace fasa;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fasa_status fail(fasa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fasa_status ok() {
+  g_last_error.clear();
+  return FASA_OK;
+}
+
+fasa_status hip_fail(hipError_t e, const char* what) {
+  return fail(FASA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t dtype_size(fasa_dtype t) { return t == FASA_BF16 ? 2 : 4; }
+
+void build_layout(fasa_ctx* c) {
+  WsLayout& w = c->ws;
+  const size_t rows = (size_t)c->batch * c->hq;
+  w.max_chunks = (c->cap + kChunk - 1) / kChunk;
+  w.fac_splits = (c->max_budget + kFacSplitRows - 1) / kFacSplitRows;
+  w.dense_splits = (c->cap + kDenseSplitTokens - 1) / kDenseSplitTokens;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  w.err = take(16);
+  w.nb = take(sizeof(int32_t) * c->batch);
+  w.qrot = take(sizeof(float) * rows * c->d);
+  w.tipw = take(sizeof(float) * c->batch * (size_t)c->P * c->G * 2);
+  w.scores = take(sizeof(float) * rows * c->cap);
+  w.hist = take(sizeof(uint32_t) * rows * kHistBins);
+  w.ticket = take(sizeof(uint32_t) * rows * kTicketsPerRow);
+  w.rowst = take(sizeof(RowState) * rows);
+  w.cand = take(sizeof(uint64_t) * rows * c->cap);
+  w.chunk_gt = take(sizeof(uint32_t) * rows * w.max_chunks);
+  w.chunk_off = take(sizeof(uint32_t) * rows * w.max_chunks);
+  w.idx = take(sizeof(int32_t) * rows * c->max_budget);
+  w.fac = take(sizeof(float) * rows * w.fac_splits * (c->d + 2));
+  w.dense = take(sizeof(float) * rows * w.dense_splits * (c->d + 2));
+  w.total = off;
+}
+
+fasa_status check_ctx(const fasa_ctx* c) {
+  if (!c) return fail(FASA_ERR_INVALID_ARG, "null context");
+  return FASA_OK;
+}
+
+fasa_status check_len(const fasa_ctx* c, int max_seq_len) {
+  if (max_seq_len < 1) return fail(FASA_ERR_INVALID_ARG, "max_seq_len %d < 1", max_seq_len);
+  if (max_seq_len > c->cap)
+    return fail(FASA_ERR_CAPACITY, "max_seq_len %d exceeds capacity %d", max_seq_len, c->cap);
+  return FASA_OK;
+}
+
+fasa_status check_budget(const fasa_ctx* c, int budget) {
+  if (budget < 1) return fail(FASA_ERR_INVALID_ARG, "budget %d < 1", budget);
+  if (budget > c->max_budget)
+    return fail(FASA_ERR_CAPACITY, "budget %d exceeds max_budget %d", budget, c->max_budget);
+  return FASA_OK;
+}
+
+#define FASA_NONNULL(p)                                                  \
+  do {                                                                   \
+    if ((p) == nullptr) return fail(FASA_ERR_INVALID_ARG, "%s is null", #p); \
+  } while (0)
+
+#define FASA_TRY(expr)                      \
+  do {                                      \
+    fasa_status _st = (expr);               \
+    if (_st != FASA_OK) return _st;         \
+  } while (0)
+
+#define FASA_HIP(expr, what)                \
+  do {                                      \
+    hipError_t _e = (expr);                 \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+fasa_status fasa_create(fasa_ctx** out, int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                        int capacity, double rope_theta, fasa_dtype dtype,
+                        const int32_t* dom_fc, int n_dom, int max_budget) {
+  if (out == nullptr) return fail(FASA_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  if (batch < 1) return fail(FASA_ERR_INVALID_ARG, "batch %d < 1", batch);
+  if (n_q_heads < 1 || n_kv_heads < 1)
+    return fail(FASA_ERR_INVALID_ARG, "head counts must be >= 1 (%d, %d)", n_q_heads, n_kv_heads);
+  if (n_q_heads % n_kv_heads)
+    return fail(FASA_ERR_INVALID_ARG, "n_q_heads %d not a multiple of n_kv_heads %d", n_q_heads,
+                n_kv_heads);
+  const int G = n_q_heads / n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(FASA_ERR_UNSUPPORTED, "query heads per KV head %d not in {1,2,4,8}", G);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(FASA_ERR_UNSUPPORTED, "head_dim %d not in {64,128}", head_dim);
+  if (capacity < 64 || capacity % 64)
+    return fail(FASA_ERR_INVALID_ARG, "capacity %d must be a positive multiple of 64", capacity);
+  if ((long long)capacity > (long long)kMaxChunks * kChunk)
+    return fail(FASA_ERR_CAPACITY, "capacity %d above %d", capacity, kMaxChunks * kChunk);
+  if (!(rope_theta > 1.0) || !std::isfinite(rope_theta))
+    return fail(FASA_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
+  if (dtype != FASA_F32 && dtype != FASA_BF16)
+    return fail(FASA_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+  if (dom_fc == nullptr) return fail(FASA_ERR_INVALID_ARG, "dom_fc is null");
+  const int C = head_dim / 2;
+  if (n_dom < 1 || n_dom > C)
+    return fail(FASA_ERR_INVALID_ARG, "n_dom %d not in [1, %d]", n_dom, C);
+  if (max_budget < 1 || max_budget > capacity)
+    return fail(FASA_ERR_INVALID_ARG, "max_budget %d not in [1, capacity]", max_budget);
+  for (int h = 0; h < n_q_heads; ++h) {
+    uint64_t seen = 0;
+    for (int f = 0; f < n_dom; ++f) {
+      const int v = dom_fc[(size_t)h * n_dom + f];
+      if (v < 0 || v >= C)
+        return fail(FASA_ERR_INVALID_ARG, "dom_fc[%d][%d] = %d outside [0, %d)", h, f, v, C);
+      if (seen >> v & 1ull)
+        return fail(FASA_ERR_INVALID_ARG, "dom_fc[%d] repeats FC %d", h, v);
+      seen |= 1ull << v;
+    }
+  }
+
+  fasa_ctx* c = new (std::nothrow) fasa_ctx();
+  if (!c) return fail(FASA_ERR_INVALID_ARG, "out of host memory");
+  c->batch = batch;
+  c->hq = n_q_heads;
+  c->hkv = n_kv_heads;
+  c->d = head_dim;
+  c->C = C;
+  c->cap = capacity;
+  c->G = G;
+  c->F = n_dom;
+  c->max_budget = max_budget;
+  c->theta = rope_theta;
+  c->dtype = dtype;
+  c->dom.assign(dom_fc, dom_fc + (size_t)n_q_heads * n_dom);
+  c->dev_alloc = nullptr;
+
+  // Sidecar planes: per KV head, the union of its query heads' dominant FCs.
+  std::vector<int32_t> fc_slot((size_t)n_kv_heads * C, -1);
+  std::vector<uint64_t> mask(n_q_heads, 0);
+  for (int h = 0; h < n_q_heads; ++h)
+    for (int f = 0; f < n_dom; ++f) mask[h] |= 1ull << c->dom[(size_t)h * n_dom + f];
+  c->plane_off.assign(n_kv_heads + 1, 0);
+  for (int g = 0; g < n_kv_heads; ++g) {
+    uint64_t uni = 0;
+    for (int k = 0; k < G; ++k) uni |= mask[(size_t)g * G + k];
+    int slot = 0;
+    for (int fc = 0; fc < C; ++fc)
+      if (uni >> fc & 1ull) {
+        fc_slot[(size_t)g * C + fc] = slot++;
+        c->plane_fc.push_back(fc);
+      }
+    c->plane_off[g + 1] = c->plane_off[g] + slot;
+  }
+  c->P = c->plane_off[n_kv_heads];
+  std::vector<double> omega(C);
+  for (int i = 0; i < C; ++i) omega[i] = std::pow(rope_theta, -2.0 * i / head_dim);
+
+  build_layout(c);
+
+  // One device allocation for the constant tables.
+  const size_t b_off = align256(sizeof(int32_t) * (n_kv_heads + 1));
+  const size_t b_slot = align256(sizeof(int32_t) * fc_slot.size());
+  const size_t b_mask = align256(sizeof(uint64_t) * mask.size());
+  const size_t b_omega = align256(sizeof(double) * C);
+  const size_t bytes = b_off + b_slot + b_mask + b_omega;
+  hipError_t e = hipGetDevice(&c->device);
+  if (e == hipSuccess) e = hipMalloc(&c->dev_alloc, bytes);
+  if (e != hipSuccess) {
+    c->dev_alloc = nullptr;
+    fasa_destroy(c);
+    return hip_fail(e, "fasa_create: device tables");
+  }
+  uint8_t* base = static_cast<uint8_t*>(c->dev_alloc);
+  c->tab.plane_off = reinterpret_cast<int32_t*>(base);
+  c->tab.fc_slot = reinterpret_cast<int32_t*>(base + b_off);
+  c->tab.dom_mask = reinterpret_cast<uint64_t*>(base + b_off + b_slot);
+  c->tab.omega = reinterpret_cast<double*>(base + b_off + b_slot + b_mask);
+  e = hipMemcpy(c->tab.plane_off, c->plane_off.data(), sizeof(int32_t) * c->plane_off.size(),
+                hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(c->tab.fc_slot, fc_slot.data(), sizeof(int32_t) * fc_slot.size(),
+                  hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(c->tab.dom_mask, mask.data(), sizeof(uint64_t) * mask.size(),
+                  hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(c->tab.omega, omega.data(), sizeof(double) * C, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    fasa_destroy(c);
+    return hip_fail(e, "fasa_create: uploading tables");
+  }
+  *out = c;
+  return ok();
+}
+
+void fasa_destroy(fasa_ctx* ctx) {
+  if (!ctx) return;
+  if (ctx->dev_alloc) (void)hipFree(ctx->dev_alloc);
+  delete ctx;
+}
+
+size_t fasa_kv_cache_bytes(const fasa_ctx* c) {
+  if (!c) return 0;
+  return (size_t)c->batch * c->hkv * c->cap * c->d * dtype_size(c->dtype);
+}
+
+size_t fasa_sidecar_bytes(const fasa_ctx* c) {
+  if (!c) return 0;
+  return (size_t)c->batch * c->P * c->cap * 2 * dtype_size(c->dtype);
+}
+
+size_t fasa_workspace_bytes(const fasa_ctx* c) { return c ? c->ws.total : 0; }
+
+int fasa_sidecar_layout(const fasa_ctx* c, int32_t* plane_offset, int32_t* plane_fc) {
+  if (!c) return (int)fail(FASA_ERR_INVALID_ARG, "null context");
+  if (plane_offset) std::memcpy(plane_offset, c->plane_off.data(), sizeof(int32_t) * (c->hkv + 1));
+  if (plane_fc && c->P) std::memcpy(plane_fc, c->plane_fc.data(), sizeof(int32_t) * c->P);
+  return c->P;
+}
+
+fasa_status fasa_workspace_init(fasa_ctx* c, void* workspace, hipStream_t stream) {
+  FASA_TRY(check_ctx(c));
+  FASA_NONNULL(workspace);
+  FASA_HIP(launch_fill_zero(workspace, c->ws.total, stream), "fasa_workspace_init");
+  return ok();
+}
+
+fasa_status fasa_append_kv(fasa_ctx* c, void* k_cache, void* v_cache, void* sidecar,
+                           const void* k_new, const void* v_new, const int32_t* start_pos,
+                           int n_new, void* workspace, hipStream_t stream) {
+  FASA_TRY(check_ctx(c));
+  if (n_new < 0) return fail(FASA_ERR_INVALID_ARG, "n_new %d < 0", n_new);
+  if (n_new > c->cap) return fail(FASA_ERR_CAPACITY, "n_new %d exceeds capacity", n_new);
+  if (n_new == 0) return ok();
+  FASA_NONNULL(k_cache);
+  FASA_NONNULL(v_cache);
+  FASA_NONNULL(sidecar);
+  FASA_NONNULL(k_new);
+  FASA_NONNULL(v_new);
+  FASA_NONNULL(start_pos);
+  FASA_NONNULL(workspace);
+  FASA_HIP(launch_append(c, k_cache, v_cache, sidecar, k_new, v_new, start_pos, n_new,
+                         static_cast<uint8_t*>(workspace), stream),
+           "fasa_append_kv");
+  return ok();
+}
+
+fasa_status fasa_tip_scores(fasa_ctx* c, const void* sidecar, const void* q,
+                            const int32_t* seq_lens, int max_seq_len, float* scores,
+                            void* workspace, hipStream_t stream) {
+  FASA_TRY(check_ctx(c));
+  FASA_TRY(check_len(c, max_seq_len));
+  FASA_NONNULL(sidecar);
+  FASA_NONNULL(q);
+  FASA_NONNULL(seq_lens);
+  FASA_NONNULL(scores);
+  FASA_NONNULL(workspace);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  PrologueArgs a{q, nullptr, nullptr, nullptr, nullptr, nullptr, seq_lens, max_seq_len};
+  FASA_HIP(launch_prologue(c, kPrologueQueryOnly, a, ws, stream), "fasa_tip_scores: prologue");
+  FASA_HIP(launch_tip(c, sidecar, reinterpret_cast<const int32_t*>(ws + c->ws.nb), max_seq_len,
+                      scores, nullptr, ws, stream),
+           "fasa_tip_scores");
+  return ok();
+}
+
+fasa_status fasa_topk(fasa_ctx* c, const float* scores, const int32_t* seq_lens,
+                      int max_seq_len, int budget, int32_t* idx, void* workspace,
+                      hipStream_t stream) {
+  FASA_TRY(check_ctx(c));
+  FASA_TRY(check_len(c, max_seq_len));
+  FASA_TRY(check_budget(c, budget));
+  FASA_NONNULL(scores);
+  FASA_NONNULL(seq_lens);
+  FASA_NONNULL(idx);
+  FASA_NONNULL(workspace);
+  FASA_HIP(launch_topk(c, scores, seq_lens, max_seq_len, budget, idx,
+                       static_cast<uint8_t*>(workspace), stream),
+           "fasa_topk");
+  return ok();
+}
+
+fasa_status fasa_sparse_attn(fasa_ctx* c, const void* k_cache, const void* v_cache,
+                             const void* q, const int32_t* seq_lens, const int32_t* idx,
+                             int budget, float* out, void* workspace, hipStream_t stream) {
+  FASA_TRY(check_ctx(c));
+  FASA_TRY(check_budget(c, budget));
+  FASA_NONNULL(k_cache);
+  FASA_NONNULL(v_cache);
+  FASA_NONNULL(q);
+  FASA_NONNULL(seq_lens);
+  FASA_NONNULL(idx);
+  FASA_NONNULL(out);
+  FASA_NONNULL(workspace);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  PrologueArgs a{q, nullptr, nullptr, nullptr, nullptr, nullptr, seq_lens, c->cap};
+  FASA_HIP(launch_prologue(c, kPrologueQueryOnly, a, ws, stream), "fasa_sparse_attn: prologue");
+  FASA_HIP(launch_fac(c, k_cache, v_cache, reinterpret_cast<const int32_t*>(ws + c->ws.nb),
+                      c->cap, idx, budget, out, ws, stream),
+           "fasa_sparse_attn");
+  return ok();
+}
+
+fasa_status fasa_decode_step(fasa_ctx* c, void* k_cache, void* v_cache, void* sidecar,
+                             const void* q, const void* k_new, const void* v_new,
+                             int32_t* seq_lens, int max_seq_len, int budget, float* out,
+                             int32_t* idx_out, void* workspace, unsigned flags,
+                             hipStream_t stream) {
+  FASA_TRY(check_ctx(c));
+  FASA_TRY(check_len(c, max_seq_len));
+  FASA_TRY(check_budget(c, budget));
+  FASA_NONNULL(k_cache);
+  FASA_NONNULL(v_cache);
+  FASA_NONNULL(sidecar);
+  FASA_NONNULL(q);
+  FASA_NONNULL(k_new);
+  FASA_NONNULL(v_new);
+  FASA_NONNULL(seq_lens);
+  FASA_NONNULL(out);
+  FASA_NONNULL(workspace);
+  if (flags & ~FASA_ADVANCE_SEQ_LENS) return fail(FASA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const int32_t* nb = reinterpret_cast<const int32_t*>(ws + c->ws.nb);
+  float* scores = reinterpret_cast<float*>(ws + c->ws.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + c->ws.idx);
+  PrologueArgs a{q, k_new, v_new, k_cache, v_cache, sidecar, seq_lens, max_seq_len};
+  FASA_HIP(launch_prologue(c, kPrologueDecode, a, ws, stream), "fasa_decode_step: append");
+  FASA_HIP(launch_tip(c, sidecar, nb, max_seq_len, scores,
+                      (flags & FASA_ADVANCE_SEQ_LENS) ? seq_lens : nullptr, ws, stream),
+           "fasa_decode_step: tip");
+  FASA_HIP(launch_topk(c, scores, nb, max_seq_len, budget, idx, ws, stream),
+           "fasa_decode_step: topk");
+  FASA_HIP(launch_fac(c, k_cache, v_cache, nb, max_seq_len, idx, budget, out, ws, stream),
+           "fasa_decode_step: fac");
+  return ok();
+}
+
+fasa_status fasa_dense_attn(fasa_ctx* c, const void* k_cache, const void* v_cache,
+                            const void* q, const int32_t* seq_lens, int max_seq_len,
+                            float* out, void* workspace, hipStream_t stream) {
+  FASA_TRY(check_ctx(c));
+  FASA_TRY(check_len(c, max_seq_len));
+  FASA_NONNULL(k_cache);
+  FASA_NONNULL(v_cache);
+  FASA_NONNULL(q);
+  FASA_NONNULL(seq_lens);
+  FASA_NONNULL(out);
+  FASA_NONNULL(workspace);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  PrologueArgs a{q, nullptr, nullptr, nullptr, nullptr, nullptr, seq_lens, max_seq_len};
+  FASA_HIP(launch_prologue(c, kPrologueQueryOnly, a, ws, stream), "fasa_dense_attn: prologue");
+  FASA_HIP(launch_dense(c, k_cache, v_cache, reinterpret_cast<const int32_t*>(ws + c->ws.nb),
+                        max_seq_len, out, ws, stream),
+           "fasa_dense_attn");
+  return ok();
+}
+
+fasa_status fasa_check(fasa_ctx* c, void* workspace, hipStream_t stream, uint32_t* flags) {
+  FASA_TRY(check_ctx(c));
+  FASA_NONNULL(workspace);
+  if (flags) *flags = 0;
+  FASA_HIP(hipStreamSynchronize(stream), "fasa_check: synchronize");
+  uint32_t v = 0;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  FASA_HIP(hipMemcpy(&v, ws + c->ws.err, sizeof v, hipMemcpyDeviceToHost), "fasa_check: read");
+  if (v) {
+    const uint32_t zero = 0;
+    FASA_HIP(hipMemcpy(ws + c->ws.err, &zero, sizeof zero, hipMemcpyHostToDevice),
+             "fasa_check: clear");
+  }
+  if (flags) *flags = v;
+  if (v) return fail(FASA_ERR_DEVICE_FLAG, "device error flag 0x%x", v);
+  return ok();
+}
+
+const char* fasa_status_string(fasa_status s) {
+  switch (s) {
+    case FASA_OK: return "ok";
+    case FASA_ERR_INVALID_ARG: return "invalid argument";
+    case FASA_ERR_CAPACITY: return "capacity exceeded";
+    case FASA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FASA_ERR_HIP: return "HIP runtime error";
+    case FASA_ERR_DEVICE_FLAG: return "device error flag set";
+  }
+  return "unknown status";
+}
+
+const char* fasa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,190 @@
+// Device-side helpers shared by the FASA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fasa {
+
+constexpr int kWave = 64;
+
+// Top-B selection geometry: a row of scores is cut into chunks of kChunk
+// tokens; the first radix digit is the top kHistBits of the 32-bit key.
+constexpr int kHistBits = 11;
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kChunk = 4096;
+constexpr int kChunkThreads = 256;
+constexpr int kPerThread = kChunk / kChunkThreads;  // 16 consecutive tokens
+constexpr int kMaxChunks = 1024;                    // rows up to 4M tokens
+
+// Tickets per row: S1 (histogram), S2 (candidates), FAC merge, dense merge.
+constexpr int kTicketsPerRow = 4;
+
+// Per-(b, h) selection state; lives in the workspace.
+struct RowState {
+  uint32_t digit1;      // top-kHistBits digit of the threshold key
+  uint32_t need;        // tokens still to take from that digit's bin
+  uint32_t cand_count;  // candidates gathered in the bin
+  uint32_t pad0;
+  uint64_t tau;         // composite threshold: selected <=> composite >= tau
+  uint64_t pad1;
+};
+
+// ---- bf16 <-> fp32 / fp64 ------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
+  return __uint_as_float(h16 << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp64 -> bf16, rounded once to nearest-even.  The fp32 intermediate is made
+// round-to-odd (exact result, or the truncated value with its last bit set),
+// which has 16 spare bits over bf16, so the second rounding is exact.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  float f = (float)x;
+  uint32_t u = __float_as_uint(f);
+  double back = (double)f;
+  if (back != x) {
+    if (fabs(back) > fabs(x)) u -= 1u;  // step the magnitude back toward zero
+    u |= 1u;
+  }
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---- ordering keys for the top-B radix select --------------------------
+
+// Order-preserving map float -> uint32 (larger float -> larger key); -0 is
+// folded onto +0 so equal scores compare equal.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Composite (key, position): higher key first, then lower position.  All
+// composites of a row are distinct, so one threshold splits selected from
+// unselected exactly.
+__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t pos) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - pos);
+}
+__device__ __forceinline__ uint32_t composite_pos(uint64_t c) {
+  return 0xffffffffu - (uint32_t)(c & 0xffffffffu);
+}
+
+// ---- cross-lane sums -------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 4, 8, 16, 32, 64);
+// every lane of the group gets the sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_mov<0xB1>(v);  // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);  // quad_perm [2,3,0,1]
+  if constexpr (N == 16 || N == 32 || N == 64) {
+    v += dpp_mov<0x124>(v);  // row_ror:4
+    v += dpp_mov<0x128>(v);  // row_ror:8
+  } else if constexpr (N == 8) {
+    v += __shfl_xor(v, 4);
+  }
+  if constexpr (N >= 32) v += __shfl_xor(v, 16);
+  if constexpr (N == 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Inclusive prefix sum of a uint32 over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    uint32_t t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over a block of NT threads (NT a multiple of 64).
+// `lds` needs NT / 64 words.  Returns the exclusive prefix; *total gets the
+// block total.  Contains __syncthreads().
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds,
+                                                         uint32_t* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  uint32_t inc = wave_inclusive_scan(v);
+  if (lane == kWave - 1) lds[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NT / kWave; ++w) {
+    uint32_t t = lds[w];
+    before += (w < wave) ? t : 0u;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + inc - v;
+}
+
+// Device-scope atomics used for cross-workgroup hand-offs.
+__device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t atomic_xchg_agent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t atomic_load_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_store_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// "Last workgroup" hand-off: every thread publishes its writes, one thread
+// takes a ticket; returns true in every thread of the workgroup that arrived
+// last (ticket == expected - 1), after an acquire.  The last one resets the
+// ticket to 0.  `flag` is one LDS word.
+__device__ __forceinline__ bool last_block_arrives(uint32_t* ticket, uint32_t expected,
+                                                   uint32_t* flag) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    bool last = (t == expected - 1u);
+    if (last) atomic_store_agent(ticket, 0u);
+    *flag = last ? 1u : 0u;
+  }
+  __syncthreads();
+  bool last = (*flag != 0u);
+  if (last) __threadfence();
+  return last;
+}
+
+__device__ __forceinline__ void raise_flag(uint32_t* err, uint32_t bit) {
+  __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// n_b of sequence b, or 0 (and the SEQ_LEN flag when `report`) when it lies
+// outside [0, min(max_seq_len, cap)].
+__device__ __forceinline__ int checked_len(const int32_t* nb, int b, int max_seq_len, int cap,
+                                           uint32_t* err, bool report) {
+  const int n = nb[b];
+  if (n < 0 || n > max_seq_len || n > cap) {
+    if (report) raise_flag(err, 1u);
+    return 0;
+  }
+  return n;
+}
+
+}  // namespace fasa

@@ -1,0 +1,219 @@
+// KV append with RoPE + FC-packed key sidecar, and the per-step query prologue.
+//
+// RoPE splits a head vector into 2-D frequency chunks (FCs), one angular
+// frequency each ("FASA: Frequency-aware Sparse Attention", gist.science/pt,
+// "Resumo Tecnico" section 2, "A Descoberta"); keys keep their original
+// absolute positions (same section, FAC third bullet).  FC c is the pair
+// (c, c + d/2), its angle at position m is m * theta^(-2c/d).  Angles and the
+// rotation are taken in fp64 so positions up to ~10^6 lose nothing, and the
+// rotated key is rounded once (nearest-even) to the cache dtype.
+//
+// The sidecar keeps, per KV head, a copy of the rotated K columns of the union
+// of its query heads' dominant FCs, one plane per FC ([b][P][cap] pairs), so
+// the TIP pass streams only those columns with coalesced 16-byte loads.
+// Storing dominant key parts apart from the rest is what FASA-M does with GPU
+// memory (same page, "Variantes de Implementacao").
+
+#include "device_common.hpp"
+#include "fasa_internal.hpp"
+
+namespace fasa {
+
+template <bool BF16>
+struct CacheT;
+template <>
+struct CacheT<true> {
+  using T = uint16_t;
+};
+template <>
+struct CacheT<false> {
+  using T = float;
+};
+
+__device__ __forceinline__ double load_elem(const uint16_t* p, size_t i) {
+  return (double)bf16_bits_to_f32(p[i]);
+}
+__device__ __forceinline__ double load_elem(const float* p, size_t i) { return (double)p[i]; }
+
+// Rotates FC c of one key row at `pos`, stores K (and V) columns c, c + C and,
+// when FC c is in the KV head's union, its sidecar pair.
+template <bool BF16>
+__device__ __forceinline__ void append_fc(const typename CacheT<BF16>::T* __restrict__ ksrc,
+                                          const typename CacheT<BF16>::T* __restrict__ vsrc,
+                                          typename CacheT<BF16>::T* __restrict__ kdst,
+                                          typename CacheT<BF16>::T* __restrict__ vdst,
+                                          void* __restrict__ sidecar, size_t plane_base,
+                                          int slot, int c, int C, int cap, long pos,
+                                          double omega) {
+  const double x0 = load_elem(ksrc, c), x1 = load_elem(ksrc, c + C);
+  double sn, cs;
+  sincos((double)pos * omega, &sn, &cs);
+  const double y0 = x0 * cs - x1 * sn;
+  const double y1 = x1 * cs + x0 * sn;
+  vdst[c] = vsrc[c];
+  vdst[c + C] = vsrc[c + C];
+  if constexpr (BF16) {
+    const uint16_t k0 = f64_to_bf16_rne(y0), k1 = f64_to_bf16_rne(y1);
+    kdst[c] = k0;
+    kdst[c + C] = k1;
+    if (slot >= 0)
+      static_cast<uint32_t*>(sidecar)[(plane_base + slot) * cap + pos] =
+          (uint32_t)k0 | ((uint32_t)k1 << 16);
+  } else {
+    const float k0 = (float)y0, k1 = (float)y1;
+    kdst[c] = k0;
+    kdst[c + C] = k1;
+    if (slot >= 0) static_cast<float2*>(sidecar)[(plane_base + slot) * cap + pos] = make_float2(k0, k1);
+  }
+}
+
+// Bulk append: thread = (row, FC).  grid (ceil(n_new / rows), Hkv, b).
+template <bool BF16>
+__global__ void __launch_bounds__(256)
+append_kernel(const void* __restrict__ k_new, const void* __restrict__ v_new,
+              void* __restrict__ k_cache, void* __restrict__ v_cache, void* __restrict__ sidecar,
+              const int32_t* __restrict__ start_pos, int n_new, int hkv, int cap, int d, int P,
+              const int32_t* __restrict__ plane_off, const int32_t* __restrict__ fc_slot,
+              const double* __restrict__ omega, uint32_t* err) {
+  using T = typename CacheT<BF16>::T;
+  const int C = d / 2;
+  const int rows = blockDim.x / C;
+  const int c = threadIdx.x % C;
+  const int t = blockIdx.x * rows + threadIdx.x / C;
+  const int g = blockIdx.y, b = blockIdx.z;
+  if (t >= n_new) return;
+  const int p0 = start_pos[b];
+  const long pos = (long)p0 + t;
+  if (p0 < 0 || pos >= cap) {
+    if (c == 0) raise_flag(err, FASA_DEVFLAG_APPEND);
+    return;
+  }
+  const size_t src = (((size_t)b * hkv + g) * n_new + t) * d;
+  const size_t dst = (((size_t)b * hkv + g) * cap + pos) * d;
+  append_fc<BF16>(static_cast<const T*>(k_new) + src, static_cast<const T*>(v_new) + src,
+                  static_cast<T*>(k_cache) + dst, static_cast<T*>(v_cache) + dst, sidecar,
+                  (size_t)b * P + plane_off[g], fc_slot[g * C + c], c, C, cap, pos, omega[c]);
+}
+
+// Per-step prologue, one workgroup per (KV head g, sequence b), G * C threads.
+// Decode mode: append the step's token at position seq_lens[b] first.
+// Both modes: rotate the group's queries to position n_b - 1 (fp64 angle,
+// kept in fp32) and write the TIP weights of the group's sidecar planes:
+// for plane u holding FC c and query head h, (q~_c, q~_{c+C}) when c is
+// dominant for h, zeros otherwise.
+template <bool BF16>
+__global__ void __launch_bounds__(512)
+prologue_kernel(int mode, const void* __restrict__ q, const void* __restrict__ k_new,
+                const void* __restrict__ v_new, void* __restrict__ k_cache,
+                void* __restrict__ v_cache, void* __restrict__ sidecar,
+                const int32_t* __restrict__ seq_lens, int max_seq_len, int hq, int hkv, int G,
+                int cap, int d, int P, const int32_t* __restrict__ plane_off,
+                const int32_t* __restrict__ fc_slot, const uint64_t* __restrict__ dom_mask,
+                const double* __restrict__ omega, int32_t* __restrict__ nb_out,
+                float* __restrict__ qrot, float* __restrict__ tipw, uint32_t* err) {
+  using T = typename CacheT<BF16>::T;
+  const int C = d / 2;
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int v = seq_lens[b];
+  const int n = (mode == kPrologueDecode) ? v + 1 : v;
+  const bool empty = (mode == kPrologueQueryOnly && v == 0);
+  const bool ok = v >= 0 && n >= 1 && n <= max_seq_len && n <= cap;
+  if (!ok) {
+    if (g == 0 && tid == 0) {
+      nb_out[b] = 0;
+      if (!empty) raise_flag(err, FASA_DEVFLAG_SEQ_LEN);
+    }
+    return;
+  }
+  if (g == 0 && tid == 0) nb_out[b] = n;
+  const long pos = n - 1;
+  const int hh = tid / C, c = tid % C;
+
+  if (mode == kPrologueDecode && hh == 0) {
+    const size_t src = ((size_t)b * hkv + g) * d;
+    const size_t dst = (((size_t)b * hkv + g) * cap + pos) * d;
+    append_fc<BF16>(static_cast<const T*>(k_new) + src, static_cast<const T*>(v_new) + src,
+                    static_cast<T*>(k_cache) + dst, static_cast<T*>(v_cache) + dst, sidecar,
+                    (size_t)b * P + plane_off[g], fc_slot[g * C + c], c, C, cap, pos, omega[c]);
+  }
+
+  const int h = g * G + hh;
+  const T* qs = static_cast<const T*>(q) + ((size_t)b * hq + h) * d;
+  const double x0 = load_elem(qs, c), x1 = load_elem(qs, c + C);
+  double sn, cs;
+  sincos((double)pos * omega[c], &sn, &cs);
+  const float y0 = (float)(x0 * cs - x1 * sn);
+  const float y1 = (float)(x1 * cs + x0 * sn);
+  float* qr = qrot + ((size_t)b * hq + h) * d;
+  qr[c] = y0;
+  qr[c + C] = y1;
+  const int slot = fc_slot[g * C + c];
+  if (slot >= 0) {
+    const bool dominant = (dom_mask[h] >> c) & 1ull;
+    float* w = tipw + (((size_t)b * P + plane_off[g] + slot) * G + hh) * 2;
+    w[0] = dominant ? y0 : 0.0f;
+    w[1] = dominant ? y1 : 0.0f;
+  }
+}
+
+__global__ void fill_zero_kernel(uint4* __restrict__ p, size_t n16, uint8_t* __restrict__ tail,
+                                 size_t ntail) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  const size_t n16 = bytes / 16;
+  const size_t ntail = bytes - n16 * 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<uint4*>(p), n16, static_cast<uint8_t*>(p) + n16 * 16, ntail);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const fasa_ctx* c, void* k_cache, void* v_cache, void* sidecar,
+                         const void* k_new, const void* v_new, const int32_t* start_pos,
+                         int n_new, uint8_t* ws, hipStream_t s) {
+  if (n_new <= 0) return hipSuccess;
+  const int rows = 256 / c->C;
+  dim3 grid((unsigned)((n_new + rows - 1) / rows), (unsigned)c->hkv, (unsigned)c->batch);
+  uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
+  if (c->dtype == FASA_BF16)
+    hipLaunchKernelGGL(append_kernel<true>, grid, dim3(rows * c->C), 0, s, k_new, v_new, k_cache,
+                       v_cache, sidecar, start_pos, n_new, c->hkv, c->cap, c->d, c->P,
+                       c->tab.plane_off, c->tab.fc_slot, c->tab.omega, err);
+  else
+    hipLaunchKernelGGL(append_kernel<false>, grid, dim3(rows * c->C), 0, s, k_new, v_new, k_cache,
+                       v_cache, sidecar, start_pos, n_new, c->hkv, c->cap, c->d, c->P,
+                       c->tab.plane_off, c->tab.fc_slot, c->tab.omega, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_prologue(const fasa_ctx* c, PrologueMode mode, const PrologueArgs& a,
+                           uint8_t* ws, hipStream_t s) {
+  dim3 grid((unsigned)c->hkv, (unsigned)c->batch);
+  dim3 block((unsigned)(c->G * c->C));
+  int32_t* nb = reinterpret_cast<int32_t*>(ws + c->ws.nb);
+  float* qrot = reinterpret_cast<float*>(ws + c->ws.qrot);
+  float* tipw = reinterpret_cast<float*>(ws + c->ws.tipw);
+  uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
+  if (c->dtype == FASA_BF16)
+    hipLaunchKernelGGL(prologue_kernel<true>, grid, block, 0, s, (int)mode, a.q, a.k_new, a.v_new,
+                       a.k_cache, a.v_cache, a.sidecar, a.seq_lens, a.max_seq_len, c->hq, c->hkv,
+                       c->G, c->cap, c->d, c->P, c->tab.plane_off, c->tab.fc_slot,
+                       c->tab.dom_mask, c->tab.omega, nb, qrot, tipw, err);
+  else
+    hipLaunchKernelGGL(prologue_kernel<false>, grid, block, 0, s, (int)mode, a.q, a.k_new,
+                       a.v_new, a.k_cache, a.v_cache, a.sidecar, a.seq_lens, a.max_seq_len,
+                       c->hq, c->hkv, c->G, c->cap, c->d, c->P, c->tab.plane_off,
+                       c->tab.fc_slot, c->tab.dom_mask, c->tab.omega, nb, qrot, tipw, err);
+  return hipGetLastError();
+}
+
+}  // namespace fasa

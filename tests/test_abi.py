@@ -1,0 +1,72 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any GPU work (CPU only: no compute calls)."""
+
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fasa.h")
+LIB = os.path.join(ROOT, "sparse_kv_cache_rope_amd", "libfasa.so")
+
+
+@pytest.fixture(scope="module")
+def fasa():
+    if not os.path.exists(LIB):
+        subprocess.run([sys.executable, "-m", "sparse_kv_cache_rope_amd.build"], cwd=ROOT,
+                       check=True, capture_output=True)
+    import sparse_kv_cache_rope_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fasa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("fasa_append_kv", "fasa_tip_scores", "fasa_topk", "fasa_sparse_attn",
+                 "fasa_decode_step", "fasa_dense_attn", "fasa_create", "fasa_destroy"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(fasa):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (fasa_\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+
+
+def test_binding_covers_every_declared_symbol(fasa):
+    assert sorted(fasa.EXPORTED) == declared_functions()
+
+
+def test_status_strings(fasa):
+    assert fasa.status_string(0) == "ok"
+    assert "invalid" in fasa.status_string(-1)
+    assert fasa.status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("args,code,msg", [
+    ((1, 3, 1, 64, 128, 1e4, 1, [[0]] * 3, 1, 8), -3, "not in {1,2,4,8}"),
+    ((1, 2, 1, 96, 128, 1e4, 1, [[0]] * 2, 1, 8), -3, "head_dim"),
+    ((1, 2, 1, 64, 100, 1e4, 1, [[0]] * 2, 1, 8), -1, "multiple of 64"),
+    ((1, 2, 1, 64, 128, 1e4, 1, [[0], [40]], 1, 8), -1, "outside"),
+    ((1, 2, 1, 64, 128, 1e4, 1, [[0, 0], [1, 2]], 2, 8), -1, "repeats"),
+    ((1, 2, 1, 64, 128, 1e4, 1, [[0], [1]], 1, 200), -1, "max_budget"),
+    ((1, 2, 1, 64, 128, 1e4, 1, [[0], [1]], 0, 8), -1, "n_dom"),
+    ((1, 2, 1, 64, 128, 0.5, 1, [[0], [1]], 1, 8), -1, "rope_theta"),
+    ((1, 2, 1, 64, 128, 1e4, 7, [[0], [1]], 1, 8), -3, "dtype"),
+    ((0, 2, 1, 64, 128, 1e4, 1, [[0], [1]], 1, 8), -1, "batch"),
+    ((1, 5, 2, 64, 128, 1e4, 1, [[0]] * 5, 1, 8), -1, "multiple"),
+    ((1, 2, 1, 64, 128, 1e4, 1, None, 1, 8), -1, "dom_fc is null"),
+])
+def test_create_rejects_bad_arguments(fasa, args, code, msg):
+    st, detail = fasa.raw_create(*args)
+    assert st == code and msg in detail, (st, detail)

@@ -1,0 +1,382 @@
+"""HIP path against the oracle, element by element, through the C ABI.
+
+Each call of include/fasa.h is checked on seeded inputs at sizes the oracle
+finishes in seconds (several tiles and a ragged tail), then the whole decode
+step on all five workloads.  Acceptance rules: tests/fasa_harness.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from fasa_harness import (GpuSetup, oracle_setup, check_index_set, check_out, tip_bound,
+                          ulp_diff_bf16, run_decode, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def small(name, **kw):
+    return W.shrink(W.get(name), **kw)
+
+
+# Shrunk workloads: same heads/dims/dtypes as the named ones, contexts the
+# oracle handles in seconds, with ragged tails (not multiples of any tile).
+SMALL = {
+    "c1": W.get("c1"),
+    "c2s": small("c2", context=5003),
+    "c3s": small("c3", batch=3, context=3001, context_min=1500),
+    "c4s": small("c4", batch=2, context=2500, budget=473, steps=3),
+    "c5s": small("c5", context=9000, budget=300, steps=2),
+}
+
+
+def _prefilled(gpu, name):
+    w = SMALL[name]
+    x = W.generate(w)
+    return w, x, GpuSetup(gpu, w, x), oracle_setup(w, x)
+
+
+# ------------------------------------------------------------- append ----
+
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s"])
+def test_append_rope_and_sidecar(gpu, name):
+    w, x, g, o = _prefilled(gpu, name)
+    K = g.k.float().cpu().numpy()
+    V = g.v.float().cpu().numpy()
+    side = g.side.float().cpu().numpy()
+    off, fcs = g.ctx.sidecar_layout()
+    half = w.head_dim // 2
+    for b in range(w.batch):
+        n0 = int(x["ctx"][b]) - 1
+        want = o.K[b, :, :n0]
+        got = K[b, :, :n0].astype(np.float64)
+        if w.dtype == "bf16":
+            ulps = ulp_diff_bf16(got.astype(np.float32), want.astype(np.float32))
+            assert ulps.max() <= 1, f"K off by {ulps.max()} ulp"
+            assert (ulps == 0).mean() >= 0.999
+        else:
+            bound = 4 * 2.0 ** -24 * (np.abs(np.concatenate([want[..., half:], want[..., :half]], -1))
+                                      + np.abs(want))
+            assert np.all(np.abs(got - want) <= bound)
+        assert np.array_equal(V[b, :, :n0], x["v_prefill"][b][:, :n0])
+        # Sidecar is bit-identical to its K columns.
+        for g_ in range(w.n_kv_heads):
+            for p in range(off[g_], off[g_ + 1]):
+                c = fcs[p]
+                assert np.array_equal(side[b, p, :n0, 0], K[b, g_, :n0, c])
+                assert np.array_equal(side[b, p, :n0, 1], K[b, g_, :n0, c + half])
+
+
+def test_append_past_capacity_raises_flag(gpu):
+    w = small("c1", context=65)
+    x = W.generate(w)
+    g = GpuSetup(gpu, w, x, capacity=64)
+    assert g.ctx.check(g.ws) == 0
+    kn = to_dev(x["k_new"][0][:, :, None, :], g.td)
+    start = torch.full((1,), 64, dtype=torch.int32, device="cuda")
+    g.ctx.append_kv(g.k, g.v, g.side, kn, kn, start, g.ws)
+    assert g.ctx.check(g.ws) & gpu.DEVFLAG_APPEND
+    assert g.ctx.check(g.ws) == 0  # cleared by the read
+
+
+# ---------------------------------------------------------------- TIP ----
+
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s"])
+def test_tip_scores(gpu, name):
+    w, x, g, o = _prefilled(gpu, name)
+    # Score the prefilled tokens with the step-0 query at position n0 - 1.
+    n = torch.from_numpy((x["ctx"] - 1).astype(np.int32)).cuda()
+    scores = torch.full((w.batch, w.n_q_heads, g.cap), np.nan, dtype=torch.float32, device="cuda")
+    q = to_dev(x["q"][0], g.td)
+    g.ctx.tip_scores(g.side, q, n, int(x["ctx"].max()), scores, g.ws)
+    s = scores.cpu().numpy().astype(np.float64)
+    assert g.ctx.check(g.ws) == 0
+    for b in range(w.batch):
+        nb = int(x["ctx"][b]) - 1
+        qr = oracle.rope.rope_rotate(x["q"][0][b], nb - 1, w.rope_theta)
+        for h in range(w.n_q_heads):
+            ks = o.K[b, h // w.group, :nb]
+            want = oracle.tip.tip_scores(qr[h], ks, x["dom"][h])
+            lim = 1e-5 * tip_bound(qr[h], ks, x["dom"][h]) + 1e-30
+            assert np.all(np.abs(s[b, h, :nb] - want) <= lim), (b, h)
+            assert np.all(np.isnan(s[b, h, nb:])), "wrote past n_b"
+
+
+# ---------------------------------------------------------------- top-B --
+
+TOPK_CASES = [
+    # (kind, rows, n, budget, ragged)
+    ("normal", 4, 5003, 256, False),
+    ("planted", 3, 32768, 256, False),
+    ("ties", 4, 9000, 700, False),
+    ("zeros", 2, 4100, 64, False),
+    ("wide", 3, 12345, 1000, True),
+    ("sorted_up", 2, 8193, 4097, False),
+    ("normal", 2, 300, 256, True),      # some rows n <= B
+    ("normal", 2, 256, 256, False),     # n == B
+    ("normal", 2, 131072, 1024, False),
+    ("normal", 1, 32831, 6193, False),
+    ("normal", 2, 4097, 1, False),
+]
+
+
+@pytest.mark.parametrize("case", TOPK_CASES, ids=lambda c: f"{c[0]}-{c[2]}-B{c[3]}")
+def test_topk_exact(gpu, case):
+    """Selection is index work: bit-exact against the oracle on the same fp32
+    scores (both sides rank the identical fp32 values)."""
+    kind, rows, n, budget, ragged = case
+    sc = W.random_scores(7, rows, n, kind)
+    cap = (n + 63) // 64 * 64
+    lens = np.full(1, n, dtype=np.int32)
+    ctx = gpu.Context(1, rows, 1 if rows in (1, 2, 4, 8) else rows, 64, cap, 1e4, "f32",
+                      np.zeros((rows, 1), np.int32), max(budget, 1))
+    buf = torch.zeros(1, rows, cap, dtype=torch.float32, device="cuda")
+    buf[0, :, :n] = torch.from_numpy(sc).cuda()
+    ws = ctx.new_workspace()
+    for rep in range(2):  # second pass checks the workspace was left clean
+        seq = n - (37 if ragged else 0)
+        lens[0] = seq
+        idx = torch.full((1, rows, budget), -7, dtype=torch.int32, device="cuda")
+        ctx.topk(buf, torch.from_numpy(lens).cuda(), n, budget, idx, ws)
+        got = idx.cpu().numpy()[0]
+        assert ctx.check(ws) == 0
+        for r in range(rows):
+            want = oracle.select.select_topb(sc[r, :seq].astype(np.float64), budget)
+            assert np.array_equal(got[r], want), (r, rep)
+
+
+def test_topk_length_beyond_max_seq_len_flags(gpu):
+    ctx = gpu.Context(1, 1, 1, 64, 128, 1e4, "f32", np.zeros((1, 1), np.int32), 8)
+    ws = ctx.new_workspace()
+    sc = torch.zeros(1, 1, 128, dtype=torch.float32, device="cuda")
+    idx = torch.zeros(1, 1, 8, dtype=torch.int32, device="cuda")
+    ctx.topk(sc, torch.tensor([100], dtype=torch.int32, device="cuda"), 64, 8, idx, ws)
+    assert ctx.check(ws) & gpu.DEVFLAG_SEQ_LEN
+    assert np.all(idx.cpu().numpy() == -1)
+
+
+# ---------------------------------------------------------------- FAC ----
+
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s"])
+def test_sparse_attn(gpu, name):
+    w, x, g, o = _prefilled(gpu, name)
+    budget = w.budget
+    rng = np.random.default_rng(3)
+    idx = np.full((w.batch, w.n_q_heads, budget), -1, dtype=np.int32)
+    for b in range(w.batch):
+        nb = int(x["ctx"][b]) - 1
+        for h in range(w.n_q_heads):
+            k = min(budget, nb) - (h % 3)  # some heads leave -1 holes at the end
+            idx[b, h, :k] = np.sort(rng.choice(nb, size=k, replace=False))
+    out = torch.empty(w.batch, w.n_q_heads, w.head_dim, dtype=torch.float32, device="cuda")
+    n = torch.from_numpy((x["ctx"] - 1).astype(np.int32)).cuda()
+    g.ctx.sparse_attn(g.k, g.v, to_dev(x["q"][0], g.td), n, to_dev(idx, torch.int32), budget,
+                      out, g.ws)
+    got = out.cpu().numpy()
+    assert g.ctx.check(g.ws) == 0
+    for b in range(w.batch):
+        nb = int(x["ctx"][b]) - 1
+        o.lens[b] = nb
+        qr = oracle.rope.rope_rotate(x["q"][0][b], nb - 1, w.rope_theta)
+        for h in range(w.n_q_heads):
+            want = o.attend(b, h, qr[h], idx[b, h])
+            check_out(got[b, h], want, w.dtype, f"b{b} h{h}")
+
+
+def test_sparse_attn_bad_index_flags(gpu):
+    w, x, g, o = _prefilled(gpu, "c1")
+    idx = np.full((1, 2, w.budget), -1, dtype=np.int32)
+    idx[0, 0, 0] = 5
+    idx[0, 1, 0] = 10_000  # beyond n_b
+    out = torch.empty(1, 2, w.head_dim, dtype=torch.float32, device="cuda")
+    n = torch.from_numpy((x["ctx"] - 1).astype(np.int32)).cuda()
+    g.ctx.sparse_attn(g.k, g.v, to_dev(x["q"][0], g.td), n, to_dev(idx, torch.int32), w.budget,
+                      out, g.ws)
+    assert g.ctx.check(g.ws) & gpu.DEVFLAG_INDEX
+    got = out.cpu().numpy()
+    assert np.array_equal(got[0, 1], np.zeros(w.head_dim, np.float32))
+    assert np.allclose(got[0, 0], x["v_prefill"][0, 0, 5], rtol=0, atol=1e-6)
+
+
+# -------------------------------------------------------------- dense ----
+
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s"])
+def test_dense_attn(gpu, name):
+    w, x, g, o = _prefilled(gpu, name)
+    n = torch.from_numpy((x["ctx"] - 1).astype(np.int32)).cuda()
+    out = torch.empty(w.batch, w.n_q_heads, w.head_dim, dtype=torch.float32, device="cuda")
+    g.ctx.dense_attn(g.k, g.v, to_dev(x["q"][0], g.td), n, int(x["ctx"].max()), out, g.ws)
+    got = out.cpu().numpy()
+    assert g.ctx.check(g.ws) == 0
+    for b in range(w.batch):
+        nb = int(x["ctx"][b]) - 1
+        o.lens[b] = nb
+        qr = oracle.rope.rope_rotate(x["q"][0][b], nb - 1, w.rope_theta)
+        for h in range(w.n_q_heads):
+            want = o.attend(b, h, qr[h], np.arange(nb))
+            check_out(got[b, h], want, w.dtype, f"b{b} h{h}")
+
+
+# -------------------------------------------------------- decode step ----
+
+def _decode_parity(gpu, w, x, steps=None, heads=None, check_steps=None):
+    g = GpuSetup(gpu, w, x)
+    o = oracle_setup(w, x)
+    steps = w.steps if steps is None else steps
+    diffs = 0
+    for t in range(steps):
+        out, idx = run_decode(g, t, w.budget)
+        want_steps = check_steps is None or t in check_steps
+        if not want_steps:
+            for b in range(w.batch):
+                o.append(b, x["k_new"][t][b][:, None, :], x["v_new"][t][b][:, None, :])
+            continue
+        got_out, got_idx = out.cpu().numpy(), idx.cpu().numpy()
+        res = o.step(x["q"][t], x["k_new"][t], x["v_new"][t], w.budget, heads=heads)
+        for b in range(w.batch):
+            n = int(o.lens[b])
+            qr = o.query_rot(b, x["q"][t][b])
+            for h in (range(w.n_q_heads) if heads is None else heads):
+                where = f"step {t} b{b} h{h}"
+                diffs += check_index_set(got_idx[b, h], res["scores"][(b, h)], w.budget, n, where)
+                want = o.attend(b, h, qr[h], got_idx[b, h])
+                check_out(got_out[b, h], want, w.dtype, where)
+    assert g.ctx.check(g.ws) == 0
+    # seq_lens advanced on the device by one per step
+    assert np.array_equal(g.seq_lens.cpu().numpy(), (x["ctx"] - 1 + steps).astype(np.int32))
+    return diffs
+
+
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "c4s", "c5s"])
+def test_decode_step_small(gpu, name):
+    w = SMALL[name]
+    _decode_parity(gpu, w, W.generate(w))
+
+
+def test_decode_step_c1_full(gpu):
+    w = W.get("c1")
+    _decode_parity(gpu, w, W.generate(w))
+
+
+def test_decode_step_c2_full(gpu):
+    """32k context, B = 256: every head of the single step."""
+    w = W.get("c2")
+    _decode_parity(gpu, w, W.generate(w))
+
+
+def test_decode_step_c3_full(gpu):
+    w = W.get("c3")
+    _decode_parity(gpu, w, W.generate(w), heads=[0, 5, 17, 31])
+
+
+def test_decode_step_c4_full(gpu):
+    """64 steps with append; the oracle checks a sample of steps and heads."""
+    w = W.get("c4")
+    _decode_parity(gpu, w, W.generate(w), heads=[0, 13, 31], check_steps={0, 1, 32, 63})
+
+
+def test_decode_step_c5_full(gpu):
+    w = W.get("c5")
+    _decode_parity(gpu, w, W.generate(w), heads=[0, 7, 30], check_steps={0, 15, 31})
+
+
+# -------------------------------------------------------- edge cases ----
+
+def test_budget_at_least_context_is_dense(gpu):
+    """B >= n: the step attends over everything and equals dense attention."""
+    w = small("c2", context=200, budget=256)
+    x = W.generate(w)
+    g = GpuSetup(gpu, w, x)
+    out, idx = run_decode(g, 0, 256)
+    got_idx = idx.cpu().numpy()
+    assert np.all(got_idx[:, :, :200] == np.arange(200)) and np.all(got_idx[:, :, 200:] == -1)
+    dense = torch.empty_like(out)
+    n = torch.full((1,), 200, dtype=torch.int32, device="cuda")
+    g.ctx.dense_attn(g.k, g.v, to_dev(x["q"][0], g.td), n, 200, dense, g.ws)
+    assert torch.allclose(out, dense, rtol=1e-5, atol=1e-6)
+
+
+def test_single_token_context(gpu):
+    w = small("c1", context=1)
+    x = W.generate(w)
+    g = GpuSetup(gpu, w, x)
+    out, idx = run_decode(g, 0, w.budget)
+    assert np.all(idx.cpu().numpy()[:, :, 0] == 0)
+    assert np.all(idx.cpu().numpy()[:, :, 1:] == -1)
+    vn = x["v_new"][0][0, 0]
+    assert np.allclose(out.cpu().numpy()[0, 0], vn, rtol=0, atol=1e-6)
+
+
+def test_zero_query_selects_lowest_positions(gpu):
+    """q = 0: every score is 0, ties go to the lower position, FAC averages."""
+    w = small("c2", context=3000)
+    x = W.generate(w)
+    x["q"][:] = 0.0
+    g = GpuSetup(gpu, w, x)
+    out, idx = run_decode(g, 0, w.budget)
+    assert np.all(idx.cpu().numpy() == np.arange(w.budget))
+    o = oracle_setup(w, x)
+    res = o.step(x["q"][0], x["k_new"][0], x["v_new"][0], w.budget, heads=[0, 31])
+    check_out(out.cpu().numpy()[0, 0], res["out"][0, 0], "bf16")
+    check_out(out.cpu().numpy()[0, 31], res["out"][0, 31], "bf16")
+
+
+def test_budget_one(gpu):
+    w = small("c2", context=4500, budget=1)
+    x = W.generate(w)
+    _decode_parity(gpu, w, x)
+
+
+def test_seq_len_beyond_max_flags_and_zeroes(gpu):
+    w = small("c1", context=300)
+    x = W.generate(w)
+    g = GpuSetup(gpu, w, x)
+    out, idx = run_decode(g, 0, w.budget, max_seq_len=100)  # n_b = 300 > 100
+    assert g.ctx.check(g.ws) & gpu.DEVFLAG_SEQ_LEN
+    assert np.all(out.cpu().numpy() == 0) and np.all(idx.cpu().numpy() == -1)
+    assert g.seq_lens.cpu().numpy()[0] == 299  # not advanced
+
+
+def test_repeat_is_bit_identical(gpu):
+    w = SMALL["c2s"]
+    x = W.generate(w)
+    g = GpuSetup(gpu, w, x)
+    a_out, a_idx = run_decode(g, 0, w.budget, advance=False)
+    b_out, b_idx = run_decode(g, 0, w.budget, advance=False)
+    assert torch.equal(a_idx, b_idx)
+    assert torch.equal(a_out, b_out)
+
+
+def test_graph_replay_matches_eager(gpu):
+    """The decode step captured in a HIP graph, replayed several times with
+    eager work in between, gives the eager result every time."""
+    w = SMALL["c2s"]
+    x = W.generate(w)
+    g = GpuSetup(gpu, w, x)
+    eager_out, eager_idx = run_decode(g, 0, w.budget, advance=False)
+    q = to_dev(x["q"][0], g.td)
+    kn = to_dev(x["k_new"][0], g.td)
+    vn = to_dev(x["v_new"][0], g.td)
+    out = torch.zeros_like(eager_out)
+    idx = torch.zeros_like(eager_idx)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g.ctx.decode_step(g.k, g.v, g.side, q, kn, vn, g.seq_lens, int(x["ctx"].max()),
+                          w.budget, out, g.ws, idx_out=idx)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.ctx.decode_step(g.k, g.v, g.side, q, kn, vn, g.seq_lens, int(x["ctx"].max()),
+                          w.budget, out, g.ws, idx_out=idx)
+    for rep in range(4):
+        out.zero_()
+        idx.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, eager_idx), rep
+        assert torch.equal(out, eager_out), rep
+        _ = run_decode(g, 0, w.budget, advance=False)  # eager work between replays

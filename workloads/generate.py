@@ -148,3 +148,31 @@ def generate(w: Workload, seed: int = 0xFA5A, with_prefill: bool = True):
 
     out["k_prefill"], out["v_prefill"] = k, v
     return out
+
+
+def random_scores(seed: int, rows: int, n: int, kind: str) -> np.ndarray:
+    """Seeded fp32 score rows [rows, n] for selection tests.
+
+    kinds: 'normal' (N(0,1)), 'ties' (few distinct values), 'zeros' (all +0
+    and -0), 'wide' (magnitudes across 1e-30..1e30, both signs), 'sorted_up'
+    (strictly increasing), 'planted' (N(0,1) with a 1% block of large values).
+    """
+    r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0xC0DE, rows, n])))
+    if kind == "normal":
+        x = r.standard_normal((rows, n))
+    elif kind == "ties":
+        x = r.integers(-3, 4, size=(rows, n)).astype(np.float64) * 0.5
+    elif kind == "zeros":
+        x = np.where(r.random((rows, n)) < 0.5, 0.0, -0.0)
+    elif kind == "wide":
+        x = r.standard_normal((rows, n)) * 10.0 ** r.uniform(-30, 30, (rows, n))
+    elif kind == "sorted_up":
+        x = np.tile(np.arange(n, dtype=np.float64), (rows, 1))
+    elif kind == "planted":
+        x = r.standard_normal((rows, n))
+        k = max(1, n // 100)
+        for i in range(rows):
+            x[i, r.choice(n, size=k, replace=False)] += 6.0
+    else:
+        raise ValueError(kind)
+    return np.ascontiguousarray(x.astype(np.float32))
