@@ -1,0 +1,253 @@
+"""Benchmark of the FASA decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2] [--layers L]
+
+Workload (default): a Llama-3-8B-shaped attention layer, one decode step at
+32768 tokens of context with B = 256 and 16 dominant FCs per query head
+(32 query heads on 8 KV heads, d = 128, bf16 caches, RoPE theta 5e5).  Inputs
+are seeded synthetic data (workloads/); they stand in for the LongBench-V1
+setting the pages quote at 256 retained tokens.
+
+A step is one fasa_decode_step (append + query rotation, TIP, top-B, FAC) on
+one layer's cache.  Steps rotate over L distinct layer caches (16 by default,
+about 2.9 GB) so that the 256 MB Infinity Cache cannot serve a repeated
+layer, as in a real multi-layer decode.  The timed steps are replayed from a
+HIP graph of L steps; inputs are resident in HBM before timing starts.
+
+Printed: one JSON line with the metric (context tokens scanned per second),
+the fraction of HBM peak on the algorithmic bytes, the dominant kernel's
+roofline figure (TIP: sidecar bytes / its average duration from HIP events
+bracketing each launch), the in-build dense decode comparator and the CPU
+oracle baseline on a bounded sample.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "context tokens scanned/s per decode step + % HBM peak (32k ctx, B=256)"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=480)
+    p.add_argument("--warmup", type=int, default=32)
+    p.add_argument("--config", default="c2")
+    p.add_argument("--layers", type=int, default=16)
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="CPU oracle sample budget (0 disables)")
+    p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--eager", action="store_true", help="time eager launches, no graph")
+    return p.parse_args()
+
+
+def sha256(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_from_profile(kernel_src):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "tip_c2_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        prof = json.load(f)
+    if prof.get("source_sha256") != sha256(kernel_src):
+        return None
+    return prof.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, budget_s):
+    """The oracle (fp64 NumPy, one thread) on consecutive decode steps of the
+    same workload until ~budget_s seconds of step time are spent."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1):
+        st = oracle.OracleState(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.rope_theta,
+                                w.dtype, x["dom"], w.capacity + 4096)
+        for b in range(w.batch):
+            n0 = int(x["ctx"][b]) - 1
+            st.append(b, x["k_prefill"][b][:, :n0], x["v_prefill"][b][:, :n0])
+        spent, steps, tokens = 0.0, 0, 0
+        while spent < budget_s and steps < 4096:
+            t = steps % w.steps
+            t0 = time.perf_counter()
+            st.step(x["q"][t], x["k_new"][t], x["v_new"][t], w.budget)
+            spent += time.perf_counter() - t0
+            tokens += int(st.lens.sum())
+            steps += 1
+    return {"value": tokens / spent, "unit": "context tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} consecutive decode steps of the same workload (all "
+                      f"{w.n_q_heads} query heads, append + TIP + top-B + FAC), fp64 NumPy "
+                      f"on one host thread, {spent:.1f} s of step time, prefill excluded"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the decode step shards by sequence / KV head with no exchange).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_kv_cache_rope_amd as fasa
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    w = W.get(args.config)
+    x = W.generate(w)
+    L = max(1, args.layers)
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    to = lambda a, dt=td: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+
+    ctx = fasa.Context(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.capacity,
+                       w.rope_theta, w.dtype, x["dom"], w.budget, device=dev)
+    ws = ctx.new_workspace()
+    layers = [ctx.new_cache() for _ in range(L)]
+    kp, vp = to(x["k_prefill"]), to(x["v_prefill"])
+    zero = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    for (k, v, s) in layers:
+        ctx.append_kv(k, v, s, kp, vp, zero, ws)
+    del kp, vp
+    seq = torch.from_numpy((x["ctx"] - 1).astype(np.int32)).to(dev)
+    n_b = x["ctx"].astype(np.int64)  # tokens attended by the timed step
+    msl = int(n_b.max())
+    q, kn, vn = to(x["q"][0]), to(x["k_new"][0]), to(x["v_new"][0])
+    out = torch.empty(w.batch, w.n_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    idx = torch.empty(w.batch, w.n_q_heads, w.budget, dtype=torch.int32, device=dev)
+    dense_out = torch.empty_like(out)
+    seq_full = seq + 1
+
+    def step(i):
+        k, v, s = layers[i % L]
+        ctx.decode_step(k, v, s, q, kn, vn, seq, msl, w.budget, out, ws, idx_out=idx)
+
+    def dense(i):
+        k, v, _ = layers[i % L]
+        ctx.dense_attn(k, v, q, seq_full, msl, dense_out, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    assert ctx.check(ws) == 0
+
+    K = max(L, (args.steps + L - 1) // L * L)
+    reps = K // L
+
+    def timed(fn, use_graph):
+        if use_graph:
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for i in range(L):
+                    fn(i)
+            torch.cuda.current_stream().wait_stream(side)
+            with torch.cuda.graph(g):
+                for i in range(L):
+                    fn(i)
+            g.replay()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        if use_graph:
+            for _ in range(reps):
+                g.replay()
+        else:
+            for i in range(K):
+                fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    use_graph = not args.eager
+    ms_step = timed(step, use_graph)
+    ms_step_eager = timed(step, False) if use_graph else ms_step
+    assert ctx.check(ws) == 0
+    ms_dense = None if args.no_dense else timed(dense, use_graph)
+
+    # Per-kernel durations: HIP events around every launch, eager, same rotation.
+    ctx.timing_enable(True)
+    fams = {}
+
+    def add(part):
+        for f, (ms, n) in part.items():
+            a = fams.get(f, (0.0, 0))
+            fams[f] = (a[0] + ms, a[1] + n)
+
+    for i in range(K):
+        step(i)
+        if (i + 1) % 256 == 0:
+            add(ctx.timing_collect())
+    add(ctx.timing_collect())
+    ctx.timing_enable(False)
+    kernel_ms = {f: ms / n for f, (ms, n) in fams.items() if n}
+
+    # Algorithmic bytes: sidecar bytes TIP reads + B * 2 * d * s per query head.
+    es = 2 if w.dtype == "bf16" else 4
+    off, _ = ctx.sidecar_layout()
+    P = int(off[-1])
+    tip_bytes = int(sum(P * n * 2 * es for n in n_b))
+    fac_bytes = int(sum(min(w.budget, n) * 2 * w.head_dim * es * w.n_q_heads for n in n_b))
+    algo_bytes = tip_bytes + fac_bytes
+    dense_bytes = int(sum(2 * n * w.head_dim * es * w.n_kv_heads for n in n_b))
+    t_step = ms_step * 1e-3
+    tokens = int(n_b.sum())
+    tip_s = kernel_ms["tip"] * 1e-3
+    achieved = tip_bytes / tip_s / 1e9
+    traffic = traffic_from_profile(os.path.join(ROOT, "sparse_kv_cache_rope_amd", "csrc", "tip.hip"))
+
+    res = {
+        "metric": METRIC,
+        "value": tokens / t_step,
+        "unit": "context tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v with planted salient keys; stands in for LongBench-V1 at B=256)",
+        "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "context": int(n_b.max()), "budget": w.budget, "n_dom": w.n_dom,
+                   "rope_theta": w.rope_theta, "layers_rotated": L,
+                   "launch": "hipgraph" if use_graph else "eager"},
+        "hbm_peak_frac": algo_bytes / t_step / (HBM_PEAK_GBS * 1e9),
+        "algorithmic_bytes_per_step": algo_bytes,
+        "decode_steps_per_s": 1.0 / t_step,
+        "ms_per_step_eager": ms_step_eager,
+        "kernel_avg_ms": kernel_ms,
+        "roofline": {"bound": "hbm", "kernel": "tip_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": tip_bytes},
+    }
+    if ms_dense is not None:
+        res["dense"] = {"ms_per_step": ms_dense, "bytes_per_step": dense_bytes,
+                        "hbm_gbps": dense_bytes / (ms_dense * 1e-3) / 1e9,
+                        "sparse_speedup": ms_dense / ms_step}
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

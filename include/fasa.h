@@ -199,6 +199,29 @@ fasa_status fasa_dense_attn(fasa_ctx* ctx, const void* k_cache, const void* v_ca
  */
 fasa_status fasa_check(fasa_ctx* ctx, void* workspace, hipStream_t stream, uint32_t* flags);
 
+/*
+ * Kernel timing with HIP events (a measurement aid, off by default).  While
+ * enabled, every launch made by the calls above is bracketed by a pair of
+ * hipEvents recorded on the call's stream, grouped by kernel family.
+ * fasa_timing_collect waits for the recorded events, adds each family's
+ * elapsed milliseconds and launch count into total_ms[FASA_K_COUNT] and
+ * launches[FASA_K_COUNT] (host arrays, may be NULL) and forgets them.  At
+ * most 4096 launches are kept between collects; later ones are not timed.
+ * Not for use under stream capture.
+ */
+typedef enum {
+  FASA_K_APPEND = 0,    /* bulk append kernel */
+  FASA_K_PROLOGUE = 1,  /* per-step append + query rotation + TIP weights */
+  FASA_K_TIP = 2,       /* TIP scoring over the sidecar */
+  FASA_K_TOPK = 3,      /* the three top-B kernels together */
+  FASA_K_FAC = 4,       /* sparse attention */
+  FASA_K_DENSE = 5,     /* dense comparator */
+  FASA_K_SELECT_FAC = 6, /* top-B fused with FAC (budgets up to 1024) */
+  FASA_K_COUNT = 7
+} fasa_kernel_family;
+fasa_status fasa_timing_enable(fasa_ctx* ctx, int enable);
+fasa_status fasa_timing_collect(fasa_ctx* ctx, double* total_ms, int32_t* launches);
+
 const char* fasa_status_string(fasa_status status);
 /* Detail of the last host-side error on the calling thread ("" if none). */
 const char* fasa_last_error(void);

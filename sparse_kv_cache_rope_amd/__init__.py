@@ -1,7 +1,7 @@
 """Python binding of libfasa, the FASA decode hot path for MI355X (gfx950).
 
 Argument marshalling only: every step of the path runs in the HIP kernels of
-``libfasa.so`` (built in-tree by ``python -m sparse_kv_cache_rope_amd.build``).
+``libfasa.so`` (built in-tree by ``python sparse_kv_cache_rope_amd/build.py``).
 PyTorch provides device memory and the current stream.  Importing this module
 without the built library raises ImportError; there is no fallback.
 
@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libfasa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing; build it with `python -m sparse_kv_cache_rope_amd.build`")
+        f"{LIB_PATH} is missing; build it with `python sparse_kv_cache_rope_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -44,11 +44,16 @@ _SIGS = {
                                   _vp, _vp, _vp, ctypes.c_uint, _vp]),
     "fasa_dense_attn": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp]),
     "fasa_check": (_c_int, [_vp, _vp, _vp, ctypes.POINTER(ctypes.c_uint32)]),
+    "fasa_timing_enable": (_c_int, [_vp, _c_int]),
+    "fasa_timing_collect": (_c_int, [_vp, ctypes.POINTER(ctypes.c_double), _i32p]),
     "fasa_status_string": (ctypes.c_char_p, [_c_int]),
     "fasa_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
-    _fn = getattr(_lib, _name)
+    try:
+        _fn = getattr(_lib, _name)
+    except AttributeError as _e:
+        raise ImportError(f"{LIB_PATH} lacks {_name}: stale build, rebuild it") from _e
     _fn.restype = _res
     _fn.argtypes = _args
 
@@ -230,6 +235,19 @@ class Context:
         _chk(_lib.fasa_dense_attn(self._h, _ptr(k_cache), _ptr(v_cache), _ptr(q),
                                   _ptr(seq_lens), int(max_seq_len), _ptr(out), _ptr(workspace),
                                   self._stream(stream)), "fasa_dense_attn")
+
+    KERNEL_FAMILIES = ("append", "prologue", "tip", "topk", "fac", "dense", "select_fac")
+
+    def timing_enable(self, enable=True):
+        _chk(_lib.fasa_timing_enable(self._h, 1 if enable else 0), "fasa_timing_enable")
+
+    def timing_collect(self):
+        """{family: (total_ms, launches)} since the last collect (waits)."""
+        n = len(self.KERNEL_FAMILIES)
+        ms = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int32 * n)()
+        _chk(_lib.fasa_timing_collect(self._h, ms, cnt), "fasa_timing_collect")
+        return {f: (ms[i], cnt[i]) for i, f in enumerate(self.KERNEL_FAMILIES)}
 
     def check(self, workspace, stream=None):
         """Synchronise; return the device error-flag bits (and clear them)."""

@@ -1,6 +1,6 @@
 """Builds libfasa.so (HIP for gfx950) in-tree with hipcc.
 
-    python -m sparse_kv_cache_rope_amd.build        # or build() from Python
+    python sparse_kv_cache_rope_amd/build.py        # or build() from Python
 
 Each source compiles to an object in parallel, then one link.  Always
 rebuilds (the build is a few tens of seconds).
@@ -17,7 +17,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfasa.so")
 ROOT = os.path.dirname(HERE)
 
-SOURCES = ["api.cpp", "rope_append.hip", "tip.hip", "topk.hip", "attention.hip"]
+SOURCES = ["api.cpp", "rope_append.hip", "tip.hip", "topk.hip", "select2.hip", "attention.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -46,7 +46,6 @@ size_t dtype_size(fasa_dtype t) { return t == FASA_BF16 ? 2 : 4; }
 void build_layout(fasa_ctx* c) {
   WsLayout& w = c->ws;
   const size_t rows = (size_t)c->batch * c->hq;
-  w.max_chunks = (c->cap + kChunk - 1) / kChunk;
   w.fac_splits = (c->max_budget + kFacSplitRows - 1) / kFacSplitRows;
   w.dense_splits = (c->cap + kDenseSplitTokens - 1) / kDenseSplitTokens;
   size_t off = 0;
@@ -60,13 +59,14 @@ void build_layout(fasa_ctx* c) {
   w.qrot = take(sizeof(float) * rows * c->d);
   w.tipw = take(sizeof(float) * c->batch * (size_t)c->P * c->G * 2);
   w.scores = take(sizeof(float) * rows * c->cap);
-  w.hist = take(sizeof(uint32_t) * rows * kHistBins);
-  w.ticket = take(sizeof(uint32_t) * rows * kTicketsPerRow);
-  w.rowst = take(sizeof(RowState) * rows);
-  w.cand = take(sizeof(uint64_t) * rows * c->cap);
-  w.chunk_gt = take(sizeof(uint32_t) * rows * w.max_chunks);
-  w.chunk_off = take(sizeof(uint32_t) * rows * w.max_chunks);
   w.idx = take(sizeof(int32_t) * rows * c->max_budget);
+  {
+    const int nch = (c->cap + kTwoStageChunk - 1) / kTwoStageChunk;
+    const int per = c->max_budget < kTwoStageChunk / 2 ? c->max_budget : kTwoStageChunk / 2;
+    const int need = nch * per < kTwoStageMaxCand ? nch * per : kTwoStageMaxCand;
+    w.cand_stride = (need + 3) & ~3;  // rows start 32-byte aligned
+    w.cand = take(sizeof(uint64_t) * rows * w.cand_stride);
+  }
   w.fac = take(sizeof(float) * rows * w.fac_splits * (c->d + 2));
   w.dense = take(sizeof(float) * rows * w.dense_splits * (c->d + 2));
   w.total = off;
@@ -90,6 +90,27 @@ fasa_status check_budget(const fasa_ctx* c, int budget) {
     return fail(FASA_ERR_CAPACITY, "budget %d exceeds max_budget %d", budget, c->max_budget);
   return FASA_OK;
 }
+
+constexpr int kTimingPairs = 4096;
+
+// Brackets one launch with a pair of events when timing is enabled.
+class Timed {
+ public:
+  Timed(fasa_ctx* c, int family, hipStream_t s) : c_(c), s_(s), pair_(-1) {
+    if (!c->timing || c->ev_used >= kTimingPairs) return;
+    pair_ = c->ev_used++;
+    c->ev_family[pair_] = family;
+    (void)hipEventRecord(c->ev[2 * pair_], s_);
+  }
+  ~Timed() {
+    if (pair_ >= 0) (void)hipEventRecord(c_->ev[2 * pair_ + 1], s_);
+  }
+
+ private:
+  fasa_ctx* c_;
+  hipStream_t s_;
+  int pair_;
+};
 
 #define FASA_NONNULL(p)                                                  \
   do {                                                                   \
@@ -130,8 +151,8 @@ fasa_status fasa_create(fasa_ctx** out, int batch, int n_q_heads, int n_kv_heads
     return fail(FASA_ERR_UNSUPPORTED, "head_dim %d not in {64,128}", head_dim);
   if (capacity < 64 || capacity % 64)
     return fail(FASA_ERR_INVALID_ARG, "capacity %d must be a positive multiple of 64", capacity);
-  if ((long long)capacity > (long long)kMaxChunks * kChunk)
-    return fail(FASA_ERR_CAPACITY, "capacity %d above %d", capacity, kMaxChunks * kChunk);
+  if (capacity > kMaxCapacity)
+    return fail(FASA_ERR_CAPACITY, "capacity %d above %d", capacity, kMaxCapacity);
   if (!(rope_theta > 1.0) || !std::isfinite(rope_theta))
     return fail(FASA_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
   if (dtype != FASA_F32 && dtype != FASA_BF16)
@@ -231,6 +252,7 @@ fasa_status fasa_create(fasa_ctx** out, int batch, int n_q_heads, int n_kv_heads
 
 void fasa_destroy(fasa_ctx* ctx) {
   if (!ctx) return;
+  for (hipEvent_t e : ctx->ev) (void)hipEventDestroy(e);
   if (ctx->dev_alloc) (void)hipFree(ctx->dev_alloc);
   delete ctx;
 }
@@ -275,9 +297,12 @@ fasa_status fasa_append_kv(fasa_ctx* c, void* k_cache, void* v_cache, void* side
   FASA_NONNULL(v_new);
   FASA_NONNULL(start_pos);
   FASA_NONNULL(workspace);
-  FASA_HIP(launch_append(c, k_cache, v_cache, sidecar, k_new, v_new, start_pos, n_new,
-                         static_cast<uint8_t*>(workspace), stream),
-           "fasa_append_kv");
+  {
+    Timed t(c, FASA_K_APPEND, stream);
+    FASA_HIP(launch_append(c, k_cache, v_cache, sidecar, k_new, v_new, start_pos, n_new,
+                           static_cast<uint8_t*>(workspace), stream),
+             "fasa_append_kv");
+  }
   return ok();
 }
 
@@ -293,10 +318,16 @@ fasa_status fasa_tip_scores(fasa_ctx* c, const void* sidecar, const void* q,
   FASA_NONNULL(workspace);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   PrologueArgs a{q, nullptr, nullptr, nullptr, nullptr, nullptr, seq_lens, max_seq_len};
-  FASA_HIP(launch_prologue(c, kPrologueQueryOnly, a, ws, stream), "fasa_tip_scores: prologue");
-  FASA_HIP(launch_tip(c, sidecar, reinterpret_cast<const int32_t*>(ws + c->ws.nb), max_seq_len,
-                      scores, nullptr, ws, stream),
-           "fasa_tip_scores");
+  {
+    Timed t(c, FASA_K_PROLOGUE, stream);
+    FASA_HIP(launch_prologue(c, kPrologueQueryOnly, a, ws, stream), "fasa_tip_scores: prologue");
+  }
+  {
+    Timed t(c, FASA_K_TIP, stream);
+    FASA_HIP(launch_tip(c, sidecar, reinterpret_cast<const int32_t*>(ws + c->ws.nb), max_seq_len,
+                        scores, nullptr, ws, stream),
+             "fasa_tip_scores");
+  }
   return ok();
 }
 
@@ -310,9 +341,17 @@ fasa_status fasa_topk(fasa_ctx* c, const float* scores, const int32_t* seq_lens,
   FASA_NONNULL(seq_lens);
   FASA_NONNULL(idx);
   FASA_NONNULL(workspace);
-  FASA_HIP(launch_topk(c, scores, seq_lens, max_seq_len, budget, idx,
-                       static_cast<uint8_t*>(workspace), stream),
-           "fasa_topk");
+  {
+    Timed t(c, FASA_K_TOPK, stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    if (two_stage_applies(max_seq_len, budget))
+      FASA_HIP(launch_two_stage(c, scores, seq_lens, max_seq_len, budget, idx, nullptr, nullptr,
+                                nullptr, ws, stream),
+               "fasa_topk: two-stage");
+    else
+      FASA_HIP(launch_topk(c, scores, seq_lens, max_seq_len, budget, idx, ws, stream),
+               "fasa_topk");
+  }
   return ok();
 }
 
@@ -330,10 +369,16 @@ fasa_status fasa_sparse_attn(fasa_ctx* c, const void* k_cache, const void* v_cac
   FASA_NONNULL(workspace);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   PrologueArgs a{q, nullptr, nullptr, nullptr, nullptr, nullptr, seq_lens, c->cap};
-  FASA_HIP(launch_prologue(c, kPrologueQueryOnly, a, ws, stream), "fasa_sparse_attn: prologue");
-  FASA_HIP(launch_fac(c, k_cache, v_cache, reinterpret_cast<const int32_t*>(ws + c->ws.nb),
-                      c->cap, idx, budget, out, ws, stream),
-           "fasa_sparse_attn");
+  {
+    Timed t(c, FASA_K_PROLOGUE, stream);
+    FASA_HIP(launch_prologue(c, kPrologueQueryOnly, a, ws, stream), "fasa_sparse_attn: prologue");
+  }
+  {
+    Timed t(c, FASA_K_FAC, stream);
+    FASA_HIP(launch_fac(c, k_cache, v_cache, reinterpret_cast<const int32_t*>(ws + c->ws.nb),
+                        c->cap, idx, budget, out, ws, stream),
+             "fasa_sparse_attn");
+  }
   return ok();
 }
 
@@ -360,14 +405,42 @@ fasa_status fasa_decode_step(fasa_ctx* c, void* k_cache, void* v_cache, void* si
   float* scores = reinterpret_cast<float*>(ws + c->ws.scores);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + c->ws.idx);
   PrologueArgs a{q, k_new, v_new, k_cache, v_cache, sidecar, seq_lens, max_seq_len};
-  FASA_HIP(launch_prologue(c, kPrologueDecode, a, ws, stream), "fasa_decode_step: append");
-  FASA_HIP(launch_tip(c, sidecar, nb, max_seq_len, scores,
-                      (flags & FASA_ADVANCE_SEQ_LENS) ? seq_lens : nullptr, ws, stream),
-           "fasa_decode_step: tip");
-  FASA_HIP(launch_topk(c, scores, nb, max_seq_len, budget, idx, ws, stream),
-           "fasa_decode_step: topk");
-  FASA_HIP(launch_fac(c, k_cache, v_cache, nb, max_seq_len, idx, budget, out, ws, stream),
-           "fasa_decode_step: fac");
+  {
+    Timed t(c, FASA_K_PROLOGUE, stream);
+    FASA_HIP(launch_prologue(c, kPrologueDecode, a, ws, stream), "fasa_decode_step: append");
+  }
+  {
+    Timed t(c, FASA_K_TIP, stream);
+    FASA_HIP(launch_tip(c, sidecar, nb, max_seq_len, scores,
+                        (flags & FASA_ADVANCE_SEQ_LENS) ? seq_lens : nullptr, ws, stream),
+             "fasa_decode_step: tip");
+  }
+  if (two_stage_applies(max_seq_len, budget)) {
+    // Chunk-local top-B, then the row's top-B fused with FAC.
+    Timed t(c, FASA_K_SELECT_FAC, stream);
+    FASA_HIP(launch_two_stage(c, scores, nb, max_seq_len, budget, idx_out, k_cache, v_cache,
+                              out, ws, stream),
+             "fasa_decode_step: two-stage select+fac");
+    return ok();
+  }
+  if (budget <= kFusedMaxBudget) {
+    // Selection and FAC in one kernel: the selected rows never leave LDS.
+    Timed t(c, FASA_K_SELECT_FAC, stream);
+    FASA_HIP(launch_select_attend(c, scores, nb, max_seq_len, budget, idx_out, k_cache, v_cache,
+                                  out, ws, stream),
+             "fasa_decode_step: select+fac");
+    return ok();
+  }
+  {
+    Timed t(c, FASA_K_TOPK, stream);
+    FASA_HIP(launch_topk(c, scores, nb, max_seq_len, budget, idx, ws, stream),
+             "fasa_decode_step: topk");
+  }
+  {
+    Timed t(c, FASA_K_FAC, stream);
+    FASA_HIP(launch_fac(c, k_cache, v_cache, nb, max_seq_len, idx, budget, out, ws, stream),
+             "fasa_decode_step: fac");
+  }
   return ok();
 }
 
@@ -384,10 +457,16 @@ fasa_status fasa_dense_attn(fasa_ctx* c, const void* k_cache, const void* v_cach
   FASA_NONNULL(workspace);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   PrologueArgs a{q, nullptr, nullptr, nullptr, nullptr, nullptr, seq_lens, max_seq_len};
-  FASA_HIP(launch_prologue(c, kPrologueQueryOnly, a, ws, stream), "fasa_dense_attn: prologue");
-  FASA_HIP(launch_dense(c, k_cache, v_cache, reinterpret_cast<const int32_t*>(ws + c->ws.nb),
-                        max_seq_len, out, ws, stream),
-           "fasa_dense_attn");
+  {
+    Timed t(c, FASA_K_PROLOGUE, stream);
+    FASA_HIP(launch_prologue(c, kPrologueQueryOnly, a, ws, stream), "fasa_dense_attn: prologue");
+  }
+  {
+    Timed t(c, FASA_K_DENSE, stream);
+    FASA_HIP(launch_dense(c, k_cache, v_cache, reinterpret_cast<const int32_t*>(ws + c->ws.nb),
+                          max_seq_len, out, ws, stream),
+             "fasa_dense_attn");
+  }
   return ok();
 }
 
@@ -406,6 +485,35 @@ fasa_status fasa_check(fasa_ctx* c, void* workspace, hipStream_t stream, uint32_
   }
   if (flags) *flags = v;
   if (v) return fail(FASA_ERR_DEVICE_FLAG, "device error flag 0x%x", v);
+  return ok();
+}
+
+fasa_status fasa_timing_enable(fasa_ctx* c, int enable) {
+  FASA_TRY(check_ctx(c));
+  if (enable && c->ev.empty()) {
+    c->ev.assign(2 * kTimingPairs, nullptr);
+    c->ev_family.assign(kTimingPairs, 0);
+    for (auto& e : c->ev) FASA_HIP(hipEventCreate(&e), "fasa_timing_enable");
+  }
+  c->timing = enable != 0;
+  return ok();
+}
+
+fasa_status fasa_timing_collect(fasa_ctx* c, double* total_ms, int32_t* launches) {
+  FASA_TRY(check_ctx(c));
+  if (total_ms)
+    for (int k = 0; k < FASA_K_COUNT; ++k) total_ms[k] = 0.0;
+  if (launches)
+    for (int k = 0; k < FASA_K_COUNT; ++k) launches[k] = 0;
+  for (int i = 0; i < c->ev_used; ++i) {
+    FASA_HIP(hipEventSynchronize(c->ev[2 * i + 1]), "fasa_timing_collect: wait");
+    float ms = 0.0f;
+    FASA_HIP(hipEventElapsedTime(&ms, c->ev[2 * i], c->ev[2 * i + 1]), "fasa_timing_collect");
+    const int f = c->ev_family[i];
+    if (total_ms) total_ms[f] += ms;
+    if (launches) launches[f] += 1;
+  }
+  c->ev_used = 0;
   return ok();
 }
 

@@ -7,155 +7,34 @@
 // positions (the cache already holds them rotated).  The dense kernel is the
 // full-KV baseline the pages compare against (same page, section 4).
 //
-// Row layout: a K or V row is d * sizeof(dtype) bytes (256 B for bf16 d=128);
-// LPR = row_bytes / 16 lanes each load 16 bytes of it, so a wave holds
-// RS = 64 / LPR rows at once.  A lane owns EPL = 16 / sizeof(dtype) dims of
-// q~ (pre-scaled by 1/sqrt(d)) and of the output accumulator.  Dot products
-// are summed across the LPR lanes of a row with DPP, each lane keeps a running
-// (max, sum, acc) over the rows it saw, and those are merged across row
-// slots, waves and then splits.  The selection is per query head, so a
-// workgroup's rows form a gather, not a dense tile: this stays on VALU and is
-// bound by the bytes moved, not by MFMA.
+// Rows are gathered 16 bytes per lane (attention_common.hpp).  A head whose
+// work spans several workgroups writes
+// per-split partials that a separate small kernel merges: no workgroup waits
+// on another.  Selection is per query head, so a workgroup's rows form a
+// gather, not a dense tile: this stays on VALU and is bound by bytes moved.
 
-#include <math.h>
-
-#include "device_common.hpp"
+#include "attention_common.hpp"
 #include "fasa_internal.hpp"
 
 namespace fasa {
 
-template <bool BF16, int D>
-struct RowGeom {
-  static constexpr int ES = BF16 ? 2 : 4;
-  static constexpr int LPR = D * ES / 16;
-  static constexpr int EPL = 16 / ES;
-  static constexpr int RS = kWave / LPR;
-  static_assert(LPR >= 4 && LPR <= 32, "row must span 4..32 lanes");
-};
-
-template <bool BF16, int EPL>
-__device__ __forceinline__ void unpack(const uint4& x, float (&f)[EPL]) {
-  if constexpr (BF16) {
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = bf16_lo(w[i]);
-      f[2 * i + 1] = bf16_hi(w[i]);
-    }
-  } else {
-    f[0] = __uint_as_float(x.x);
-    f[1] = __uint_as_float(x.y);
-    f[2] = __uint_as_float(x.z);
-    f[3] = __uint_as_float(x.w);
-  }
-}
-
-// Online-softmax state of one lane.
-template <int EPL>
-struct Soft {
-  float m, l, a[EPL];
-  __device__ __forceinline__ void init() {
-    m = -INFINITY;
-    l = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) a[e] = 0.0f;
-  }
-  // Adds one row with logit z (-inf = absent) and values v.
-  __device__ __forceinline__ void add(float z, const float (&v)[EPL]) {
-    if (z == -INFINITY) return;
-    const float mn = fmaxf(m, z);
-    const float sc = expf(m - mn);  // m = -inf gives 0
-    const float p = expf(z - mn);
-    l = l * sc + p;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) a[e] = fmaf(p, v[e], a[e] * sc);
-    m = mn;
-  }
-  __device__ __forceinline__ void merge(float m2, float l2, const float (&a2)[EPL]) {
-    const float mn = fmaxf(m, m2);
-    if (mn == -INFINITY) return;
-    const float s1 = expf(m - mn), s2 = expf(m2 - mn);
-    l = l * s1 + l2 * s2;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) a[e] = a[e] * s1 + a2[e] * s2;
-    m = mn;
-  }
-  // Merge with the lane `off` away (xor).
-  __device__ __forceinline__ void merge_xor(int off) {
-    float a2[EPL];
-    const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) a2[e] = __shfl_xor(a[e], off);
-    merge(m2, l2, a2);
-  }
-};
-
-// Merges the row slots of each wave, then the NW waves through LDS; on return
-// wave 0 lanes 0..LPR-1 hold the workgroup's state.  `lds` needs
-// NW * (D + 2 * LPR) floats.
-template <int D, int LPR, int EPL, int NW>
-__device__ __forceinline__ void merge_block(Soft<EPL>& st, float* lds) {
-#pragma unroll
-  for (int off = LPR; off < kWave; off <<= 1) st.merge_xor(off);
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  float* mine = lds + wave * (D + 2 * LPR);
-  if (lane < LPR) {
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) mine[lane * EPL + e] = st.a[e];
-    mine[D + lane] = st.m;
-    mine[D + LPR + lane] = st.l;
-  }
-  __syncthreads();
-  if (wave == 0 && lane < LPR) {
-#pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      const float* o = lds + w * (D + 2 * LPR);
-      float a2[EPL];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) a2[e] = o[lane * EPL + e];
-      st.merge(o[D + lane], o[D + LPR + lane], a2);
-    }
-  }
-}
-
-// Merges the per-split partials [nsplit][D + 2] (m, l, acc) of one row into
-// out[D]; called by one workgroup.
-template <int D>
-__device__ __forceinline__ void merge_splits(const float* __restrict__ part, int nsplit,
-                                             float* __restrict__ out) {
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part[(size_t)s * (D + 2)]);
-    float L = 0.0f, A = 0.0f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < nsplit; ++s) {
-        const float* p = part + (size_t)s * (D + 2);
-        const float w = expf(p[0] - M);
-        L = fmaf(p[1], w, L);
-        A = fmaf(p[2 + d], w, A);
-      }
-    }
-    out[d] = (L > 0.0f) ? A / L : 0.0f;
-  }
-}
-
 // ---------------------------------------------------------------- FAC ----
 
-// grid (splits, Hq, b), 256 threads; split s covers idx entries
-// [s * kFacSplitRows, ...) of the first min(budget, n_b).
+constexpr int kFacThreads = 1024;
+
+// grid (splits, Hq, b); split s covers idx entries [s * kFacSplitRows, ...)
+// of the first min(budget, n_b).
 template <bool BF16, int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kFacThreads)
 fac_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
            const float* __restrict__ qrot, const int32_t* __restrict__ nb, int max_seq_len,
            const int32_t* __restrict__ idx, int budget, int hq, int hkv, int G, int cap,
-           float* __restrict__ partial, int max_splits, uint32_t* __restrict__ tickets,
-           float* __restrict__ out, uint32_t* err) {
+           float* __restrict__ partial, int max_splits, float* __restrict__ out, uint32_t* err) {
   using Geo = RowGeom<BF16, D>;
-  constexpr int LPR = Geo::LPR, EPL = Geo::EPL, RS = Geo::RS, NW = 4;
+  constexpr int LPR = Geo::LPR, EPL = Geo::EPL, RS = Geo::RS, NW = kFacThreads / kWave;
   constexpr int ITERS = kFacSplitRows / (RS * NW);
-  static_assert(ITERS >= 1, "split smaller than one pass");
+  static_assert(ITERS >= 1 && ITERS * RS * NW == kFacSplitRows, "split geometry");
   __shared__ float lds[NW * (D + 2 * LPR)];
-  __shared__ uint32_t flag;
 
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t row = (size_t)b * hq + h;
@@ -166,7 +45,7 @@ fac_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
   float* o = out + row * D;
   if (nsplit == 0) {
     if (split == 0)
-      for (int d = threadIdx.x; d < D; d += 256) o[d] = 0.0f;
+      for (int d = threadIdx.x; d < D; d += kFacThreads) o[d] = 0.0f;
     return;
   }
   if (split >= nsplit) return;
@@ -221,45 +100,28 @@ fac_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
     st.add(jr[it] >= 0 ? z : -INFINITY, vf);
   }
   merge_block<D, LPR, EPL, NW>(st, lds);
-
-  if (nsplit == 1) {
-    if (wave == 0 && lane < LPR) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[lane * EPL + e] = (st.l > 0.0f) ? st.a[e] / st.l : 0.0f;
-    }
-    return;
-  }
-  float* part = partial + row * max_splits * (D + 2);
-  if (wave == 0 && lane < LPR) {
-    float* p = part + (size_t)split * (D + 2);
-    if (lane == 0) {
-      p[0] = st.m;
-      p[1] = st.l;
-    }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) p[2 + lane * EPL + e] = st.a[e];
-  }
-  if (!last_block_arrives(&tickets[row * kTicketsPerRow + 2], (uint32_t)nsplit, &flag)) return;
-  merge_splits<D>(part, nsplit, o);
+  write_state<D, LPR, EPL>(st, nsplit == 1, o,
+                           partial + (row * max_splits + split) * (D + 2));
 }
 
 // -------------------------------------------------------------- dense ----
 
-// grid (splits, Hkv, b), 256 threads; split s covers tokens
-// [s * kDenseSplitTokens, ...) for all G query heads of KV head g.
+constexpr int kDenseThreads = 512;
+
+// grid (splits, Hkv, b); split s covers tokens [s * kDenseSplitTokens, ...)
+// for all G query heads of KV head g.
 template <bool BF16, int D, int G>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kDenseThreads)
 dense_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
              const float* __restrict__ qrot, const int32_t* __restrict__ nb, int max_seq_len,
              int hq, int hkv, int cap, float* __restrict__ partial, int max_splits,
-             uint32_t* __restrict__ tickets, float* __restrict__ out, uint32_t* err) {
+             float* __restrict__ out, uint32_t* err) {
   using Geo = RowGeom<BF16, D>;
-  constexpr int LPR = Geo::LPR, EPL = Geo::EPL, RS = Geo::RS, NW = 4;
+  constexpr int LPR = Geo::LPR, EPL = Geo::EPL, RS = Geo::RS, NW = kDenseThreads / kWave;
   constexpr int ITERS = kDenseSplitTokens / (RS * NW);
   constexpr int BATCH = 4;
-  static_assert(ITERS % BATCH == 0, "token split must be a multiple of one batch");
+  static_assert(ITERS % BATCH == 0 && ITERS * RS * NW == kDenseSplitTokens, "split geometry");
   __shared__ float lds[NW * (D + 2 * LPR)];
-  __shared__ uint32_t flag;
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int n = checked_len(nb, b, max_seq_len, cap, err, false);
@@ -267,7 +129,7 @@ dense_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
   const size_t row0 = (size_t)b * hq + (size_t)g * G;
   if (nsplit == 0) {
     if (split == 0)
-      for (int i = threadIdx.x; i < G * D; i += 256) out[row0 * D + i] = 0.0f;
+      for (int i = threadIdx.x; i < G * D; i += kDenseThreads) out[row0 * D + i] = 0.0f;
     return;
   }
   if (split >= nsplit) return;
@@ -318,49 +180,109 @@ dense_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     merge_block<D, LPR, EPL, NW>(st[hh], lds);
-    if (wave == 0 && lane < LPR) {
-      if (nsplit == 1) {
+    write_state<D, LPR, EPL>(st[hh], nsplit == 1, out + (row0 + hh) * D,
+                             partial + ((row0 + hh) * max_splits + split) * (D + 2));
+  }
+}
+
+// -------------------------------------------------------------- merge ----
+
+// One 1024-thread workgroup per (h, b) combines the per-split partials
+// (m, l, acc) of a row whose work spanned more than one split.  `unit` is the
+// rows (FAC: of min(budget, n)) or tokens (dense: of n) per split.  Every
+// split's partial is loaded at once (thread = split x 16 dims) and summed
+// through LDS, so the merge costs one memory round trip per 1024/(D/16)
+// splits instead of one per split.
+constexpr int kMergeThreads = 1024;
+
+template <int D>
+__global__ void __launch_bounds__(kMergeThreads)
+merge_kernel(const float* __restrict__ partial, int max_splits, const int32_t* __restrict__ nb,
+             int max_seq_len, int cap, int budget, int unit, int hq, float* __restrict__ out) {
+  constexpr int DPT = 16;                      // dims per thread
+  constexpr int TPS = D / DPT;                 // threads per split
+  constexpr int SPB = kMergeThreads / TPS;     // splits per pass
+  __shared__ float red[SPB][D + 1];
+  __shared__ float lred[SPB];
+  __shared__ float wmax[kMergeThreads / kWave];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const size_t row = (size_t)b * hq + h;
+  int n = nb[b];
+  if (n < 0 || n > max_seq_len || n > cap) n = 0;
+  const int work = (budget > 0 && budget < n) ? budget : n;
+  const int nsplit = (work + unit - 1) / unit;
+  if (nsplit <= 1) return;  // written directly by the split kernel
+  const float* p = partial + row * max_splits * (D + 2);
+  const int t = threadIdx.x;
+
+  float m = -INFINITY;
+  for (int s = t; s < nsplit; s += kMergeThreads) m = fmaxf(m, p[(size_t)s * (D + 2)]);
+  m = wave_max(m);
+  if ((t & (kWave - 1)) == 0) wmax[t / kWave] = m;
+  __syncthreads();
+  float M = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e)
-          out[(row0 + hh) * D + lane * EPL + e] = (st[hh].l > 0.0f) ? st[hh].a[e] / st[hh].l : 0.0f;
-      } else {
-        float* p = partial + ((row0 + hh) * max_splits + split) * (D + 2);
-        if (lane == 0) {
-          p[0] = st[hh].m;
-          p[1] = st[hh].l;
-        }
+  for (int w = 0; w < kMergeThreads / kWave; ++w) M = fmaxf(M, wmax[w]);
+
+  float A = 0.0f, L = 0.0f;
+  const int sl = t / TPS, dd = (t % TPS) * DPT;
+  for (int c0 = 0; c0 < nsplit; c0 += SPB) {
+    const int s = c0 + sl;
+    float v[DPT];
+    float l = 0.0f;
+    if (s < nsplit && M != -INFINITY) {
+      const float* q = p + (size_t)s * (D + 2);
+      const float w = expf(q[0] - M);
+      l = q[1] * w;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) p[2 + lane * EPL + e] = st[hh].a[e];
+      for (int i = 0; i < DPT; ++i) v[i] = q[2 + dd + i] * w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < DPT; ++i) v[i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) red[sl][dd + i] = v[i];
+    if (dd == 0) lred[sl] = l;
+    __syncthreads();
+    if (t < D) {
+      const int lim = min(SPB, nsplit - c0);
+      for (int r = 0; r < lim; ++r) {
+        A += red[r][t];
+        L += lred[r];
       }
     }
     __syncthreads();
   }
-  if (nsplit == 1) return;
-  if (!last_block_arrives(&tickets[((size_t)b * hkv + g) * kTicketsPerRow + 3], (uint32_t)nsplit,
-                          &flag))
-    return;
-#pragma unroll 1
-  for (int hh = 0; hh < G; ++hh)
-    merge_splits<D>(partial + (row0 + hh) * max_splits * (D + 2), nsplit, out + (row0 + hh) * D);
+  if (t < D) out[row * D + t] = (L > 0.0f) ? A / L : 0.0f;
 }
 
 // ------------------------------------------------------------ launchers --
 
+static void launch_merge(const fasa_ctx* c, const float* part, int max_splits, const int32_t* nb,
+                         int max_seq_len, int budget, int unit, float* out, hipStream_t s) {
+  dim3 grid((unsigned)c->hq, (unsigned)c->batch);
+  if (c->d == 128)
+    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, s, part, max_splits, nb,
+                       max_seq_len, c->cap, budget, unit, c->hq, out);
+  else
+    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeThreads), 0, s, part, max_splits, nb,
+                       max_seq_len, c->cap, budget, unit, c->hq, out);
+}
+
 hipError_t launch_fac(const fasa_ctx* c, const void* k_cache, const void* v_cache,
                       const int32_t* nb, int max_seq_len, const int32_t* idx, int budget,
                       float* out, uint8_t* ws, hipStream_t s) {
-  int take = budget < max_seq_len ? budget : max_seq_len;
+  const int take = budget < max_seq_len ? budget : max_seq_len;
   int splits = (take + kFacSplitRows - 1) / kFacSplitRows;
   if (splits < 1) splits = 1;
   dim3 grid((unsigned)splits, (unsigned)c->hq, (unsigned)c->batch);
   const float* qrot = reinterpret_cast<const float*>(ws + c->ws.qrot);
   float* part = reinterpret_cast<float*>(ws + c->ws.fac);
-  uint32_t* tickets = reinterpret_cast<uint32_t*>(ws + c->ws.ticket);
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
-#define FASA_FAC(BF, DD)                                                                     \
-  hipLaunchKernelGGL((fac_kernel<BF, DD>), grid, dim3(256), 0, s, k_cache, v_cache, qrot, nb, \
-                     max_seq_len, idx, budget, c->hq, c->hkv, c->G, c->cap, part,             \
-                     c->ws.fac_splits, tickets, out, err)
+#define FASA_FAC(BF, DD)                                                                      \
+  hipLaunchKernelGGL((fac_kernel<BF, DD>), grid, dim3(kFacThreads), 0, s, k_cache, v_cache, qrot, \
+                     nb, max_seq_len, idx, budget, c->hq, c->hkv, c->G, c->cap, part,          \
+                     c->ws.fac_splits, out, err)
   const bool bf = (c->dtype == FASA_BF16);
   if (c->d == 128) {
     if (bf) FASA_FAC(true, 128); else FASA_FAC(false, 128);
@@ -368,18 +290,19 @@ hipError_t launch_fac(const fasa_ctx* c, const void* k_cache, const void* v_cach
     if (bf) FASA_FAC(true, 64); else FASA_FAC(false, 64);
   }
 #undef FASA_FAC
+  if (splits > 1)
+    launch_merge(c, part, c->ws.fac_splits, nb, max_seq_len, budget, kFacSplitRows, out, s);
   return hipGetLastError();
 }
 
 template <bool BF, int DD>
 static void launch_dense_g(const fasa_ctx* c, dim3 grid, hipStream_t s, const void* k_cache,
                            const void* v_cache, const float* qrot, const int32_t* nb,
-                           int max_seq_len, float* part, uint32_t* tickets, float* out,
-                           uint32_t* err) {
-#define FASA_DENSE(GG)                                                                         \
-  hipLaunchKernelGGL((dense_kernel<BF, DD, GG>), grid, dim3(256), 0, s, k_cache, v_cache, qrot, \
-                     nb, max_seq_len, c->hq, c->hkv, c->cap, part, c->ws.dense_splits, tickets, \
-                     out, err)
+                           int max_seq_len, float* part, float* out, uint32_t* err) {
+#define FASA_DENSE(GG)                                                                          \
+  hipLaunchKernelGGL((dense_kernel<BF, DD, GG>), grid, dim3(kDenseThreads), 0, s, k_cache,       \
+                     v_cache, qrot, nb, max_seq_len, c->hq, c->hkv, c->cap, part,                \
+                     c->ws.dense_splits, out, err)
   switch (c->G) {
     case 1: FASA_DENSE(1); break;
     case 2: FASA_DENSE(2); break;
@@ -397,16 +320,17 @@ hipError_t launch_dense(const fasa_ctx* c, const void* k_cache, const void* v_ca
   dim3 grid((unsigned)splits, (unsigned)c->hkv, (unsigned)c->batch);
   const float* qrot = reinterpret_cast<const float*>(ws + c->ws.qrot);
   float* part = reinterpret_cast<float*>(ws + c->ws.dense);
-  uint32_t* tickets = reinterpret_cast<uint32_t*>(ws + c->ws.ticket);
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
   const bool bf = (c->dtype == FASA_BF16);
   if (c->d == 128) {
-    if (bf) launch_dense_g<true, 128>(c, grid, s, k_cache, v_cache, qrot, nb, max_seq_len, part, tickets, out, err);
-    else launch_dense_g<false, 128>(c, grid, s, k_cache, v_cache, qrot, nb, max_seq_len, part, tickets, out, err);
+    if (bf) launch_dense_g<true, 128>(c, grid, s, k_cache, v_cache, qrot, nb, max_seq_len, part, out, err);
+    else launch_dense_g<false, 128>(c, grid, s, k_cache, v_cache, qrot, nb, max_seq_len, part, out, err);
   } else {
-    if (bf) launch_dense_g<true, 64>(c, grid, s, k_cache, v_cache, qrot, nb, max_seq_len, part, tickets, out, err);
-    else launch_dense_g<false, 64>(c, grid, s, k_cache, v_cache, qrot, nb, max_seq_len, part, tickets, out, err);
+    if (bf) launch_dense_g<true, 64>(c, grid, s, k_cache, v_cache, qrot, nb, max_seq_len, part, out, err);
+    else launch_dense_g<false, 64>(c, grid, s, k_cache, v_cache, qrot, nb, max_seq_len, part, out, err);
   }
+  if (splits > 1)
+    launch_merge(c, part, c->ws.dense_splits, nb, max_seq_len, 0, kDenseSplitTokens, out, s);
   return hipGetLastError();
 }
 

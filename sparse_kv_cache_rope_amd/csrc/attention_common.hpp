@@ -1,0 +1,251 @@
+// Attention building blocks shared by the FAC, fused select+FAC and dense
+// kernels: row geometry, unpacking, per-lane online softmax and its merges.
+//
+// Row layout: a K or V row is d * sizeof(dtype) bytes (256 B for bf16 d=128);
+// LPR = row_bytes / 16 lanes each load 16 bytes of it, so a wave holds
+// RS = 64 / LPR rows at once.  A lane owns EPL = 16 / sizeof(dtype) dims of
+// q~ (pre-scaled by 1/sqrt(d)) and of the output accumulator.  Dot products
+// are summed across the LPR lanes of a row with DPP, each lane keeps a running
+// (max, sum, acc) over the rows it saw, and those are merged across row
+// slots and waves in LDS.
+#pragma once
+
+#include <math.h>
+
+#include "device_common.hpp"
+
+namespace fasa {
+
+template <bool BF16, int D>
+struct RowGeom {
+  static constexpr int ES = BF16 ? 2 : 4;
+  static constexpr int LPR = D * ES / 16;
+  static constexpr int EPL = 16 / ES;
+  static constexpr int RS = kWave / LPR;
+  static_assert(LPR >= 4 && LPR <= 32, "row must span 4..32 lanes");
+};
+
+template <bool BF16, int EPL>
+__device__ __forceinline__ void unpack(const uint4& x, float (&f)[EPL]) {
+  if constexpr (BF16) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(w[i]);
+      f[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+    f[0] = __uint_as_float(x.x);
+    f[1] = __uint_as_float(x.y);
+    f[2] = __uint_as_float(x.z);
+    f[3] = __uint_as_float(x.w);
+  }
+}
+
+// Online-softmax state of one lane.
+template <int EPL>
+struct Soft {
+  float m, l, a[EPL];
+  __device__ __forceinline__ void init() {
+    m = -INFINITY;
+    l = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) a[e] = 0.0f;
+  }
+  // Adds one row with logit z (-inf = absent) and values v.
+  __device__ __forceinline__ void add(float z, const float (&v)[EPL]) {
+    if (z == -INFINITY) return;
+    const float mn = fmaxf(m, z);
+    const float sc = expf(m - mn);  // m = -inf gives 0
+    const float p = expf(z - mn);
+    l = l * sc + p;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) a[e] = fmaf(p, v[e], a[e] * sc);
+    m = mn;
+  }
+  __device__ __forceinline__ void merge(float m2, float l2, const float (&a2)[EPL]) {
+    const float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) return;
+    const float s1 = expf(m - mn), s2 = expf(m2 - mn);
+    l = l * s1 + l2 * s2;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) a[e] = a[e] * s1 + a2[e] * s2;
+    m = mn;
+  }
+  __device__ __forceinline__ void merge_xor(int off) {
+    float a2[EPL];
+    const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) a2[e] = __shfl_xor(a[e], off);
+    merge(m2, l2, a2);
+  }
+};
+
+// Merges the row slots of each wave, then the NW waves through LDS; on return
+// wave 0 lanes 0..LPR-1 hold the workgroup's state.  `lds` needs
+// NW * (D + 2 * LPR) floats.  Ends with the LDS free for reuse.
+template <int D, int LPR, int EPL, int NW>
+__device__ __forceinline__ void merge_block(Soft<EPL>& st, float* lds) {
+#pragma unroll
+  for (int off = LPR; off < kWave; off <<= 1) st.merge_xor(off);
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  float* mine = lds + wave * (D + 2 * LPR);
+  if (lane < LPR) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) mine[lane * EPL + e] = st.a[e];
+    mine[D + lane] = st.m;
+    mine[D + LPR + lane] = st.l;
+  }
+  __syncthreads();
+  if (wave == 0 && lane < LPR) {
+    for (int w = 1; w < NW; ++w) {
+      const float* o = lds + w * (D + 2 * LPR);
+      float a2[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a2[e] = o[lane * EPL + e];
+      st.merge(o[D + lane], o[D + LPR + lane], a2);
+    }
+  }
+  __syncthreads();
+}
+
+// Wave 0 lanes < LPR write the workgroup's result: the normalised output when
+// it is the only split, else the partial (m, l, acc[D]).
+template <int D, int LPR, int EPL>
+__device__ __forceinline__ void write_state(const Soft<EPL>& st, bool only, float* out_row,
+                                            float* part) {
+  const int lane = threadIdx.x & (kWave - 1);
+  if (threadIdx.x >= kWave || lane >= LPR) return;
+  if (only) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) out_row[lane * EPL + e] = (st.l > 0.0f) ? st.a[e] / st.l : 0.0f;
+  } else {
+    if (lane == 0) {
+      part[0] = st.m;
+      part[1] = st.l;
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) part[2 + lane * EPL + e] = st.a[e];
+  }
+}
+
+}  // namespace fasa
+
+namespace fasa {
+
+// Final merge of NS per-lane-group softmax states through LDS in one parallel
+// step (no sequential state-by-state merging): every (wave, row slot) state
+// is written out, wave 0 forms the global max and the per-state weights, and
+// each output dim is a weighted sum over the states.  `scratch` needs
+// NS * (D + 3) + 1 + (blockDim.x / D) * D floats.  Writes out_row[0 .. D).
+template <int D, int LPR, int EPL, int NS>
+__device__ __forceinline__ void merge_states_lds(const Soft<EPL>& st, int state, float* scratch,
+                                                 float* __restrict__ out_row) {
+  float* A = scratch;          // [NS][D]
+  float* Mv = A + NS * D;      // [NS]
+  float* Lv = Mv + NS;         // [NS]
+  float* W = Lv + NS;          // [NS]
+  float* tot = W + NS;         // [1]
+  const int lane = threadIdx.x & (kWave - 1);
+  const int sub = lane % LPR;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) A[state * D + sub * EPL + e] = st.a[e];
+  if (sub == 0) {
+    Mv[state] = st.m;
+    Lv[state] = st.l;
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    float m = -INFINITY;
+    for (int s = lane; s < NS; s += kWave) m = fmaxf(m, Mv[s]);
+    m = wave_max(m);
+    float l = 0.0f;
+    for (int s = lane; s < NS; s += kWave) {
+      const float w = (m == -INFINITY) ? 0.0f : expf(Mv[s] - m);
+      W[s] = w;
+      l = fmaf(Lv[s], w, l);
+    }
+    l = group_sum<kWave>(l);
+    if (lane == 0) tot[0] = l;
+  }
+  __syncthreads();
+  // Each dim's weighted sum over the NS states, split over all threads: part
+  // p of dim d covers states p, p + P, ...; the parts meet in LDS.
+  const float L = tot[0];
+  const int nthreads = blockDim.x;
+  const int parts = nthreads >= 2 * D ? nthreads / D : 1;
+  float* part_sum = W + NS + 1;  // [parts][D]
+  if (threadIdx.x < parts * D) {
+    const int d = threadIdx.x % D, p = threadIdx.x / D;
+    float acc = 0.0f;
+    for (int s = p; s < NS; s += parts) acc = fmaf(A[s * D + d], W[s], acc);
+    part_sum[p * D + d] = acc;
+  }
+  __syncthreads();
+  for (int d = threadIdx.x; d < D; d += nthreads) {
+    float acc = 0.0f;
+    for (int p = 0; p < parts; ++p) acc += part_sum[p * D + d];
+    out_row[d] = (L > 0.0f) ? acc / L : 0.0f;
+  }
+}
+
+}  // namespace fasa
+
+namespace fasa {
+
+// FAC of query head `row` over the cache rows sel[0 .. take) (sel in LDS),
+// NW waves: softmax(q~ . K[j] / sqrt(d)) weighted sum of V[j].  `scratch`
+// is LDS for the state merge (NW * RS * (D + 3) + 1 + NW * 64 floats).
+template <bool BF16, int D, int NW>
+__device__ void attend_rows(const int32_t* sel, int take, const void* __restrict__ k_cache,
+                            const void* __restrict__ v_cache, const float* __restrict__ qrot,
+                            size_t row, size_t kvbase, float* __restrict__ out_row,
+                            float* scratch) {
+  using Geo = RowGeom<BF16, D>;
+  constexpr int LPR = Geo::LPR, EPL = Geo::EPL, RS = Geo::RS;
+  constexpr int BATCH = 4;
+  constexpr int PER_BATCH = BATCH * RS * NW;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int slot = lane / LPR, sub = lane % LPR;
+  const float scale = 1.0f / sqrtf((float)D);
+  float qv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qv[e] = qrot[row * D + sub * EPL + e] * scale;
+  const uint4* K = static_cast<const uint4*>(k_cache);
+  const uint4* V = static_cast<const uint4*>(v_cache);
+  Soft<EPL> st;
+  st.init();
+  for (int r0 = 0; r0 < take; r0 += PER_BATCH) {
+    int jr[BATCH];
+    uint4 kc[BATCH], vc[BATCH];
+#pragma unroll
+    for (int it = 0; it < BATCH; ++it) {
+      const int r = r0 + it * RS * NW + wave * RS + slot;
+      jr[it] = (r < take) ? sel[r] : -1;
+      if (jr[it] >= 0) {
+        const size_t off = (kvbase + jr[it]) * LPR + sub;
+        kc[it] = K[off];
+        vc[it] = V[off];
+      } else {
+        kc[it] = make_uint4(0, 0, 0, 0);
+        vc[it] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < BATCH; ++it) {
+      float kf[EPL], vf[EPL];
+      unpack<BF16, EPL>(kc[it], kf);
+      float z = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) z = fmaf(qv[e], kf[e], z);
+      z = group_sum<LPR>(z);
+      unpack<BF16, EPL>(vc[it], vf);
+      st.add(jr[it] >= 0 ? z : -INFINITY, vf);
+    }
+  }
+  __syncthreads();  // scratch may alias LDS the caller read above
+  merge_states_lds<D, LPR, EPL, NW * RS>(st, wave * RS + slot, scratch, out_row);
+}
+
+}  // namespace fasa
+

@@ -8,27 +8,13 @@ namespace fasa {
 
 constexpr int kWave = 64;
 
-// Top-B selection geometry: a row of scores is cut into chunks of kChunk
-// tokens; the first radix digit is the top kHistBits of the 32-bit key.
+// First radix digit of the top-B select: the top kHistBits of the key.
 constexpr int kHistBits = 11;
 constexpr int kHistBins = 1 << kHistBits;
-constexpr int kChunk = 4096;
-constexpr int kChunkThreads = 256;
-constexpr int kPerThread = kChunk / kChunkThreads;  // 16 consecutive tokens
-constexpr int kMaxChunks = 1024;                    // rows up to 4M tokens
 
-// Tickets per row: S1 (histogram), S2 (candidates), FAC merge, dense merge.
-constexpr int kTicketsPerRow = 4;
-
-// Per-(b, h) selection state; lives in the workspace.
-struct RowState {
-  uint32_t digit1;      // top-kHistBits digit of the threshold key
-  uint32_t need;        // tokens still to take from that digit's bin
-  uint32_t cand_count;  // candidates gathered in the bin
-  uint32_t pad0;
-  uint64_t tau;         // composite threshold: selected <=> composite >= tau
-  uint64_t pad1;
-};
+// Largest cache capacity (positions must fit the composite's 32-bit field and
+// the grids' int arithmetic with room to spare).
+constexpr int kMaxCapacity = 1 << 24;
 
 // ---- bf16 <-> fp32 / fp64 ------------------------------------------------
 
@@ -135,40 +121,6 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* l
   __syncthreads();
   *total = all;
   return before + inc - v;
-}
-
-// Device-scope atomics used for cross-workgroup hand-offs.
-__device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t atomic_xchg_agent(uint32_t* p, uint32_t v) {
-  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t atomic_load_agent(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void atomic_store_agent(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// "Last workgroup" hand-off: every thread publishes its writes, one thread
-// takes a ticket; returns true in every thread of the workgroup that arrived
-// last (ticket == expected - 1), after an acquire.  The last one resets the
-// ticket to 0.  `flag` is one LDS word.
-__device__ __forceinline__ bool last_block_arrives(uint32_t* ticket, uint32_t expected,
-                                                   uint32_t* flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    bool last = (t == expected - 1u);
-    if (last) atomic_store_agent(ticket, 0u);
-    *flag = last ? 1u : 0u;
-  }
-  __syncthreads();
-  bool last = (*flag != 0u);
-  if (last) __threadfence();
-  return last;
 }
 
 __device__ __forceinline__ void raise_flag(uint32_t* err, uint32_t bit) {

@@ -21,24 +21,19 @@ struct DeviceTables {
 
 // Byte offsets of the workspace regions (each 256-byte aligned).
 struct WsLayout {
-  size_t err = 0;       // uint32 [4]
+  size_t err = 0;       // uint32 [4]: device error flag
   size_t nb = 0;        // int32 [b]: tokens attended by the current call
   size_t qrot = 0;      // float [b][Hq][d]: rotated queries
   size_t tipw = 0;      // float [b][P][G][2]: TIP weights per sidecar plane
   size_t scores = 0;    // float [b][Hq][cap]
-  size_t hist = 0;      // uint32 [b*Hq][kHistBins]
-  size_t ticket = 0;    // uint32 [b*Hq][kTicketsPerRow]
-  size_t rowst = 0;     // RowState [b*Hq]
-  size_t cand = 0;      // uint64 [b*Hq][cap]
-  size_t chunk_gt = 0;  // uint32 [b*Hq][max_chunks]
-  size_t chunk_off = 0; // uint32 [b*Hq][max_chunks]
   size_t idx = 0;       // int32 [b][Hq][max_budget]
+  size_t cand = 0;      // uint64 [b*Hq][cand_stride]: two-stage top-B candidates
   size_t fac = 0;       // float [b*Hq][fac_splits][d + 2]
   size_t dense = 0;     // float [b*Hq][dense_splits][d + 2]
   size_t total = 0;
-  int max_chunks = 0;
   int fac_splits = 0;
   int dense_splits = 0;
+  int cand_stride = 0;
 };
 
 }  // namespace fasa
@@ -55,13 +50,23 @@ struct fasa_ctx {
   void* dev_alloc;
   fasa::DeviceTables tab;
   fasa::WsLayout ws;
+  // Event timing (fasa_timing_enable / fasa_timing_collect).
+  bool timing = false;
+  std::vector<hipEvent_t> ev;     // pairs: ev[2i] start, ev[2i+1] stop
+  std::vector<int> ev_family;     // family of each recorded pair
+  int ev_used = 0;
 };
 
 namespace fasa {
 
 // Rows of a FAC split and tokens of a dense split (one workgroup each).
-constexpr int kFacSplitRows = 64;
-constexpr int kDenseSplitTokens = 256;
+constexpr int kFacSplitRows = 256;
+constexpr int kDenseSplitTokens = 512;
+// Largest budget the fused select + FAC kernels keep in LDS.
+constexpr int kFusedMaxBudget = 1024;
+// Two-stage top-B: chunk size and the most candidates the second stage takes.
+constexpr int kTwoStageChunk = 4096;
+constexpr int kTwoStageMaxCand = 8192;
 
 // Modes of the query-rotation prologue.
 enum PrologueMode : int {
@@ -100,6 +105,17 @@ hipError_t launch_fac(const fasa_ctx* c, const void* k_cache, const void* v_cach
 hipError_t launch_dense(const fasa_ctx* c, const void* k_cache, const void* v_cache,
                         const int32_t* nb, int max_seq_len, float* out, uint8_t* ws,
                         hipStream_t s);
+// Top-B selection fused with FAC (budget <= kFusedMaxBudget): one workgroup
+// per (h, b) selects and attends; idx may be null.
+hipError_t launch_select_attend(const fasa_ctx* c, const float* scores, const int32_t* nb,
+                                int max_seq_len, int budget, int32_t* idx, const void* k_cache,
+                                const void* v_cache, float* out, uint8_t* ws, hipStream_t s);
+// Two-stage top-B (when two_stage_applies(max_seq_len, budget)), fused with
+// FAC when `out` is given (then k_cache / v_cache too); idx may be null then.
+bool two_stage_applies(int max_seq_len, int budget);
+hipError_t launch_two_stage(const fasa_ctx* c, const float* scores, const int32_t* nb,
+                            int max_seq_len, int budget, int32_t* idx, const void* k_cache,
+                            const void* v_cache, float* out, uint8_t* ws, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace fasa

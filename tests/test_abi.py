@@ -16,7 +16,7 @@ LIB = os.path.join(ROOT, "sparse_kv_cache_rope_amd", "libfasa.so")
 @pytest.fixture(scope="module")
 def fasa():
     if not os.path.exists(LIB):
-        subprocess.run([sys.executable, "-m", "sparse_kv_cache_rope_amd.build"], cwd=ROOT,
+        subprocess.run([sys.executable, os.path.join(ROOT, "sparse_kv_cache_rope_amd", "build.py")], cwd=ROOT,
                        check=True, capture_output=True)
     import sparse_kv_cache_rope_amd as m
     return m

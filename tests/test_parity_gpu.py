@@ -119,6 +119,13 @@ TOPK_CASES = [
     ("normal", 2, 131072, 1024, False),
     ("normal", 1, 32831, 6193, False),
     ("normal", 2, 4097, 1, False),
+    # Two-stage path (chunks of 4096): ties across chunk edges, a last chunk
+    # shorter than B, one exactly B long, and the largest candidate count.
+    ("ties", 2, 20000, 1024, False),
+    ("normal", 2, 4096 * 2 + 5, 256, False),
+    ("planted", 2, 4096 * 3 + 256, 256, False),
+    ("normal", 2, 32768, 256, True),
+    ("wide", 1, 8 * 4096, 1024, False),
 ]
 
 
