@@ -16,8 +16,8 @@ HIP graph of L steps; inputs are resident in HBM before timing starts.
 
 Printed: one JSON line with the metric (context tokens scanned per second),
 the fraction of HBM peak on the algorithmic bytes, the dominant kernel's
-roofline figure (TIP: sidecar bytes / its average duration from HIP events
-bracketing each launch), the in-build dense decode comparator and the CPU
+roofline figure (TIP: sidecar bytes read + score bytes written / its average
+duration from HIP events bracketing each launch), the in-build dense decode comparator and the CPU
 oracle baseline on a bounded sample.
 """
 
@@ -199,11 +199,13 @@ def main():
     ctx.timing_enable(False)
     kernel_ms = {f: ms / n for f, (ms, n) in fams.items() if n}
 
-    # Algorithmic bytes: sidecar bytes TIP reads + B * 2 * d * s per query head.
+    # Algorithmic bytes: TIP reads the sidecar pairs (P planes x 2 elements per
+    # token) and writes one fp32 score per query head and token; FAC reads
+    # B * 2 * d elements per query head.
     es = 2 if w.dtype == "bf16" else 4
     off, _ = ctx.sidecar_layout()
     P = int(off[-1])
-    tip_bytes = int(sum(P * n * 2 * es for n in n_b))
+    tip_bytes = int(sum((P * 2 * es + w.n_q_heads * 4) * n for n in n_b))
     fac_bytes = int(sum(min(w.budget, n) * 2 * w.head_dim * es * w.n_q_heads for n in n_b))
     algo_bytes = tip_bytes + fac_bytes
     dense_bytes = int(sum(2 * n * w.head_dim * es * w.n_kv_heads for n in n_b))

@@ -57,7 +57,6 @@ void build_layout(fasa_ctx* c) {
   w.err = take(16);
   w.nb = take(sizeof(int32_t) * c->batch);
   w.qrot = take(sizeof(float) * rows * c->d);
-  w.tipw = take(sizeof(float) * c->batch * (size_t)c->P * c->G * 2);
   w.scores = take(sizeof(float) * rows * c->cap);
   w.idx = take(sizeof(int32_t) * rows * c->max_budget);
   {
@@ -145,6 +144,8 @@ fasa_status fasa_create(fasa_ctx** out, int batch, int n_q_heads, int n_kv_heads
     return fail(FASA_ERR_INVALID_ARG, "n_q_heads %d not a multiple of n_kv_heads %d", n_q_heads,
                 n_kv_heads);
   const int G = n_q_heads / n_kv_heads;
+  if (n_kv_heads > kArgKvHeads)
+    return fail(FASA_ERR_UNSUPPORTED, "n_kv_heads %d above %d", n_kv_heads, kArgKvHeads);
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(FASA_ERR_UNSUPPORTED, "query heads per KV head %d not in {1,2,4,8}", G);
   if (head_dim != 64 && head_dim != 128)
@@ -317,16 +318,11 @@ fasa_status fasa_tip_scores(fasa_ctx* c, const void* sidecar, const void* q,
   FASA_NONNULL(scores);
   FASA_NONNULL(workspace);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  PrologueArgs a{q, nullptr, nullptr, nullptr, nullptr, nullptr, seq_lens, max_seq_len};
-  {
-    Timed t(c, FASA_K_PROLOGUE, stream);
-    FASA_HIP(launch_prologue(c, kPrologueQueryOnly, a, ws, stream), "fasa_tip_scores: prologue");
-  }
+  TipArgs a{const_cast<void*>(sidecar), q, nullptr, nullptr, nullptr, nullptr, seq_lens,
+            max_seq_len};
   {
     Timed t(c, FASA_K_TIP, stream);
-    FASA_HIP(launch_tip(c, sidecar, reinterpret_cast<const int32_t*>(ws + c->ws.nb), max_seq_len,
-                        scores, nullptr, ws, stream),
-             "fasa_tip_scores");
+    FASA_HIP(launch_tip(c, kPrologueQueryOnly, a, scores, ws, stream), "fasa_tip_scores");
   }
   return ok();
 }
@@ -346,10 +342,10 @@ fasa_status fasa_topk(fasa_ctx* c, const float* scores, const int32_t* seq_lens,
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     if (two_stage_applies(max_seq_len, budget))
       FASA_HIP(launch_two_stage(c, scores, seq_lens, max_seq_len, budget, idx, nullptr, nullptr,
-                                nullptr, ws, stream),
+                                nullptr, nullptr, ws, stream),
                "fasa_topk: two-stage");
     else
-      FASA_HIP(launch_topk(c, scores, seq_lens, max_seq_len, budget, idx, ws, stream),
+      FASA_HIP(launch_topk(c, scores, seq_lens, max_seq_len, budget, idx, nullptr, ws, stream),
                "fasa_topk");
   }
   return ok();
@@ -368,10 +364,9 @@ fasa_status fasa_sparse_attn(fasa_ctx* c, const void* k_cache, const void* v_cac
   FASA_NONNULL(out);
   FASA_NONNULL(workspace);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  PrologueArgs a{q, nullptr, nullptr, nullptr, nullptr, nullptr, seq_lens, c->cap};
   {
     Timed t(c, FASA_K_PROLOGUE, stream);
-    FASA_HIP(launch_prologue(c, kPrologueQueryOnly, a, ws, stream), "fasa_sparse_attn: prologue");
+    FASA_HIP(launch_prologue(c, q, seq_lens, c->cap, ws, stream), "fasa_sparse_attn: prologue");
   }
   {
     Timed t(c, FASA_K_FAC, stream);
@@ -404,22 +399,18 @@ fasa_status fasa_decode_step(fasa_ctx* c, void* k_cache, void* v_cache, void* si
   const int32_t* nb = reinterpret_cast<const int32_t*>(ws + c->ws.nb);
   float* scores = reinterpret_cast<float*>(ws + c->ws.scores);
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + c->ws.idx);
-  PrologueArgs a{q, k_new, v_new, k_cache, v_cache, sidecar, seq_lens, max_seq_len};
+  int32_t* advance = (flags & FASA_ADVANCE_SEQ_LENS) ? seq_lens : nullptr;
+  TipArgs a{sidecar, q, k_new, v_new, k_cache, v_cache, seq_lens, max_seq_len};
   {
-    Timed t(c, FASA_K_PROLOGUE, stream);
-    FASA_HIP(launch_prologue(c, kPrologueDecode, a, ws, stream), "fasa_decode_step: append");
-  }
-  {
+    // Append, query rotation and TIP in one launch.
     Timed t(c, FASA_K_TIP, stream);
-    FASA_HIP(launch_tip(c, sidecar, nb, max_seq_len, scores,
-                        (flags & FASA_ADVANCE_SEQ_LENS) ? seq_lens : nullptr, ws, stream),
-             "fasa_decode_step: tip");
+    FASA_HIP(launch_tip(c, kPrologueDecode, a, scores, ws, stream), "fasa_decode_step: tip");
   }
   if (two_stage_applies(max_seq_len, budget)) {
     // Chunk-local top-B, then the row's top-B fused with FAC.
     Timed t(c, FASA_K_SELECT_FAC, stream);
     FASA_HIP(launch_two_stage(c, scores, nb, max_seq_len, budget, idx_out, k_cache, v_cache,
-                              out, ws, stream),
+                              out, advance, ws, stream),
              "fasa_decode_step: two-stage select+fac");
     return ok();
   }
@@ -427,13 +418,13 @@ fasa_status fasa_decode_step(fasa_ctx* c, void* k_cache, void* v_cache, void* si
     // Selection and FAC in one kernel: the selected rows never leave LDS.
     Timed t(c, FASA_K_SELECT_FAC, stream);
     FASA_HIP(launch_select_attend(c, scores, nb, max_seq_len, budget, idx_out, k_cache, v_cache,
-                                  out, ws, stream),
+                                  out, advance, ws, stream),
              "fasa_decode_step: select+fac");
     return ok();
   }
   {
     Timed t(c, FASA_K_TOPK, stream);
-    FASA_HIP(launch_topk(c, scores, nb, max_seq_len, budget, idx, ws, stream),
+    FASA_HIP(launch_topk(c, scores, nb, max_seq_len, budget, idx, advance, ws, stream),
              "fasa_decode_step: topk");
   }
   {
@@ -456,10 +447,9 @@ fasa_status fasa_dense_attn(fasa_ctx* c, const void* k_cache, const void* v_cach
   FASA_NONNULL(out);
   FASA_NONNULL(workspace);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  PrologueArgs a{q, nullptr, nullptr, nullptr, nullptr, nullptr, seq_lens, max_seq_len};
   {
     Timed t(c, FASA_K_PROLOGUE, stream);
-    FASA_HIP(launch_prologue(c, kPrologueQueryOnly, a, ws, stream), "fasa_dense_attn: prologue");
+    FASA_HIP(launch_prologue(c, q, seq_lens, max_seq_len, ws, stream), "fasa_dense_attn: prologue");
   }
   {
     Timed t(c, FASA_K_DENSE, stream);

@@ -6,6 +6,10 @@
 
 namespace fasa {
 
+// Word 3 of a raw buffer resource on gfx950 (32-bit dwords, no swizzle):
+// out-of-range lanes of a buffer load read zero and fetch nothing.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 constexpr int kWave = 64;
 
 // First radix digit of the top-B select: the top kHistBits of the key.

@@ -24,7 +24,6 @@ struct WsLayout {
   size_t err = 0;       // uint32 [4]: device error flag
   size_t nb = 0;        // int32 [b]: tokens attended by the current call
   size_t qrot = 0;      // float [b][Hq][d]: rotated queries
-  size_t tipw = 0;      // float [b][P][G][2]: TIP weights per sidecar plane
   size_t scores = 0;    // float [b][Hq][cap]
   size_t idx = 0;       // int32 [b][Hq][max_budget]
   size_t cand = 0;      // uint64 [b*Hq][cand_stride]: two-stage top-B candidates
@@ -68,19 +67,25 @@ constexpr int kFusedMaxBudget = 1024;
 constexpr int kTwoStageChunk = 4096;
 constexpr int kTwoStageMaxCand = 8192;
 
-// Modes of the query-rotation prologue.
+// How a launch reads seq_lens.
 enum PrologueMode : int {
   kPrologueQueryOnly = 0,  // seq_lens = n_b; rotate q at n_b - 1
   kPrologueDecode = 1      // seq_lens = cached tokens; append at that position first
 };
 
-struct PrologueArgs {
+// Most KV heads whose sidecar plane offsets travel as a kernel argument.
+constexpr int kArgKvHeads = 128;
+struct PlaneOffsets {
+  int32_t off[kArgKvHeads + 1];
+};
+
+struct TipArgs {
+  void* sidecar;
   const void* q;
   const void* k_new;  // decode mode only
   const void* v_new;
   void* k_cache;
   void* v_cache;
-  void* sidecar;
   const int32_t* seq_lens;
   int max_seq_len;
 };
@@ -91,14 +96,19 @@ struct PrologueArgs {
 hipError_t launch_append(const fasa_ctx* c, void* k_cache, void* v_cache, void* sidecar,
                          const void* k_new, const void* v_new, const int32_t* start_pos,
                          int n_new, uint8_t* ws, hipStream_t s);
-// Writes ws.nb, ws.qrot and ws.tipw (and, in decode mode, appends the token).
-hipError_t launch_prologue(const fasa_ctx* c, PrologueMode mode, const PrologueArgs& a,
-                           uint8_t* ws, hipStream_t s);
-hipError_t launch_tip(const fasa_ctx* c, const void* sidecar, const int32_t* nb,
-                      int max_seq_len, float* scores, int32_t* advance_seq_lens,
+// Query-only mode: writes ws.nb and ws.qrot (queries rotated to n_b - 1).
+hipError_t launch_prologue(const fasa_ctx* c, const void* q, const int32_t* seq_lens,
+                           int max_seq_len, uint8_t* ws, hipStream_t s);
+// TIP scores with the step's prologue fused in: writes ws.nb, ws.qrot and
+// scores; in decode mode also appends the step's token.  Never writes
+// seq_lens (see `advance` below).
+hipError_t launch_tip(const fasa_ctx* c, PrologueMode mode, const TipArgs& a, float* scores,
                       uint8_t* ws, hipStream_t s);
+// The launchers below that take `advance` (may be null) store n_b into
+// advance[b] from a kernel that reads only ws.nb, so it can be seq_lens.
 hipError_t launch_topk(const fasa_ctx* c, const float* scores, const int32_t* nb,
-                       int max_seq_len, int budget, int32_t* idx, uint8_t* ws, hipStream_t s);
+                       int max_seq_len, int budget, int32_t* idx, int32_t* advance, uint8_t* ws,
+                       hipStream_t s);
 hipError_t launch_fac(const fasa_ctx* c, const void* k_cache, const void* v_cache,
                       const int32_t* nb, int max_seq_len, const int32_t* idx, int budget,
                       float* out, uint8_t* ws, hipStream_t s);
@@ -109,13 +119,15 @@ hipError_t launch_dense(const fasa_ctx* c, const void* k_cache, const void* v_ca
 // per (h, b) selects and attends; idx may be null.
 hipError_t launch_select_attend(const fasa_ctx* c, const float* scores, const int32_t* nb,
                                 int max_seq_len, int budget, int32_t* idx, const void* k_cache,
-                                const void* v_cache, float* out, uint8_t* ws, hipStream_t s);
+                                const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
+                                hipStream_t s);
 // Two-stage top-B (when two_stage_applies(max_seq_len, budget)), fused with
 // FAC when `out` is given (then k_cache / v_cache too); idx may be null then.
 bool two_stage_applies(int max_seq_len, int budget);
 hipError_t launch_two_stage(const fasa_ctx* c, const float* scores, const int32_t* nb,
                             int max_seq_len, int budget, int32_t* idx, const void* k_cache,
-                            const void* v_cache, float* out, uint8_t* ws, hipStream_t s);
+                            const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
+                            hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace fasa

@@ -1,4 +1,4 @@
-// KV append with RoPE + FC-packed key sidecar, and the per-step query prologue.
+// KV append with RoPE + FC-packed key sidecar, and the query-only prologue.
 //
 // RoPE splits a head vector into 2-D frequency chunks (FCs), one angular
 // frequency each ("FASA: Frequency-aware Sparse Attention", gist.science/pt,
@@ -47,66 +47,39 @@ append_kernel(const void* __restrict__ k_new, const void* __restrict__ v_new,
                   (size_t)b * P + plane_off[g], fc_slot[g * C + c], c, C, cap, pos, omega[c]);
 }
 
-// Per-step prologue, one workgroup per (KV head g, sequence b), G * C threads.
-// Decode mode: append the step's token at position seq_lens[b] first.
-// Both modes: rotate the group's queries to position n_b - 1 (fp64 angle,
-// kept in fp32) and write the TIP weights of the group's sidecar planes:
-// for plane u holding FC c and query head h, (q~_c, q~_{c+C}) when c is
-// dominant for h, zeros otherwise.
+// Query prologue of the entry points that take no TIP pass, one workgroup per
+// (KV head g, sequence b), G * C threads: validate n_b = seq_lens[b] and
+// rotate the group's queries to position n_b - 1 (fp64 angle, kept in fp32).
 template <bool BF16>
 __global__ void __launch_bounds__(512)
-prologue_kernel(int mode, const void* __restrict__ q, const void* __restrict__ k_new,
-                const void* __restrict__ v_new, void* __restrict__ k_cache,
-                void* __restrict__ v_cache, void* __restrict__ sidecar,
-                const int32_t* __restrict__ seq_lens, int max_seq_len, int hq, int hkv, int G,
-                int cap, int d, int P, const int32_t* __restrict__ plane_off,
-                const int32_t* __restrict__ fc_slot, const uint64_t* __restrict__ dom_mask,
+prologue_kernel(const void* __restrict__ q, const int32_t* __restrict__ seq_lens,
+                int max_seq_len, int hq, int G, int cap, int d,
                 const double* __restrict__ omega, int32_t* __restrict__ nb_out,
-                float* __restrict__ qrot, float* __restrict__ tipw, uint32_t* err) {
+                float* __restrict__ qrot, uint32_t* err) {
   using T = typename CacheT<BF16>::T;
   const int C = d / 2;
   const int g = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x;
-  const int v = seq_lens[b];
-  const int n = (mode == kPrologueDecode) ? v + 1 : v;
-  const bool empty = (mode == kPrologueQueryOnly && v == 0);
-  const bool ok = v >= 0 && n >= 1 && n <= max_seq_len && n <= cap;
+  const int n = seq_lens[b];
+  const bool ok = n >= 1 && n <= max_seq_len && n <= cap;
   if (!ok) {
     if (g == 0 && tid == 0) {
       nb_out[b] = 0;
-      if (!empty) raise_flag(err, FASA_DEVFLAG_SEQ_LEN);
+      if (n != 0) raise_flag(err, FASA_DEVFLAG_SEQ_LEN);
     }
     return;
   }
   if (g == 0 && tid == 0) nb_out[b] = n;
   const long pos = n - 1;
   const int hh = tid / C, c = tid % C;
-
-  if (mode == kPrologueDecode && hh == 0) {
-    const size_t src = ((size_t)b * hkv + g) * d;
-    const size_t dst = (((size_t)b * hkv + g) * cap + pos) * d;
-    append_fc<BF16>(static_cast<const T*>(k_new) + src, static_cast<const T*>(v_new) + src,
-                    static_cast<T*>(k_cache) + dst, static_cast<T*>(v_cache) + dst, sidecar,
-                    (size_t)b * P + plane_off[g], fc_slot[g * C + c], c, C, cap, pos, omega[c]);
-  }
-
   const int h = g * G + hh;
   const T* qs = static_cast<const T*>(q) + ((size_t)b * hq + h) * d;
   const double x0 = load_elem(qs, c), x1 = load_elem(qs, c + C);
   double sn, cs;
   sincos((double)pos * omega[c], &sn, &cs);
-  const float y0 = (float)(x0 * cs - x1 * sn);
-  const float y1 = (float)(x1 * cs + x0 * sn);
   float* qr = qrot + ((size_t)b * hq + h) * d;
-  qr[c] = y0;
-  qr[c + C] = y1;
-  const int slot = fc_slot[g * C + c];
-  if (slot >= 0) {
-    const bool dominant = (dom_mask[h] >> c) & 1ull;
-    float* w = tipw + (((size_t)b * P + plane_off[g] + slot) * G + hh) * 2;
-    w[0] = dominant ? y0 : 0.0f;
-    w[1] = dominant ? y1 : 0.0f;
-  }
+  qr[c] = (float)(x0 * cs - x1 * sn);
+  qr[c + C] = (float)(x1 * cs + x0 * sn);
 }
 
 __global__ void fill_zero_kernel(uint4* __restrict__ p, size_t n16, uint8_t* __restrict__ tail,
@@ -147,24 +120,19 @@ hipError_t launch_append(const fasa_ctx* c, void* k_cache, void* v_cache, void* 
   return hipGetLastError();
 }
 
-hipError_t launch_prologue(const fasa_ctx* c, PrologueMode mode, const PrologueArgs& a,
-                           uint8_t* ws, hipStream_t s) {
+hipError_t launch_prologue(const fasa_ctx* c, const void* q, const int32_t* seq_lens,
+                           int max_seq_len, uint8_t* ws, hipStream_t s) {
   dim3 grid((unsigned)c->hkv, (unsigned)c->batch);
   dim3 block((unsigned)(c->G * c->C));
   int32_t* nb = reinterpret_cast<int32_t*>(ws + c->ws.nb);
   float* qrot = reinterpret_cast<float*>(ws + c->ws.qrot);
-  float* tipw = reinterpret_cast<float*>(ws + c->ws.tipw);
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
   if (c->dtype == FASA_BF16)
-    hipLaunchKernelGGL(prologue_kernel<true>, grid, block, 0, s, (int)mode, a.q, a.k_new, a.v_new,
-                       a.k_cache, a.v_cache, a.sidecar, a.seq_lens, a.max_seq_len, c->hq, c->hkv,
-                       c->G, c->cap, c->d, c->P, c->tab.plane_off, c->tab.fc_slot,
-                       c->tab.dom_mask, c->tab.omega, nb, qrot, tipw, err);
+    hipLaunchKernelGGL(prologue_kernel<true>, grid, block, 0, s, q, seq_lens, max_seq_len, c->hq,
+                       c->G, c->cap, c->d, c->tab.omega, nb, qrot, err);
   else
-    hipLaunchKernelGGL(prologue_kernel<false>, grid, block, 0, s, (int)mode, a.q, a.k_new,
-                       a.v_new, a.k_cache, a.v_cache, a.sidecar, a.seq_lens, a.max_seq_len,
-                       c->hq, c->hkv, c->G, c->cap, c->d, c->P, c->tab.plane_off,
-                       c->tab.fc_slot, c->tab.dom_mask, c->tab.omega, nb, qrot, tipw, err);
+    hipLaunchKernelGGL(prologue_kernel<false>, grid, block, 0, s, q, seq_lens, max_seq_len, c->hq,
+                       c->G, c->cap, c->d, c->tab.omega, nb, qrot, err);
   return hipGetLastError();
 }
 

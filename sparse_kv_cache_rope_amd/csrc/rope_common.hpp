@@ -26,20 +26,21 @@ __device__ __forceinline__ double load_elem(const uint16_t* p, size_t i) {
   return (double)bf16_bits_to_f32(p[i]);
 }
 __device__ __forceinline__ double load_elem(const float* p, size_t i) { return (double)p[i]; }
+__device__ __forceinline__ double to_f64(uint16_t bits) { return (double)bf16_bits_to_f32(bits); }
+__device__ __forceinline__ double to_f64(float x) { return (double)x; }
 
-// Rotates FC c of one key row at `pos`, stores K (and V) columns c, c + C and,
-// when FC c is in the KV head's union, its sidecar pair.
+// Rotates FC c = (x0, x1) of one key row by the angle whose sine and cosine
+// are given, stores K (and V) columns c, c + C and, when FC c is in the KV
+// head's union (slot >= 0), its sidecar pair.  Returns the bit patterns of the
+// stored pair (bf16: one packed word in .x; fp32: the two floats).
 template <bool BF16>
-__device__ __forceinline__ void append_fc(const typename CacheT<BF16>::T* __restrict__ ksrc,
-                                          const typename CacheT<BF16>::T* __restrict__ vsrc,
-                                          typename CacheT<BF16>::T* __restrict__ kdst,
-                                          typename CacheT<BF16>::T* __restrict__ vdst,
-                                          void* __restrict__ sidecar, size_t plane_base,
-                                          int slot, int c, int C, int cap, long pos,
-                                          double omega) {
-  const double x0 = load_elem(ksrc, c), x1 = load_elem(ksrc, c + C);
-  double sn, cs;
-  sincos((double)pos * omega, &sn, &cs);
+__device__ __forceinline__ uint2 store_rotated_fc(double x0, double x1,
+                                                  const typename CacheT<BF16>::T* __restrict__ vsrc,
+                                                  typename CacheT<BF16>::T* __restrict__ kdst,
+                                                  typename CacheT<BF16>::T* __restrict__ vdst,
+                                                  void* __restrict__ sidecar, size_t plane_base,
+                                                  int slot, int c, int C, int cap, long pos,
+                                                  double sn, double cs) {
   const double y0 = x0 * cs - x1 * sn;
   const double y1 = x1 * cs + x0 * sn;
   vdst[c] = vsrc[c];
@@ -48,15 +49,30 @@ __device__ __forceinline__ void append_fc(const typename CacheT<BF16>::T* __rest
     const uint16_t k0 = f64_to_bf16_rne(y0), k1 = f64_to_bf16_rne(y1);
     kdst[c] = k0;
     kdst[c + C] = k1;
-    if (slot >= 0)
-      static_cast<uint32_t*>(sidecar)[(plane_base + slot) * cap + pos] =
-          (uint32_t)k0 | ((uint32_t)k1 << 16);
+    const uint32_t pair = (uint32_t)k0 | ((uint32_t)k1 << 16);
+    if (slot >= 0) static_cast<uint32_t*>(sidecar)[(plane_base + slot) * cap + pos] = pair;
+    return make_uint2(pair, 0u);
   } else {
     const float k0 = (float)y0, k1 = (float)y1;
     kdst[c] = k0;
     kdst[c + C] = k1;
     if (slot >= 0) static_cast<float2*>(sidecar)[(plane_base + slot) * cap + pos] = make_float2(k0, k1);
+    return make_uint2(__float_as_uint(k0), __float_as_uint(k1));
   }
+}
+
+// store_rotated_fc at the RoPE angle of FC c at position pos (fp64).
+template <bool BF16>
+__device__ __forceinline__ void append_fc(const typename CacheT<BF16>::T* __restrict__ ksrc,
+                                          const typename CacheT<BF16>::T* __restrict__ vsrc,
+                                          typename CacheT<BF16>::T* __restrict__ kdst,
+                                          typename CacheT<BF16>::T* __restrict__ vdst,
+                                          void* __restrict__ sidecar, size_t plane_base,
+                                          int slot, int c, int C, int cap, long pos,
+                                          double omega) {
+  double sn, cs;
+  sincos((double)pos * omega, &sn, &cs);
+  store_rotated_fc<BF16>(load_elem(ksrc, c), load_elem(ksrc, c + C), vsrc, kdst, vdst, sidecar, plane_base, slot, c, C, cap, pos, sn, cs);
 }
 
 }  // namespace fasa

@@ -119,11 +119,12 @@ final_select_kernel(const float* __restrict__ scores, const int32_t* __restrict_
                     const uint64_t* __restrict__ cand, int cand_stride, int32_t* __restrict__ idx,
                     const void* __restrict__ k_cache, const void* __restrict__ v_cache,
                     const float* __restrict__ qrot, int hkv, int G, float* __restrict__ out,
-                    uint32_t* err) {
+                    int32_t* __restrict__ advance, uint32_t* err) {
   __shared__ FinalLds L;
   const int h = blockIdx.x, b = blockIdx.y;
   const size_t row = (size_t)b * hq + h;
   const int n = checked_len(nb, b, max_seq_len, cap, err, h == 0 && threadIdx.x == 0);
+  if (advance != nullptr && h == 0 && threadIdx.x == 0 && n > 0) advance[b] = n;
   const int t = threadIdx.x;
   int32_t* o = idx ? idx + row * budget : nullptr;
   const int take = n < budget ? n : budget;
@@ -218,15 +219,16 @@ template <bool ATT, bool BF, int DD>
 static void launch_final(const fasa_ctx* c, hipStream_t s, const float* scores, const int32_t* nb,
                          int max_seq_len, int budget, const uint64_t* cand, int stride,
                          int32_t* idx, const void* k, const void* v, const float* qrot, float* out,
-                         uint32_t* err) {
+                         int32_t* advance, uint32_t* err) {
   hipLaunchKernelGGL((final_select_kernel<ATT, BF, DD>), dim3((unsigned)c->hq, (unsigned)c->batch),
                      dim3(kFinalThreads), 0, s, scores, nb, max_seq_len, c->hq, c->cap, budget,
-                     cand, stride, idx, k, v, qrot, c->hkv, c->G, out, err);
+                     cand, stride, idx, k, v, qrot, c->hkv, c->G, out, advance, err);
 }
 
 hipError_t launch_two_stage(const fasa_ctx* c, const float* scores, const int32_t* nb,
                             int max_seq_len, int budget, int32_t* idx, const void* k_cache,
-                            const void* v_cache, float* out, uint8_t* ws, hipStream_t s) {
+                            const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
+                            hipStream_t s) {
   if (!two_stage_applies(max_seq_len, budget)) return hipErrorInvalidValue;
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
   const float* qrot = reinterpret_cast<const float*>(ws + c->ws.qrot);
@@ -239,16 +241,16 @@ hipError_t launch_two_stage(const fasa_ctx* c, const float* scores, const int32_
                        cand, stride);
   if (out == nullptr) {
     launch_final<false, true, 128>(c, s, scores, nb, max_seq_len, budget, cand, stride, idx,
-                                   nullptr, nullptr, nullptr, nullptr, err);
+                                   nullptr, nullptr, nullptr, nullptr, advance, err);
     return hipGetLastError();
   }
   const bool bf = (c->dtype == FASA_BF16);
   if (c->d == 128) {
-    if (bf) launch_final<true, true, 128>(c, s, scores, nb, max_seq_len, budget, cand, stride, idx, k_cache, v_cache, qrot, out, err);
-    else launch_final<true, false, 128>(c, s, scores, nb, max_seq_len, budget, cand, stride, idx, k_cache, v_cache, qrot, out, err);
+    if (bf) launch_final<true, true, 128>(c, s, scores, nb, max_seq_len, budget, cand, stride, idx, k_cache, v_cache, qrot, out, advance, err);
+    else launch_final<true, false, 128>(c, s, scores, nb, max_seq_len, budget, cand, stride, idx, k_cache, v_cache, qrot, out, advance, err);
   } else {
-    if (bf) launch_final<true, true, 64>(c, s, scores, nb, max_seq_len, budget, cand, stride, idx, k_cache, v_cache, qrot, out, err);
-    else launch_final<true, false, 64>(c, s, scores, nb, max_seq_len, budget, cand, stride, idx, k_cache, v_cache, qrot, out, err);
+    if (bf) launch_final<true, true, 64>(c, s, scores, nb, max_seq_len, budget, cand, stride, idx, k_cache, v_cache, qrot, out, advance, err);
+    else launch_final<true, false, 64>(c, s, scores, nb, max_seq_len, budget, cand, stride, idx, k_cache, v_cache, qrot, out, advance, err);
   }
   return hipGetLastError();
 }

@@ -386,11 +386,12 @@ select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ nb, 
               int hq, int cap, int budget, int32_t* __restrict__ idx,
               const void* __restrict__ k_cache, const void* __restrict__ v_cache,
               const float* __restrict__ qrot, int hkv, int G, float* __restrict__ out,
-              uint32_t* err) {
+              int32_t* __restrict__ advance, uint32_t* err) {
   __shared__ SelectLds L;
   const int h = blockIdx.x, b = blockIdx.y;
   const size_t row = (size_t)b * hq + h;
   const int n = checked_len(nb, b, max_seq_len, cap, err, h == 0 && threadIdx.x == 0);
+  if (advance != nullptr && h == 0 && threadIdx.x == 0 && n > 0) advance[b] = n;
   int32_t* o = idx ? idx + row * budget : nullptr;
   const int take = n < budget ? n : budget;
   if (n <= budget) {
@@ -417,17 +418,18 @@ select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ nb, 
 }
 
 hipError_t launch_topk(const fasa_ctx* c, const float* scores, const int32_t* nb,
-                       int max_seq_len, int budget, int32_t* idx, uint8_t* ws, hipStream_t s) {
+                       int max_seq_len, int budget, int32_t* idx, int32_t* advance, uint8_t* ws,
+                       hipStream_t s) {
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
   dim3 grid((unsigned)c->hq, (unsigned)c->batch);
   if (kUseCachedKeys && max_seq_len <= kCachedRow)
     hipLaunchKernelGGL((select_kernel<true, false, true, 128>), grid, dim3(kSelThreads), 0, s,
                        scores, nb, max_seq_len, c->hq, c->cap, budget, idx, nullptr, nullptr,
-                       nullptr, c->hkv, c->G, nullptr, err);
+                       nullptr, c->hkv, c->G, nullptr, advance, err);
   else
     hipLaunchKernelGGL((select_kernel<false, false, true, 128>), grid, dim3(kSelThreads), 0, s,
                        scores, nb, max_seq_len, c->hq, c->cap, budget, idx, nullptr, nullptr,
-                       nullptr, c->hkv, c->G, nullptr, err);
+                       nullptr, c->hkv, c->G, nullptr, advance, err);
   return hipGetLastError();
 }
 
@@ -435,20 +437,21 @@ template <bool BF, int DD>
 static void launch_sel_att(const fasa_ctx* c, dim3 grid, hipStream_t s, bool cached,
                            const float* scores, const int32_t* nb, int max_seq_len, int budget,
                            int32_t* idx, const void* k, const void* v, const float* qrot,
-                           float* out, uint32_t* err) {
+                           float* out, int32_t* advance, uint32_t* err) {
   if (cached)
     hipLaunchKernelGGL((select_kernel<true, true, BF, DD>), grid, dim3(kSelThreads), 0, s, scores,
                        nb, max_seq_len, c->hq, c->cap, budget, idx, k, v, qrot, c->hkv, c->G,
-                       out, err);
+                       out, advance, err);
   else
     hipLaunchKernelGGL((select_kernel<false, true, BF, DD>), grid, dim3(kSelThreads), 0, s, scores,
                        nb, max_seq_len, c->hq, c->cap, budget, idx, k, v, qrot, c->hkv, c->G,
-                       out, err);
+                       out, advance, err);
 }
 
 hipError_t launch_select_attend(const fasa_ctx* c, const float* scores, const int32_t* nb,
                                 int max_seq_len, int budget, int32_t* idx, const void* k_cache,
-                                const void* v_cache, float* out, uint8_t* ws, hipStream_t s) {
+                                const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
+                                hipStream_t s) {
   if (budget > kFusedMaxBudget) return hipErrorInvalidValue;
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
   const float* qrot = reinterpret_cast<const float*>(ws + c->ws.qrot);
@@ -456,11 +459,11 @@ hipError_t launch_select_attend(const fasa_ctx* c, const float* scores, const in
   const bool cached = kUseCachedKeys && max_seq_len <= kCachedRow;
   const bool bf = (c->dtype == FASA_BF16);
   if (c->d == 128) {
-    if (bf) launch_sel_att<true, 128>(c, grid, s, cached, scores, nb, max_seq_len, budget, idx, k_cache, v_cache, qrot, out, err);
-    else launch_sel_att<false, 128>(c, grid, s, cached, scores, nb, max_seq_len, budget, idx, k_cache, v_cache, qrot, out, err);
+    if (bf) launch_sel_att<true, 128>(c, grid, s, cached, scores, nb, max_seq_len, budget, idx, k_cache, v_cache, qrot, out, advance, err);
+    else launch_sel_att<false, 128>(c, grid, s, cached, scores, nb, max_seq_len, budget, idx, k_cache, v_cache, qrot, out, advance, err);
   } else {
-    if (bf) launch_sel_att<true, 64>(c, grid, s, cached, scores, nb, max_seq_len, budget, idx, k_cache, v_cache, qrot, out, err);
-    else launch_sel_att<false, 64>(c, grid, s, cached, scores, nb, max_seq_len, budget, idx, k_cache, v_cache, qrot, out, err);
+    if (bf) launch_sel_att<true, 64>(c, grid, s, cached, scores, nb, max_seq_len, budget, idx, k_cache, v_cache, qrot, out, advance, err);
+    else launch_sel_att<false, 64>(c, grid, s, cached, scores, nb, max_seq_len, budget, idx, k_cache, v_cache, qrot, out, advance, err);
   }
   return hipGetLastError();
 }
