@@ -82,8 +82,9 @@ typedef enum { FASA_F32 = 0, FASA_BF16 = 1 } fasa_dtype;
  *   indices I_dom of each query head (gist.science/pt, "Resumo Tecnico"
  *   section 2, TIP "Calibracao Offline"), each in [0, C), distinct per head.
  *   Copied; the caller keeps ownership.
- * Limits: head_dim 64 or 128; G in {1, 2, 4, 8}; capacity a positive multiple
- *   of 64; 1 <= n_dom <= C; 1 <= max_budget <= capacity.
+ * Limits: head_dim 64 or 128; G in {1, 2, 4, 8}; n_kv_heads <= 128
+ *   (FASA_ERR_UNSUPPORTED above); capacity a positive multiple of 64, at most
+ *   2^24; 1 <= n_dom <= C; 1 <= max_budget <= capacity.
  * Allocates the constant tables on the current HIP device (the device every
  * later call must run on).  *out is NULL on failure.
  */
@@ -211,8 +212,9 @@ fasa_status fasa_check(fasa_ctx* ctx, void* workspace, hipStream_t stream, uint3
  */
 typedef enum {
   FASA_K_APPEND = 0,    /* bulk append kernel */
-  FASA_K_PROLOGUE = 1,  /* per-step append + query rotation + TIP weights */
-  FASA_K_TIP = 2,       /* TIP scoring over the sidecar */
+  FASA_K_PROLOGUE = 1,  /* query rotation of fasa_sparse_attn / fasa_dense_attn */
+  FASA_K_TIP = 2,       /* TIP scoring over the sidecar, with the step's query
+                           rotation and (fasa_decode_step) token append fused in */
   FASA_K_TOPK = 3,      /* the three top-B kernels together */
   FASA_K_FAC = 4,       /* sparse attention */
   FASA_K_DENSE = 5,     /* dense comparator */

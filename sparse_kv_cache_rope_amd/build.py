@@ -27,6 +27,9 @@ FLAGS = [
     # No packed-fp32 instructions in device code (the host pass warns that it
     # does not know the feature; that is harmless).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # The hardware loads the first 16 dwords of kernel arguments into SGPRs
+    # at wave launch, so a kernel's first loads need not wait for them.
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -10,6 +10,15 @@ namespace fasa {
 // out-of-range lanes of a buffer load read zero and fetch nothing.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
+// A pointer into global memory (address space 1): loads through it are
+// global_load, never flat_load.
+template <typename T>
+using global_ptr = __attribute__((address_space(1))) T*;
+template <typename T>
+__device__ __forceinline__ global_ptr<T> to_global(T* p) {
+  return (global_ptr<T>)p;
+}
+
 constexpr int kWave = 64;
 
 // First radix digit of the top-B select: the top kHistBits of the key.

@@ -38,15 +38,18 @@ constexpr int kTipThreads = kTipWaves * kWave;
 constexpr int kTipTokens = kWave * 4;  // tokens per workgroup
 constexpr int kMaxPlanes = 64;         // d/2 FCs at d = 128
 
+// The arguments needed first lead the list: the build preloads the first 16
+// dwords of kernel arguments into registers, which saves a dependent load
+// before the stream starts.
 template <bool BF16, int G, int D>
 __global__ void __launch_bounds__(kTipThreads)
-tip_kernel(int mode, PlaneOffsets po, void* sidecar, const void* __restrict__ q,
-           const void* __restrict__ k_new, const void* __restrict__ v_new,
-           void* __restrict__ k_cache, void* __restrict__ v_cache,
-           const int32_t* __restrict__ seq_lens, int max_seq_len, int hq, int hkv, int cap, int P,
-           const int32_t* __restrict__ fc_slot, const uint64_t* __restrict__ dom_mask,
-           const double* __restrict__ omega, int32_t* __restrict__ nb_out,
-           float* __restrict__ qrot, float* __restrict__ scores, uint32_t* err) {
+tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int max_seq_len,
+           int cap, int P, int hq, int hkv, const void* __restrict__ q,
+           const double* __restrict__ omega, const int32_t* __restrict__ fc_slot,
+           const uint64_t* __restrict__ dom_mask, const void* __restrict__ k_new,
+           const void* __restrict__ v_new, void* __restrict__ k_cache,
+           void* __restrict__ v_cache, int32_t* __restrict__ nb_out, float* __restrict__ qrot,
+           float* __restrict__ scores, uint32_t* err, PlaneOffsets po) {
   using T = typename CacheT<BF16>::T;
   constexpr int C = D / 2;
   constexpr int PW = kMaxPlanes / kTipWaves;  // planes per wave, at most
@@ -60,8 +63,21 @@ tip_kernel(int mode, PlaneOffsets po, void* sidecar, const void* __restrict__ q,
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int tile0 = tile * kTipTokens;
   const int j0 = tile0 + lane * 4;
-  const int p0 = po.off[g];
-  const int U = po.off[g + 1] - p0;
+
+  // The length, the plane offsets and the argument pointers used before the
+  // stream are independent scalar loads: joining them in one (empty) asm
+  // makes all of them issue before any is waited on.
+  int v = seq_lens[b];
+  int p0 = po.off[g];
+  int p1 = po.off[g + 1];
+  asm volatile("" : "+s"(v), "+s"(p0), "+s"(p1), "+s"(fc_slot), "+s"(dom_mask), "+s"(k_new),
+               "+s"(nb_out));
+  // The asm hides that these point to global memory; say it again so that
+  // loads through them stay global (not flat) loads.
+  const global_ptr<const int32_t> fc_slot_g = to_global(fc_slot);
+  const global_ptr<const uint64_t> dom_mask_g = to_global(dom_mask);
+  const global_ptr<const T> k_new_g = to_global(static_cast<const T*>(k_new));
+  const int U = p1 - p0;
   const size_t plane0 = (size_t)b * P + p0;
 
   // Query elements and tables of this thread's (head, FC) pairs, and the
@@ -81,18 +97,18 @@ tip_kernel(int mode, PlaneOffsets po, void* sidecar, const void* __restrict__ q,
     qr0[r] = qs[c];
     qr1[r] = qs[c + C];
     om[r] = omega[c];
-    slot[r] = fc_slot[g * C + c];
-    dmask[r] = dom_mask[g * G + hh];
+    slot[r] = fc_slot_g[g * C + c];
+    dmask[r] = dom_mask_g[g * G + hh];
   }
   // Query-only launches have no key row (k_new may be null): they read the
   // same (unused) indexes of q instead, which holds b * Hq * d >= b * Hkv * d
   // elements.
   const size_t kv_src = ((size_t)b * hkv + g) * D;
-  const T* ksrc = static_cast<const T*>(mode == kPrologueDecode ? k_new : q);
+  const global_ptr<const T> ksrc =
+      (mode == kPrologueDecode) ? k_new_g : to_global(static_cast<const T*>(q));
   const T kr0 = ksrc[kv_src + tid % C];
   const T kr1 = ksrc[kv_src + tid % C + C];
 
-  const int v = seq_lens[b];
   const int n = (mode == kPrologueDecode) ? v + 1 : v;
   const bool ok = v >= 0 && n >= 1 && n <= max_seq_len && n <= cap;
   const bool lead = (tile == 0 && g == 0 && tid == 0);
@@ -255,10 +271,10 @@ template <bool BF16, int G, int D>
 static void launch_tip_t(dim3 grid, hipStream_t s, int mode, const PlaneOffsets& po,
                          const TipArgs& a, const fasa_ctx* c, int32_t* nb, float* qrot,
                          float* scores, uint32_t* err) {
-  hipLaunchKernelGGL((tip_kernel<BF16, G, D>), grid, dim3(kTipThreads), 0, s, mode, po,
-                     a.sidecar, a.q, a.k_new, a.v_new, a.k_cache, a.v_cache, a.seq_lens,
-                     a.max_seq_len, c->hq, c->hkv, c->cap, c->P, c->tab.fc_slot, c->tab.dom_mask,
-                     c->tab.omega, nb, qrot, scores, err);
+  hipLaunchKernelGGL((tip_kernel<BF16, G, D>), grid, dim3(kTipThreads), 0, s, a.seq_lens,
+                     a.sidecar, mode, a.max_seq_len, c->cap, c->P, c->hq, c->hkv, a.q,
+                     c->tab.omega, c->tab.fc_slot, c->tab.dom_mask, a.k_new, a.v_new, a.k_cache,
+                     a.v_cache, nb, qrot, scores, err, po);
 }
 
 template <int G>
