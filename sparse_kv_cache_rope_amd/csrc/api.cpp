@@ -60,9 +60,11 @@ void build_layout(fasa_ctx* c) {
   w.scores = take(sizeof(float) * rows * c->cap);
   w.idx = take(sizeof(int32_t) * rows * c->max_budget);
   {
-    const int nch = (c->cap + kTwoStageChunk - 1) / kTwoStageChunk;
-    const int per = c->max_budget < kTwoStageChunk / 2 ? c->max_budget : kTwoStageChunk / 2;
-    const int need = nch * per < kTwoStageMaxCand ? nch * per : kTwoStageMaxCand;
+    // Chunk candidates of the longest row (chunks of 4096 positions or more;
+    // the select never takes more than kTwoStageMaxCand).
+    const long long nch = (c->cap + 4095) / 4096;
+    const long long all = nch * c->max_budget;
+    const int need = all < kTwoStageMaxCand ? (int)all : kTwoStageMaxCand;
     w.cand_stride = (need + 3) & ~3;  // rows start 32-byte aligned
     w.cand = take(sizeof(uint64_t) * rows * w.cand_stride);
   }
@@ -340,10 +342,10 @@ fasa_status fasa_topk(fasa_ctx* c, const float* scores, const int32_t* seq_lens,
   {
     Timed t(c, FASA_K_TOPK, stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    if (two_stage_applies(max_seq_len, budget))
-      FASA_HIP(launch_two_stage(c, scores, seq_lens, max_seq_len, budget, idx, nullptr, nullptr,
-                                nullptr, nullptr, ws, stream),
-               "fasa_topk: two-stage");
+    if (select_path_applies(max_seq_len, budget))
+      FASA_HIP(launch_select(c, scores, seq_lens, max_seq_len, budget, idx, nullptr, nullptr,
+                             nullptr, nullptr, ws, stream),
+               "fasa_topk: row select");
     else
       FASA_HIP(launch_topk(c, scores, seq_lens, max_seq_len, budget, idx, nullptr, ws, stream),
                "fasa_topk");
@@ -406,12 +408,27 @@ fasa_status fasa_decode_step(fasa_ctx* c, void* k_cache, void* v_cache, void* si
     Timed t(c, FASA_K_TIP, stream);
     FASA_HIP(launch_tip(c, kPrologueDecode, a, scores, ws, stream), "fasa_decode_step: tip");
   }
-  if (two_stage_applies(max_seq_len, budget)) {
-    // Chunk-local top-B, then the row's top-B fused with FAC.
-    Timed t(c, FASA_K_SELECT_FAC, stream);
-    FASA_HIP(launch_two_stage(c, scores, nb, max_seq_len, budget, idx_out, k_cache, v_cache,
-                              out, advance, ws, stream),
-             "fasa_decode_step: two-stage select+fac");
+  if (select_path_applies(max_seq_len, budget)) {
+    if (budget <= kFusedMaxBudget) {
+      // Selection and FAC in one workgroup per row: the selected rows never
+      // leave LDS.
+      Timed t(c, FASA_K_SELECT_FAC, stream);
+      FASA_HIP(launch_select(c, scores, nb, max_seq_len, budget, idx_out, k_cache, v_cache, out,
+                             advance, ws, stream),
+               "fasa_decode_step: select+fac");
+      return ok();
+    }
+    {
+      Timed t(c, FASA_K_TOPK, stream);
+      FASA_HIP(launch_select(c, scores, nb, max_seq_len, budget, idx, nullptr, nullptr, nullptr,
+                             advance, ws, stream),
+               "fasa_decode_step: select");
+    }
+    {
+      Timed t(c, FASA_K_FAC, stream);
+      FASA_HIP(launch_fac(c, k_cache, v_cache, nb, max_seq_len, idx, budget, out, ws, stream),
+               "fasa_decode_step: fac");
+    }
     return ok();
   }
   if (budget <= kFusedMaxBudget) {

@@ -197,7 +197,7 @@ namespace fasa {
 // NW waves: softmax(q~ . K[j] / sqrt(d)) weighted sum of V[j].  `scratch`
 // is LDS for the state merge (NW * RS * (D + 3) + 1 + NW * 64 floats).
 template <bool BF16, int D, int NW>
-__device__ void attend_rows(const int32_t* sel, int take, const void* __restrict__ k_cache,
+__device__ __forceinline__ void attend_rows(const int32_t* sel, int take, const void* __restrict__ k_cache,
                             const void* __restrict__ v_cache, const float* __restrict__ qrot,
                             size_t row, size_t kvbase, float* __restrict__ out_row,
                             float* scratch) {

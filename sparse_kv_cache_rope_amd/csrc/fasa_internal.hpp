@@ -63,9 +63,10 @@ constexpr int kFacSplitRows = 256;
 constexpr int kDenseSplitTokens = 512;
 // Largest budget the fused select + FAC kernels keep in LDS.
 constexpr int kFusedMaxBudget = 1024;
-// Two-stage top-B: chunk size and the most candidates the second stage takes.
-constexpr int kTwoStageChunk = 4096;
-constexpr int kTwoStageMaxCand = 8192;
+// Row select (select2.hip): positions per chunk of a long row (at most), and
+// the most chunk candidates the final selection takes.
+constexpr int kSelectChunk = 16384;
+constexpr int kTwoStageMaxCand = 16384;
 
 // How a launch reads seq_lens.
 enum PrologueMode : int {
@@ -121,13 +122,16 @@ hipError_t launch_select_attend(const fasa_ctx* c, const float* scores, const in
                                 int max_seq_len, int budget, int32_t* idx, const void* k_cache,
                                 const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
                                 hipStream_t s);
-// Two-stage top-B (when two_stage_applies(max_seq_len, budget)), fused with
-// FAC when `out` is given (then k_cache / v_cache too); idx may be null then.
-bool two_stage_applies(int max_seq_len, int budget);
-hipError_t launch_two_stage(const fasa_ctx* c, const float* scores, const int32_t* nb,
-                            int max_seq_len, int budget, int32_t* idx, const void* k_cache,
-                            const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
-                            hipStream_t s);
+// Register-resident top-B (when select_path_applies(max_seq_len, budget)):
+// rows up to kSelectChunk positions in one workgroup each, longer rows in
+// chunks of kSelectChunk then their candidates.  Fused with FAC when `out` is
+// given (then budget <= kFusedMaxBudget and k_cache / v_cache too); idx may be
+// null then.
+bool select_path_applies(int max_seq_len, int budget);
+hipError_t launch_select(const fasa_ctx* c, const float* scores, const int32_t* nb,
+                         int max_seq_len, int budget, int32_t* idx, const void* k_cache,
+                         const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
+                         hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace fasa

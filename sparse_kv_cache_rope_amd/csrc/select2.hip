@@ -1,25 +1,21 @@
-// Two-stage top-B selection with FAC fused into the second stage.
+// Top-B selection of the critical token set, fused with FAC when B is small.
 //
 // "FASA: Frequency-aware Sparse Attention", gist.science/pt, "Resumo Tecnico"
 // section 2, FAC bullets: select the critical token set T_t from the TIP
-// scores, then run full attention over T_t only.  Same selection as the
-// one-stage kernels (topk.hip): the min(B, n) highest scores, equal scores to
-// the lower position, ascending; exact radix select on 64-bit composites
-// (select_common.hpp).
+// scores, then run full attention over T_t only.  Selection: the min(B, n)
+// highest scores of each (sequence, query head) row, equal scores to the
+// lower position, listed ascending; exact, by range refinement over 64-bit
+// composites (select_common.hpp).
 //
-// A single workgroup cannot stream a 32k-token row of scores quickly enough
-// (each dependent pass costs a memory round trip), and workgroups of one
-// row must not wait on each other (device-wide hand-offs are expensive on a
-// multi-die GPU).  So the row is cut into chunks of 4096 positions:
-//   stage 1 (chunk_select_kernel): one 1024-thread workgroup per chunk keeps
-//     the chunk's scores in registers (4 per thread, one round trip) and
-//     writes the chunk's own top-B composites, ascending.  The row's top B
-//     are among these candidates.
-//   stage 2 (final_select_kernel): one 1024-thread workgroup per row loads
-//     all candidates at once (<= 8192, ascending across chunks), selects the
-//     row's top B among them, writes idx, keeps the positions in LDS and runs
-//     FAC over them.
-// A row of at most one chunk skips stage 1: stage 2 reads its scores directly.
+// A row of up to 8192 positions (or up to 16384 when chunking cannot reduce
+// it) is held whole in the registers of one 512-thread workgroup (one round
+// of coalesced loads), selected there, and, for B <= 1024, attended in the
+// same workgroup: one launch after TIP.  No workgroup ever waits on another
+// (device-wide hand-offs are expensive on a multi-die GPU).
+//
+// Longer rows are cut into chunks: chunk_select_kernel writes each chunk's
+// own top-B composites (the row's top B are among them), and
+// row_select_kernel then selects among those candidates (at most 16384).
 
 #include "attention_common.hpp"
 #include "fasa_internal.hpp"
@@ -27,100 +23,172 @@
 
 namespace fasa {
 
-// Many waves with few elements each: a wave's instructions form a dependent
-// chain, so the work per wave, not the thread count, sets the latency.
-constexpr int kChunkThreads = 1024;
-constexpr int kChunkE = kTwoStageChunk / kChunkThreads;  // 4 scores per thread
-constexpr int kFinalThreads = 1024;
-constexpr int kFinalE = kTwoStageMaxCand / kFinalThreads;  // 8 candidates per thread
+// 8 waves (2 per SIMD) with up to 32 elements each: every wave repeats the
+// fixed work of a pass (scans, picks), so fewer waves with more elements
+// finish a pass sooner than 16 waves with fewer, and 2 waves per SIMD leave
+// 256 VGPRs each, enough to hold 32 keys or composites without spilling.
+constexpr int kRowThreads = 512;
+constexpr int kMaxE = 32;  // scores per thread, at most
+static_assert(kSelectChunk == kRowThreads * kMaxE, "the longest chunk is one workgroup's registers");
+static_assert(kTwoStageMaxCand <= kRowThreads * kMaxE, "candidates fit one workgroup");
+constexpr int kHistCopiesSel = 4;
+constexpr int kCandCapSel = 4096;
 
-using ChunkLds = RegSelectLds<kChunkThreads, 8, 1024>;
+template <int NT>
+using SelLds = RegSelectLds<NT, kHistCopiesSel, kCandCapSel>;
 
-struct FinalLds {
-  RegSelectLds<kFinalThreads, 8, 4096> s;
+// LDS the fused FAC needs for its state merge (attend_rows), worst case over
+// the head sizes and dtypes built (bf16, d = 64: 128 states of 64 dims).
+constexpr int kAttendScratch = 9728;
+
+template <int NT>
+struct RowLds {
+  union {
+    SelLds<NT> s;
+    float att[kAttendScratch];
+  };
   int32_t sel[kFusedMaxBudget];
 };
 
-__device__ __forceinline__ int chunks_of(int n) { return (n + kTwoStageChunk - 1) / kTwoStageChunk; }
-
-// Candidates stage 1 leaves for a row of n > budget positions.
-__device__ __forceinline__ int candidates_of(int n, int budget) {
-  const int nch = chunks_of(n);
-  const int last = n - (nch - 1) * kTwoStageChunk;
-  return (nch - 1) * budget + (last < budget ? last : budget);
+// Candidates the chunk stage leaves for a row of n positions in chunks of
+// `chunk`: min(B, chunk) per full chunk, min(B, rest) for the last.
+__device__ __forceinline__ int candidates_of(int n, int budget, int chunk) {
+  const int nch = (n + chunk - 1) / chunk;
+  const int last = n - (nch - 1) * chunk;
+  return (nch - 1) * (budget < chunk ? budget : chunk) + (last < budget ? last : budget);
 }
 
-__global__ void __launch_bounds__(kChunkThreads)
+// Scores of one row segment held in registers: element e of thread t is
+// position first + 4 * 1024 * (e / 4) + (e % 4), first = segment + 4 t
+// (coalesced float4 slabs).  Only keys are kept (0 for a position past the
+// segment, at least 1 otherwise); positions follow from the indexes.
+template <int E, int NT = kRowThreads>
+struct ScoreSrc {
+  uint32_t k[E];
+  int first;  // position of element 0 of this thread
+  __device__ __forceinline__ int pos(int e) const {
+    return first + (e / 4) * 4 * NT + (e & 3);
+  }
+  __device__ __forceinline__ uint32_t key(int e) const { return k[e]; }
+  __device__ __forceinline__ uint32_t low(int e) const { return 0xffffffffu - (uint32_t)pos(e); }
+};
+
+// Candidate composites held in registers as their two halves (key 0 where
+// there is none); same slab layout as ScoreSrc.
+template <int E, int NT = kRowThreads>
+struct CandSrc {
+  uint32_t hi[E], lo[E];
+  __device__ __forceinline__ uint32_t key(int e) const { return hi[e]; }
+  __device__ __forceinline__ uint32_t low(int e) const { return lo[e]; }
+};
+
+// Loads positions [seg, seg + cn) of a row's scores as E keys per thread with
+// range-limited buffer loads: quads past cn read zeros (and get key 0), so no
+// load waits behind a branch.  Keys of real positions are raised to at least
+// 1, which only merges the two lowest keys (NaN patterns below every number).
+template <int E, int NT>
+__device__ __forceinline__ void load_scores(ScoreSrc<E, NT>& src, const float* row_scores,
+                                            int seg, int cn) {
+  const int t = threadIdx.x;
+  // The resource must be wave-uniform (SGPRs); say so.
+  const uint64_t base = (uint64_t)(row_scores + seg);
+  const uint32_t blo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+  const uint32_t bhi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
+  const int range = __builtin_amdgcn_readfirstlane(((cn + 3) & ~3) * 4);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void*>(((uint64_t)bhi << 32) | blo), (short)0, range, kBufferRsrcWord3);
+  float4 v[E / 4];
+#pragma unroll
+  for (int g = 0; g < E / 4; ++g) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(
+        rs, (uint32_t)(4 * (g * NT + t)) * 4u, 0, 0);
+    v[g] = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
+                       __uint_as_float(x[3]));
+  }
+  src.first = seg + 4 * t;
+  const int lim = cn - 4 * t;  // element e is valid when (e / 4) * 4096 + e % 4 < lim
+#pragma unroll
+  for (int g = 0; g < E / 4; ++g) {
+    const float f[4] = {v[g].x, v[g].y, v[g].z, v[g].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t k = score_key(f[e]);
+      src.k[4 * g + e] = (g * 4 * NT + e < lim) ? (k ? k : 1u) : 0u;
+    }
+  }
+}
+
+// Selected elements (composite >= tau, tau >= 2^32) in ascending position
+// order: calls f(rank, element) for the first `limit` of them.  One barrier.
+template <int E, int NT, class Src, class LdsT, class F>
+__device__ __forceinline__ void emit_ordered(const Src& src, uint64_t tau, uint32_t limit,
+                                             LdsT& L, F f) {
+  uint32_t m4[E / 4], off[E / 4];
+#pragma unroll
+  for (int g = 0; g < E / 4; ++g) {
+    m4[g] = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m4[g] |= (is_selected(src, 4 * g + e, tau) ? 1u : 0u) << e;
+  }
+  ordered_offsets<NT>(m4, off, L);
+#pragma unroll
+  for (int g = 0; g < E / 4; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((m4[g] >> e) & 1u) {
+        if (off[g] < limit) f(off[g], 4 * g + e);
+        ++off[g];
+      }
+}
+
+// Stage 1 for rows of several chunks (E * 1024 positions each): the chunk's
+// own top-B composites, ascending, at cand[row][chunk * min(B, chunk) ...].
+// The row's top B are among them.
+template <int E, int NT>
+__global__ void __launch_bounds__(NT)
 chunk_select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ nb,
                     int max_seq_len, int hq, int cap, int budget, uint64_t* __restrict__ cand,
                     int cand_stride) {
-  __shared__ ChunkLds L;
+  constexpr int kChunk = E * NT;
+  __shared__ RegSelectLds<NT, kHistCopiesSel, kCandCapSel> L;
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t row = (size_t)b * hq + h;
   int n = nb[b];
   if (n < 0 || n > max_seq_len || n > cap) n = 0;
-  const int nch = chunks_of(n);
-  if (n <= budget || nch <= 1 || chunk >= nch) return;
-  const int c0 = chunk * kTwoStageChunk;
-  const int cn = min(kTwoStageChunk, n - c0);
-  const float* __restrict__ src = scores + row * cap + c0;
-  const int t = threadIdx.x;
-
-  // Slab i holds positions c0 + i * 4 * kChunkThreads + 4t .. +3 (coalesced
-  // float4 loads).
-  uint64_t cv[kChunkE];
-  uint32_t vmask = 0;
-#pragma unroll
-  for (int i = 0; i < kChunkE / 4; ++i) {
-    const int o = i * 4 * kChunkThreads + 4 * t;
-    float v[4];
-    if (o + 4 <= cn) {
-      const float4 x = *reinterpret_cast<const float4*>(src + o);
-      v[0] = x.x;
-      v[1] = x.y;
-      v[2] = x.z;
-      v[3] = x.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (o + e < cn) ? src[o + e] : 0.0f;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      cv[4 * i + e] = composite(score_key(v[e]), (uint32_t)(c0 + o + e));
-      vmask |= (o + e < cn ? 1u : 0u) << (4 * i + e);
-    }
-  }
-  const uint64_t tau =
-      (cn > budget) ? reg_select<kChunkThreads, kChunkE>(cv, vmask, (uint32_t)budget, L) : 0ull;
-  uint64_t* out = cand + row * cand_stride + (size_t)chunk * budget;
-  uint32_t m4[kChunkE / 4], off[kChunkE / 4];
-#pragma unroll
-  for (int i = 0; i < kChunkE / 4; ++i) {
-    m4[i] = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      m4[i] |= ((((vmask >> (4 * i + e)) & 1u) && cv[4 * i + e] >= tau) ? 1u : 0u) << e;
-  }
-  ordered_offsets<kChunkThreads>(m4, off, L);
-#pragma unroll
-  for (int i = 0; i < kChunkE / 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if ((m4[i] >> e) & 1u) {
-        if (off[i] < (uint32_t)budget) out[off[i]] = cv[4 * i + e];
-        ++off[i];
-      }
+  const int nch = (n + kChunk - 1) / kChunk;
+  if (n <= budget || chunk >= nch) return;  // a one-chunk row is a chunk too
+  const int c0 = chunk * kChunk;
+  const int cn = min(kChunk, n - c0);
+  ScoreSrc<E, NT> src;
+  load_scores<E, NT>(src, scores + row * cap, c0, cn);
+  // A short last chunk keeps all its positions (need = cn selects them all).
+  const uint32_t need = (uint32_t)(cn > budget ? budget : cn);
+  const uint64_t tau = adaptive_select<NT, E>(src, need, L);
+  const int per = budget < kChunk ? budget : kChunk;
+  uint64_t* out = cand + row * cand_stride + (size_t)chunk * per;
+  emit_ordered<E, NT>(src, tau, (uint32_t)per, L, [&](uint32_t r, int e) {
+    out[r] = ((uint64_t)src.key(e) << 32) | src.low(e);
+  });
 }
 
-template <bool ATTEND, bool BF16, int D>
-__global__ void __launch_bounds__(kFinalThreads)
-final_select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ nb,
-                    int max_seq_len, int hq, int cap, int budget,
-                    const uint64_t* __restrict__ cand, int cand_stride, int32_t* __restrict__ idx,
-                    const void* __restrict__ k_cache, const void* __restrict__ v_cache,
-                    const float* __restrict__ qrot, int hkv, int G, float* __restrict__ out,
-                    int32_t* __restrict__ advance, uint32_t* err) {
-  __shared__ FinalLds L;
+// Selects a row's top B from its raw scores (FROM_CAND = false, n <= E * 1024)
+// or from the chunk stage's candidates (FROM_CAND = true, chunks of `chunk`
+// positions, at most E * 1024 candidates), writes idx
+// (if given) and, with ATTEND, runs FAC over the selection in LDS.  Also
+// stores n_b into advance[b] (if given): seq_lens may be advanced here since
+// no kernel of this launch reads it.
+template <bool ATTEND, bool BF16, int D, int E, bool FROM_CAND, int NT>
+__global__ void __launch_bounds__(NT)
+row_select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ nb,
+                  int max_seq_len, int hq, int cap, int budget,
+                  const uint64_t* __restrict__ cand, int cand_stride, int chunk,
+                  int32_t* __restrict__ idx, const void* __restrict__ k_cache,
+                  const void* __restrict__ v_cache, const float* __restrict__ qrot, int hkv,
+                  int G, float* __restrict__ out, int32_t* __restrict__ advance, uint32_t* err) {
+  static_assert(NT / kWave * RowGeom<BF16, D>::RS * (D + 3) + 1 + NT <=
+                    kAttendScratch,
+                "attend_rows scratch");
+  __shared__ RowLds<NT> L;
   const int h = blockIdx.x, b = blockIdx.y;
   const size_t row = (size_t)b * hq + h;
   const int n = checked_len(nb, b, max_seq_len, cap, err, h == 0 && threadIdx.x == 0);
@@ -130,128 +198,180 @@ final_select_kernel(const float* __restrict__ scores, const int32_t* __restrict_
   const int take = n < budget ? n : budget;
 
   if (n <= budget) {
-    for (int j = t; j < budget; j += kFinalThreads) {
+    for (int j = t; j < budget; j += NT) {
       if (o) o[j] = (j < n) ? j : -1;
       if (ATTEND && j < kFusedMaxBudget) L.sel[j] = j;
     }
+  } else if constexpr (!FROM_CAND) {
+    ScoreSrc<E, NT> src;
+    load_scores<E, NT>(src, scores + row * cap, 0, n);
+    const uint64_t tau = adaptive_select<NT, E>(src, (uint32_t)budget, L.s);
+    emit_ordered<E, NT>(src, tau, (uint32_t)budget, L.s, [&](uint32_t r, int e) {
+      const int pos = src.pos(e);
+      if (o) o[r] = pos;
+      if (ATTEND) L.sel[r] = pos;
+    });
   } else {
-    // Candidate k = 4 (g * kFinalThreads + t) + e: group g holds 4 consecutive
-    // candidates per thread; k ascends with position.
-    const bool direct = chunks_of(n) <= 1;
-    const int M = direct ? n : candidates_of(n, budget);
-    uint64_t cv[kFinalE];
-    uint32_t vmask = 0;
+    const int M = candidates_of(n, budget, chunk);
+    const uint64_t* __restrict__ src_c = cand + row * cand_stride;
+    CandSrc<E, NT> src;
 #pragma unroll
-    for (int g = 0; g < kFinalE / 4; ++g) {
-      const int k0 = 4 * (g * kFinalThreads + t);
-      if (direct) {
-        const float* __restrict__ src = scores + row * cap;
-        if (k0 + 4 <= M) {
-          const float4 x = *reinterpret_cast<const float4*>(src + k0);
-          const float v[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) cv[4 * g + e] = composite(score_key(v[e]), (uint32_t)(k0 + e));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            cv[4 * g + e] = (k0 + e < M) ? composite(score_key(src[k0 + e]), (uint32_t)(k0 + e)) : 0ull;
-        }
+    for (int g = 0; g < E / 4; ++g) {
+      const int k0 = 4 * (g * NT + t);
+      uint64_t c[4];
+      if (k0 + 4 <= M) {
+        const ulonglong2 a = *reinterpret_cast<const ulonglong2*>(src_c + k0);
+        const ulonglong2 c2 = *reinterpret_cast<const ulonglong2*>(src_c + k0 + 2);
+        c[0] = a.x;
+        c[1] = a.y;
+        c[2] = c2.x;
+        c[3] = c2.y;
       } else {
-        const uint64_t* __restrict__ src = cand + row * cand_stride;
-        if (k0 + 4 <= M) {
-          const ulonglong2 a = *reinterpret_cast<const ulonglong2*>(src + k0);
-          const ulonglong2 c2 = *reinterpret_cast<const ulonglong2*>(src + k0 + 2);
-          cv[4 * g] = a.x;
-          cv[4 * g + 1] = a.y;
-          cv[4 * g + 2] = c2.x;
-          cv[4 * g + 3] = c2.y;
-        } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) cv[4 * g + e] = (k0 + e < M) ? src[k0 + e] : 0ull;
-        }
+        for (int e = 0; e < 4; ++e) c[e] = (k0 + e < M) ? src_c[k0 + e] : 0ull;
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vmask |= (k0 + e < M ? 1u : 0u) << (4 * g + e);
+      for (int e = 0; e < 4; ++e) {
+        src.hi[4 * g + e] = (uint32_t)(c[e] >> 32);
+        src.lo[4 * g + e] = (uint32_t)c[e];
+      }
     }
-    const uint64_t tau = reg_select<kFinalThreads, kFinalE>(cv, vmask, (uint32_t)budget, L.s);
-    uint32_t m4[kFinalE / 4], off[kFinalE / 4];
-#pragma unroll
-    for (int g = 0; g < kFinalE / 4; ++g) {
-      m4[g] = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        m4[g] |= ((((vmask >> (4 * g + e)) & 1u) && cv[4 * g + e] >= tau) ? 1u : 0u) << e;
-    }
-    ordered_offsets<kFinalThreads>(m4, off, L.s);
-#pragma unroll
-    for (int g = 0; g < kFinalE / 4; ++g)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((m4[g] >> e) & 1u) {
-          if (off[g] < (uint32_t)budget) {
-            const int pos = (int)composite_pos(cv[4 * g + e]);
-            if (o) o[off[g]] = pos;
-            if (ATTEND) L.sel[off[g]] = pos;
-          }
-          ++off[g];
-        }
+    const uint64_t tau = adaptive_select<NT, E>(src, (uint32_t)budget, L.s);
+    emit_ordered<E, NT>(src, tau, (uint32_t)budget, L.s, [&](uint32_t r, int e) {
+      const int pos = (int)(0xffffffffu - src.lo[e]);
+      if (o) o[r] = pos;
+      if (ATTEND) L.sel[r] = pos;
+    });
   }
   if constexpr (ATTEND) {
     __syncthreads();
     float* out_row = out + row * D;
     if (take == 0) {
-      for (int d = t; d < D; d += kFinalThreads) out_row[d] = 0.0f;
+      for (int d = t; d < D; d += NT) out_row[d] = 0.0f;
       return;
     }
     const size_t kvbase = ((size_t)b * hkv + h / G) * cap;
-    attend_rows<BF16, D, kFinalThreads / kWave>(L.sel, take, k_cache, v_cache, qrot, row, kvbase,
-                                                out_row, reinterpret_cast<float*>(&L.s.hist[0][0]));
+    attend_rows<BF16, D, NT / kWave>(L.sel, take, k_cache, v_cache, qrot, row, kvbase,
+                                              out_row, L.att);
   }
 }
 
-bool two_stage_applies(int max_seq_len, int budget) {
-  const int nch = (max_seq_len + kTwoStageChunk - 1) / kTwoStageChunk;
-  return budget <= kFusedMaxBudget && 2 * budget <= kTwoStageChunk &&
-         (long long)nch * budget <= kTwoStageMaxCand && max_seq_len > 0;
+// How a (max_seq_len, budget) pair is selected: a row held whole by one
+// workgroup (direct_e scores per thread), or chunks of chunk_e * 1024
+// positions and then their candidates (cand_e per thread).
+struct SelectPlan {
+  int direct_e = 0, chunk_e = 0, cand_e = 0;
+  bool ok() const { return direct_e || chunk_e; }
+};
+
+static int round_e(int per_thread) {
+  return per_thread <= 4 ? 4 : per_thread <= 8 ? 8 : per_thread <= 16 ? 16 : 32;
 }
 
-template <bool ATT, bool BF, int DD>
-static void launch_final(const fasa_ctx* c, hipStream_t s, const float* scores, const int32_t* nb,
-                         int max_seq_len, int budget, const uint64_t* cand, int stride,
-                         int32_t* idx, const void* k, const void* v, const float* qrot, float* out,
-                         int32_t* advance, uint32_t* err) {
-  hipLaunchKernelGGL((final_select_kernel<ATT, BF, DD>), dim3((unsigned)c->hq, (unsigned)c->batch),
-                     dim3(kFinalThreads), 0, s, scores, nb, max_seq_len, c->hq, c->cap, budget,
-                     cand, stride, idx, k, v, qrot, c->hkv, c->G, out, advance, err);
+// Short rows go whole to one workgroup (one launch).  Longer rows are cut
+// into the shortest chunks (4096 positions and up) that leave at most 16384
+// candidates and whose chunk is longer than B: more workgroups with fewer
+// scores each finish sooner than one workgroup per row.  Rows where no chunk
+// reduces anything but that fit one workgroup are held whole.
+static SelectPlan select_plan(int max_seq_len, int budget) {
+  SelectPlan p;
+  if (max_seq_len <= 0 || budget < 1) return p;
+  if (max_seq_len <= 16 * kRowThreads) {
+    p.direct_e = round_e((max_seq_len + kRowThreads - 1) / kRowThreads);
+    return p;
+  }
+  for (int e = 8; e <= kMaxE; e *= 2) {
+    const long long chunk = (long long)e * kRowThreads;
+    const long long nch = (max_seq_len + chunk - 1) / chunk;
+    if (nch > 1 && budget < chunk && nch * budget <= kTwoStageMaxCand) {
+      p.chunk_e = e;
+      p.cand_e = round_e((int)((nch * budget + kRowThreads - 1) / kRowThreads));
+      return p;
+    }
+  }
+  if (max_seq_len <= kMaxE * kRowThreads)
+    p.direct_e = round_e((max_seq_len + kRowThreads - 1) / kRowThreads);
+  return p;
 }
 
-hipError_t launch_two_stage(const fasa_ctx* c, const float* scores, const int32_t* nb,
-                            int max_seq_len, int budget, int32_t* idx, const void* k_cache,
-                            const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
-                            hipStream_t s) {
-  if (!two_stage_applies(max_seq_len, budget)) return hipErrorInvalidValue;
+bool select_path_applies(int max_seq_len, int budget) {
+  return select_plan(max_seq_len, budget).ok();
+}
+
+template <bool ATT, bool BF, int DD, int E, bool FC>
+static void launch_row(const fasa_ctx* c, hipStream_t s, const float* scores, const int32_t* nb,
+                       int max_seq_len, int budget, const uint64_t* cand, int stride, int chunk,
+                       int32_t* idx, const void* k, const void* v, const float* qrot, float* out,
+                       int32_t* advance, uint32_t* err) {
+  hipLaunchKernelGGL((row_select_kernel<ATT, BF, DD, E, FC, kRowThreads>),
+                     dim3((unsigned)c->hq, (unsigned)c->batch), dim3(kRowThreads), 0, s, scores,
+                     nb, max_seq_len, c->hq, c->cap, budget, cand, stride, chunk, idx, k, v, qrot,
+                     c->hkv, c->G, out, advance, err);
+}
+
+template <int E, bool FC>
+static void launch_row_e(const fasa_ctx* c, hipStream_t s, const float* scores,
+                         const int32_t* nb, int max_seq_len, int budget, const uint64_t* cand,
+                         int stride, int chunk, int32_t* idx, const void* k, const void* v,
+                         const float* qrot, float* out, int32_t* advance, uint32_t* err) {
+  if (out == nullptr) {
+    launch_row<false, true, 128, E, FC>(c, s, scores, nb, max_seq_len, budget, cand, stride,
+                                        chunk, idx, nullptr, nullptr, nullptr, nullptr, advance,
+                                        err);
+    return;
+  }
+  const bool bf = (c->dtype == FASA_BF16);
+#define FASA_ROW(BFV, DV)                                                                       \
+  launch_row<true, BFV, DV, E, FC>(c, s, scores, nb, max_seq_len, budget, cand, stride, chunk, \
+                                   idx, k, v, qrot, out, advance, err)
+  if (c->d == 128) {
+    if (bf) FASA_ROW(true, 128); else FASA_ROW(false, 128);
+  } else {
+    if (bf) FASA_ROW(true, 64); else FASA_ROW(false, 64);
+  }
+#undef FASA_ROW
+}
+
+hipError_t launch_select(const fasa_ctx* c, const float* scores, const int32_t* nb,
+                         int max_seq_len, int budget, int32_t* idx, const void* k_cache,
+                         const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
+                         hipStream_t s) {
+  const SelectPlan p = select_plan(max_seq_len, budget);
+  if (!p.ok() || (out != nullptr && budget > kFusedMaxBudget)) return hipErrorInvalidValue;
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
   const float* qrot = reinterpret_cast<const float*>(ws + c->ws.qrot);
   uint64_t* cand = reinterpret_cast<uint64_t*>(ws + c->ws.cand);
   const int stride = c->ws.cand_stride;
-  const int nch = (max_seq_len + kTwoStageChunk - 1) / kTwoStageChunk;
-  if (nch > 1)
-    hipLaunchKernelGGL(chunk_select_kernel, dim3((unsigned)nch, (unsigned)c->hq, (unsigned)c->batch),
-                       dim3(kChunkThreads), 0, s, scores, nb, max_seq_len, c->hq, c->cap, budget,
-                       cand, stride);
-  if (out == nullptr) {
-    launch_final<false, true, 128>(c, s, scores, nb, max_seq_len, budget, cand, stride, idx,
-                                   nullptr, nullptr, nullptr, nullptr, advance, err);
+#define FASA_ROWE(EV, FC, CH)                                                                  \
+  launch_row_e<EV, FC>(c, s, scores, nb, max_seq_len, budget, cand, stride, CH, idx, k_cache, \
+                       v_cache, qrot, out, advance, err)
+  if (p.direct_e) {
+    switch (p.direct_e) {
+      case 4: FASA_ROWE(4, false, 0); break;
+      case 8: FASA_ROWE(8, false, 0); break;
+      case 16: FASA_ROWE(16, false, 0); break;
+      default: FASA_ROWE(32, false, 0); break;
+    }
     return hipGetLastError();
   }
-  const bool bf = (c->dtype == FASA_BF16);
-  if (c->d == 128) {
-    if (bf) launch_final<true, true, 128>(c, s, scores, nb, max_seq_len, budget, cand, stride, idx, k_cache, v_cache, qrot, out, advance, err);
-    else launch_final<true, false, 128>(c, s, scores, nb, max_seq_len, budget, cand, stride, idx, k_cache, v_cache, qrot, out, advance, err);
-  } else {
-    if (bf) launch_final<true, true, 64>(c, s, scores, nb, max_seq_len, budget, cand, stride, idx, k_cache, v_cache, qrot, out, advance, err);
-    else launch_final<true, false, 64>(c, s, scores, nb, max_seq_len, budget, cand, stride, idx, k_cache, v_cache, qrot, out, advance, err);
+  const int chunk = p.chunk_e * kRowThreads;
+  const dim3 grid((unsigned)((max_seq_len + chunk - 1) / chunk), (unsigned)c->hq,
+                  (unsigned)c->batch);
+#define FASA_CHUNK(EV)                                                                        \
+  hipLaunchKernelGGL((chunk_select_kernel<EV, kRowThreads>), grid, dim3(kRowThreads), 0, s,    \
+                     scores, nb,                                                              \
+                     max_seq_len, c->hq, c->cap, budget, cand, stride)
+  switch (p.chunk_e) {
+    case 8: FASA_CHUNK(8); break;
+    case 16: FASA_CHUNK(16); break;
+    default: FASA_CHUNK(32); break;
   }
+  if (p.cand_e <= 4) FASA_ROWE(4, true, chunk);
+  else if (p.cand_e <= 8) FASA_ROWE(8, true, chunk);
+  else if (p.cand_e <= 16) FASA_ROWE(16, true, chunk);
+  else FASA_ROWE(32, true, chunk);
+#undef FASA_CHUNK
+#undef FASA_ROWE
   return hipGetLastError();
 }
 

@@ -1,12 +1,17 @@
-// Radix-select building blocks shared by the two-stage top-B kernels.
+// Radix-select building blocks shared by the top-B kernels of select2.hip.
 //
 // Order: 64-bit composites, the order-preserving 32-bit key of an fp32 score
 // in the high half and the inverted position in the low half (higher score
 // first, then lower position).  All composites of a row differ, so the B-th
-// largest one, tau, splits the row exactly: selected <=> composite >= tau.
-// tau is found digit by digit (11 bits at a time) from LDS histograms; once
-// the bin holding the B-th largest is small it is gathered into LDS and the
-// remaining digits are resolved there.
+// largest one splits the row exactly: selected <=> composite >= tau.
+//
+// tau is found by range refinement: the composites still in play lie in
+// [lo, hi]; a pass histograms (c - lo) >> s into 2048 LDS bins (s is the
+// smallest shift that fits the range into them), finds the bin holding the
+// need-th largest and narrows [lo, hi] to that bin.  The first range is the
+// row's own [min, max], so the bins follow the data instead of fixed key
+// digits, and each pass shrinks the range by up to 2048x.  Once the bin's
+// population is small it is gathered into LDS and the passes continue there.
 //
 // With one or two waves per SIMD nothing hides latency, so every step here is
 // built to keep dependent LDS round trips and barriers few: wave scans use
@@ -19,6 +24,10 @@
 
 namespace fasa {
 
+// Histogram of one refinement pass: 1024 bins (10 bits per pass).
+constexpr int kSelBits = 10;
+constexpr int kSelBins = 1 << kSelBits;
+
 struct BinPick {
   uint32_t bin, above, count;
 };
@@ -29,10 +38,14 @@ struct RegSelectLds {
   static constexpr int kWaves = NT / kWave;
   // Each copy has kWave spare words past the bins: lanes that count nothing
   // add 0 there (one word per lane) instead of hammering one bin address.
-  uint32_t hist[COPIES][kHistBins + kWave];
+  uint32_t hist[COPIES][kSelBins + kWave];
   uint64_t cand[CAP];
   uint32_t wsum[kWaves];
   uint32_t slab_cnt[8][kWaves];
+  uint32_t rmin[kWaves], rmax[kWaves];
+  float fmin[kWaves], fmax[kWaves];
+  uint32_t fin[kWaves];
+  uint64_t tau;
   uint32_t pick[4];
   uint32_t cand_n;
 };
@@ -65,46 +78,31 @@ __device__ __forceinline__ uint64_t lanes_below() { return (1ull << lane_id()) -
 // a barrier.
 template <int NT, int COPIES, int CAP>
 __device__ __forceinline__ void zero_hist(RegSelectLds<NT, COPIES, CAP>& L, int copies) {
-  constexpr int kRow4 = (kHistBins + kWave) / 4;
+  constexpr int kRow4 = (kSelBins + kWave) / 4;
   uint4* h = reinterpret_cast<uint4*>(&L.hist[0][0]);
   for (int i = threadIdx.x; i < copies * kRow4; i += NT)
-    if (i % kRow4 < kHistBins / 4) h[i] = make_uint4(0, 0, 0, 0);
+    if (i % kRow4 < kSelBins / 4) h[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 }
 
 // Sums `copies` histogram copies and finds, scanning from the top bin down,
 // the bin where the running count reaches `need` (1 <= need <= total).
-// Thread t owns the PER bins of ranks [PER t, PER t + PER), read with vector
-// LDS loads.  Two barriers.
+// Thread t owns the PER = kSelBins / NT bins of ranks PER t .. PER t + PER - 1
+// (rank 0 = the top bin); a wave scan and the waves' totals in LDS give each
+// thread its running count.  Two barriers, few registers.
 template <int NT, int COPIES, int CAP>
-__device__ __forceinline__ BinPick fold_and_pick(RegSelectLds<NT, COPIES, CAP>& L, int bins,
-                                                 int copies, uint32_t need) {
-  constexpr int PER = kHistBins / NT;  // 8, 4 or 2 bins per thread
-  static_assert(PER == 2 || PER == 4 || PER == 8, "bins per thread");
+__device__ __forceinline__ BinPick fold_and_pick(RegSelectLds<NT, COPIES, CAP>& L, int copies,
+                                                 uint32_t need) {
+  constexpr int PER = kSelBins / NT;
+  static_assert(PER >= 1 && PER * NT == kSelBins, "bins per thread");
   const int t = threadIdx.x;
-  const int lo = bins - PER * (t + 1);  // lowest bin index of this thread's ranks
+  const int lo = kSelBins - PER * (t + 1);  // lowest bin of this thread's ranks
   uint32_t c[PER];
 #pragma unroll
   for (int r = 0; r < PER; ++r) c[r] = 0u;
-  if (lo >= 0) {
-    for (int k = 0; k < copies; ++k) {
-      if constexpr (PER == 2) {
-        const uint2 v = *reinterpret_cast<const uint2*>(&L.hist[k][lo]);
-        c[1] += v.x;
-        c[0] += v.y;
-      } else {
+  for (int k = 0; k < copies; ++k)
 #pragma unroll
-        for (int q = 0; q < PER / 4; ++q) {
-          const uint4 v = *reinterpret_cast<const uint4*>(&L.hist[k][lo + 4 * q]);
-          // bin lo + i has rank PER t + PER - 1 - i
-          c[PER - 1 - 4 * q] += v.x;
-          c[PER - 2 - 4 * q] += v.y;
-          c[PER - 3 - 4 * q] += v.z;
-          c[PER - 4 - 4 * q] += v.w;
-        }
-      }
-    }
-  }
+    for (int r = 0; r < PER; ++r) c[r] += L.hist[k][lo + PER - 1 - r];  // rank order
   uint32_t local = 0;
 #pragma unroll
   for (int r = 0; r < PER; ++r) local += c[r];
@@ -131,72 +129,260 @@ __device__ __forceinline__ BinPick fold_and_pick(RegSelectLds<NT, COPIES, CAP>& 
   return BinPick{L.pick[0], L.pick[1], L.pick[2]};
 }
 
-__device__ __forceinline__ bool has_prefix64(uint64_t c, uint64_t prefix, int known) {
-  return known == 0 || (c >> (64 - known)) == prefix;
+// Block-wide min and max of lo / hi (in place).  One barrier.
+template <int NT, int COPIES, int CAP>
+__device__ __forceinline__ void block_minmax(uint32_t& lo, uint32_t& hi,
+                                             RegSelectLds<NT, COPIES, CAP>& L) {
+#pragma unroll
+  for (int m = kWave / 2; m > 0; m >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, m));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, m));
+  }
+  const int wave = threadIdx.x / kWave;
+  if (lane_id() == 0) {
+    L.rmin[wave] = lo;
+    L.rmax[wave] = hi;
+  }
+  __syncthreads();
+  lo = L.rmin[0];
+  hi = L.rmax[0];
+#pragma unroll
+  for (int w = 1; w < NT / kWave; ++w) {
+    lo = min(lo, L.rmin[w]);
+    hi = max(hi, L.rmax[w]);
+  }
 }
 
-// tau = the need-th largest of the valid composites held in registers
-// (c[e] valid when bit e of vmask is set); need >= 1 and <= the valid count.
-template <int NT, int E, int COPIES, int CAP>
-__device__ uint64_t reg_select(const uint64_t (&c)[E], uint32_t vmask, uint32_t need,
-                               RegSelectLds<NT, COPIES, CAP>& L) {
-  static_assert(E <= 32, "validity mask is 32 bits");
+// Block-wide key min / max, value min / max and all-finite flag.  One barrier.
+template <int NT, int COPIES, int CAP>
+__device__ __forceinline__ void block_ranges(uint32_t& kmin, uint32_t& kmax, float& vmin,
+                                             float& vmax, uint32_t& fin,
+                                             RegSelectLds<NT, COPIES, CAP>& L) {
+#pragma unroll
+  for (int m = kWave / 2; m > 0; m >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, m));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m));
+    vmin = fminf(vmin, __shfl_xor(vmin, m));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, m));
+    fin &= (uint32_t)__shfl_xor((int)fin, m);
+  }
+  const int wave = threadIdx.x / kWave;
+  if (lane_id() == 0) {
+    L.rmin[wave] = kmin;
+    L.rmax[wave] = kmax;
+    L.fmin[wave] = vmin;
+    L.fmax[wave] = vmax;
+    L.fin[wave] = fin;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NT / kWave; ++w) {
+    kmin = min(kmin, L.rmin[w]);
+    kmax = max(kmax, L.rmax[w]);
+    vmin = fminf(vmin, L.fmin[w]);
+    vmax = fmaxf(vmax, L.fmax[w]);
+    fin &= L.fin[w];
+  }
+}
+
+// The fp32 score of an order-preserving key (inverse of score_key; -0 reads
+// as +0).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Shift that maps [lo, lo + span] onto at most kSelBins bins.
+__device__ __forceinline__ int range_shift(uint64_t span) {
+  return span < (uint64_t)kSelBins ? 0 : (64 - __clzll(span) - kSelBits);
+}
+
+// Gathers the thread's elements that satisfy `in(e)` into L.cand (one LDS
+// atomic per wave reserves the wave's slots) and returns how many the block
+// gathered (all of them fit: the caller knows the count is <= CAP).  Two
+// barriers.
+template <int NT, int E, int COPIES, int CAP, class Src, class In>
+__device__ __forceinline__ uint32_t gather_cand(const Src& src, In in,
+                                                RegSelectLds<NT, COPIES, CAP>& L) {
+  const int tid = threadIdx.x;
+  uint32_t mine = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) mine += in(e) ? 1u : 0u;
+  if (tid == 0) L.cand_n = 0;
+  __syncthreads();
+  const uint32_t incl = wave_scan_incl(mine);
+  uint32_t base = 0;
+  if (lane_id() == kWave - 1 && incl) base = atomicAdd(&L.cand_n, incl);
+  base = (uint32_t)__builtin_amdgcn_readlane((int)base, kWave - 1);
+  uint32_t slot = base + incl - mine;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (in(e)) {
+      if (slot < (uint32_t)CAP) L.cand[slot] = ((uint64_t)src.key(e) << 32) | src.low(e);
+      ++slot;
+    }
+  }
+  __syncthreads();
+  return min(L.cand_n, (uint32_t)CAP);
+}
+
+// Candidates at most this many are resolved by direct ranking.
+constexpr uint32_t kRankMax = 128;
+
+// The need-th largest of the M (<= kRankMax) distinct composites in L.cand:
+// thread i counts the candidates above candidate i.  One barrier.
+template <int NT, int COPIES, int CAP>
+__device__ __forceinline__ uint64_t rank_resolve(uint32_t M, uint32_t need,
+                                                 RegSelectLds<NT, COPIES, CAP>& L) {
+  const uint32_t i = threadIdx.x;
+  if (i < M) {
+    const uint64_t c = L.cand[i];
+    uint32_t above = 0;
+    for (uint32_t j = 0; j < M; ++j) above += (L.cand[j] > c) ? 1u : 0u;
+    if (above == need - 1) L.tau = c;
+  }
+  __syncthreads();
+  return L.tau;
+}
+
+// The need-th largest of the composites in [lo, hi], held by the threads'
+// elements (in_lds = false) or by L.cand[0..M) (in_lds = true): range
+// refinement, see adaptive_select.
+template <int NT, int E, int COPIES, int CAP, class Src>
+__device__ __forceinline__ uint64_t refine(const Src& src, uint32_t need, uint64_t lo, uint64_t hi, bool in_lds,
+                           uint32_t M, RegSelectLds<NT, COPIES, CAP>& L) {
   const int tid = threadIdx.x;
   const int copy = (tid / kWave) % COPIES;
-  uint64_t prefix = 0;
-  int known = 0;
-  bool in_lds = false;
-  uint32_t M = 0;
   for (;;) {
-    const int width = (64 - known < kHistBits) ? (64 - known) : kHistBits;
-    const int shift = 64 - known - width;
-    const uint32_t mask = (1u << width) - 1u;
+    if (in_lds && M <= kRankMax) return rank_resolve(M, need, L);
+    const int s = range_shift(hi - lo);
+    const bool keyed = s >= 32;
+    const uint32_t klo = (uint32_t)(lo >> 32), khi = (uint32_t)(hi >> 32);
+    const int ks = keyed ? s - 32 : 0;
     if (!in_lds) {
       zero_hist(L, COPIES);
-      const uint32_t spare = (uint32_t)(kHistBins + lane_id());
+      const uint32_t spare = (uint32_t)(kSelBins + lane_id());
+      if (keyed) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const bool take = ((vmask >> e) & 1u) && has_prefix64(c[e], prefix, known);
-        atomicAdd(&L.hist[copy][take ? ((uint32_t)(c[e] >> shift) & mask) : spare], take ? 1u : 0u);
+        for (int e = 0; e < E; ++e) {
+          const uint32_t k = src.key(e);
+          const bool take = k >= klo && k <= khi;
+          atomicAdd(&L.hist[copy][take ? (k - klo) >> ks : spare], take ? 1u : 0u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint64_t c = ((uint64_t)src.key(e) << 32) | src.low(e);
+          const bool take = src.key(e) != 0u && c >= lo && c <= hi;
+          atomicAdd(&L.hist[copy][take ? (uint32_t)((c - lo) >> s) : spare], take ? 1u : 0u);
+        }
       }
     } else {
       zero_hist(L, 1);
       for (uint32_t i = tid; i < M; i += NT) {
-        const uint64_t v = L.cand[i];
-        if (has_prefix64(v, prefix, known)) atomicAdd(&L.hist[0][(uint32_t)(v >> shift) & mask], 1u);
+        const uint64_t c = L.cand[i];
+        if (c >= lo && c <= hi) atomicAdd(&L.hist[0][(uint32_t)((c - lo) >> s)], 1u);
       }
     }
     __syncthreads();
-    const BinPick p = fold_and_pick(L, 1 << width, in_lds ? 1 : COPIES, need);
-    prefix = (prefix << width) | p.bin;
-    known += width;
+    const BinPick p = fold_and_pick(L, in_lds ? 1 : COPIES, need);
+    const uint64_t blo = lo + ((uint64_t)p.bin << s);
     need -= p.above;
-    if (p.count == need || known == 64) break;  // the whole bin is taken
+    if (p.count == need) return blo;  // the whole bin is taken
+    // A bin of one value (s == 0) holds one composite, so it ends above.
+    const uint64_t bhi = blo + ((1ull << s) - 1ull);
+    lo = blo;
+    hi = bhi < hi ? bhi : hi;
     if (!in_lds && p.count <= (uint32_t)CAP) {
-      // Gather the bin: one LDS atomic per wave reserves the wave's slots.
-      uint32_t mine = 0;
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        mine += (((vmask >> e) & 1u) && has_prefix64(c[e], prefix, known)) ? 1u : 0u;
-      if (tid == 0) L.cand_n = 0;
-      __syncthreads();
-      const uint32_t incl = wave_scan_incl(mine);
-      uint32_t base = 0;
-      if (lane_id() == kWave - 1 && incl) base = atomicAdd(&L.cand_n, incl);
-      base = (uint32_t)__builtin_amdgcn_readlane((int)base, kWave - 1);
-      uint32_t slot = base + incl - mine;
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (((vmask >> e) & 1u) && has_prefix64(c[e], prefix, known)) {
-          if (slot < (uint32_t)CAP) L.cand[slot] = c[e];
-          ++slot;
-        }
-      __syncthreads();
-      M = min(L.cand_n, (uint32_t)CAP);
+      const uint64_t glo = lo, ghi = hi;
+      const bool gkeyed = (uint32_t)glo == 0u && (uint32_t)ghi == 0xffffffffu;
+      M = gather_cand<NT, E>(src, [&](int e) {
+        const uint32_t k = src.key(e);
+        if (gkeyed) return k >= (uint32_t)(glo >> 32) && k <= (uint32_t)(ghi >> 32);
+        const uint64_t c = ((uint64_t)k << 32) | src.low(e);
+        return k != 0u && c >= glo && c <= ghi;
+      }, L);
       in_lds = true;
     }
   }
-  return (known >= 64) ? prefix : (prefix << (64 - known));
+}
+
+// tau = the need-th largest composite of the row (1 <= need <= the number of
+// valid elements); selected <=> composite >= tau, and tau >= 2^32.
+//
+// Src gives the thread's elements for compile-time e < E (so they stay in
+// registers): key(e), the high half of the composite, 0 for an invalid
+// element and >= 1 otherwise, and low(e), the low half.
+//
+// First pass, when every score is finite: 1024 bins linear in the score over
+// [min, max] (fp32 arithmetic, monotone in the score, so a bin is a run of
+// the order), which spreads typical score distributions over many bins; the
+// bin holding the need-th largest is gathered into LDS and resolved there.
+// Otherwise, or when that bin is too large, range refinement on keys: the
+// range spans whole keys, [kmin << 32, (kmax << 32) | 0xffffffff], and bins
+// of 2^s with s >= 32 keep it key-aligned, so while s >= 32 every test and bin
+// needs the 32-bit key alone; only a range inside one key (ties) uses both
+// halves.  Invalid elements (key 0) fall below every range.
+template <int NT, int E, int COPIES, int CAP, class Src>
+__device__ __forceinline__ uint64_t adaptive_select(const Src& src, uint32_t need,
+                                    RegSelectLds<NT, COPIES, CAP>& L) {
+  const int copy = (threadIdx.x / kWave) % COPIES;
+  uint32_t kmin = ~0u, kmax = 0u, fin = 1u;
+  float vmin = INFINITY, vmax = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t k = src.key(e);
+    const float v = key_value(k);
+    kmin = min(kmin, k ? k : ~0u);
+    kmax = max(kmax, k);
+    fin &= (k == 0u || isfinite(v)) ? 1u : 0u;
+    vmin = k ? fminf(vmin, v) : vmin;
+    vmax = k ? fmaxf(vmax, v) : vmax;
+  }
+  block_ranges(kmin, kmax, vmin, vmax, fin, L);
+  const float span = vmax - vmin;
+  const float scale = (float)kSelBins / span;
+  if (fin && span > 0.0f && isfinite(span) && isfinite(scale)) {
+    auto bin_of = [&](uint32_t k) {
+      return min(kSelBins - 1, (int)((key_value(k) - vmin) * scale));
+    };
+    zero_hist(L, COPIES);
+    const uint32_t spare = (uint32_t)(kSelBins + lane_id());
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint32_t k = src.key(e);
+      atomicAdd(&L.hist[copy][k ? (uint32_t)bin_of(k) : spare], k ? 1u : 0u);
+    }
+    __syncthreads();
+    const BinPick p = fold_and_pick(L, COPIES, need);
+    if (p.count <= (uint32_t)CAP) {
+      const int b = (int)p.bin;
+      const uint32_t M = gather_cand<NT, E>(
+          src, [&](int e) { const uint32_t k = src.key(e); return k != 0u && bin_of(k) == b; },
+          L);
+      const uint32_t rest = need - p.above;
+      if (M <= kRankMax) return rank_resolve(M, rest, L);
+      // Range of the gathered composites, then refinement in LDS.
+      uint32_t glo = ~0u, ghi = 0u;
+      for (uint32_t i = threadIdx.x; i < M; i += NT) {
+        const uint32_t k = (uint32_t)(L.cand[i] >> 32);
+        glo = min(glo, k);
+        ghi = max(ghi, k);
+      }
+      block_minmax(glo, ghi, L);
+      return refine<NT, E>(src, rest, (uint64_t)glo << 32, ((uint64_t)ghi << 32) | 0xffffffffull,
+                           true, M, L);
+    }
+  }
+  return refine<NT, E>(src, need, (uint64_t)kmin << 32, ((uint64_t)kmax << 32) | 0xffffffffull,
+                       false, 0u, L);
+}
+
+// Whether element e is selected by threshold tau (>= 2^32): 32-bit tests.
+template <class Src>
+__device__ __forceinline__ bool is_selected(const Src& src, int e, uint64_t tau) {
+  const uint32_t tk = (uint32_t)(tau >> 32), tl = (uint32_t)tau;
+  const uint32_t k = src.key(e);
+  return k > tk || (k == tk && src.low(e) >= tl);
 }
 
 // Output offsets for an ordered compaction over S slabs: element e of slab s
