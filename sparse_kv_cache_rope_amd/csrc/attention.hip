@@ -52,7 +52,7 @@ fac_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
 
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int slot = lane / LPR, sub = lane % LPR;
-  const float scale = 1.0f / sqrtf((float)D);
+  const float scale = logit_scale<D>();
   float qv[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) qv[e] = qrot[row * D + sub * EPL + e] * scale;
@@ -88,17 +88,19 @@ fac_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
   }
   Soft<EPL> st;
   st.init();
+  float z[ITERS], vf[ITERS][EPL];
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
-    float kf[EPL], vf[EPL];
+    float kf[EPL];
     unpack<BF16, EPL>(kc[it], kf);
-    float z = 0.0f;
+    float s = 0.0f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) z = fmaf(qv[e], kf[e], z);
-    z = group_sum<LPR>(z);
-    unpack<BF16, EPL>(vc[it], vf);
-    st.add(jr[it] >= 0 ? z : -INFINITY, vf);
+    for (int e = 0; e < EPL; ++e) s = fmaf(qv[e], kf[e], s);
+    s = group_sum<LPR>(s);
+    z[it] = jr[it] >= 0 ? s : -INFINITY;
+    unpack<BF16, EPL>(vc[it], vf[it]);
   }
+  st.template add_batch<ITERS>(z, vf);
   merge_block<D, LPR, EPL, NW>(st, lds);
   write_state<D, LPR, EPL>(st, nsplit == 1, o,
                            partial + (row * max_splits + split) * (D + 2));
@@ -136,7 +138,7 @@ dense_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
 
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int slot = lane / LPR, sub = lane % LPR;
-  const float scale = 1.0f / sqrtf((float)D);
+  const float scale = logit_scale<D>();
   float qv[G][EPL];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh)
@@ -151,31 +153,43 @@ dense_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
   Soft<EPL> st[G];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) st[hh].init();
-  for (int it0 = 0; it0 < ITERS; it0 += BATCH) {
-    uint4 kc[BATCH], vc[BATCH];
-    bool ok[BATCH];
+  // Batches of BATCH rows per row slot, double-buffered: the next batch's
+  // loads are issued before the current batch is used, so every workgroup
+  // keeps loads in flight while it computes.  Rows past n read row 0 and are
+  // masked.
+  auto load = [&](int i0, uint4 (&kc)[BATCH], uint4 (&vc)[BATCH]) {
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
-      const int j = t0 + (it0 + i) * RS * NW + wave * RS + slot;
-      ok[i] = j < n;
-      const size_t off = (kvbase + (ok[i] ? j : 0)) * LPR + sub;
+      const int j = t0 + (i0 + i) * RS * NW + wave * RS + slot;
+      const size_t off = (kvbase + (j < n ? j : 0)) * LPR + sub;
       kc[i] = K[off];
       vc[i] = V[off];
     }
+  };
+  uint4 kb[2][BATCH], vb[2][BATCH];
+  load(0, kb[0], vb[0]);
+#pragma unroll
+  for (int i0 = 0; i0 < ITERS; i0 += BATCH) {
+    const int cur = (i0 / BATCH) & 1;
+    if (i0 + BATCH < ITERS) load(i0 + BATCH, kb[cur ^ 1], vb[cur ^ 1]);
+    float z[G][BATCH], vf[BATCH][EPL];
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
-      float kf[EPL], vf[EPL];
-      unpack<BF16, EPL>(kc[i], kf);
-      unpack<BF16, EPL>(vc[i], vf);
+      const bool ok = t0 + (i0 + i) * RS * NW + wave * RS + slot < n;
+      float kf[EPL];
+      unpack<BF16, EPL>(kb[cur][i], kf);
+      unpack<BF16, EPL>(vb[cur][i], vf[i]);
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        float z = 0.0f;
+        float s = 0.0f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) z = fmaf(qv[hh][e], kf[e], z);
-        z = group_sum<LPR>(z);
-        st[hh].add(ok[i] ? z : -INFINITY, vf);
+        for (int e = 0; e < EPL; ++e) s = fmaf(qv[hh][e], kf[e], s);
+        s = group_sum<LPR>(s);
+        z[hh][i] = ok ? s : -INFINITY;
       }
     }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) st[hh].template add_batch<BATCH>(z[hh], vf);
   }
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
@@ -232,7 +246,7 @@ merge_kernel(const float* __restrict__ partial, int max_splits, const int32_t* _
     float l = 0.0f;
     if (s < nsplit && M != -INFINITY) {
       const float* q = p + (size_t)s * (D + 2);
-      const float w = expf(q[0] - M);
+      const float w = exp2f(q[0] - M);
       l = q[1] * w;
 #pragma unroll
       for (int i = 0; i < DPT; ++i) v[i] = q[2 + dd + i] * w;

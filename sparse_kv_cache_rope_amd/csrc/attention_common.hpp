@@ -4,7 +4,8 @@
 // Row layout: a K or V row is d * sizeof(dtype) bytes (256 B for bf16 d=128);
 // LPR = row_bytes / 16 lanes each load 16 bytes of it, so a wave holds
 // RS = 64 / LPR rows at once.  A lane owns EPL = 16 / sizeof(dtype) dims of
-// q~ (pre-scaled by 1/sqrt(d)) and of the output accumulator.  Dot products
+// q~ (pre-scaled by log2(e)/sqrt(d), so logits are in log2 units and every
+// softmax weight is one exp2) and of the output accumulator.  Dot products
 // are summed across the LPR lanes of a row with DPP, each lane keeps a running
 // (max, sum, acc) over the rows it saw, and those are merged across row
 // slots and waves in LDS.
@@ -15,6 +16,13 @@
 #include "device_common.hpp"
 
 namespace fasa {
+
+// Factor applied to q~: 1/sqrt(d) of the attention scale times log2(e), so
+// that exp2 of a logit difference is the softmax weight.
+template <int D>
+__device__ __forceinline__ float logit_scale() {
+  return 1.44269504088896340736f / sqrtf((float)D);
+}
 
 template <bool BF16, int D>
 struct RowGeom {
@@ -42,7 +50,7 @@ __device__ __forceinline__ void unpack(const uint4& x, float (&f)[EPL]) {
   }
 }
 
-// Online-softmax state of one lane.
+// Online-softmax state of one lane (logits in log2 units).
 template <int EPL>
 struct Soft {
   float m, l, a[EPL];
@@ -52,21 +60,31 @@ struct Soft {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) a[e] = 0.0f;
   }
-  // Adds one row with logit z (-inf = absent) and values v.
-  __device__ __forceinline__ void add(float z, const float (&v)[EPL]) {
-    if (z == -INFINITY) return;
-    const float mn = fmaxf(m, z);
-    const float sc = expf(m - mn);  // m = -inf gives 0
-    const float p = expf(z - mn);
-    l = l * sc + p;
+  // Adds R rows with logits z (-inf = absent) and values v: one rescale of the
+  // running state per batch, and the rows' weights independent of each other.
+  template <int R>
+  __device__ __forceinline__ void add_batch(const float (&z)[R], const float (&v)[R][EPL]) {
+    float mn = m;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) a[e] = fmaf(p, v[e], a[e] * sc);
+    for (int r = 0; r < R; ++r) mn = fmaxf(mn, z[r]);
+    if (mn == -INFINITY) return;
+    const float sc = exp2f(m - mn);  // m = -inf gives 0
+    l *= sc;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) a[e] *= sc;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float p = exp2f(z[r] - mn);  // z = -inf gives 0
+      l += p;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a[e] = fmaf(p, v[r][e], a[e]);
+    }
     m = mn;
   }
   __device__ __forceinline__ void merge(float m2, float l2, const float (&a2)[EPL]) {
     const float mn = fmaxf(m, m2);
     if (mn == -INFINITY) return;
-    const float s1 = expf(m - mn), s2 = expf(m2 - mn);
+    const float s1 = exp2f(m - mn), s2 = exp2f(m2 - mn);
     l = l * s1 + l2 * s2;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) a[e] = a[e] * s1 + a2[e] * s2;
@@ -161,7 +179,7 @@ __device__ __forceinline__ void merge_states_lds(const Soft<EPL>& st, int state,
     m = wave_max(m);
     float l = 0.0f;
     for (int s = lane; s < NS; s += kWave) {
-      const float w = (m == -INFINITY) ? 0.0f : expf(Mv[s] - m);
+      const float w = (m == -INFINITY) ? 0.0f : exp2f(Mv[s] - m);
       W[s] = w;
       l = fmaf(Lv[s], w, l);
     }
@@ -203,11 +221,13 @@ __device__ __forceinline__ void attend_rows(const int32_t* sel, int take, const 
                             float* scratch) {
   using Geo = RowGeom<BF16, D>;
   constexpr int LPR = Geo::LPR, EPL = Geo::EPL, RS = Geo::RS;
-  constexpr int BATCH = 4;
+  // Rows per row slot loaded before any is used: enough that a 256-row
+  // selection is one round of loads.
+  constexpr int BATCH = (256 / (RS * NW)) < 4 ? 4 : (256 / (RS * NW)) > 8 ? 8 : (256 / (RS * NW));
   constexpr int PER_BATCH = BATCH * RS * NW;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int slot = lane / LPR, sub = lane % LPR;
-  const float scale = 1.0f / sqrtf((float)D);
+  const float scale = logit_scale<D>();
   float qv[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) qv[e] = qrot[row * D + sub * EPL + e] * scale;
@@ -231,17 +251,19 @@ __device__ __forceinline__ void attend_rows(const int32_t* sel, int take, const 
         vc[it] = make_uint4(0, 0, 0, 0);
       }
     }
+    float z[BATCH], vf[BATCH][EPL];
 #pragma unroll
     for (int it = 0; it < BATCH; ++it) {
-      float kf[EPL], vf[EPL];
+      float kf[EPL];
       unpack<BF16, EPL>(kc[it], kf);
-      float z = 0.0f;
+      float s = 0.0f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) z = fmaf(qv[e], kf[e], z);
-      z = group_sum<LPR>(z);
-      unpack<BF16, EPL>(vc[it], vf);
-      st.add(jr[it] >= 0 ? z : -INFINITY, vf);
+      for (int e = 0; e < EPL; ++e) s = fmaf(qv[e], kf[e], s);
+      s = group_sum<LPR>(s);
+      z[it] = jr[it] >= 0 ? s : -INFINITY;
+      unpack<BF16, EPL>(vc[it], vf[it]);
     }
+    st.template add_batch<BATCH>(z, vf);
   }
   __syncthreads();  // scratch may alias LDS the caller read above
   merge_states_lds<D, LPR, EPL, NW * RS>(st, wave * RS + slot, scratch, out_row);

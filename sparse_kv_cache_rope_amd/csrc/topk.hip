@@ -339,7 +339,7 @@ __device__ void attend_selected(SelectLds& L, int take, const void* __restrict__
   constexpr int PER_BATCH = BATCH * RS * NW;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int slot = lane / LPR, sub = lane % LPR;
-  const float scale = 1.0f / sqrtf((float)D);
+  const float scale = logit_scale<D>();
   float qv[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) qv[e] = qrot[row * D + sub * EPL + e] * scale;
@@ -363,17 +363,19 @@ __device__ void attend_selected(SelectLds& L, int take, const void* __restrict__
         vc[it] = make_uint4(0, 0, 0, 0);
       }
     }
+    float z[BATCH], vf[BATCH][EPL];
 #pragma unroll
     for (int it = 0; it < BATCH; ++it) {
-      float kf[EPL], vf[EPL];
+      float kf[EPL];
       unpack<BF16, EPL>(kc[it], kf);
-      float z = 0.0f;
+      float s = 0.0f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) z = fmaf(qv[e], kf[e], z);
-      z = group_sum<LPR>(z);
-      unpack<BF16, EPL>(vc[it], vf);
-      st.add(jr[it] >= 0 ? z : -INFINITY, vf);
+      for (int e = 0; e < EPL; ++e) s = fmaf(qv[e], kf[e], s);
+      s = group_sum<LPR>(s);
+      z[it] = jr[it] >= 0 ? s : -INFINITY;
+      unpack<BF16, EPL>(vc[it], vf[it]);
     }
+    st.template add_batch<BATCH>(z, vf);
   }
   __syncthreads();  // the histogram LDS becomes merge scratch
   merge_block<D, LPR, EPL, NW>(st, reinterpret_cast<float*>(&L.hist[0][0]));
