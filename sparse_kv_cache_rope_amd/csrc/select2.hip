@@ -283,9 +283,12 @@ static SelectPlan select_plan(int max_seq_len, int budget) {
   for (int e = 8; e <= kMaxE; e *= 2) {
     const long long chunk = (long long)e * kRowThreads;
     const long long nch = (max_seq_len + chunk - 1) / chunk;
-    if (nch > 1 && budget < chunk && nch * budget <= kTwoStageMaxCand) {
+    const long long last = max_seq_len - (nch - 1) * chunk;
+    // Candidates of the longest row (no row of the launch has more).
+    const long long cands = (nch - 1) * budget + (last < budget ? last : budget);
+    if (nch > 1 && budget < chunk && cands <= kTwoStageMaxCand) {
       p.chunk_e = e;
-      p.cand_e = round_e((int)((nch * budget + kRowThreads - 1) / kRowThreads));
+      p.cand_e = round_e((int)((cands + kRowThreads - 1) / kRowThreads));
       return p;
     }
   }

@@ -126,6 +126,11 @@ TOPK_CASES = [
     ("planted", 2, 4096 * 3 + 256, 256, False),
     ("normal", 2, 32768, 256, True),
     ("wide", 1, 8 * 4096, 1024, False),
+    # Row held whole at 8 per thread; 16384-position chunks with the largest
+    # candidate set; a row held whole at 32 per thread (no chunk reduces B).
+    ("normal", 2, 3000, 100, False),
+    ("planted", 1, 24000, 8000, False),
+    ("ties", 1, 16000, 8500, True),
 ]
 
 
