@@ -21,6 +21,9 @@ What it computes follows "FASA: Frequency-aware Sparse Attention":
 * ``decode.py`` strings these together into a decode step over a KV cache that
   grows by one row per generated token (same page, section 1, "O Problema").
 * ``loops.py`` restates every step as pure-Python loops for small inputs.
+* ``calibrate.py`` finds each head's dominant FCs offline from the agreement
+  of single-FC scores with the full head's (same section, TIP, "Calibracao
+  Offline").
 
 Readings where the pages are silent (rotate-half pairing, frequencies
 theta^(-2c/d), the query's position, tie order, the softmax scale) are stated
@@ -32,7 +35,7 @@ against full attention on a trained model is parity unpinned (it needs
 weights and data that are not part of this project).
 """
 
-from . import rope, tip, select, fac, decode, loops  # noqa: F401
+from . import rope, tip, select, fac, decode, loops, calibrate  # noqa: F401
 from .rope import inv_freq, rope_rotate, round_to_dtype  # noqa: F401
 from .tip import tip_scores  # noqa: F401
 from .select import select_topb  # noqa: F401

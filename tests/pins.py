@@ -373,4 +373,88 @@ def pin_loops_agree():
                        atol=1e-13)
 
 
+# ---------------------------------------------------------- calibration ----
+# gist.science/pt, "Resumo Tecnico" section 2, TIP "Calibracao Offline": the
+# agreement of one FC's scores with the full head's picks I_dom.
+
+def _topk_by_sort(s, k):
+    """Top-k positions by Python's own sort on (-score, position)."""
+    return sorted(range(len(s)), key=lambda j: (-s[j], j))[:k]
+
+
+def pin_calib_fc_scores_complex():
+    # FC c's score is Re[(q_c + i q_{c+C}) conj(k_c + i k_{c+C})].
+    r = _rng(40)
+    d, half = 16, 8
+    q = r.standard_normal(d)
+    k = r.standard_normal((5, d))
+    got = oracle.calibrate.fc_scores(q, k)
+    assert got.shape == (half, 5)
+    for c in range(half):
+        zq = complex(q[c], q[c + half])
+        for j in range(5):
+            zk = complex(k[j, c], k[j, c + half])
+            assert abs(got[c, j] - (zq * zk.conjugate()).real) < 1e-12
+
+
+def pin_calib_fc_scores_sum_to_full_dot():
+    r = _rng(41)
+    q = r.standard_normal(64)
+    k = r.standard_normal((30, 64))
+    assert np.allclose(oracle.calibrate.fc_scores(q, k).sum(axis=0), k @ q, atol=1e-12)
+
+
+def pin_calib_single_signal_fc():
+    # A query carrying FC 3 alone: the head's scores are FC 3's, so CA(3) = 1.
+    # An FC whose key columns are zero scores every token 0, so its top-k is
+    # the k lowest positions.
+    r = _rng(42)
+    d, half, n, k = 16, 8, 40, 6
+    q = np.zeros(d)
+    q[3], q[3 + half] = r.standard_normal(2)
+    keys = r.standard_normal((n, d))
+    keys[:, 5] = 0.0
+    keys[:, 5 + half] = 0.0
+    ca = oracle.calibrate.contextual_agreement(q, keys, k)
+    assert ca[3] == 1.0
+    full = _topk_by_sort((keys @ q).tolist(), k)
+    assert ca[5] == len(set(full) & set(range(k))) / k
+
+
+def pin_calib_topk_covering_all_agrees():
+    r = _rng(43)
+    q = r.standard_normal(32)
+    keys = r.standard_normal((7, 32))
+    assert np.all(oracle.calibrate.contextual_agreement(q, keys, 7) == 1.0)
+    assert np.all(oracle.calibrate.contextual_agreement(q, keys, 50) == 1.0)
+
+
+def pin_calib_brute_force():
+    r = _rng(44)
+    for _ in range(40):
+        n = int(r.integers(2, 10))
+        k = int(r.integers(1, 5))
+        d = 8
+        # Small integers force many ties in both the FC and the full scores.
+        q = r.integers(-2, 3, size=d).astype(np.float64)
+        keys = r.integers(-2, 3, size=(n, d)).astype(np.float64)
+        got = oracle.calibrate.contextual_agreement(q, keys, k)
+        kk = min(k, n)
+        full = _topk_by_sort([float(np.dot(keys[j], q)) for j in range(n)], kk)
+        for c in range(d // 2):
+            s = [q[c] * keys[j, c] + q[c + 4] * keys[j, c + 4] for j in range(n)]
+            want = len(set(_topk_by_sort(s, kk)) & set(full)) / kk
+            assert got[c] == want, (c, got[c], want)
+
+
+def pin_calib_dominant_hand_example():
+    # [samples, heads, C]; means per head: [0.5, 0.4, 0.8, 0.1] and
+    # [0.1, 0.3, 0.2, 0.3] (worked by hand).
+    ca = np.array([[[0.5, 0.5, 0.9, 0.1], [0.2, 0.2, 0.2, 0.2]],
+                   [[0.5, 0.3, 0.7, 0.1], [0.0, 0.4, 0.2, 0.4]]])
+    assert oracle.calibrate.dominant_from_ca(ca, 2).tolist() == [[0, 2], [1, 3]]
+    assert oracle.calibrate.dominant_from_ca(ca, 1).tolist() == [[2], [1]]
+    assert oracle.calibrate.dominant_from_ca(ca[0], 3).tolist() == [[0, 1, 2], [0, 1, 2]]
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

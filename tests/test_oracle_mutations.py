@@ -19,6 +19,9 @@ _select = oracle.select.select_topb
 _attend = oracle.fac.attend_subset
 _query_rot = oracle.decode.OracleState.query_rot
 _append = oracle.decode.OracleState.append
+_fc_scores = oracle.calibrate.fc_scores
+_ca = oracle.calibrate.contextual_agreement
+_dominant = oracle.calibrate.dominant_from_ca
 
 
 def rope_interleaved(x, pos, theta):
@@ -123,6 +126,34 @@ def append_rotates_v(self, b, k_new, v_new):
     _append(self, b, k_new, oracle.rope.rope_rotate(v_new, pos[None, :], self.theta))
 
 
+def fc_scores_swapped_partner(q, k):
+    q, k = np.asarray(q, np.float64), np.asarray(k, np.float64)
+    half = q.shape[-1] // 2
+    return (k[:, :half] * q[None, half:]).T + (k[:, half:] * q[None, :half]).T
+
+
+def ca_unnormalised(q, k, topk):
+    return _ca(q, k, topk) * min(topk, np.asarray(k).shape[0])
+
+
+def ca_against_first_fc(q, k, topk):
+    s_c = oracle.calibrate.fc_scores(q, k)
+    kk = min(topk, s_c.shape[1])
+    ref = set(oracle.select.select_topb(s_c[0], kk).tolist())
+    return np.array([len(ref & set(oracle.select.select_topb(s, kk).tolist())) / kk for s in s_c])
+
+
+def dominant_lowest(ca, n_dom):
+    return _dominant(-np.asarray(ca, np.float64), n_dom)
+
+
+def dominant_ties_high(ca, n_dom):
+    a = np.asarray(ca, np.float64)
+    a = a.mean(axis=0) if a.ndim == 3 else a
+    picks = [np.sort(np.lexsort((-np.arange(a.shape[1]), -row))[:n_dom]) for row in a]
+    return np.array(picks, dtype=np.int32)
+
+
 MUTATIONS = {
     "rope_interleaved_pairs": (oracle.rope, "rope_rotate", rope_interleaved),
     "rope_backwards": (oracle.rope, "rope_rotate", rope_backwards),
@@ -140,6 +171,11 @@ MUTATIONS = {
     "fac_keys_as_values": (oracle.fac, "attend_subset", attend_k_for_v),
     "decode_query_at_n": (oracle.decode.OracleState, "query_rot", query_at_n),
     "decode_rotates_values": (oracle.decode.OracleState, "append", append_rotates_v),
+    "calib_swapped_partner": (oracle.calibrate, "fc_scores", fc_scores_swapped_partner),
+    "calib_ca_unnormalised": (oracle.calibrate, "contextual_agreement", ca_unnormalised),
+    "calib_ca_wrong_reference": (oracle.calibrate, "contextual_agreement", ca_against_first_fc),
+    "calib_dominant_lowest": (oracle.calibrate, "dominant_from_ca", dominant_lowest),
+    "calib_dominant_ties_high": (oracle.calibrate, "dominant_from_ca", dominant_ties_high),
 }
 
 
