@@ -194,6 +194,43 @@ fasa_status fasa_dense_attn(fasa_ctx* ctx, const void* k_cache, const void* v_ca
                             float* out, void* workspace, hipStream_t stream);
 
 /*
+ * Offline calibration of the dominant FCs (gist.science/pt, "Resumo Tecnico"
+ * section 2, TIP "Calibracao Offline": I_dom of each head comes from a
+ * contextual agreement between one FC's attention scores and the full
+ * head's on a small calibration set).  The pages give no formula; here the
+ * agreement of FC c for one calibration query of head h is
+ *   CA = |top_k(s_c) intersect top_k(s)| / min(k, n_b),
+ * with s_c[j] = q~_c K[j][c] + q~_{c+C} K[j][c+C] FC c's score, s = sum_c s_c
+ * the full head's, and top_k the selection rule of fasa_topk (ties to the
+ * lower position).  Each sequence b of the context is one calibration
+ * sample: q is its query (pre-RoPE, rotated to position n_b - 1),
+ * seq_lens[b] = n_b its cached tokens in k_cache (filled by fasa_append_kv).
+ * The context's own dominant FCs are not used (any valid set will do).
+ * k_cache: device [b][Hkv][cap][d] dtype; q: device [b][Hq][d] dtype;
+ * seq_lens: device int32 [b]; topk in [1, min(8192, capacity)]; ca: device
+ * float [b][Hq][C], written.  workspace: device, at least
+ * fasa_calibrate_workspace_bytes(ctx, topk) bytes, zero-filled once with
+ * fasa_workspace_init-style zeros (any earlier fasa_calibrate leaves it
+ * valid); holds the full score matrix, b * Hq * (C + 1) * cap floats.
+ * Errors: host-checkable arguments as the other calls; lengths outside
+ * [0, min(max_seq_len, capacity)] raise FASA_DEVFLAG_SEQ_LEN (zeros written).
+ */
+size_t fasa_calibrate_workspace_bytes(const fasa_ctx* ctx, int topk);
+fasa_status fasa_calibrate(fasa_ctx* ctx, const void* k_cache, const void* q,
+                           const int32_t* seq_lens, int max_seq_len, int topk, float* ca,
+                           void* workspace, hipStream_t stream);
+
+/*
+ * Host-only: I_dom from agreement values (no GPU call).  ca: host float
+ * [samples][n_q_heads][n_fc]; per head the n_dom FCs of highest mean
+ * agreement over the samples, equal means to the lower FC, written ascending
+ * to dom_out: host int32 [n_q_heads][n_dom].  FASA_ERR_INVALID_ARG for a null
+ * pointer or sizes out of range (1 <= n_dom <= n_fc, samples >= 1).
+ */
+fasa_status fasa_select_dominant(const float* ca, int samples, int n_q_heads, int n_fc,
+                                 int n_dom, int32_t* dom_out);
+
+/*
  * Synchronise `stream`, read and clear the workspace's device error flag.
  * *flags (may be NULL) receives the FASA_DEVFLAG_* bits.  Returns
  * FASA_ERR_DEVICE_FLAG when any bit was set.
@@ -219,7 +256,8 @@ typedef enum {
   FASA_K_FAC = 4,       /* sparse attention */
   FASA_K_DENSE = 5,     /* dense comparator */
   FASA_K_SELECT_FAC = 6, /* top-B fused with FAC (budgets up to 1024) */
-  FASA_K_COUNT = 7
+  FASA_K_CALIBRATE = 7, /* fasa_calibrate, all its kernels together */
+  FASA_K_COUNT = 8
 } fasa_kernel_family;
 fasa_status fasa_timing_enable(fasa_ctx* ctx, int enable);
 fasa_status fasa_timing_collect(fasa_ctx* ctx, double* total_ms, int32_t* launches);

@@ -43,6 +43,10 @@ _SIGS = {
     "fasa_decode_step": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int,
                                   _vp, _vp, _vp, ctypes.c_uint, _vp]),
     "fasa_dense_attn": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp]),
+    "fasa_calibrate_workspace_bytes": (_c_size, [_vp, _c_int]),
+    "fasa_calibrate": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp]),
+    "fasa_select_dominant": (_c_int, [ctypes.POINTER(ctypes.c_float), _c_int, _c_int, _c_int,
+                                      _c_int, _i32p]),
     "fasa_check": (_c_int, [_vp, _vp, _vp, ctypes.POINTER(ctypes.c_uint32)]),
     "fasa_timing_enable": (_c_int, [_vp, _c_int]),
     "fasa_timing_collect": (_c_int, [_vp, ctypes.POINTER(ctypes.c_double), _i32p]),
@@ -236,7 +240,25 @@ class Context:
                                   _ptr(seq_lens), int(max_seq_len), _ptr(out), _ptr(workspace),
                                   self._stream(stream)), "fasa_dense_attn")
 
-    KERNEL_FAMILIES = ("append", "prologue", "tip", "topk", "fac", "dense", "select_fac")
+    def calibrate_workspace_bytes(self, topk):
+        return int(_lib.fasa_calibrate_workspace_bytes(self._h, int(topk)))
+
+    def new_calibration_workspace(self, topk):
+        return torch.zeros(self.calibrate_workspace_bytes(topk), dtype=torch.uint8,
+                           device=self.device)
+
+    def calibrate(self, k_cache, q, seq_lens, max_seq_len, topk, ca, workspace, stream=None):
+        """Contextual agreement ca[b][h][c] of every FC with the full head (see
+        fasa_calibrate in include/fasa.h); each sequence is one sample."""
+        self._want(q, "q", self.torch_dtype, (self.batch, self.n_q_heads, self.head_dim))
+        self._want(ca, "ca", torch.float32, (self.batch, self.n_q_heads, self.head_dim // 2))
+        self._want(seq_lens, "seq_lens", torch.int32, (self.batch,))
+        _chk(_lib.fasa_calibrate(self._h, _ptr(k_cache), _ptr(q), _ptr(seq_lens),
+                                 int(max_seq_len), int(topk), _ptr(ca), _ptr(workspace),
+                                 self._stream(stream)), "fasa_calibrate")
+
+    KERNEL_FAMILIES = ("append", "prologue", "tip", "topk", "fac", "dense", "select_fac",
+                       "calibrate")
 
     def timing_enable(self, enable=True):
         _chk(_lib.fasa_timing_enable(self._h, 1 if enable else 0), "fasa_timing_enable")
@@ -256,6 +278,20 @@ class Context:
         if st not in (0, -5):
             raise FasaError(st, "fasa_check")
         return int(flags.value)
+
+
+def select_dominant(ca, n_dom):
+    """I_dom from agreement values (host, fasa_select_dominant): ca is a host
+    array [samples, heads, C] (or [heads, C]); returns int32 [heads, n_dom]."""
+    a = np.ascontiguousarray(np.asarray(ca, dtype=np.float32))
+    if a.ndim == 2:
+        a = a[None]
+    samples, heads, n_fc = a.shape
+    out = np.empty((heads, int(n_dom)), dtype=np.int32)
+    _chk(_lib.fasa_select_dominant(a.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), samples,
+                                   heads, n_fc, int(n_dom), out.ctypes.data_as(_i32p)),
+         "fasa_select_dominant")
+    return out
 
 
 def status_string(status):

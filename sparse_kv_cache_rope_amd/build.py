@@ -17,7 +17,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfasa.so")
 ROOT = os.path.dirname(HERE)
 
-SOURCES = ["api.cpp", "rope_append.hip", "tip.hip", "topk.hip", "select2.hip", "attention.hip"]
+SOURCES = ["api.cpp", "rope_append.hip", "tip.hip", "topk.hip", "select2.hip", "attention.hip",
+           "calibrate.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -473,6 +474,58 @@ fasa_status fasa_dense_attn(fasa_ctx* c, const void* k_cache, const void* v_cach
     FASA_HIP(launch_dense(c, k_cache, v_cache, reinterpret_cast<const int32_t*>(ws + c->ws.nb),
                           max_seq_len, out, ws, stream),
              "fasa_dense_attn");
+  }
+  return ok();
+}
+
+size_t fasa_calibrate_workspace_bytes(const fasa_ctx* c, int topk) {
+  if (!c || topk < 1) return 0;
+  return calib_layout(c, topk).ws.total;
+}
+
+fasa_status fasa_calibrate(fasa_ctx* c, const void* k_cache, const void* q,
+                           const int32_t* seq_lens, int max_seq_len, int topk, float* ca,
+                           void* workspace, hipStream_t stream) {
+  FASA_TRY(check_ctx(c));
+  FASA_TRY(check_len(c, max_seq_len));
+  if (topk < 1 || topk > c->cap || topk > kCalibMaxTopk)
+    return fail(FASA_ERR_INVALID_ARG, "topk %d not in [1, min(%d, capacity)]", topk,
+                kCalibMaxTopk);
+  FASA_NONNULL(k_cache);
+  FASA_NONNULL(q);
+  FASA_NONNULL(seq_lens);
+  FASA_NONNULL(ca);
+  FASA_NONNULL(workspace);
+  {
+    Timed t(c, FASA_K_CALIBRATE, stream);
+    FASA_HIP(launch_calibrate(c, k_cache, q, seq_lens, max_seq_len, topk, ca,
+                              static_cast<uint8_t*>(workspace), stream),
+             "fasa_calibrate");
+  }
+  return ok();
+}
+
+fasa_status fasa_select_dominant(const float* ca, int samples, int n_q_heads, int n_fc,
+                                 int n_dom, int32_t* dom_out) {
+  if (!ca || !dom_out) return fail(FASA_ERR_INVALID_ARG, "null pointer");
+  if (samples < 1 || n_q_heads < 1 || n_fc < 1 || n_dom < 1 || n_dom > n_fc)
+    return fail(FASA_ERR_INVALID_ARG, "sizes out of range (samples %d, heads %d, fc %d, dom %d)",
+                samples, n_q_heads, n_fc, n_dom);
+  std::vector<double> mean(n_fc);
+  std::vector<int> order(n_fc);
+  for (int h = 0; h < n_q_heads; ++h) {
+    for (int f = 0; f < n_fc; ++f) {
+      double s = 0.0;
+      for (int b = 0; b < samples; ++b) s += ca[((size_t)b * n_q_heads + h) * n_fc + f];
+      mean[f] = s / samples;
+      order[f] = f;
+    }
+    // Highest mean first, equal means to the lower FC.
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int x, int y) { return mean[x] > mean[y]; });
+    std::vector<int> pick(order.begin(), order.begin() + n_dom);
+    std::sort(pick.begin(), pick.end());
+    for (int f = 0; f < n_dom; ++f) dom_out[(size_t)h * n_dom + f] = pick[f];
   }
   return ok();
 }

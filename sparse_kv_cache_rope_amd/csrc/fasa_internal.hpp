@@ -134,4 +134,16 @@ hipError_t launch_select(const fasa_ctx* c, const float* scores, const int32_t* 
                          hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
+// Calibration (calibrate.hip): its workspace regions (err, nb, qrot, scores
+// [b][Hq (C + 1)][cap], idx [b][Hq (C + 1)][topk], cand), and the launcher.
+struct CalLayout {
+  WsLayout ws;
+};
+CalLayout calib_layout(const fasa_ctx* c, int topk);
+// Largest k the agreement kernel keeps in LDS.
+constexpr int kCalibMaxTopk = 8192;
+hipError_t launch_calibrate(const fasa_ctx* c, const void* k_cache, const void* q,
+                            const int32_t* seq_lens, int max_seq_len, int topk, float* ca,
+                            uint8_t* ws, hipStream_t s);
+
 }  // namespace fasa
