@@ -48,6 +48,8 @@ def parse():
                    help="CPU oracle sample budget (0 disables)")
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--eager", action="store_true", help="time eager launches, no graph")
+    p.add_argument("--no-calibration", action="store_true",
+                   help="skip timing fasa_calibrate (offline I_dom calibration)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run 4 plain device-to-device copies of MIB MiB (the "
                         "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -84,6 +86,37 @@ def traffic_from_profile():
     if prof.get("source_sha256") != h.hexdigest():
         return None
     return prof.get("hbm_bytes_per_launch")
+
+
+def calibration_timing(ctx, k_cache, q, seq_full, msl, w, reps, topk=256):
+    """fasa_calibrate on one layer of the workload (each sequence one
+    calibration sample): HIP events around `reps` back-to-back calls."""
+    import torch
+    ws = ctx.new_calibration_workspace(topk)
+    ca = torch.zeros(w.batch, w.n_q_heads, w.head_dim // 2, dtype=torch.float32,
+                     device=q.device)
+    for _ in range(2):
+        ctx.calibrate(k_cache, q, seq_full, msl, topk, ca, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(4, min(reps, 32))
+    e0.record()
+    for _ in range(reps):
+        ctx.calibrate(k_cache, q, seq_full, msl, topk, ca, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    assert ctx.check(ws) == 0
+    ms = e0.elapsed_time(e1) / reps
+    n = int(seq_full.sum().item())
+    C = w.head_dim // 2
+    es = 2 if w.dtype == "bf16" else 4
+    # K rows read once per KV head, every FC score row written once.
+    score_bytes = n * w.n_q_heads * (C + 1) * 4
+    k_bytes = n * w.n_kv_heads * w.head_dim * es
+    return {"topk": topk, "ms_per_call": ms, "samples_per_call": w.batch,
+            "score_rows_per_sample": w.n_q_heads * (C + 1),
+            "k_plus_score_bytes": k_bytes + score_bytes,
+            "gbps_on_those_bytes": (k_bytes + score_bytes) / (ms * 1e-3) / 1e9}
 
 
 def cpu_baseline(w, x, budget_s):
@@ -287,6 +320,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": tip_bytes},
     }
+    if not args.no_calibration:
+        res["calibration"] = calibration_timing(ctx, layers[0][0], q, seq_full, msl, w, K)
     if ms_dense is not None:
         res["dense"] = {"ms_per_step": ms_dense, "bytes_per_step": dense_bytes,
                         "hbm_gbps": dense_bytes / (ms_dense * 1e-3) / 1e9,
