@@ -17,8 +17,9 @@ HIP graph of L steps; inputs are resident in HBM before timing starts.
 Printed: one JSON line with the metric (context tokens scanned per second),
 the fraction of HBM peak on the algorithmic bytes, the dominant kernel's
 roofline figure (TIP: sidecar bytes read + score bytes written / its average
-duration from HIP events bracketing each launch), the in-build dense decode comparator and the CPU
-oracle baseline on a bounded sample.
+duration from HIP events over back-to-back launches), the in-build dense
+decode comparator, the step with K/V caches in pinned host memory (FASA-M)
+and the CPU oracle baseline on a bounded sample.
 """
 
 import argparse
@@ -50,6 +51,8 @@ def parse():
     p.add_argument("--eager", action="store_true", help="time eager launches, no graph")
     p.add_argument("--no-calibration", action="store_true",
                    help="skip timing fasa_calibrate (offline I_dom calibration)")
+    p.add_argument("--no-fasa-m", action="store_true",
+                   help="skip timing the step with K/V caches in pinned host memory")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run 4 plain device-to-device copies of MIB MiB (the "
                         "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -117,6 +120,60 @@ def calibration_timing(ctx, k_cache, q, seq_full, msl, w, reps, topk=256):
             "score_rows_per_sample": w.n_q_heads * (C + 1),
             "k_plus_score_bytes": k_bytes + score_bytes,
             "gbps_on_those_bytes": (k_bytes + score_bytes) / (ms * 1e-3) / 1e9}
+
+
+def fasa_m_timing(ctx, w, x, q, kn, vn, seq, seq_full, msl, reps, with_dense):
+    """FASA-M: one layer with its K and V caches in pinned host memory (the
+    device reaches them over the host link), the sidecar in HBM.  HIP events
+    around `reps` back-to-back decode steps, and around dense decode over the
+    same host-resident caches for comparison."""
+    import torch
+    dev = q.device
+    k, v, side = ctx.new_cache(kv_on_host=True)
+    ws = ctx.new_workspace()
+    td = k.dtype
+    zero = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    ctx.append_kv(k, v, side, torch.from_numpy(x["k_prefill"]).to(dev, td),
+                  torch.from_numpy(x["v_prefill"]).to(dev, td), zero, ws)
+    out = torch.empty(w.batch, w.n_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    idx = torch.empty(w.batch, w.n_q_heads, w.budget, dtype=torch.int32, device=dev)
+
+    def run(fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms = run(lambda: ctx.decode_step(k, v, side, q, kn, vn, seq, msl, w.budget, out, ws,
+                                     idx_out=idx), max(8, min(reps, 64)))
+    assert ctx.check(ws) == 0
+    es = k.element_size()
+    n_b = x["ctx"].astype(np.int64)
+    # Host-link bytes of a step: the B selected K and V rows per query head
+    # (FAC) and the appended K and V rows.
+    link = int(sum(min(w.budget, n) for n in n_b)) * 2 * w.head_dim * es * w.n_q_heads \
+        + w.batch * w.n_kv_heads * 2 * w.head_dim * es
+    kv_bytes = 2 * k.numel() * es
+    res = {"ms_per_step": ms, "value": float(n_b.sum()) / (ms * 1e-3),
+           "unit": "context tokens/s", "host_link_bytes_per_step": link,
+           "host_link_gbps": link / (ms * 1e-3) / 1e9,
+           "device_bytes_per_layer": ctx.sidecar_bytes,
+           "device_bytes_per_layer_fasa_c": ctx.sidecar_bytes + kv_bytes,
+           "device_kv_compression": (ctx.sidecar_bytes + kv_bytes) / ctx.sidecar_bytes,
+           "host_bytes_per_layer": kv_bytes}
+    if with_dense:
+        dense_out = torch.empty_like(out)
+        res["dense_from_host_ms"] = run(
+            lambda: ctx.dense_attn(k, v, q, seq_full, msl, dense_out, ws), 4)
+        res["sparse_speedup_from_host"] = res["dense_from_host_ms"] / ms
+    del k, v
+    return res
 
 
 def cpu_baseline(w, x, budget_s):
@@ -322,6 +379,9 @@ def main():
     }
     if not args.no_calibration:
         res["calibration"] = calibration_timing(ctx, layers[0][0], q, seq_full, msl, w, K)
+    if not args.no_fasa_m:
+        res["fasa_m"] = fasa_m_timing(ctx, w, x, q, kn, vn, seq, seq_full, msl, K,
+                                      not args.no_dense)
     if ms_dense is not None:
         res["dense"] = {"ms_per_step": ms_dense, "bytes_per_step": dense_bytes,
                         "hbm_gbps": dense_bytes / (ms_dense * 1e-3) / 1e9,

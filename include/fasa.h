@@ -22,6 +22,9 @@
  *   Accumulation is fp32; outputs and scores are float.
  * - K cache, V cache: [b][Hkv][cap][d] dtype.  Slot j holds absolute position
  *   j.  K holds RoPE(k, j) rounded once (nearest-even) to dtype; V holds v.
+ *   Both may live in device memory or (FASA-M, same page, "Variantes de
+ *   Implementacao") in pinned host memory the device maps at the same address
+ *   (fasa_pointer_kind() says which); every other buffer is device memory.
  * - Sidecar: the K columns of each KV head's union U_g of its query heads'
  *   dominant FCs, packed FC-major so TIP reads them with coalesced loads:
  *   [b][P][cap] pairs, P = sum_g |U_g|, plane fasa_sidecar_layout() gives the
@@ -229,6 +232,20 @@ fasa_status fasa_calibrate(fasa_ctx* ctx, const void* k_cache, const void* q,
  */
 fasa_status fasa_select_dominant(const float* ca, int samples, int n_q_heads, int n_fc,
                                  int n_dom, int32_t* dom_out);
+
+/*
+ * Where a buffer lives, for callers that place the K and V caches in host
+ * memory (FASA-M, gist.science/pt, "Resumo Tecnico" section 2, "Variantes de
+ * Implementacao": the value cache and the non-dominant key parts go to CPU
+ * memory, the GPU keeps what TIP needs, here the sidecar).  Every call takes
+ * such caches unchanged: kernels read and write them through the host link.
+ * Returns FASA_PTR_DEVICE for device memory, FASA_PTR_HOST_MAPPED for pinned
+ * host memory the current device reaches at the same address (hipHostMalloc,
+ * torch pin_memory), FASA_PTR_UNUSABLE otherwise (pageable host memory, or a
+ * pinned buffer whose device alias differs).  No GPU work is enqueued.
+ */
+typedef enum { FASA_PTR_UNUSABLE = 0, FASA_PTR_DEVICE = 1, FASA_PTR_HOST_MAPPED = 2 } fasa_ptr_kind;
+fasa_ptr_kind fasa_pointer_kind(const void* ptr);
 
 /*
  * Synchronise `stream`, read and clear the workspace's device error flag.

@@ -47,6 +47,7 @@ _SIGS = {
     "fasa_calibrate": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp]),
     "fasa_select_dominant": (_c_int, [ctypes.POINTER(ctypes.c_float), _c_int, _c_int, _c_int,
                                       _c_int, _i32p]),
+    "fasa_pointer_kind": (_c_int, [_vp]),
     "fasa_check": (_c_int, [_vp, _vp, _vp, ctypes.POINTER(ctypes.c_uint32)]),
     "fasa_timing_enable": (_c_int, [_vp, _c_int]),
     "fasa_timing_collect": (_c_int, [_vp, ctypes.POINTER(ctypes.c_double), _i32p]),
@@ -143,11 +144,22 @@ class Context:
         return off, fc[:P]
 
     # -- allocation helpers (plain torch memory) ----------------------------
-    def new_cache(self):
-        """Zeroed K cache, V cache and sidecar tensors."""
+    def new_cache(self, kv_on_host=False):
+        """Zeroed K cache, V cache and sidecar tensors.  With kv_on_host the K
+        and V caches are pinned host memory the GPU reads and writes in place
+        (FASA-M); the sidecar, which TIP streams, stays on the device."""
         shape = (self.batch, self.n_kv_heads, self.capacity, self.head_dim)
-        k = torch.zeros(shape, dtype=self.torch_dtype, device=self.device)
-        v = torch.zeros(shape, dtype=self.torch_dtype, device=self.device)
+        if kv_on_host:
+            k = torch.zeros(shape, dtype=self.torch_dtype, pin_memory=True)
+            v = torch.zeros(shape, dtype=self.torch_dtype, pin_memory=True)
+            for name, t in (("K", k), ("V", v)):
+                kind = pointer_kind(t)
+                if kind != PTR_HOST_MAPPED:
+                    raise RuntimeError(f"pinned {name} cache is not reachable from the device "
+                                       f"at its host address (kind {kind})")
+        else:
+            k = torch.zeros(shape, dtype=self.torch_dtype, device=self.device)
+            v = torch.zeros(shape, dtype=self.torch_dtype, device=self.device)
         P = _lib.fasa_sidecar_layout(self._h, None, None)
         side = torch.zeros((self.batch, P, self.capacity, 2), dtype=self.torch_dtype,
                            device=self.device)
@@ -161,6 +173,20 @@ class Context:
     def _stream(self, stream):
         s = stream if stream is not None else torch.cuda.current_stream(self.device)
         return _vp(s.cuda_stream)
+
+    def _cache(self, t, name):
+        """A K or V cache: on the context's device, or pinned host memory the
+        device maps at the same address (FASA-M); anything else would fault."""
+        shape = (self.batch, self.n_kv_heads, self.capacity, self.head_dim)
+        if t.dtype != self.torch_dtype or not t.is_contiguous() or tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be a contiguous {self.torch_dtype} tensor of shape "
+                             f"{shape} (got {t.dtype}, {tuple(t.shape)})")
+        if t.device == self.device:
+            return _ptr(t)
+        if t.device.type == "cpu" and pointer_kind(t) == PTR_HOST_MAPPED:
+            return _ptr(t)
+        raise ValueError(f"{name} must be on {self.device} or pinned host memory mapped "
+                         f"into it (got {t.device})")
 
     def _want(self, t, name, dtype, shape=None):
         if t.device != self.device:
@@ -183,7 +209,7 @@ class Context:
         self._want(k_new, "k_new", self.torch_dtype, (b, hkv, n_new, d))
         self._want(v_new, "v_new", self.torch_dtype, (b, hkv, n_new, d))
         self._want(start_pos, "start_pos", torch.int32, (b,))
-        _chk(_lib.fasa_append_kv(self._h, _ptr(k_cache), _ptr(v_cache), _ptr(sidecar),
+        _chk(_lib.fasa_append_kv(self._h, self._cache(k_cache, 'k_cache'), self._cache(v_cache, 'v_cache'), _ptr(sidecar),
                                  _ptr(k_new), _ptr(v_new), _ptr(start_pos), n_new,
                                  _ptr(workspace), self._stream(stream)), "fasa_append_kv")
 
@@ -211,7 +237,7 @@ class Context:
         self._want(idx, "idx", torch.int32, (self.batch, self.n_q_heads, budget))
         self._want(out, "out", torch.float32, (self.batch, self.n_q_heads, self.head_dim))
         self._want(seq_lens, "seq_lens", torch.int32, (self.batch,))
-        _chk(_lib.fasa_sparse_attn(self._h, _ptr(k_cache), _ptr(v_cache), _ptr(q),
+        _chk(_lib.fasa_sparse_attn(self._h, self._cache(k_cache, 'k_cache'), self._cache(v_cache, 'v_cache'), _ptr(q),
                                    _ptr(seq_lens), _ptr(idx), int(budget), _ptr(out),
                                    _ptr(workspace), self._stream(stream)), "fasa_sparse_attn")
 
@@ -225,7 +251,7 @@ class Context:
         self._want(out, "out", torch.float32, (b, hq, d))
         if idx_out is not None:
             self._want(idx_out, "idx_out", torch.int32, (b, hq, budget))
-        _chk(_lib.fasa_decode_step(self._h, _ptr(k_cache), _ptr(v_cache), _ptr(sidecar),
+        _chk(_lib.fasa_decode_step(self._h, self._cache(k_cache, 'k_cache'), self._cache(v_cache, 'v_cache'), _ptr(sidecar),
                                    _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(seq_lens),
                                    int(max_seq_len), int(budget), _ptr(out), _ptr(idx_out),
                                    _ptr(workspace), ADVANCE_SEQ_LENS if advance else 0,
@@ -236,7 +262,7 @@ class Context:
         self._want(q, "q", self.torch_dtype, (self.batch, self.n_q_heads, self.head_dim))
         self._want(out, "out", torch.float32, (self.batch, self.n_q_heads, self.head_dim))
         self._want(seq_lens, "seq_lens", torch.int32, (self.batch,))
-        _chk(_lib.fasa_dense_attn(self._h, _ptr(k_cache), _ptr(v_cache), _ptr(q),
+        _chk(_lib.fasa_dense_attn(self._h, self._cache(k_cache, 'k_cache'), self._cache(v_cache, 'v_cache'), _ptr(q),
                                   _ptr(seq_lens), int(max_seq_len), _ptr(out), _ptr(workspace),
                                   self._stream(stream)), "fasa_dense_attn")
 
@@ -253,7 +279,7 @@ class Context:
         self._want(q, "q", self.torch_dtype, (self.batch, self.n_q_heads, self.head_dim))
         self._want(ca, "ca", torch.float32, (self.batch, self.n_q_heads, self.head_dim // 2))
         self._want(seq_lens, "seq_lens", torch.int32, (self.batch,))
-        _chk(_lib.fasa_calibrate(self._h, _ptr(k_cache), _ptr(q), _ptr(seq_lens),
+        _chk(_lib.fasa_calibrate(self._h, self._cache(k_cache, 'k_cache'), _ptr(q), _ptr(seq_lens),
                                  int(max_seq_len), int(topk), _ptr(ca), _ptr(workspace),
                                  self._stream(stream)), "fasa_calibrate")
 
@@ -278,6 +304,14 @@ class Context:
         if st not in (0, -5):
             raise FasaError(st, "fasa_check")
         return int(flags.value)
+
+
+PTR_UNUSABLE, PTR_DEVICE, PTR_HOST_MAPPED = 0, 1, 2
+
+
+def pointer_kind(t):
+    """fasa_pointer_kind of a tensor's storage."""
+    return int(_lib.fasa_pointer_kind(_vp(t.data_ptr())))
 
 
 def select_dominant(ca, n_dom):

@@ -530,6 +530,18 @@ fasa_status fasa_select_dominant(const float* ca, int samples, int n_q_heads, in
   return ok();
 }
 
+fasa_ptr_kind fasa_pointer_kind(const void* ptr) {
+  if (!ptr) return FASA_PTR_UNUSABLE;
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, ptr) != hipSuccess) {
+    (void)hipGetLastError();  // pageable memory reports an error: clear it
+    return FASA_PTR_UNUSABLE;
+  }
+  if (attr.type == hipMemoryTypeDevice) return FASA_PTR_DEVICE;
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer == ptr) return FASA_PTR_HOST_MAPPED;
+  return FASA_PTR_UNUSABLE;
+}
+
 fasa_status fasa_check(fasa_ctx* c, void* workspace, hipStream_t stream, uint32_t* flags) {
   FASA_TRY(check_ctx(c));
   FASA_NONNULL(workspace);

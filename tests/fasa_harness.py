@@ -33,12 +33,12 @@ class GpuSetup:
     """Context, caches and workspace for workload ``w`` with inputs ``x``,
     prefilled with ctx[b] - 1 tokens per sequence."""
 
-    def __init__(self, fasa, w, x, max_budget=None, capacity=None):
+    def __init__(self, fasa, w, x, max_budget=None, capacity=None, kv_on_host=False):
         self.w, self.x = w, x
         self.cap = capacity or w.capacity
         self.ctx = fasa.Context(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, self.cap,
                                 w.rope_theta, w.dtype, x["dom"], max_budget or w.budget)
-        self.k, self.v, self.side = self.ctx.new_cache()
+        self.k, self.v, self.side = self.ctx.new_cache(kv_on_host=kv_on_host)
         self.ws = self.ctx.new_workspace()
         self.td = torch_dtype(w)
         L = x["k_prefill"].shape[2]
