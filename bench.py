@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--eager", action="store_true", help="time eager launches, no graph")
     p.add_argument("--no-calibration", action="store_true",
                    help="skip timing fasa_calibrate (offline I_dom calibration)")
+    p.add_argument("--no-per-head", action="store_true",
+                   help="skip timing the step with a budget per query head")
     p.add_argument("--no-fasa-m", action="store_true",
                    help="skip timing the step with K/V caches in pinned host memory")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -174,6 +176,59 @@ def fasa_m_timing(ctx, w, x, q, kn, vn, seq, seq_full, msl, reps, with_dense):
         res["sparse_speedup_from_host"] = res["dense_from_host_ms"] / ms
     del k, v
     return res
+
+
+def per_head_timing(fasa, w, x, layers, q, kn, vn, seq, msl, dev, reps):
+    """Budgets per query head: a linear allocation over the heads (head h gets
+    round(2B (h + 0.5) / Hq), mean B, at most 2B) on the same rotated layers,
+    replayed from a HIP graph like the uniform step."""
+    import torch
+    import workloads as W
+    top = 2 * w.budget
+    ctx2 = fasa.Context(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.capacity,
+                        w.rope_theta, w.dtype, x["dom"], top, device=dev)
+    ws2 = ctx2.new_workspace()
+    hb = W.head_budgets(0, w.n_q_heads, top, "ramp")
+    hb_d = torch.from_numpy(hb).to(dev)
+    out = torch.empty(w.batch, w.n_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    idx = torch.empty(w.batch, w.n_q_heads, top, dtype=torch.int32, device=dev)
+    L = len(layers)
+
+    def one(i):
+        k, v, sd = layers[i % L]
+        ctx2.decode_step(k, v, sd, q, kn, vn, seq, msl, top, out, ws2, idx_out=idx,
+                         head_budgets=hb_d)
+
+    for i in range(L):
+        one(i)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(L):
+            one(i)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(L):
+            one(i)
+    g.replay()
+    torch.cuda.synchronize()
+    n_rep = max(1, reps // L)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n_rep):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    assert ctx2.check(ws2) == 0
+    got = (idx.cpu().numpy() >= 0).sum(axis=2)
+    assert np.array_equal(got, np.minimum(hb[None, :], x["ctx"][:, None]))
+    ms = e0.elapsed_time(e1) / (n_rep * L)
+    return {"allocation": "linear over heads, round(2B (h + 0.5) / Hq)", "mean_budget":
+            float(hb.mean()), "min_budget": int(hb.min()), "max_budget": int(hb.max()),
+            "ms_per_step": ms, "value": float(x["ctx"].sum()) / (ms * 1e-3),
+            "unit": "context tokens/s"}
 
 
 def cpu_baseline(w, x, budget_s):
@@ -379,6 +434,9 @@ def main():
     }
     if not args.no_calibration:
         res["calibration"] = calibration_timing(ctx, layers[0][0], q, seq_full, msl, w, K)
+    if not args.no_per_head and 2 * w.budget <= w.capacity:
+        res["per_head_budgets"] = per_head_timing(fasa, w, x, layers, q, kn, vn, seq, msl, dev,
+                                                  K)
     if not args.no_fasa_m:
         res["fasa_m"] = fasa_m_timing(ctx, w, x, q, kn, vn, seq, seq_full, msl, K,
                                       not args.no_dense)

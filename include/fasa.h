@@ -78,6 +78,7 @@ typedef enum { FASA_F32 = 0, FASA_BF16 = 1 } fasa_dtype;
 #define FASA_DEVFLAG_SEQ_LEN 1u   /* a sequence length outside [1, max_seq_len] or > cap */
 #define FASA_DEVFLAG_INDEX 2u     /* an index >= its sequence length */
 #define FASA_DEVFLAG_APPEND 4u    /* an append beyond cap */
+#define FASA_DEVFLAG_BUDGET 8u    /* a per-head budget outside [0, budget] (clamped) */
 
 /*
  * Create a context for one attention layer's shapes.
@@ -157,6 +158,21 @@ fasa_status fasa_topk(fasa_ctx* ctx, const float* scores, const int32_t* seq_len
                       hipStream_t stream);
 
 /*
+ * Top-B with a budget per query head (the pages' "Variantes de Implementacao"
+ * note that FASA composes with budget allocation across layers; a per-layer
+ * budget is the `budget` of each layer's call, and this call lets the heads
+ * of one layer differ too).  As fasa_topk with B = head_budget[h] for query
+ * head h: idx[b][h][0 .. min(B, n_b)) holds the set, ascending, and -1 fills
+ * the row up to `budget`.  head_budget: device int32 [Hq], each in
+ * [0, budget] (0: the head selects nothing); a value outside is clamped into
+ * that range and raises FASA_DEVFLAG_BUDGET.  budget: as for fasa_topk, the
+ * idx row width and an upper bound on every head_budget[h].
+ */
+fasa_status fasa_topk_per_head(fasa_ctx* ctx, const float* scores, const int32_t* seq_lens,
+                               int max_seq_len, const int32_t* head_budget, int budget,
+                               int32_t* idx, void* workspace, hipStream_t stream);
+
+/*
  * FAC (gist.science/pt, "Resumo Tecnico" section 2, FAC second and third
  * bullets): per (b, h), attention of q~ = RoPE(q, n_b - 1) over the rows
  * idx[b][h][0 .. min(budget, n_b)) of the caches only:
@@ -186,6 +202,19 @@ fasa_status fasa_decode_step(fasa_ctx* ctx, void* k_cache, void* v_cache, void* 
                              int32_t* seq_lens, int max_seq_len, int budget, float* out,
                              int32_t* idx_out, void* workspace, unsigned flags,
                              hipStream_t stream);
+
+/*
+ * fasa_decode_step with a budget per query head: the top-B stage is
+ * fasa_topk_per_head's, so query head h attends over its min(head_budget[h],
+ * n_b) selected rows (a head with budget 0 outputs zeros).  head_budget:
+ * device int32 [Hq] in [0, budget]; budget: idx_out row width and upper bound.
+ */
+fasa_status fasa_decode_step_per_head(fasa_ctx* ctx, void* k_cache, void* v_cache,
+                                      void* sidecar, const void* q, const void* k_new,
+                                      const void* v_new, int32_t* seq_lens, int max_seq_len,
+                                      const int32_t* head_budget, int budget, float* out,
+                                      int32_t* idx_out, void* workspace, unsigned flags,
+                                      hipStream_t stream);
 
 /*
  * Dense full-KV decode attention over all n_b cached tokens (the comparator

@@ -65,15 +65,20 @@ class OracleState:
         g = self.kv_head(h)
         return fac.attend_subset(q_rot_h, self.K[b, g, :n], self.V[b, g, :n], subset)
 
-    def step(self, q, k_new, v_new, budget, heads=None):
+    def step(self, q, k_new, v_new, budget, heads=None, head_budgets=None):
         """One decode step for every sequence.
 
         q: [b, Hq, d] pre-RoPE queries; k_new, v_new: [b, Hkv, d] pre-RoPE.
         ``heads`` limits the query heads computed (the rest stay zero / -1).
-        Returns dict with idx [b, Hq, budget], out [b, Hq, d], tau [b, Hq] and
-        the per-(b, h) score vectors in ``scores``.
+        ``head_budgets`` ([Hq], each in [0, budget]) gives query head h the
+        budget head_budgets[h] (select.py, budgets per head); idx rows stay
+        ``budget`` wide.
+        Returns dict with idx [b, Hq, budget], out [b, Hq, d], tau [b, Hq]
+        (NaN for a head of budget 0) and the per-(b, h) score vectors in
+        ``scores``.
         """
         heads = range(self.hq) if heads is None else heads
+        bh = [budget] * self.hq if head_budgets is None else [int(x) for x in head_budgets]
         idx = np.full((self.batch, self.hq, budget), -1, dtype=np.int64)
         out = np.zeros((self.batch, self.hq, self.d), dtype=np.float64)
         tau = np.zeros((self.batch, self.hq), dtype=np.float64)
@@ -84,9 +89,9 @@ class OracleState:
             qr = self.query_rot(b, np.asarray(q)[b])
             for h in heads:
                 s = self.head_scores(b, h, qr[h])
-                sel = select.select_topb(s, budget)
+                sel = select.select_topb_width(s, bh[h], budget)
                 idx[b, h] = sel
-                tau[b, h] = select.threshold(s, budget)
+                tau[b, h] = select.threshold(s, bh[h]) if bh[h] > 0 else np.nan
                 out[b, h] = self.attend(b, h, qr[h], sel)
                 scores[(b, h)] = s
         return {"idx": idx, "out": out, "tau": tau, "scores": scores}

@@ -34,3 +34,13 @@ def threshold(scores, budget: int) -> float:
     """tau: the score of the budget-th ranked token (the smallest kept score)."""
     s = np.sort(np.asarray(scores, dtype=np.float64))[::-1]
     return float(s[min(budget, s.shape[0]) - 1])
+
+
+def select_topb_width(scores, budget: int, width: int) -> np.ndarray:
+    """T_t of a head whose budget is ``budget`` (0 <= budget <= width), in a
+    row ``width`` wide: the set ascending, then -1 padding.  int64 [width]."""
+    if not 0 <= budget <= width:
+        raise ValueError(f"budget {budget} not in [0, {width}]")
+    out = np.full(width, -1, dtype=np.int64)
+    out[:budget] = select_topb(scores, budget)
+    return out

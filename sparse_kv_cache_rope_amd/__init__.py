@@ -39,9 +39,12 @@ _SIGS = {
     "fasa_append_kv": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp]),
     "fasa_tip_scores": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp]),
     "fasa_topk": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp]),
+    "fasa_topk_per_head": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_int, _vp, _vp, _vp]),
     "fasa_sparse_attn": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp]),
     "fasa_decode_step": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int,
                                   _vp, _vp, _vp, ctypes.c_uint, _vp]),
+    "fasa_decode_step_per_head": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _vp,
+                                           _c_int, _vp, _vp, _vp, ctypes.c_uint, _vp]),
     "fasa_dense_attn": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp]),
     "fasa_calibrate_workspace_bytes": (_c_size, [_vp, _c_int]),
     "fasa_calibrate": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp]),
@@ -66,7 +69,7 @@ EXPORTED = tuple(_SIGS)
 
 F32, BF16 = 0, 1
 ADVANCE_SEQ_LENS = 1
-DEVFLAG_SEQ_LEN, DEVFLAG_INDEX, DEVFLAG_APPEND = 1, 2, 4
+DEVFLAG_SEQ_LEN, DEVFLAG_INDEX, DEVFLAG_APPEND, DEVFLAG_BUDGET = 1, 2, 4, 8
 _DTYPES = {"f32": (F32, torch.float32), "bf16": (BF16, torch.bfloat16)}
 
 
@@ -222,14 +225,24 @@ class Context:
                                   int(max_seq_len), _ptr(scores), _ptr(workspace),
                                   self._stream(stream)), "fasa_tip_scores")
 
-    def topk(self, scores, seq_lens, max_seq_len, budget, idx, workspace, stream=None):
+    def topk(self, scores, seq_lens, max_seq_len, budget, idx, workspace, stream=None,
+             head_budgets=None):
+        """Top-B per (b, h).  head_budgets (device int32 [Hq], each in
+        [0, budget]) gives each query head its own B; idx rows stay budget wide."""
         self._want(scores, "scores", torch.float32,
                    (self.batch, self.n_q_heads, self.capacity))
         self._want(idx, "idx", torch.int32, (self.batch, self.n_q_heads, budget))
         self._want(seq_lens, "seq_lens", torch.int32, (self.batch,))
-        _chk(_lib.fasa_topk(self._h, _ptr(scores), _ptr(seq_lens), int(max_seq_len),
-                            int(budget), _ptr(idx), _ptr(workspace), self._stream(stream)),
-             "fasa_topk")
+        if head_budgets is None:
+            _chk(_lib.fasa_topk(self._h, _ptr(scores), _ptr(seq_lens), int(max_seq_len),
+                                int(budget), _ptr(idx), _ptr(workspace), self._stream(stream)),
+                 "fasa_topk")
+            return
+        self._want(head_budgets, "head_budgets", torch.int32, (self.n_q_heads,))
+        _chk(_lib.fasa_topk_per_head(self._h, _ptr(scores), _ptr(seq_lens), int(max_seq_len),
+                                     _ptr(head_budgets), int(budget), _ptr(idx),
+                                     _ptr(workspace), self._stream(stream)),
+             "fasa_topk_per_head")
 
     def sparse_attn(self, k_cache, v_cache, q, seq_lens, idx, budget, out, workspace,
                     stream=None):
@@ -242,7 +255,10 @@ class Context:
                                    _ptr(workspace), self._stream(stream)), "fasa_sparse_attn")
 
     def decode_step(self, k_cache, v_cache, sidecar, q, k_new, v_new, seq_lens, max_seq_len,
-                    budget, out, workspace, idx_out=None, advance=False, stream=None):
+                    budget, out, workspace, idx_out=None, advance=False, stream=None,
+                    head_budgets=None):
+        """One decode step.  head_budgets (device int32 [Hq], each in
+        [0, budget]) gives each query head its own B."""
         b, hq, hkv, d = self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim
         self._want(q, "q", self.torch_dtype, (b, hq, d))
         self._want(k_new, "k_new", self.torch_dtype, (b, hkv, d))
@@ -251,6 +267,15 @@ class Context:
         self._want(out, "out", torch.float32, (b, hq, d))
         if idx_out is not None:
             self._want(idx_out, "idx_out", torch.int32, (b, hq, budget))
+        if head_budgets is not None:
+            self._want(head_budgets, "head_budgets", torch.int32, (hq,))
+            _chk(_lib.fasa_decode_step_per_head(
+                self._h, self._cache(k_cache, 'k_cache'), self._cache(v_cache, 'v_cache'),
+                _ptr(sidecar), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(seq_lens),
+                int(max_seq_len), _ptr(head_budgets), int(budget), _ptr(out), _ptr(idx_out),
+                _ptr(workspace), ADVANCE_SEQ_LENS if advance else 0, self._stream(stream)),
+                "fasa_decode_step_per_head")
+            return
         _chk(_lib.fasa_decode_step(self._h, self._cache(k_cache, 'k_cache'), self._cache(v_cache, 'v_cache'), _ptr(sidecar),
                                    _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(seq_lens),
                                    int(max_seq_len), int(budget), _ptr(out), _ptr(idx_out),

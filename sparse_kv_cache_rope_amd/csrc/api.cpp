@@ -330,9 +330,9 @@ fasa_status fasa_tip_scores(fasa_ctx* c, const void* sidecar, const void* q,
   return ok();
 }
 
-fasa_status fasa_topk(fasa_ctx* c, const float* scores, const int32_t* seq_lens,
-                      int max_seq_len, int budget, int32_t* idx, void* workspace,
-                      hipStream_t stream) {
+static fasa_status topk_impl(fasa_ctx* c, const float* scores, const int32_t* seq_lens,
+                             int max_seq_len, const int32_t* head_budget, int budget,
+                             int32_t* idx, void* workspace, hipStream_t stream) {
   FASA_TRY(check_ctx(c));
   FASA_TRY(check_len(c, max_seq_len));
   FASA_TRY(check_budget(c, budget));
@@ -345,13 +345,28 @@ fasa_status fasa_topk(fasa_ctx* c, const float* scores, const int32_t* seq_lens,
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     if (select_path_applies(max_seq_len, budget))
       FASA_HIP(launch_select(c, scores, seq_lens, max_seq_len, budget, idx, nullptr, nullptr,
-                             nullptr, nullptr, ws, stream),
+                             nullptr, nullptr, ws, stream, head_budget),
                "fasa_topk: row select");
     else
-      FASA_HIP(launch_topk(c, scores, seq_lens, max_seq_len, budget, idx, nullptr, ws, stream),
+      FASA_HIP(launch_topk(c, scores, seq_lens, max_seq_len, budget, idx, nullptr, ws, stream,
+                           head_budget),
                "fasa_topk");
   }
   return ok();
+}
+
+fasa_status fasa_topk(fasa_ctx* c, const float* scores, const int32_t* seq_lens,
+                      int max_seq_len, int budget, int32_t* idx, void* workspace,
+                      hipStream_t stream) {
+  return topk_impl(c, scores, seq_lens, max_seq_len, nullptr, budget, idx, workspace, stream);
+}
+
+fasa_status fasa_topk_per_head(fasa_ctx* c, const float* scores, const int32_t* seq_lens,
+                               int max_seq_len, const int32_t* head_budget, int budget,
+                               int32_t* idx, void* workspace, hipStream_t stream) {
+  FASA_NONNULL(head_budget);
+  return topk_impl(c, scores, seq_lens, max_seq_len, head_budget, budget, idx, workspace,
+                   stream);
 }
 
 fasa_status fasa_sparse_attn(fasa_ctx* c, const void* k_cache, const void* v_cache,
@@ -380,11 +395,11 @@ fasa_status fasa_sparse_attn(fasa_ctx* c, const void* k_cache, const void* v_cac
   return ok();
 }
 
-fasa_status fasa_decode_step(fasa_ctx* c, void* k_cache, void* v_cache, void* sidecar,
-                             const void* q, const void* k_new, const void* v_new,
-                             int32_t* seq_lens, int max_seq_len, int budget, float* out,
-                             int32_t* idx_out, void* workspace, unsigned flags,
-                             hipStream_t stream) {
+static fasa_status decode_impl(fasa_ctx* c, void* k_cache, void* v_cache, void* sidecar,
+                               const void* q, const void* k_new, const void* v_new,
+                               int32_t* seq_lens, int max_seq_len, const int32_t* head_budget,
+                               int budget, float* out, int32_t* idx_out, void* workspace,
+                               unsigned flags, hipStream_t stream) {
   FASA_TRY(check_ctx(c));
   FASA_TRY(check_len(c, max_seq_len));
   FASA_TRY(check_budget(c, budget));
@@ -415,14 +430,14 @@ fasa_status fasa_decode_step(fasa_ctx* c, void* k_cache, void* v_cache, void* si
       // leave LDS.
       Timed t(c, FASA_K_SELECT_FAC, stream);
       FASA_HIP(launch_select(c, scores, nb, max_seq_len, budget, idx_out, k_cache, v_cache, out,
-                             advance, ws, stream),
+                             advance, ws, stream, head_budget),
                "fasa_decode_step: select+fac");
       return ok();
     }
     {
       Timed t(c, FASA_K_TOPK, stream);
       FASA_HIP(launch_select(c, scores, nb, max_seq_len, budget, idx, nullptr, nullptr, nullptr,
-                             advance, ws, stream),
+                             advance, ws, stream, head_budget),
                "fasa_decode_step: select");
     }
     {
@@ -436,13 +451,14 @@ fasa_status fasa_decode_step(fasa_ctx* c, void* k_cache, void* v_cache, void* si
     // Selection and FAC in one kernel: the selected rows never leave LDS.
     Timed t(c, FASA_K_SELECT_FAC, stream);
     FASA_HIP(launch_select_attend(c, scores, nb, max_seq_len, budget, idx_out, k_cache, v_cache,
-                                  out, advance, ws, stream),
+                                  out, advance, ws, stream, head_budget),
              "fasa_decode_step: select+fac");
     return ok();
   }
   {
     Timed t(c, FASA_K_TOPK, stream);
-    FASA_HIP(launch_topk(c, scores, nb, max_seq_len, budget, idx, advance, ws, stream),
+    FASA_HIP(launch_topk(c, scores, nb, max_seq_len, budget, idx, advance, ws, stream,
+                         head_budget),
              "fasa_decode_step: topk");
   }
   {
@@ -451,6 +467,26 @@ fasa_status fasa_decode_step(fasa_ctx* c, void* k_cache, void* v_cache, void* si
              "fasa_decode_step: fac");
   }
   return ok();
+}
+
+fasa_status fasa_decode_step(fasa_ctx* c, void* k_cache, void* v_cache, void* sidecar,
+                             const void* q, const void* k_new, const void* v_new,
+                             int32_t* seq_lens, int max_seq_len, int budget, float* out,
+                             int32_t* idx_out, void* workspace, unsigned flags,
+                             hipStream_t stream) {
+  return decode_impl(c, k_cache, v_cache, sidecar, q, k_new, v_new, seq_lens, max_seq_len,
+                     nullptr, budget, out, idx_out, workspace, flags, stream);
+}
+
+fasa_status fasa_decode_step_per_head(fasa_ctx* c, void* k_cache, void* v_cache, void* sidecar,
+                                      const void* q, const void* k_new, const void* v_new,
+                                      int32_t* seq_lens, int max_seq_len,
+                                      const int32_t* head_budget, int budget, float* out,
+                                      int32_t* idx_out, void* workspace, unsigned flags,
+                                      hipStream_t stream) {
+  FASA_NONNULL(head_budget);
+  return decode_impl(c, k_cache, v_cache, sidecar, q, k_new, v_new, seq_lens, max_seq_len,
+                     head_budget, budget, out, idx_out, workspace, flags, stream);
 }
 
 fasa_status fasa_dense_attn(fasa_ctx* c, const void* k_cache, const void* v_cache,

@@ -107,9 +107,12 @@ hipError_t launch_tip(const fasa_ctx* c, PrologueMode mode, const TipArgs& a, fl
                       uint8_t* ws, hipStream_t s);
 // The launchers below that take `advance` (may be null) store n_b into
 // advance[b] from a kernel that reads only ws.nb, so it can be seq_lens.
+// Those that take `head_budget` (device int32 [Hq], may be null) give query
+// head h the budget head_budget[h] (in [0, budget]) instead of `budget`; idx
+// rows stay `budget` wide.
 hipError_t launch_topk(const fasa_ctx* c, const float* scores, const int32_t* nb,
                        int max_seq_len, int budget, int32_t* idx, int32_t* advance, uint8_t* ws,
-                       hipStream_t s);
+                       hipStream_t s, const int32_t* head_budget = nullptr);
 hipError_t launch_fac(const fasa_ctx* c, const void* k_cache, const void* v_cache,
                       const int32_t* nb, int max_seq_len, const int32_t* idx, int budget,
                       float* out, uint8_t* ws, hipStream_t s);
@@ -121,7 +124,7 @@ hipError_t launch_dense(const fasa_ctx* c, const void* k_cache, const void* v_ca
 hipError_t launch_select_attend(const fasa_ctx* c, const float* scores, const int32_t* nb,
                                 int max_seq_len, int budget, int32_t* idx, const void* k_cache,
                                 const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
-                                hipStream_t s);
+                                hipStream_t s, const int32_t* head_budget = nullptr);
 // Register-resident top-B (when select_path_applies(max_seq_len, budget)):
 // rows up to kSelectChunk positions in one workgroup each, longer rows in
 // chunks of kSelectChunk then their candidates.  Fused with FAC when `out` is
@@ -131,7 +134,7 @@ bool select_path_applies(int max_seq_len, int budget);
 hipError_t launch_select(const fasa_ctx* c, const float* scores, const int32_t* nb,
                          int max_seq_len, int budget, int32_t* idx, const void* k_cache,
                          const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
-                         hipStream_t s);
+                         hipStream_t s, const int32_t* head_budget = nullptr);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 // Calibration (calibrate.hip): its workspace regions (err, nb, qrot, scores

@@ -18,6 +18,7 @@
 // row_select_kernel then selects among those candidates (at most 16384).
 
 #include "attention_common.hpp"
+#include "budget.hpp"
 #include "fasa_internal.hpp"
 #include "select_common.hpp"
 
@@ -142,12 +143,13 @@ __device__ __forceinline__ void emit_ordered(const Src& src, uint64_t tau, uint3
 }
 
 // Stage 1 for rows of several chunks (E * 1024 positions each): the chunk's
-// own top-B composites, ascending, at cand[row][chunk * min(B, chunk) ...].
-// The row's top B are among them.
+// own top-B composites, ascending, at cand[row][chunk * min(B, chunk) ...],
+// B the row's budget (see row_budget).  The row's top B are among them.
 template <int E, int NT>
 __global__ void __launch_bounds__(NT)
 chunk_select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ nb,
-                    int max_seq_len, int hq, int cap, int budget, uint64_t* __restrict__ cand,
+                    int max_seq_len, int hq, int cap, int budget,
+                    const int32_t* __restrict__ head_budget, uint64_t* __restrict__ cand,
                     int cand_stride) {
   constexpr int kChunk = E * NT;
   __shared__ RegSelectLds<NT, kHistCopiesSel, kCandCapSel> L;
@@ -156,7 +158,10 @@ chunk_select_kernel(const float* __restrict__ scores, const int32_t* __restrict_
   int n = nb[b];
   if (n < 0 || n > max_seq_len || n > cap) n = 0;
   const int nch = (n + kChunk - 1) / kChunk;
-  if (n <= budget || chunk >= nch) return;  // a one-chunk row is a chunk too
+  budget = row_budget(head_budget, h, budget, nullptr, false);
+  // Rows the second stage takes whole (n <= B, or B = 0) need no candidates;
+  // a one-chunk row is a chunk too.
+  if (budget == 0 || n <= budget || chunk >= nch) return;
   const int c0 = chunk * kChunk;
   const int cn = min(kChunk, n - c0);
   ScoreSrc<E, NT> src;
@@ -174,13 +179,15 @@ chunk_select_kernel(const float* __restrict__ scores, const int32_t* __restrict_
 // Selects a row's top B from its raw scores (FROM_CAND = false, n <= E * 1024)
 // or from the chunk stage's candidates (FROM_CAND = true, chunks of `chunk`
 // positions, at most E * 1024 candidates), writes idx
-// (if given) and, with ATTEND, runs FAC over the selection in LDS.  Also
-// stores n_b into advance[b] (if given): seq_lens may be advanced here since
-// no kernel of this launch reads it.
+// (if given) and, with ATTEND, runs FAC over the selection in LDS.  B is the
+// row's budget (row_budget); idx rows are `budget` wide, -1 past the set.
+// Also stores n_b into advance[b] (if given): seq_lens may be advanced here
+// since no kernel of this launch reads it.
 template <bool ATTEND, bool BF16, int D, int E, bool FROM_CAND, int NT>
 __global__ void __launch_bounds__(NT)
 row_select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ nb,
                   int max_seq_len, int hq, int cap, int budget,
+                  const int32_t* __restrict__ head_budget,
                   const uint64_t* __restrict__ cand, int cand_stride, int chunk,
                   int32_t* __restrict__ idx, const void* __restrict__ k_cache,
                   const void* __restrict__ v_cache, const float* __restrict__ qrot, int hkv,
@@ -195,24 +202,26 @@ row_select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ 
   if (advance != nullptr && h == 0 && threadIdx.x == 0 && n > 0) advance[b] = n;
   const int t = threadIdx.x;
   int32_t* o = idx ? idx + row * budget : nullptr;
-  const int take = n < budget ? n : budget;
+  const int bh = row_budget(head_budget, h, budget, err, b == 0 && t == 0);
+  const int take = n < bh ? n : bh;
+  const bool whole = n <= bh || bh == 0;  // every position, or none
 
-  if (n <= budget) {
+  if (whole) {
     for (int j = t; j < budget; j += NT) {
-      if (o) o[j] = (j < n) ? j : -1;
+      if (o) o[j] = (j < take) ? j : -1;
       if (ATTEND && j < kFusedMaxBudget) L.sel[j] = j;
     }
   } else if constexpr (!FROM_CAND) {
     ScoreSrc<E, NT> src;
     load_scores<E, NT>(src, scores + row * cap, 0, n);
-    const uint64_t tau = adaptive_select<NT, E>(src, (uint32_t)budget, L.s);
-    emit_ordered<E, NT>(src, tau, (uint32_t)budget, L.s, [&](uint32_t r, int e) {
+    const uint64_t tau = adaptive_select<NT, E>(src, (uint32_t)bh, L.s);
+    emit_ordered<E, NT>(src, tau, (uint32_t)bh, L.s, [&](uint32_t r, int e) {
       const int pos = src.pos(e);
       if (o) o[r] = pos;
       if (ATTEND) L.sel[r] = pos;
     });
   } else {
-    const int M = candidates_of(n, budget, chunk);
+    const int M = candidates_of(n, bh, chunk);
     const uint64_t* __restrict__ src_c = cand + row * cand_stride;
     CandSrc<E, NT> src;
 #pragma unroll
@@ -236,13 +245,15 @@ row_select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ 
         src.lo[4 * g + e] = (uint32_t)c[e];
       }
     }
-    const uint64_t tau = adaptive_select<NT, E>(src, (uint32_t)budget, L.s);
-    emit_ordered<E, NT>(src, tau, (uint32_t)budget, L.s, [&](uint32_t r, int e) {
+    const uint64_t tau = adaptive_select<NT, E>(src, (uint32_t)bh, L.s);
+    emit_ordered<E, NT>(src, tau, (uint32_t)bh, L.s, [&](uint32_t r, int e) {
       const int pos = (int)(0xffffffffu - src.lo[e]);
       if (o) o[r] = pos;
       if (ATTEND) L.sel[r] = pos;
     });
   }
+  if (!whole && o != nullptr)
+    for (int j = bh + t; j < budget; j += NT) o[j] = -1;
   if constexpr (ATTEND) {
     __syncthreads();
     float* out_row = out + row * D;
@@ -303,30 +314,31 @@ bool select_path_applies(int max_seq_len, int budget) {
 
 template <bool ATT, bool BF, int DD, int E, bool FC>
 static void launch_row(const fasa_ctx* c, hipStream_t s, const float* scores, const int32_t* nb,
-                       int max_seq_len, int budget, const uint64_t* cand, int stride, int chunk,
-                       int32_t* idx, const void* k, const void* v, const float* qrot, float* out,
-                       int32_t* advance, uint32_t* err) {
+                       int max_seq_len, int budget, const int32_t* hb, const uint64_t* cand,
+                       int stride, int chunk, int32_t* idx, const void* k, const void* v,
+                       const float* qrot, float* out, int32_t* advance, uint32_t* err) {
   hipLaunchKernelGGL((row_select_kernel<ATT, BF, DD, E, FC, kRowThreads>),
                      dim3((unsigned)c->hq, (unsigned)c->batch), dim3(kRowThreads), 0, s, scores,
-                     nb, max_seq_len, c->hq, c->cap, budget, cand, stride, chunk, idx, k, v, qrot,
-                     c->hkv, c->G, out, advance, err);
+                     nb, max_seq_len, c->hq, c->cap, budget, hb, cand, stride, chunk, idx, k, v,
+                     qrot, c->hkv, c->G, out, advance, err);
 }
 
 template <int E, bool FC>
 static void launch_row_e(const fasa_ctx* c, hipStream_t s, const float* scores,
-                         const int32_t* nb, int max_seq_len, int budget, const uint64_t* cand,
-                         int stride, int chunk, int32_t* idx, const void* k, const void* v,
-                         const float* qrot, float* out, int32_t* advance, uint32_t* err) {
+                         const int32_t* nb, int max_seq_len, int budget, const int32_t* hb,
+                         const uint64_t* cand, int stride, int chunk, int32_t* idx,
+                         const void* k, const void* v, const float* qrot, float* out,
+                         int32_t* advance, uint32_t* err) {
   if (out == nullptr) {
-    launch_row<false, true, 128, E, FC>(c, s, scores, nb, max_seq_len, budget, cand, stride,
+    launch_row<false, true, 128, E, FC>(c, s, scores, nb, max_seq_len, budget, hb, cand, stride,
                                         chunk, idx, nullptr, nullptr, nullptr, nullptr, advance,
                                         err);
     return;
   }
   const bool bf = (c->dtype == FASA_BF16);
 #define FASA_ROW(BFV, DV)                                                                       \
-  launch_row<true, BFV, DV, E, FC>(c, s, scores, nb, max_seq_len, budget, cand, stride, chunk, \
-                                   idx, k, v, qrot, out, advance, err)
+  launch_row<true, BFV, DV, E, FC>(c, s, scores, nb, max_seq_len, budget, hb, cand, stride,   \
+                                   chunk, idx, k, v, qrot, out, advance, err)
   if (c->d == 128) {
     if (bf) FASA_ROW(true, 128); else FASA_ROW(false, 128);
   } else {
@@ -338,7 +350,7 @@ static void launch_row_e(const fasa_ctx* c, hipStream_t s, const float* scores,
 hipError_t launch_select(const fasa_ctx* c, const float* scores, const int32_t* nb,
                          int max_seq_len, int budget, int32_t* idx, const void* k_cache,
                          const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
-                         hipStream_t s) {
+                         hipStream_t s, const int32_t* head_budget) {
   const SelectPlan p = select_plan(max_seq_len, budget);
   if (!p.ok() || (out != nullptr && budget > kFusedMaxBudget)) return hipErrorInvalidValue;
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
@@ -346,8 +358,8 @@ hipError_t launch_select(const fasa_ctx* c, const float* scores, const int32_t* 
   uint64_t* cand = reinterpret_cast<uint64_t*>(ws + c->ws.cand);
   const int stride = c->ws.cand_stride;
 #define FASA_ROWE(EV, FC, CH)                                                                  \
-  launch_row_e<EV, FC>(c, s, scores, nb, max_seq_len, budget, cand, stride, CH, idx, k_cache, \
-                       v_cache, qrot, out, advance, err)
+  launch_row_e<EV, FC>(c, s, scores, nb, max_seq_len, budget, head_budget, cand, stride, CH,  \
+                       idx, k_cache, v_cache, qrot, out, advance, err)
   if (p.direct_e) {
     switch (p.direct_e) {
       case 4: FASA_ROWE(4, false, 0); break;
@@ -363,7 +375,7 @@ hipError_t launch_select(const fasa_ctx* c, const float* scores, const int32_t* 
 #define FASA_CHUNK(EV)                                                                        \
   hipLaunchKernelGGL((chunk_select_kernel<EV, kRowThreads>), grid, dim3(kRowThreads), 0, s,    \
                      scores, nb,                                                              \
-                     max_seq_len, c->hq, c->cap, budget, cand, stride)
+                     max_seq_len, c->hq, c->cap, budget, head_budget, cand, stride)
   switch (p.chunk_e) {
     case 8: FASA_CHUNK(8); break;
     case 16: FASA_CHUNK(16); break;

@@ -29,6 +29,7 @@
 // Rows with n <= B take every position and are padded with -1.
 
 #include "attention_common.hpp"
+#include "budget.hpp"
 #include "fasa_internal.hpp"
 
 namespace fasa {
@@ -385,7 +386,8 @@ __device__ void attend_selected(SelectLds& L, int take, const void* __restrict__
 template <bool CACHED, bool ATTEND, bool BF16, int D>
 __global__ void __launch_bounds__(kSelThreads)
 select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ nb, int max_seq_len,
-              int hq, int cap, int budget, int32_t* __restrict__ idx,
+              int hq, int cap, int budget, const int32_t* __restrict__ head_budget,
+              int32_t* __restrict__ idx,
               const void* __restrict__ k_cache, const void* __restrict__ v_cache,
               const float* __restrict__ qrot, int hkv, int G, float* __restrict__ out,
               int32_t* __restrict__ advance, uint32_t* err) {
@@ -395,17 +397,20 @@ select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ nb, 
   const int n = checked_len(nb, b, max_seq_len, cap, err, h == 0 && threadIdx.x == 0);
   if (advance != nullptr && h == 0 && threadIdx.x == 0 && n > 0) advance[b] = n;
   int32_t* o = idx ? idx + row * budget : nullptr;
-  const int take = n < budget ? n : budget;
-  if (n <= budget) {
+  const int bh = row_budget(head_budget, h, budget, err, b == 0 && threadIdx.x == 0);
+  const int take = n < bh ? n : bh;
+  if (n <= bh || bh == 0) {
     for (int j = threadIdx.x; j < budget; j += kSelThreads) {
-      if (o) o[j] = (j < n) ? j : -1;
+      if (o) o[j] = (j < take) ? j : -1;
       if (ATTEND && j < kFusedMaxBudget) L.sel[j] = j;
     }
   } else {
     RowKeys<CACHED> rk;
     rk.init(scores + row * cap, n);
-    const uint64_t tau = select_threshold<CACHED>(rk, budget, L);
-    emit_selected<CACHED>(rk, tau, budget, o, ATTEND, L);
+    const uint64_t tau = select_threshold<CACHED>(rk, bh, L);
+    emit_selected<CACHED>(rk, tau, bh, o, ATTEND, L);
+    if (o != nullptr)
+      for (int j = bh + threadIdx.x; j < budget; j += kSelThreads) o[j] = -1;
   }
   if constexpr (ATTEND) {
     __syncthreads();
@@ -421,39 +426,39 @@ select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ nb, 
 
 hipError_t launch_topk(const fasa_ctx* c, const float* scores, const int32_t* nb,
                        int max_seq_len, int budget, int32_t* idx, int32_t* advance, uint8_t* ws,
-                       hipStream_t s) {
+                       hipStream_t s, const int32_t* head_budget) {
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
   dim3 grid((unsigned)c->hq, (unsigned)c->batch);
   if (kUseCachedKeys && max_seq_len <= kCachedRow)
     hipLaunchKernelGGL((select_kernel<true, false, true, 128>), grid, dim3(kSelThreads), 0, s,
-                       scores, nb, max_seq_len, c->hq, c->cap, budget, idx, nullptr, nullptr,
-                       nullptr, c->hkv, c->G, nullptr, advance, err);
+                       scores, nb, max_seq_len, c->hq, c->cap, budget, head_budget, idx, nullptr,
+                       nullptr, nullptr, c->hkv, c->G, nullptr, advance, err);
   else
     hipLaunchKernelGGL((select_kernel<false, false, true, 128>), grid, dim3(kSelThreads), 0, s,
-                       scores, nb, max_seq_len, c->hq, c->cap, budget, idx, nullptr, nullptr,
-                       nullptr, c->hkv, c->G, nullptr, advance, err);
+                       scores, nb, max_seq_len, c->hq, c->cap, budget, head_budget, idx, nullptr,
+                       nullptr, nullptr, c->hkv, c->G, nullptr, advance, err);
   return hipGetLastError();
 }
 
 template <bool BF, int DD>
 static void launch_sel_att(const fasa_ctx* c, dim3 grid, hipStream_t s, bool cached,
                            const float* scores, const int32_t* nb, int max_seq_len, int budget,
-                           int32_t* idx, const void* k, const void* v, const float* qrot,
-                           float* out, int32_t* advance, uint32_t* err) {
+                           const int32_t* hb, int32_t* idx, const void* k, const void* v,
+                           const float* qrot, float* out, int32_t* advance, uint32_t* err) {
   if (cached)
     hipLaunchKernelGGL((select_kernel<true, true, BF, DD>), grid, dim3(kSelThreads), 0, s, scores,
-                       nb, max_seq_len, c->hq, c->cap, budget, idx, k, v, qrot, c->hkv, c->G,
+                       nb, max_seq_len, c->hq, c->cap, budget, hb, idx, k, v, qrot, c->hkv, c->G,
                        out, advance, err);
   else
     hipLaunchKernelGGL((select_kernel<false, true, BF, DD>), grid, dim3(kSelThreads), 0, s, scores,
-                       nb, max_seq_len, c->hq, c->cap, budget, idx, k, v, qrot, c->hkv, c->G,
+                       nb, max_seq_len, c->hq, c->cap, budget, hb, idx, k, v, qrot, c->hkv, c->G,
                        out, advance, err);
 }
 
 hipError_t launch_select_attend(const fasa_ctx* c, const float* scores, const int32_t* nb,
                                 int max_seq_len, int budget, int32_t* idx, const void* k_cache,
                                 const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
-                                hipStream_t s) {
+                                hipStream_t s, const int32_t* head_budget) {
   if (budget > kFusedMaxBudget) return hipErrorInvalidValue;
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
   const float* qrot = reinterpret_cast<const float*>(ws + c->ws.qrot);
@@ -461,11 +466,11 @@ hipError_t launch_select_attend(const fasa_ctx* c, const float* scores, const in
   const bool cached = kUseCachedKeys && max_seq_len <= kCachedRow;
   const bool bf = (c->dtype == FASA_BF16);
   if (c->d == 128) {
-    if (bf) launch_sel_att<true, 128>(c, grid, s, cached, scores, nb, max_seq_len, budget, idx, k_cache, v_cache, qrot, out, advance, err);
-    else launch_sel_att<false, 128>(c, grid, s, cached, scores, nb, max_seq_len, budget, idx, k_cache, v_cache, qrot, out, advance, err);
+    if (bf) launch_sel_att<true, 128>(c, grid, s, cached, scores, nb, max_seq_len, budget, head_budget, idx, k_cache, v_cache, qrot, out, advance, err);
+    else launch_sel_att<false, 128>(c, grid, s, cached, scores, nb, max_seq_len, budget, head_budget, idx, k_cache, v_cache, qrot, out, advance, err);
   } else {
-    if (bf) launch_sel_att<true, 64>(c, grid, s, cached, scores, nb, max_seq_len, budget, idx, k_cache, v_cache, qrot, out, advance, err);
-    else launch_sel_att<false, 64>(c, grid, s, cached, scores, nb, max_seq_len, budget, idx, k_cache, v_cache, qrot, out, advance, err);
+    if (bf) launch_sel_att<true, 64>(c, grid, s, cached, scores, nb, max_seq_len, budget, head_budget, idx, k_cache, v_cache, qrot, out, advance, err);
+    else launch_sel_att<false, 64>(c, grid, s, cached, scores, nb, max_seq_len, budget, head_budget, idx, k_cache, v_cache, qrot, out, advance, err);
   }
   return hipGetLastError();
 }

@@ -213,6 +213,36 @@ def pin_select_budget_ge_n():
     assert got.tolist() == list(range(10)) + [-1] * 6
 
 
+def pin_select_per_head_budget_brute_force():
+    """A head of budget B_h in a row of width W: the brute-force top-B_h set
+    (B_h = 0 keeps nothing), padded with -1 to W."""
+    r = _rng(14)
+    for trial in range(60):
+        n = int(r.integers(1, 10))
+        width = int(r.integers(1, 6))
+        bh = int(r.integers(0, width + 1))
+        s = r.integers(-2, 3, size=n).astype(np.float64)
+        got = oracle.select.select_topb_width(s, bh, width).tolist()
+        want = _brute_force_topb(s.tolist(), bh) + [-1] * (width - bh)
+        assert got == want, (s, bh, width, got)
+
+
+def pin_select_sets_nest_with_budget():
+    """Raising the budget only adds tokens: T(B) is a subset of T(B + 1), and
+    the token added is the best one outside T(B) (ties to the lower position)."""
+    r = _rng(15)
+    s = np.round(r.standard_normal(40), 1)
+    prev = set()
+    for b in range(0, 41):
+        cur = set(oracle.select.select_topb_width(s, b, 40)[:b].tolist())
+        assert prev <= cur and len(cur) == b
+        if b:
+            (new,) = cur - prev
+            rest = [j for j in range(40) if j not in prev]
+            assert new == min(rest, key=lambda j: (-s[j], j))
+        prev = cur
+
+
 # ------------------------------------------------------------------ FAC ----
 
 def _sdpa(q, k, v):
@@ -317,6 +347,38 @@ def pin_decode_dense_equivalence():
         # The oracle rounds K to fp32 once; allow for that rounding only.
         assert np.allclose(res["out"][0, h], want, rtol=1e-6, atol=1e-6), h
         assert res["idx"][0, h].tolist()[:n] == list(range(n))
+
+
+def pin_decode_per_head_budgets():
+    """Budgets per head: a head with B_h >= n is dense attention (closed form
+    with complex rotations), a head with B_h = 0 outputs zeros and selects
+    nothing, and a head with B_h = 1 outputs the V row of its best-scoring
+    token."""
+    r = _rng(23)
+    d, n, theta, width = 64, 24, 1e4, 32
+    dom = np.tile(np.arange(32), (3, 1))
+    st = _state(3, 1, d, theta, "f32", dom, 32)
+    k = r.standard_normal((1, n - 1, d)).astype(np.float32).astype(np.float64)
+    v = r.standard_normal((1, n - 1, d))
+    st.append(0, k, v)
+    q = r.standard_normal((1, 3, d))
+    kn, vn = r.standard_normal((1, 1, d)), r.standard_normal((1, 1, d))
+    res = st.step(q, kn, vn, budget=width, head_budgets=[width, 0, 1])
+    kall = np.concatenate([k[0], kn[0]], axis=0)
+    vall = np.concatenate([v[0], vn[0]], axis=0)
+
+    def rot(x, m):
+        z = x[:32] + 1j * x[32:]
+        z = z * np.exp(1j * m * theta ** (-2.0 * np.arange(32) / d))
+        return np.concatenate([z.real, z.imag])
+    kr = np.stack([rot(kall[j], j) for j in range(n)])
+    want0 = _sdpa(rot(q[0, 0], n - 1), kr, vall)
+    assert np.allclose(res["out"][0, 0], want0, rtol=1e-6, atol=1e-6)
+    assert res["idx"][0, 0].tolist() == list(range(n)) + [-1] * (width - n)
+    assert np.all(res["out"][0, 1] == 0) and np.all(res["idx"][0, 1] == -1)
+    best = int(np.argmax(kr @ rot(q[0, 2], n - 1)))
+    assert res["idx"][0, 2].tolist() == [best] + [-1] * (width - 1)
+    assert np.allclose(res["out"][0, 2], vall[best], rtol=0, atol=1e-12)
 
 
 def pin_decode_query_position():

@@ -16,6 +16,8 @@ _rope_rotate = oracle.rope.rope_rotate
 _round = oracle.rope.round_to_dtype
 _tip = oracle.tip.tip_scores
 _select = oracle.select.select_topb
+_select_width = oracle.select.select_topb_width
+_step = oracle.decode.OracleState.step
 _attend = oracle.fac.attend_subset
 _query_rot = oracle.decode.OracleState.query_rot
 _append = oracle.decode.OracleState.append
@@ -154,6 +156,19 @@ def dominant_ties_high(ca, n_dom):
     return np.array(picks, dtype=np.int32)
 
 
+def width_ignores_budget(scores, budget, width):
+    return _select_width(scores, width, width)
+
+
+def width_zero_keeps_one(scores, budget, width):
+    return _select_width(scores, max(budget, 1), width)
+
+
+def step_budgets_reversed(self, q, k_new, v_new, budget, heads=None, head_budgets=None):
+    hb = None if head_budgets is None else list(head_budgets)[::-1]
+    return _step(self, q, k_new, v_new, budget, heads=heads, head_budgets=hb)
+
+
 MUTATIONS = {
     "rope_interleaved_pairs": (oracle.rope, "rope_rotate", rope_interleaved),
     "rope_backwards": (oracle.rope, "rope_rotate", rope_backwards),
@@ -166,6 +181,9 @@ MUTATIONS = {
     "select_ties_to_higher": (oracle.select, "select_topb", select_ties_high),
     "select_lowest_scores": (oracle.select, "select_topb", select_lowest),
     "select_one_short": (oracle.select, "select_topb", select_one_short),
+    "select_width_ignores_budget": (oracle.select, "select_topb_width", width_ignores_budget),
+    "select_width_zero_keeps_one": (oracle.select, "select_topb_width", width_zero_keeps_one),
+    "decode_head_budgets_reversed": (oracle.decode.OracleState, "step", step_budgets_reversed),
     "fac_missing_scale": (oracle.fac, "attend_subset", attend_no_scale),
     "fac_ignores_subset": (oracle.fac, "attend_subset", attend_all_rows),
     "fac_keys_as_values": (oracle.fac, "attend_subset", attend_k_for_v),

@@ -7,4 +7,4 @@ HIP path's tests/benchmark and the oracle receive its arrays unchanged.
 """
 
 from .configs import Workload, CONFIGS, get, shrink  # noqa: F401
-from .generate import generate, to_bf16_bits, round_bf16, random_scores  # noqa: F401
+from .generate import generate, to_bf16_bits, round_bf16, random_scores, head_budgets  # noqa: F401

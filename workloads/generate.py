@@ -176,3 +176,24 @@ def random_scores(seed: int, rows: int, n: int, kind: str) -> np.ndarray:
     else:
         raise ValueError(kind)
     return np.ascontiguousarray(x.astype(np.float32))
+
+
+def head_budgets(seed: int, n_heads: int, budget: int, kind: str) -> np.ndarray:
+    """Seeded per-query-head budgets int32 [n_heads], each in [0, budget].
+
+    kinds: 'edges' (0, 1, budget, budget - 1, then uniform draws), 'uniform'
+    (uniform draws in [0, budget]), 'ramp' (round(budget (h + 0.5) / n_heads):
+    a linear allocation whose mean is budget / 2).
+    """
+    r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0xB0D6, n_heads, budget])))
+    if kind == "ramp":
+        x = np.round(budget * (np.arange(n_heads) + 0.5) / n_heads)
+    elif kind == "uniform":
+        x = r.integers(0, budget + 1, size=n_heads)
+    elif kind == "edges":
+        x = r.integers(0, budget + 1, size=n_heads)
+        head = [0, 1, budget, max(budget - 1, 0)]
+        x[:min(4, n_heads)] = head[:min(4, n_heads)]
+    else:
+        raise ValueError(kind)
+    return np.clip(x, 0, budget).astype(np.int32)
