@@ -24,20 +24,24 @@ import numpy as np
 from . import select
 
 
-def fc_scores(q_rot, k_rot) -> np.ndarray:
+def fc_scores(q_rot, k_rot, pairs=None) -> np.ndarray:
     """Per-FC scores of one query head: fp64 [C, n], s_c[j] as above.
 
-    q_rot: [d] rotated query; k_rot: [n, d] rotated keys.
+    q_rot: [d] rotated query; k_rot: [n, d] rotated keys; pairs: (lo, hi)
+    dimensions of every FC (rope.fc_pairs), None for the full layout.
     """
     q = np.asarray(q_rot, dtype=np.float64)
     k = np.asarray(k_rot, dtype=np.float64)
     half = q.shape[-1] // 2
-    return (k[:, :half] * q[None, :half]).T + (k[:, half:] * q[None, half:]).T
+    if pairs is None:
+        return (k[:, :half] * q[None, :half]).T + (k[:, half:] * q[None, half:]).T
+    lo, hi = np.asarray(pairs[0]), np.asarray(pairs[1])
+    return (k[:, lo] * q[None, lo]).T + (k[:, hi] * q[None, hi]).T
 
 
-def contextual_agreement(q_rot, k_rot, topk: int) -> np.ndarray:
+def contextual_agreement(q_rot, k_rot, topk: int, pairs=None) -> np.ndarray:
     """CA of every FC for one calibration query: fp64 [C] in [0, 1]."""
-    s_c = fc_scores(q_rot, k_rot)
+    s_c = fc_scores(q_rot, k_rot, pairs)
     n = s_c.shape[1]
     k = min(topk, n)
     full = set(select.select_topb(s_c.sum(axis=0), k).tolist())

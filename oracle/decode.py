@@ -27,7 +27,7 @@ class OracleState:
     """fp64 copy of the cache: K~ (rotated, dtype-rounded) and V per sequence."""
 
     def __init__(self, batch, n_q_heads, n_kv_heads, head_dim, rope_theta,
-                 dtype, dom, capacity):
+                 dtype, dom, capacity, rotary_dim=None):
         if n_q_heads % n_kv_heads:
             raise ValueError("n_q_heads must be a multiple of n_kv_heads")
         self.batch, self.hq, self.hkv = batch, n_q_heads, n_kv_heads
@@ -37,6 +37,15 @@ class OracleState:
         self.K = np.zeros((batch, n_kv_heads, capacity, head_dim), np.float64)
         self.V = np.zeros((batch, n_kv_heads, capacity, head_dim), np.float64)
         self.lens = np.zeros(batch, dtype=np.int64)
+        # Partial RoPE (rope.py): rotary_dim < head_dim rotates the first
+        # rotary_dim dims only; None or head_dim is full RoPE.
+        self.rotary_dim = None if rotary_dim in (None, head_dim) else int(rotary_dim)
+        self.pairs = None if self.rotary_dim is None else rope.fc_pairs(head_dim, self.rotary_dim)
+
+    def _rotate(self, x, pos):
+        if self.rotary_dim is None:
+            return rope.rope_rotate(x, pos, self.theta)
+        return rope.rope_rotate_partial(x, pos, self.theta, self.rotary_dim)
 
     def append(self, b, k_new, v_new):
         """Append rows at positions lens[b] ..; k_new, v_new: [Hkv, n_new, d]."""
@@ -45,20 +54,21 @@ class OracleState:
         p0 = int(self.lens[b])
         pos = np.arange(p0, p0 + n_new)
         self.K[b, :, p0:p0 + n_new] = rope.round_to_dtype(
-            rope.rope_rotate(k_new, pos[None, :], self.theta), self.dtype)
+            self._rotate(k_new, pos[None, :]), self.dtype)
         self.V[b, :, p0:p0 + n_new] = np.asarray(v_new, dtype=np.float64)
         self.lens[b] = p0 + n_new
 
     def query_rot(self, b, q):
         """Rotated queries [Hq, d] at position lens[b] - 1 (not re-rounded)."""
-        return rope.rope_rotate(q, int(self.lens[b]) - 1, self.theta)
+        return self._rotate(q, int(self.lens[b]) - 1)
 
     def kv_head(self, h):
         return h // self.group
 
     def head_scores(self, b, h, q_rot_h):
         n = int(self.lens[b])
-        return tip.tip_scores(q_rot_h, self.K[b, self.kv_head(h), :n], self.dom[h])
+        return tip.tip_scores(q_rot_h, self.K[b, self.kv_head(h), :n], self.dom[h],
+                              self.pairs)
 
     def attend(self, b, h, q_rot_h, subset):
         n = int(self.lens[b])

@@ -12,6 +12,16 @@ frequency.  The page gives no formula; the readings used here are:
 
 Rounding to the cache dtype happens once, round-to-nearest-even, on the fp64
 rotated value (``round_to_dtype``).
+
+Partial RoPE.  The same page's "Contribuicoes" claim that the functional
+sparsity also holds under Partial-RoPE; it gives no layout.  Reading: only the
+first r (even) dimensions of a head are rotated, rotate-half within them, with
+frequencies theta ** (-2c/r), c < R = r/2; dimensions r .. d-1 pass through.
+The FCs are then:
+* c < R: the pair (c, c + R) at omega_c = theta ** (-2c/r);
+* c >= R: the pass-through dimensions paired the same way,
+  (r + i, r + i + (d - r)/2) with i = c - R, at frequency 0 (no rotation).
+With r = d this is the full layout above.
 """
 
 import numpy as np
@@ -43,6 +53,39 @@ def rope_rotate(x, pos, theta: float) -> np.ndarray:
     cos, sin = np.cos(phi), np.sin(phi)
     lo, hi = x[..., :half], x[..., half:]
     return np.concatenate([lo * cos - hi * sin, hi * cos + lo * sin], axis=-1)
+
+
+def rope_rotate_partial(x, pos, theta: float, rotary_dim: int) -> np.ndarray:
+    """Partial RoPE: rotate-half over the first ``rotary_dim`` dims of ``x``
+    at absolute position ``pos`` with frequencies theta ** (-2c/rotary_dim);
+    the remaining dims are returned unchanged.  fp64 [..., d]."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    r = int(rotary_dim)
+    if r % 2 or not 2 <= r <= d:
+        raise ValueError(f"rotary_dim {r} must be even and in [2, {d}]")
+    R = r // 2
+    w = np.power(np.float64(theta), -2.0 * np.arange(R, dtype=np.float64) / r)
+    phi = np.asarray(pos, dtype=np.float64)[..., None] * w
+    cos, sin = np.cos(phi), np.sin(phi)
+    a, b = x[..., :R], x[..., R:r]
+    out = x.copy()
+    out[..., :R] = a * cos - b * sin
+    out[..., R:r] = b * cos + a * sin
+    return out
+
+
+def fc_pairs(head_dim: int, rotary_dim: int = None):
+    """Dimension pair (lo[c], hi[c]) of every FC c = 0 .. d/2 - 1 (module
+    docstring: full and partial RoPE).  int64 arrays [d/2]."""
+    d = int(head_dim)
+    r = d if rotary_dim is None else int(rotary_dim)
+    R, P = r // 2, (d - r) // 2
+    c = np.arange(d // 2, dtype=np.int64)
+    i = c - R
+    lo = np.where(c < R, c, r + i)
+    hi = np.where(c < R, c + R, r + i + P)
+    return lo, hi
 
 
 def round_to_dtype(x, dtype: str) -> np.ndarray:

@@ -89,6 +89,62 @@ def pin_rope_complex_form():
         assert abs(z.real - y[c]) < 1e-12 and abs(z.imag - y[c + 32]) < 1e-12
 
 
+def pin_rope_partial_with_full_rotary_dim_is_full():
+    x = _rng(40).standard_normal((3, 64))
+    pos = np.array([0, 7, 123456])
+    got = oracle.rope.rope_rotate_partial(x, pos, 1e4, 64)
+    assert np.allclose(got, oracle.rope.rope_rotate(x, pos, 1e4), rtol=0, atol=1e-12)
+
+
+def pin_rope_partial_complex_form():
+    """r = 24 of d = 64: (x_c + i x_{c+12}) exp(i m theta^(-2c/24)) on the
+    rotated dims, the other 40 dims unchanged bit for bit."""
+    r = _rng(41)
+    x = r.standard_normal(64)
+    for m in (0, 1, 999, 65535):
+        got = oracle.rope.rope_rotate_partial(x, m, 5e5, 24)
+        z = (x[:12] + 1j * x[12:24]) * np.exp(1j * m * 5e5 ** (-np.arange(12) / 12.0))
+        assert np.allclose(got[:12], z.real, rtol=0, atol=1e-12)
+        assert np.allclose(got[12:24], z.imag, rtol=0, atol=1e-12)
+        assert np.array_equal(got[24:], x[24:])
+
+
+def pin_fc_pairs_partial_layout():
+    """FC pairs partition the dims; full layout is (c, c + d/2); with r = 16 of
+    d = 64 the rotated FCs are (c, c + 8) and the pass-through pairs are
+    (16 + i, 16 + i + 24)."""
+    lo, hi = oracle.rope.fc_pairs(64, 64)
+    assert lo.tolist() == list(range(32)) and hi.tolist() == list(range(32, 64))
+    lo, hi = oracle.rope.fc_pairs(64, 16)
+    assert sorted(lo.tolist() + hi.tolist()) == list(range(64))
+    assert lo[:8].tolist() == list(range(8)) and hi[:8].tolist() == list(range(8, 16))
+    assert lo[8:].tolist() == list(range(16, 40)) and hi[8:].tolist() == list(range(40, 64))
+
+
+def pin_tip_partial_all_fcs_is_full_dot_and_relative():
+    """Partial RoPE: with every FC dominant TIP is the full dot product, and
+    the score depends on the two positions only through their difference."""
+    r = _rng(42)
+    d, rd, theta = 64, 16, 1e4
+    pairs = oracle.rope.fc_pairs(d, rd)
+    q, k = r.standard_normal(d), r.standard_normal((5, d))
+    dom = np.arange(d // 2)
+    for (m, n, t) in ((10, 3, 100), (4000, 17, 12345)):
+        qa = oracle.rope.rope_rotate_partial(q, m, theta, rd)
+        ka = oracle.rope.rope_rotate_partial(k, n, theta, rd)
+        qb = oracle.rope.rope_rotate_partial(q, m + t, theta, rd)
+        kb = oracle.rope.rope_rotate_partial(k, n + t, theta, rd)
+        sa = oracle.tip.tip_scores(qa, ka, dom, pairs)
+        assert np.allclose(sa, ka @ qa, rtol=1e-12, atol=1e-12)
+        assert np.allclose(sa, oracle.tip.tip_scores(qb, kb, dom, pairs), rtol=1e-9, atol=1e-9)
+    # A pass-through FC alone does not depend on the positions at all.
+    c = 20
+    s1 = oracle.tip.tip_scores(oracle.rope.rope_rotate_partial(q, 5, theta, rd),
+                               oracle.rope.rope_rotate_partial(k, 2, theta, rd), [c], pairs)
+    lo, hi = pairs[0][c], pairs[1][c]
+    assert np.allclose(s1, k[:, lo] * q[lo] + k[:, hi] * q[hi], rtol=0, atol=1e-12)
+
+
 def pin_round_to_dtype():
     rd = oracle.rope.round_to_dtype
     # bf16: 8 significant bits.  Representable values stay put.
@@ -379,6 +435,36 @@ def pin_decode_per_head_budgets():
     best = int(np.argmax(kr @ rot(q[0, 2], n - 1)))
     assert res["idx"][0, 2].tolist() == [best] + [-1] * (width - 1)
     assert np.allclose(res["out"][0, 2], vall[best], rtol=0, atol=1e-12)
+
+
+def pin_decode_partial_rope_dense_equivalence():
+    """Partial RoPE (r = 32 of d = 64), all FCs dominant, B >= n: the step is
+    dense attention with the first 32 dims rotated (complex phasors) and the
+    rest as given."""
+    r = _rng(24)
+    d, rd, n, theta = 64, 32, 29, 1e4
+    dom = np.tile(np.arange(32), (2, 1))
+    st = oracle.decode.OracleState(1, 2, 1, d, theta, "f32", dom, 64, rotary_dim=rd)
+    k = r.standard_normal((1, n - 1, d)).astype(np.float32).astype(np.float64)
+    v = r.standard_normal((1, n - 1, d))
+    st.append(0, k, v)
+    q = r.standard_normal((1, 2, d))
+    kn = r.standard_normal((1, 1, d)).astype(np.float32).astype(np.float64)
+    vn = r.standard_normal((1, 1, d))
+    res = st.step(q, kn, vn, budget=64)
+    kall = np.concatenate([k[0], kn[0]], axis=0)
+    vall = np.concatenate([v[0], vn[0]], axis=0)
+
+    def rot(x, m):
+        z = (x[:16] + 1j * x[16:32]) * np.exp(1j * m * theta ** (-2.0 * np.arange(16) / rd))
+        return np.concatenate([z.real, z.imag, x[32:]])
+    kr = np.stack([rot(kall[j], j) for j in range(n)])
+    for h in range(2):
+        want = _sdpa(rot(q[0, h], n - 1), kr, vall)
+        assert np.allclose(res["out"][0, h], want, rtol=1e-6, atol=1e-6), h
+        assert res["idx"][0, h].tolist()[:n] == list(range(n))
+    # Pass-through dims of the cache are the inputs, unrotated.
+    assert np.array_equal(st.K[0, 0, :n, 32:], kall[:, 32:])
 
 
 def pin_decode_query_position():

@@ -22,6 +22,8 @@ _attend = oracle.fac.attend_subset
 _query_rot = oracle.decode.OracleState.query_rot
 _append = oracle.decode.OracleState.append
 _fc_scores = oracle.calibrate.fc_scores
+_rope_partial = oracle.rope.rope_rotate_partial
+_fc_pairs = oracle.rope.fc_pairs
 _ca = oracle.calibrate.contextual_agreement
 _dominant = oracle.calibrate.dominant_from_ca
 
@@ -65,19 +67,19 @@ def round_truncate(x, dtype):
     return np.trunc(x / sp) * sp
 
 
-def tip_drop_second_half(q, k, dom):
+def tip_drop_second_half(q, k, dom, pairs=None):
     q, k = np.asarray(q, np.float64), np.asarray(k, np.float64)
     return k[:, np.asarray(dom)] @ q[np.asarray(dom)]
 
 
-def tip_adjacent_pairs(q, k, dom):
+def tip_adjacent_pairs(q, k, dom, pairs=None):
     q, k = np.asarray(q, np.float64), np.asarray(k, np.float64)
     dom = np.asarray(dom)
     cols = np.concatenate([2 * dom, 2 * dom + 1])
     return k[:, cols] @ q[cols]
 
 
-def tip_wrong_partner(q, k, dom):
+def tip_wrong_partner(q, k, dom, pairs=None):
     q, k = np.asarray(q, np.float64), np.asarray(k, np.float64)
     half = q.shape[-1] // 2
     dom = np.asarray(dom)
@@ -128,18 +130,18 @@ def append_rotates_v(self, b, k_new, v_new):
     _append(self, b, k_new, oracle.rope.rope_rotate(v_new, pos[None, :], self.theta))
 
 
-def fc_scores_swapped_partner(q, k):
+def fc_scores_swapped_partner(q, k, pairs=None):
     q, k = np.asarray(q, np.float64), np.asarray(k, np.float64)
     half = q.shape[-1] // 2
     return (k[:, :half] * q[None, half:]).T + (k[:, half:] * q[None, :half]).T
 
 
-def ca_unnormalised(q, k, topk):
-    return _ca(q, k, topk) * min(topk, np.asarray(k).shape[0])
+def ca_unnormalised(q, k, topk, pairs=None):
+    return _ca(q, k, topk, pairs) * min(topk, np.asarray(k).shape[0])
 
 
-def ca_against_first_fc(q, k, topk):
-    s_c = oracle.calibrate.fc_scores(q, k)
+def ca_against_first_fc(q, k, topk, pairs=None):
+    s_c = oracle.calibrate.fc_scores(q, k, pairs)
     kk = min(topk, s_c.shape[1])
     ref = set(oracle.select.select_topb(s_c[0], kk).tolist())
     return np.array([len(ref & set(oracle.select.select_topb(s, kk).tolist())) / kk for s in s_c])
@@ -169,6 +171,27 @@ def step_budgets_reversed(self, q, k_new, v_new, budget, heads=None, head_budget
     return _step(self, q, k_new, v_new, budget, heads=heads, head_budgets=hb)
 
 
+def partial_freq_over_d(x, pos, theta, rotary_dim):
+    # frequencies spaced over the head dim instead of the rotary dim
+    x = np.asarray(x, np.float64)
+    d, R = x.shape[-1], rotary_dim // 2
+    w = np.power(float(theta), -2.0 * np.arange(R) / d)
+    phi = np.asarray(pos, np.float64)[..., None] * w
+    out = x.copy()
+    a, b = x[..., :R], x[..., R:rotary_dim]
+    out[..., :R] = a * np.cos(phi) - b * np.sin(phi)
+    out[..., R:rotary_dim] = b * np.cos(phi) + a * np.sin(phi)
+    return out
+
+
+def partial_rotates_all(x, pos, theta, rotary_dim):
+    return _rope_rotate(x, pos, theta)
+
+
+def pairs_full_layout(head_dim, rotary_dim=None):
+    return _fc_pairs(head_dim, None)
+
+
 MUTATIONS = {
     "rope_interleaved_pairs": (oracle.rope, "rope_rotate", rope_interleaved),
     "rope_backwards": (oracle.rope, "rope_rotate", rope_backwards),
@@ -188,6 +211,9 @@ MUTATIONS = {
     "fac_ignores_subset": (oracle.fac, "attend_subset", attend_all_rows),
     "fac_keys_as_values": (oracle.fac, "attend_subset", attend_k_for_v),
     "decode_query_at_n": (oracle.decode.OracleState, "query_rot", query_at_n),
+    "partial_freq_over_head_dim": (oracle.rope, "rope_rotate_partial", partial_freq_over_d),
+    "partial_rotates_pass_through": (oracle.rope, "rope_rotate_partial", partial_rotates_all),
+    "partial_pairs_full_layout": (oracle.rope, "fc_pairs", pairs_full_layout),
     "decode_rotates_values": (oracle.decode.OracleState, "append", append_rotates_v),
     "calib_swapped_partner": (oracle.calibrate, "fc_scores", fc_scores_swapped_partner),
     "calib_ca_unnormalised": (oracle.calibrate, "contextual_agreement", ca_unnormalised),

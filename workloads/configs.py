@@ -34,10 +34,15 @@ class Workload:
     planted_count: Optional[int] = None  # fixed count, else round(frac * context)
     planted_frac: Optional[float] = None
     spans: Optional[Tuple[int, int]] = None  # (count, length) clusters for planting
+    rotary_dim: Optional[int] = None    # partial RoPE: dims rotated (None = all)
 
     @property
     def n_fc(self) -> int:
         return self.head_dim // 2
+
+    @property
+    def rotated(self) -> int:
+        return self.head_dim if self.rotary_dim is None else self.rotary_dim
 
     @property
     def group(self) -> int:
@@ -80,6 +85,13 @@ CONFIGS = {
                    n_kv_heads=8, head_dim=128, context=131072, rope_theta=5e5,
                    dtype="bf16", budget=1024, n_dom=8, plant_mult=3.0,
                    planted_frac=0.005, steps=32, spans=(16, 64)),
+    # Partial RoPE: the 32k Llama-3-shaped layer with only the first half of
+    # each head rotated (rotary_dim 64 of 128, theta 1e4); the pages name no
+    # model for it, so the shape is the 32k layer's.
+    "c6": Workload("partial_rope_r64_ctx32k_b256", 6, batch=1, n_q_heads=32,
+                   n_kv_heads=8, head_dim=128, context=32768, rope_theta=1e4,
+                   dtype="bf16", budget=256, n_dom=16, plant_mult=3.0,
+                   planted_frac=0.01, rotary_dim=64),
 }
 
 

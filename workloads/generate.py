@@ -21,8 +21,10 @@ Recipe (every choice is a reading; the pages fix none of it):
   N(0, 1).
 
 Planting needs the relative angle between the query's and the key's
-positions, (t_q - t_k) * theta^(-2c/d); it is formed here with a complex
-phasor purely to shape the inputs.  Nothing downstream reads it, and a
+positions, (t_q - t_k) * omega_c, omega_c = theta^(-2c/r) for the r rotated
+dims (r = d unless the workload has a rotary_dim; pass-through pairs have
+omega 0), and each FC's dimension pair; both are formed here, with a complex
+phasor, purely to shape the inputs.  Nothing downstream reads it, and a
 mistake in it would only make planted tokens less salient.
 """
 
@@ -123,7 +125,12 @@ def generate(w: Workload, seed: int = 0xFA5A, with_prefill: bool = True):
     v = _normal(_rng(seed, cid, S_V), (b, hkv, L, d), w.dtype)
 
     # Planting (see module docstring).
-    omega = np.power(float(w.rope_theta), -2.0 * np.arange(half) / d)
+    r_dim = w.rotated
+    R = r_dim // 2
+    ci = np.arange(half)
+    omega = np.where(ci < R, np.power(float(w.rope_theta), -2.0 * np.minimum(ci, R) / r_dim), 0.0)
+    lo_d = np.where(ci < R, ci, r_dim + ci - R)
+    hi_d = np.where(ci < R, ci + R, r_dim + ci - R + (d - r_dim) // 2)
     for i in range(b):
         pos = planted[i]
         if pos.size == 0:
@@ -137,14 +144,15 @@ def generate(w: Workload, seed: int = 0xFA5A, with_prefill: bool = True):
                         owner[c] = h
             cs = np.nonzero(owner >= 0)[0]
             hs = owner[cs]
-            zq = q[0, i, hs, cs].astype(np.float64) + 1j * q[0, i, hs, cs + half]
-            zk = (k[i, g][np.ix_(pos, cs)].astype(np.float64)
-                  + 1j * k[i, g][np.ix_(pos, cs + half)])
+            lo, hi = lo_d[cs], hi_d[cs]
+            zq = q[0, i, hs, lo].astype(np.float64) + 1j * q[0, i, hs, hi]
+            zk = (k[i, g][np.ix_(pos, lo)].astype(np.float64)
+                  + 1j * k[i, g][np.ix_(pos, hi)])
             phase = np.exp(1j * np.outer(t_q - pos, omega[cs]))
             nz = np.where(np.abs(zq) > 0, zq / np.maximum(np.abs(zq), 1e-300), 1.0)
             znew = w.plant_mult * np.abs(zk) * nz[None, :] * phase
-            k[i, g][np.ix_(pos, cs)] = _cast(znew.real, w.dtype)
-            k[i, g][np.ix_(pos, cs + half)] = _cast(znew.imag, w.dtype)
+            k[i, g][np.ix_(pos, lo)] = _cast(znew.real, w.dtype)
+            k[i, g][np.ix_(pos, hi)] = _cast(znew.imag, w.dtype)
 
     out["k_prefill"], out["v_prefill"] = k, v
     return out
