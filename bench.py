@@ -51,6 +51,12 @@ def parse():
     p.add_argument("--eager", action="store_true", help="time eager launches, no graph")
     p.add_argument("--no-calibration", action="store_true",
                    help="skip timing fasa_calibrate (offline I_dom calibration)")
+    p.add_argument("--step-only", action="store_true",
+                   help="time only the step, its TIP kernel and the dense comparator: no "
+                        "calibration, per-head, partial-RoPE or FASA-M fields (for profiling "
+                        "the step's own kernels)")
+    p.add_argument("--no-partial-rope", action="store_true",
+                   help="skip timing the partial-RoPE layer")
     p.add_argument("--no-per-head", action="store_true",
                    help="skip timing the step with a budget per query head")
     p.add_argument("--no-fasa-m", action="store_true",
@@ -231,6 +237,78 @@ def per_head_timing(fasa, w, x, layers, q, kn, vn, seq, msl, dev, reps):
             "unit": "context tokens/s"}
 
 
+def partial_rope_timing(fasa, dev, L, reps):
+    """The 32k partial-RoPE layer (rotary_dim 64 of 128): the same decode step
+    over L rotated layer caches, replayed from a HIP graph, and its TIP kernel
+    back-to-back."""
+    import torch
+    import workloads as W
+    w = W.get("c6")
+    x = W.generate(w)
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev, td)
+    ctx = fasa.Context(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.capacity,
+                       w.rope_theta, w.dtype, x["dom"], w.budget, device=dev,
+                       rotary_dim=w.rotary_dim)
+    ws = ctx.new_workspace()
+    layers = [ctx.new_cache() for _ in range(L)]
+    kp, vp = to(x["k_prefill"]), to(x["v_prefill"])
+    zero = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    for (k, v, sd) in layers:
+        ctx.append_kv(k, v, sd, kp, vp, zero, ws)
+    del kp, vp
+    seq = torch.from_numpy((x["ctx"] - 1).astype(np.int32)).to(dev)
+    msl = int(x["ctx"].max())
+    q, kn, vn = to(x["q"][0]), to(x["k_new"][0]), to(x["v_new"][0])
+    out = torch.empty(w.batch, w.n_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    idx = torch.empty(w.batch, w.n_q_heads, w.budget, dtype=torch.int32, device=dev)
+    scores = torch.empty(w.batch, w.n_q_heads, w.capacity, dtype=torch.float32, device=dev)
+    seq_full = seq + 1
+
+    def one(i):
+        k, v, sd = layers[i % L]
+        ctx.decode_step(k, v, sd, q, kn, vn, seq, msl, w.budget, out, ws, idx_out=idx)
+
+    for i in range(L):
+        one(i)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(L):
+            one(i)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(L):
+            one(i)
+    g.replay()
+    torch.cuda.synchronize()
+    n_rep = max(1, reps // L)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n_rep):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (n_rep * L)
+    e0.record()
+    for i in range(n_rep * L):
+        ctx.tip_scores(layers[i % L][2], q, seq_full, msl, scores, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    tip_ms = e0.elapsed_time(e1) / (n_rep * L)
+    assert ctx.check(ws) == 0
+    es = 2 if w.dtype == "bf16" else 4
+    off, _ = ctx.sidecar_layout()
+    n = int(x["ctx"].sum())
+    tip_bytes = (int(off[-1]) * 2 * es + w.n_q_heads * 4) * n
+    del layers
+    return {"workload": w.name, "rotary_dim": w.rotary_dim, "ms_per_step": ms,
+            "value": n / (ms * 1e-3), "unit": "context tokens/s", "tip_kernel_avg_ms": tip_ms,
+            "tip_gbps": tip_bytes / (tip_ms * 1e-3) / 1e9}
+
+
 def cpu_baseline(w, x, budget_s):
     """The oracle (fp64 NumPy, one thread) on consecutive decode steps of the
     same workload until ~budget_s seconds of step time are spent."""
@@ -259,6 +337,8 @@ def cpu_baseline(w, x, budget_s):
 
 def main():
     args = parse()
+    if args.step_only:
+        args.no_calibration = args.no_per_head = args.no_partial_rope = args.no_fasa_m = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(the decode step shards by sequence / KV head with no exchange).",
@@ -437,6 +517,8 @@ def main():
     if not args.no_per_head and 2 * w.budget <= w.capacity:
         res["per_head_budgets"] = per_head_timing(fasa, w, x, layers, q, kn, vn, seq, msl, dev,
                                                   K)
+    if not args.no_partial_rope:
+        res["partial_rope"] = partial_rope_timing(fasa, dev, L, K)
     if not args.no_fasa_m:
         res["fasa_m"] = fasa_m_timing(ctx, w, x, q, kn, vn, seq, seq_full, msl, K,
                                       not args.no_dense)

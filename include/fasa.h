@@ -16,7 +16,10 @@
  *   Query head h reads KV head h / G.
  * - FC c is the dimension pair (c, c + C) (rotate-half); its frequency is
  *   theta^(-2c/d); the angle at absolute position m is m * theta^(-2c/d),
- *   formed in fp64.
+ *   formed in fp64.  Under partial RoPE (fasa_create_partial_rope) only the
+ *   first r = rotary_dim dims rotate: with R = r / 2, FC c < R is the pair
+ *   (c, c + R) at theta^(-2c/r), and FC c >= R is the pass-through pair
+ *   (c + R, c + C) at frequency 0 (stored and used as given).
  * - Element type ("dtype") of q, k_new, v_new, the K/V caches and the sidecar:
  *   FASA_F32 = float, FASA_BF16 = bfloat16 (raw 16-bit patterns).
  *   Accumulation is fp32; outputs and scores are float.
@@ -28,8 +31,8 @@
  * - Sidecar: the K columns of each KV head's union U_g of its query heads'
  *   dominant FCs, packed FC-major so TIP reads them with coalesced loads:
  *   [b][P][cap] pairs, P = sum_g |U_g|, plane fasa_sidecar_layout() gives the
- *   FC of each plane; a pair is (K[.., c], K[.., c + C]) (bf16: low half is
- *   column c; f32: two floats).  It is bit-identical to those K columns.
+ *   FC of each plane; a pair is the K columns of the FC's two dims, lower dim
+ *   first (bf16: low half; f32: two floats).  It is bit-identical to them.
  * - seq_lens: device int32 [b].  Its meaning is stated per call.
  * - max_seq_len: host-side upper bound on every sequence length the call
  *   will see on the device (sizes the launch grid); must be <= cap.
@@ -96,6 +99,21 @@ fasa_status fasa_create(fasa_ctx** out, int batch, int n_q_heads, int n_kv_heads
                         int head_dim, int capacity, double rope_theta,
                         fasa_dtype dtype, const int32_t* dom_fc, int n_dom,
                         int max_budget);
+
+/*
+ * fasa_create for heads with partial RoPE (gist.science/pt, "Resumo
+ * Tecnico", "Contribuicoes": the functional sparsity also holds under
+ * Partial-RoPE): only the first rotary_dim dims of each q and k row are
+ * rotated (rotate-half within them, frequencies theta^(-2c/rotary_dim)); the
+ * other dims pass through and are paired into zero-frequency FCs (see the
+ * conventions above), which calibration and I_dom treat like any other FC.
+ * rotary_dim: even, in [2, head_dim]; head_dim gives fasa_create.  Every other
+ * argument and limit as fasa_create.
+ */
+fasa_status fasa_create_partial_rope(fasa_ctx** out, int batch, int n_q_heads, int n_kv_heads,
+                                     int head_dim, int rotary_dim, int capacity,
+                                     double rope_theta, fasa_dtype dtype, const int32_t* dom_fc,
+                                     int n_dom, int max_budget);
 void fasa_destroy(fasa_ctx* ctx);
 
 /* Sizes in bytes of one K (or V) cache, the sidecar and the workspace. */

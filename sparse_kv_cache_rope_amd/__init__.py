@@ -30,6 +30,9 @@ _i32p = ctypes.POINTER(ctypes.c_int32)
 _SIGS = {
     "fasa_create": (_c_int, [ctypes.POINTER(_vp), _c_int, _c_int, _c_int, _c_int, _c_int,
                              ctypes.c_double, _c_int, _i32p, _c_int, _c_int]),
+    "fasa_create_partial_rope": (_c_int, [ctypes.POINTER(_vp), _c_int, _c_int, _c_int, _c_int,
+                                          _c_int, _c_int, ctypes.c_double, _c_int, _i32p, _c_int,
+                                          _c_int]),
     "fasa_destroy": (None, [_vp]),
     "fasa_kv_cache_bytes": (_c_size, [_vp]),
     "fasa_sidecar_bytes": (_c_size, [_vp]),
@@ -91,10 +94,11 @@ def _ptr(t):
 
 
 class Context:
-    """One attention layer's FASA context (``fasa_create``)."""
+    """One attention layer's FASA context (``fasa_create``; with rotary_dim,
+    partial RoPE over the first rotary_dim dims, ``fasa_create_partial_rope``)."""
 
     def __init__(self, batch, n_q_heads, n_kv_heads, head_dim, capacity, rope_theta,
-                 dtype, dom_fc, max_budget, device=None):
+                 dtype, dom_fc, max_budget, device=None, rotary_dim=None):
         if dtype not in _DTYPES:
             raise ValueError(f"dtype must be one of {list(_DTYPES)}")
         self.dtype_name = dtype
@@ -106,12 +110,20 @@ class Context:
         if dom.ndim != 2 or dom.shape[0] != n_q_heads:
             raise ValueError("dom_fc must be [n_q_heads, n_dom]")
         self.dom_fc = dom
+        self.rotary_dim = head_dim if rotary_dim is None else int(rotary_dim)
         handle = _vp()
         with torch.cuda.device(self.device):
-            _chk(_lib.fasa_create(ctypes.byref(handle), batch, n_q_heads, n_kv_heads, head_dim,
-                                  capacity, float(rope_theta), self.dtype_code,
-                                  dom.ctypes.data_as(_i32p), dom.shape[1], max_budget),
-                 "fasa_create")
+            if rotary_dim is None:
+                _chk(_lib.fasa_create(ctypes.byref(handle), batch, n_q_heads, n_kv_heads,
+                                      head_dim, capacity, float(rope_theta), self.dtype_code,
+                                      dom.ctypes.data_as(_i32p), dom.shape[1], max_budget),
+                     "fasa_create")
+            else:
+                _chk(_lib.fasa_create_partial_rope(
+                    ctypes.byref(handle), batch, n_q_heads, n_kv_heads, head_dim,
+                    self.rotary_dim, capacity, float(rope_theta), self.dtype_code,
+                    dom.ctypes.data_as(_i32p), dom.shape[1], max_budget),
+                    "fasa_create_partial_rope")
         self._h = handle
 
     def close(self):
@@ -358,14 +370,19 @@ def status_string(status):
 
 
 def raw_create(batch, n_q_heads, n_kv_heads, head_dim, capacity, rope_theta, dtype_code,
-               dom_fc, n_dom, max_budget):
-    """fasa_create with raw arguments: (status, handle or None, message)."""
+               dom_fc, n_dom, max_budget, rotary_dim=None):
+    """fasa_create (fasa_create_partial_rope with rotary_dim) with raw
+    arguments: (status, message)."""
     dom = np.ascontiguousarray(np.asarray(dom_fc, dtype=np.int32)) if dom_fc is not None else None
+    dp = dom.ctypes.data_as(_i32p) if dom is not None else None
     handle = _vp()
-    st = _lib.fasa_create(ctypes.byref(handle), batch, n_q_heads, n_kv_heads, head_dim,
-                          capacity, float(rope_theta), dtype_code,
-                          dom.ctypes.data_as(_i32p) if dom is not None else None, n_dom,
-                          max_budget)
+    if rotary_dim is None:
+        st = _lib.fasa_create(ctypes.byref(handle), batch, n_q_heads, n_kv_heads, head_dim,
+                              capacity, float(rope_theta), dtype_code, dp, n_dom, max_budget)
+    else:
+        st = _lib.fasa_create_partial_rope(ctypes.byref(handle), batch, n_q_heads, n_kv_heads,
+                                           head_dim, rotary_dim, capacity, float(rope_theta),
+                                           dtype_code, dp, n_dom, max_budget)
     msg = _lib.fasa_last_error().decode()
     if st == 0:
         _lib.fasa_destroy(handle)

@@ -138,6 +138,14 @@ extern "C" {
 fasa_status fasa_create(fasa_ctx** out, int batch, int n_q_heads, int n_kv_heads, int head_dim,
                         int capacity, double rope_theta, fasa_dtype dtype,
                         const int32_t* dom_fc, int n_dom, int max_budget) {
+  return fasa_create_partial_rope(out, batch, n_q_heads, n_kv_heads, head_dim, head_dim,
+                                  capacity, rope_theta, dtype, dom_fc, n_dom, max_budget);
+}
+
+fasa_status fasa_create_partial_rope(fasa_ctx** out, int batch, int n_q_heads, int n_kv_heads,
+                                     int head_dim, int rotary_dim, int capacity,
+                                     double rope_theta, fasa_dtype dtype, const int32_t* dom_fc,
+                                     int n_dom, int max_budget) {
   if (out == nullptr) return fail(FASA_ERR_INVALID_ARG, "out is null");
   *out = nullptr;
   if (batch < 1) return fail(FASA_ERR_INVALID_ARG, "batch %d < 1", batch);
@@ -153,6 +161,9 @@ fasa_status fasa_create(fasa_ctx** out, int batch, int n_q_heads, int n_kv_heads
     return fail(FASA_ERR_UNSUPPORTED, "query heads per KV head %d not in {1,2,4,8}", G);
   if (head_dim != 64 && head_dim != 128)
     return fail(FASA_ERR_UNSUPPORTED, "head_dim %d not in {64,128}", head_dim);
+  if (rotary_dim < 2 || rotary_dim > head_dim || rotary_dim % 2)
+    return fail(FASA_ERR_INVALID_ARG, "rotary_dim %d must be even and in [2, %d]", rotary_dim,
+                head_dim);
   if (capacity < 64 || capacity % 64)
     return fail(FASA_ERR_INVALID_ARG, "capacity %d must be a positive multiple of 64", capacity);
   if (capacity > kMaxCapacity)
@@ -186,6 +197,7 @@ fasa_status fasa_create(fasa_ctx** out, int batch, int n_q_heads, int n_kv_heads
   c->hkv = n_kv_heads;
   c->d = head_dim;
   c->C = C;
+  c->R = rotary_dim / 2;
   c->cap = capacity;
   c->G = G;
   c->F = n_dom;
@@ -213,8 +225,9 @@ fasa_status fasa_create(fasa_ctx** out, int batch, int n_q_heads, int n_kv_heads
     c->plane_off[g + 1] = c->plane_off[g] + slot;
   }
   c->P = c->plane_off[n_kv_heads];
-  std::vector<double> omega(C);
-  for (int i = 0; i < C; ++i) omega[i] = std::pow(rope_theta, -2.0 * i / head_dim);
+  // Rotated FCs at theta^(-2c/rotary_dim); pass-through FCs at frequency 0.
+  std::vector<double> omega(C, 0.0);
+  for (int i = 0; i < c->R; ++i) omega[i] = std::pow(rope_theta, -2.0 * i / rotary_dim);
 
   build_layout(c);
 

@@ -10,8 +10,9 @@
 // FCs of highest agreement.
 //
 // Rows of the score matrix, per sequence: row h (C + 1) + c holds FC c's
-// scores s_c[j] = q~_c K[j][c] + q~_{c+C} K[j][c+C] of query head h, row
-// h (C + 1) + C the full head's s[j] = sum_c s_c[j] (fp32, c ascending).
+// scores s_c[j] = q~_c K[j][c] + q~_{c+C} K[j][c+C] of query head h (under
+// partial RoPE the FC's dims are fc_lo / fc_hi), row h (C + 1) + C the full
+// head's s[j] = sum_c s_c[j] (fp32, c ascending).
 // Selection over those rows reuses the decode path's top-B kernels.
 
 #include "device_common.hpp"
@@ -29,7 +30,7 @@ template <bool BF16, int D, int G>
 __global__ void __launch_bounds__(kCalTokens * G)
 calib_scores_kernel(const void* __restrict__ k_cache, const float* __restrict__ qrot,
                     const int32_t* __restrict__ nb, int max_seq_len, int hq, int hkv, int cap,
-                    float* __restrict__ scores, uint32_t* err) {
+                    int R, float* __restrict__ scores, uint32_t* err) {
   constexpr int C = D / 2;
   constexpr int RW = D + 1;  // padded LDS row
   __shared__ float kt[kCalTokens * RW];
@@ -65,7 +66,8 @@ calib_scores_kernel(const void* __restrict__ k_cache, const float* __restrict__ 
   float full = 0.0f;
 #pragma unroll 8
   for (int c = 0; c < C; ++c) {
-    const float s = fmaf(q[c + C], k[c + C], q[c] * k[c]);
+    const int lo = fc_lo(c, R), hi = fc_hi(c, R, C);
+    const float s = fmaf(q[hi], k[hi], q[lo] * k[lo]);
     row[(size_t)c * cap] = s;
     full += s;
   }
@@ -111,7 +113,7 @@ static void launch_scores_d(const fasa_ctx* c, dim3 grid, hipStream_t s, const v
                             uint32_t* err) {
 #define FASA_CAL(GG)                                                                          \
   hipLaunchKernelGGL((calib_scores_kernel<BF16, D, GG>), grid, dim3(kCalTokens * GG), 0, s,   \
-                     k_cache, qrot, nb, max_seq_len, c->hq, c->hkv, c->cap, scores, err)
+                     k_cache, qrot, nb, max_seq_len, c->hq, c->hkv, c->cap, c->R, scores, err)
   switch (c->G) {
     case 1: FASA_CAL(1); break;
     case 2: FASA_CAL(2); break;

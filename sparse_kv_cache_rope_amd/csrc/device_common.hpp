@@ -152,4 +152,11 @@ __device__ __forceinline__ int checked_len(const int32_t* nb, int b, int max_seq
   return n;
 }
 
+// Dimension pair (fc_lo, fc_hi) of FC c of a head of C = d/2 FCs whose first
+// 2R dims are rotated (rotate-half within them) and whose other dims pass
+// through, paired the same way: (c, c + R) for c < R, (c + R, c + C) for
+// c >= R.  R = C is full RoPE, (c, c + C).
+__device__ __forceinline__ int fc_lo(int c, int R) { return c < R ? c : c + R; }
+__device__ __forceinline__ int fc_hi(int c, int R, int C) { return c < R ? c + R : c + C; }
+
 }  // namespace fasa

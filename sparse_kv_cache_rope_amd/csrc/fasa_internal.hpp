@@ -39,6 +39,7 @@ struct WsLayout {
 
 struct fasa_ctx {
   int batch, hq, hkv, d, C, cap, G, F, max_budget;
+  int R;  // rotated FCs: rotary_dim / 2 (C for full RoPE)
   double theta;
   fasa_dtype dtype;
   int device;

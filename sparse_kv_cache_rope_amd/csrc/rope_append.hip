@@ -26,7 +26,7 @@ append_kernel(const void* __restrict__ k_new, const void* __restrict__ v_new,
               void* __restrict__ k_cache, void* __restrict__ v_cache, void* __restrict__ sidecar,
               const int32_t* __restrict__ start_pos, int n_new, int hkv, int cap, int d, int P,
               const int32_t* __restrict__ plane_off, const int32_t* __restrict__ fc_slot,
-              const double* __restrict__ omega, uint32_t* err) {
+              const double* __restrict__ omega, int R, uint32_t* err) {
   using T = typename CacheT<BF16>::T;
   const int C = d / 2;
   const int rows = blockDim.x / C;
@@ -44,17 +44,19 @@ append_kernel(const void* __restrict__ k_new, const void* __restrict__ v_new,
   const size_t dst = (((size_t)b * hkv + g) * cap + pos) * d;
   append_fc<BF16>(static_cast<const T*>(k_new) + src, static_cast<const T*>(v_new) + src,
                   static_cast<T*>(k_cache) + dst, static_cast<T*>(v_cache) + dst, sidecar,
-                  (size_t)b * P + plane_off[g], fc_slot[g * C + c], c, C, cap, pos, omega[c]);
+                  (size_t)b * P + plane_off[g], fc_slot[g * C + c], fc_lo(c, R), fc_hi(c, R, C),
+                  cap, pos, omega[c]);
 }
 
 // Query prologue of the entry points that take no TIP pass, one workgroup per
 // (KV head g, sequence b), G * C threads: validate n_b = seq_lens[b] and
-// rotate the group's queries to position n_b - 1 (fp64 angle, kept in fp32).
+// rotate the group's queries to position n_b - 1 (fp64 angle, kept in fp32;
+// pass-through FCs copied).
 template <bool BF16>
 __global__ void __launch_bounds__(512)
 prologue_kernel(const void* __restrict__ q, const int32_t* __restrict__ seq_lens,
                 int max_seq_len, int hq, int G, int cap, int d,
-                const double* __restrict__ omega, int32_t* __restrict__ nb_out,
+                const double* __restrict__ omega, int R, int32_t* __restrict__ nb_out,
                 float* __restrict__ qrot, uint32_t* err) {
   using T = typename CacheT<BF16>::T;
   const int C = d / 2;
@@ -74,12 +76,14 @@ prologue_kernel(const void* __restrict__ q, const int32_t* __restrict__ seq_lens
   const int hh = tid / C, c = tid % C;
   const int h = g * G + hh;
   const T* qs = static_cast<const T*>(q) + ((size_t)b * hq + h) * d;
-  const double x0 = load_elem(qs, c), x1 = load_elem(qs, c + C);
+  const int lo = fc_lo(c, R), hi = fc_hi(c, R, C);
+  const double x0 = load_elem(qs, lo), x1 = load_elem(qs, hi);
+  const double w = omega[c];
   double sn, cs;
-  sincos((double)pos * omega[c], &sn, &cs);
+  sincos((double)pos * w, &sn, &cs);
   float* qr = qrot + ((size_t)b * hq + h) * d;
-  qr[c] = (float)(x0 * cs - x1 * sn);
-  qr[c + C] = (float)(x1 * cs + x0 * sn);
+  qr[lo] = (float)(w == 0.0 ? x0 : x0 * cs - x1 * sn);
+  qr[hi] = (float)(w == 0.0 ? x1 : x1 * cs + x0 * sn);
 }
 
 __global__ void fill_zero_kernel(uint4* __restrict__ p, size_t n16, uint8_t* __restrict__ tail,
@@ -112,11 +116,11 @@ hipError_t launch_append(const fasa_ctx* c, void* k_cache, void* v_cache, void* 
   if (c->dtype == FASA_BF16)
     hipLaunchKernelGGL(append_kernel<true>, grid, dim3(rows * c->C), 0, s, k_new, v_new, k_cache,
                        v_cache, sidecar, start_pos, n_new, c->hkv, c->cap, c->d, c->P,
-                       c->tab.plane_off, c->tab.fc_slot, c->tab.omega, err);
+                       c->tab.plane_off, c->tab.fc_slot, c->tab.omega, c->R, err);
   else
     hipLaunchKernelGGL(append_kernel<false>, grid, dim3(rows * c->C), 0, s, k_new, v_new, k_cache,
                        v_cache, sidecar, start_pos, n_new, c->hkv, c->cap, c->d, c->P,
-                       c->tab.plane_off, c->tab.fc_slot, c->tab.omega, err);
+                       c->tab.plane_off, c->tab.fc_slot, c->tab.omega, c->R, err);
   return hipGetLastError();
 }
 
@@ -129,10 +133,10 @@ hipError_t launch_prologue(const fasa_ctx* c, const void* q, const int32_t* seq_
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
   if (c->dtype == FASA_BF16)
     hipLaunchKernelGGL(prologue_kernel<true>, grid, block, 0, s, q, seq_lens, max_seq_len, c->hq,
-                       c->G, c->cap, c->d, c->tab.omega, nb, qrot, err);
+                       c->G, c->cap, c->d, c->tab.omega, c->R, nb, qrot, err);
   else
     hipLaunchKernelGGL(prologue_kernel<false>, grid, block, 0, s, q, seq_lens, max_seq_len, c->hq,
-                       c->G, c->cap, c->d, c->tab.omega, nb, qrot, err);
+                       c->G, c->cap, c->d, c->tab.omega, c->R, nb, qrot, err);
   return hipGetLastError();
 }
 

@@ -3,8 +3,12 @@
 // FC c is the dimension pair (c, c + d/2), its angle at absolute position m is
 // m * theta^(-2c/d) ("FASA: Frequency-aware Sparse Attention", gist.science/pt,
 // "Resumo Tecnico" section 2, "A Descoberta": 2-D subspaces with one angular
-// frequency each).  Angles and the rotation are taken in fp64 and the rotated
-// key is rounded once (nearest-even) to the cache dtype.
+// frequency each).  Under partial RoPE (same page, "Contribuicoes": the
+// sparsity holds for Partial-RoPE too) only the first r dims rotate, at
+// theta^(-2c/r); FC c is then the pair fc_lo / fc_hi gives, and pass-through
+// pairs have frequency 0 and are stored as given.  Angles and the rotation
+// are taken in fp64 and the rotated key is rounded once (nearest-even) to the
+// cache dtype.
 #pragma once
 
 #include "device_common.hpp"
@@ -30,49 +34,52 @@ __device__ __forceinline__ double to_f64(uint16_t bits) { return (double)bf16_bi
 __device__ __forceinline__ double to_f64(float x) { return (double)x; }
 
 // Rotates FC c = (x0, x1) of one key row by the angle whose sine and cosine
-// are given, stores K (and V) columns c, c + C and, when FC c is in the KV
-// head's union (slot >= 0), its sidecar pair.  Returns the bit patterns of the
-// stored pair (bf16: one packed word in .x; fp32: the two floats).
+// are given (pass: a pass-through FC, kept as given), stores K (and V)
+// columns lo, hi (the FC's dims) and, when FC c is in the KV head's union
+// (slot >= 0), its sidecar pair.  Returns the bit patterns of the stored pair
+// (bf16: one packed word in .x; fp32: the two floats).
 template <bool BF16>
 __device__ __forceinline__ uint2 store_rotated_fc(double x0, double x1,
                                                   const typename CacheT<BF16>::T* __restrict__ vsrc,
                                                   typename CacheT<BF16>::T* __restrict__ kdst,
                                                   typename CacheT<BF16>::T* __restrict__ vdst,
                                                   void* __restrict__ sidecar, size_t plane_base,
-                                                  int slot, int c, int C, int cap, long pos,
-                                                  double sn, double cs) {
-  const double y0 = x0 * cs - x1 * sn;
-  const double y1 = x1 * cs + x0 * sn;
-  vdst[c] = vsrc[c];
-  vdst[c + C] = vsrc[c + C];
+                                                  int slot, int lo, int hi, int cap, long pos,
+                                                  double sn, double cs, bool pass) {
+  const double y0 = pass ? x0 : x0 * cs - x1 * sn;
+  const double y1 = pass ? x1 : x1 * cs + x0 * sn;
+  vdst[lo] = vsrc[lo];
+  vdst[hi] = vsrc[hi];
   if constexpr (BF16) {
     const uint16_t k0 = f64_to_bf16_rne(y0), k1 = f64_to_bf16_rne(y1);
-    kdst[c] = k0;
-    kdst[c + C] = k1;
+    kdst[lo] = k0;
+    kdst[hi] = k1;
     const uint32_t pair = (uint32_t)k0 | ((uint32_t)k1 << 16);
     if (slot >= 0) static_cast<uint32_t*>(sidecar)[(plane_base + slot) * cap + pos] = pair;
     return make_uint2(pair, 0u);
   } else {
     const float k0 = (float)y0, k1 = (float)y1;
-    kdst[c] = k0;
-    kdst[c + C] = k1;
+    kdst[lo] = k0;
+    kdst[hi] = k1;
     if (slot >= 0) static_cast<float2*>(sidecar)[(plane_base + slot) * cap + pos] = make_float2(k0, k1);
     return make_uint2(__float_as_uint(k0), __float_as_uint(k1));
   }
 }
 
-// store_rotated_fc at the RoPE angle of FC c at position pos (fp64).
+// store_rotated_fc at the RoPE angle of FC c (dims lo, hi) at position pos
+// (fp64); omega = 0 marks a pass-through FC.
 template <bool BF16>
 __device__ __forceinline__ void append_fc(const typename CacheT<BF16>::T* __restrict__ ksrc,
                                           const typename CacheT<BF16>::T* __restrict__ vsrc,
                                           typename CacheT<BF16>::T* __restrict__ kdst,
                                           typename CacheT<BF16>::T* __restrict__ vdst,
                                           void* __restrict__ sidecar, size_t plane_base,
-                                          int slot, int c, int C, int cap, long pos,
+                                          int slot, int lo, int hi, int cap, long pos,
                                           double omega) {
   double sn, cs;
   sincos((double)pos * omega, &sn, &cs);
-  store_rotated_fc<BF16>(load_elem(ksrc, c), load_elem(ksrc, c + C), vsrc, kdst, vdst, sidecar, plane_base, slot, c, C, cap, pos, sn, cs);
+  store_rotated_fc<BF16>(load_elem(ksrc, lo), load_elem(ksrc, hi), vsrc, kdst, vdst, sidecar,
+                         plane_base, slot, lo, hi, cap, pos, sn, cs, omega == 0.0);
 }
 
 }  // namespace fasa

@@ -7,7 +7,8 @@
 // dominant FCs only.  For query head h and token j:
 //   s[h][j] = sum_{c in I_dom(h)} q~_c K[j][c] + q~_{c+C} K[j][c+C],
 // with q~ the query rotated to the current position n - 1 (the query is the
-// newest token).
+// newest token).  Under partial RoPE FC c is the dim pair fc_lo / fc_hi name
+// (R rotated FCs; R = C is full RoPE).
 //
 // One workgroup (4 waves) covers 256 consecutive tokens of one (sequence, KV
 // head) and all G query heads of that KV head.  The KV head's sidecar planes
@@ -44,7 +45,7 @@ constexpr int kMaxPlanes = 64;         // d/2 FCs at d = 128
 template <bool BF16, int G, int D>
 __global__ void __launch_bounds__(kTipThreads)
 tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int max_seq_len,
-           int cap, int P, int hq, int hkv, const void* __restrict__ q,
+           int cap, int P, int R, int hkv, const void* __restrict__ q,
            const double* __restrict__ omega, const int32_t* __restrict__ fc_slot,
            const uint64_t* __restrict__ dom_mask, const void* __restrict__ k_new,
            const void* __restrict__ v_new, void* __restrict__ k_cache,
@@ -53,6 +54,7 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
   using T = typename CacheT<BF16>::T;
   constexpr int C = D / 2;
   constexpr int PW = kMaxPlanes / kTipWaves;  // planes per wave, at most
+  const int hq = hkv * G;
   __shared__ float4 red[kTipWaves][G][kWave];
   __shared__ float2 wts[kMaxPlanes][G];
   __shared__ uint2 patch[kMaxPlanes];
@@ -94,8 +96,8 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
     const int i = min(tid + r * kTipThreads, G * C - 1);
     const int hh = i / C, c = i % C;
     const T* qs = static_cast<const T*>(q) + ((size_t)b * hq + g * G + hh) * D;
-    qr0[r] = qs[c];
-    qr1[r] = qs[c + C];
+    qr0[r] = qs[fc_lo(c, R)];
+    qr1[r] = qs[fc_hi(c, R, C)];
     om[r] = omega[c];
     slot[r] = fc_slot_g[g * C + c];
     dmask[r] = dom_mask_g[g * G + hh];
@@ -106,8 +108,8 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
   const size_t kv_src = ((size_t)b * hkv + g) * D;
   const global_ptr<const T> ksrc =
       (mode == kPrologueDecode) ? k_new_g : to_global(static_cast<const T*>(q));
-  const T kr0 = ksrc[kv_src + tid % C];
-  const T kr1 = ksrc[kv_src + tid % C + C];
+  const T kr0 = ksrc[kv_src + fc_lo(tid % C, R)];
+  const T kr1 = ksrc[kv_src + fc_hi(tid % C, R, C)];
 
   const int n = (mode == kPrologueDecode) ? v + 1 : v;
   const bool ok = v >= 0 && n >= 1 && n <= max_seq_len && n <= cap;
@@ -155,22 +157,25 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
     if (i < G * C) {
       const int hh = i / C, c = i % C;
       const bool dom = (dmask[r] >> c) & 1ull;
+      const int lo = fc_lo(c, R), hi = fc_hi(c, R, C);
+      const bool pass = om[r] == 0.0;  // pass-through FC
       const double qx0 = to_f64(qr0[r]), qx1 = to_f64(qr1[r]);
       double sn, cs;
       sincos((double)pos * om[r], &sn, &cs);
-      const float y0 = (float)(qx0 * cs - qx1 * sn);
-      const float y1 = (float)(qx1 * cs + qx0 * sn);
+      const float y0 = (float)(pass ? qx0 : qx0 * cs - qx1 * sn);
+      const float y1 = (float)(pass ? qx1 : qx1 * cs + qx0 * sn);
       if (tile == 0) {
         float* qr = qrot + ((size_t)b * hq + g * G + hh) * D;
-        qr[c] = y0;
-        qr[c + C] = y1;
+        qr[lo] = y0;
+        qr[hi] = y1;
       }
       if (slot[r] >= 0) wts[slot[r]][hh] = dom ? make_float2(y0, y1) : make_float2(0.0f, 0.0f);
       if (owner && i < C) {
         const size_t dst = (((size_t)b * hkv + g) * cap + pos) * D;
         const uint2 pair = store_rotated_fc<BF16>(
             to_f64(kr0), to_f64(kr1), static_cast<const T*>(v_new) + kv_src, static_cast<T*>(k_cache) + dst,
-            static_cast<T*>(v_cache) + dst, sidecar, plane0, slot[r], c, C, cap, pos, sn, cs);
+            static_cast<T*>(v_cache) + dst, sidecar, plane0, slot[r], lo, hi, cap, pos, sn, cs,
+            pass);
         if (slot[r] >= 0) patch[slot[r]] = pair;
       }
     }
@@ -272,7 +277,7 @@ static void launch_tip_t(dim3 grid, hipStream_t s, int mode, const PlaneOffsets&
                          const TipArgs& a, const fasa_ctx* c, int32_t* nb, float* qrot,
                          float* scores, uint32_t* err) {
   hipLaunchKernelGGL((tip_kernel<BF16, G, D>), grid, dim3(kTipThreads), 0, s, a.seq_lens,
-                     a.sidecar, mode, a.max_seq_len, c->cap, c->P, c->hq, c->hkv, a.q,
+                     a.sidecar, mode, a.max_seq_len, c->cap, c->P, c->R, c->hkv, a.q,
                      c->tab.omega, c->tab.fc_slot, c->tab.dom_mask, a.k_new, a.v_new, a.k_cache,
                      a.v_cache, nb, qrot, scores, err, po);
 }

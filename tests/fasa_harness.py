@@ -37,7 +37,8 @@ class GpuSetup:
         self.w, self.x = w, x
         self.cap = capacity or w.capacity
         self.ctx = fasa.Context(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, self.cap,
-                                w.rope_theta, w.dtype, x["dom"], max_budget or w.budget)
+                                w.rope_theta, w.dtype, x["dom"], max_budget or w.budget,
+                                rotary_dim=w.rotary_dim)
         self.k, self.v, self.side = self.ctx.new_cache(kv_on_host=kv_on_host)
         self.ws = self.ctx.new_workspace()
         self.td = torch_dtype(w)
@@ -58,7 +59,7 @@ class GpuSetup:
 
 def oracle_setup(w, x, capacity=None):
     st = oracle.OracleState(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.rope_theta,
-                            w.dtype, x["dom"], capacity or w.capacity)
+                            w.dtype, x["dom"], capacity or w.capacity, rotary_dim=w.rotary_dim)
     for b in range(w.batch):
         n0 = int(x["ctx"][b]) - 1
         st.append(b, x["k_prefill"][b][:, :n0], x["v_prefill"][b][:, :n0])
@@ -93,9 +94,13 @@ def check_out(got, want, dtype, where=""):
     return float((err / lim).max()) if err.size else 0.0
 
 
-def tip_bound(q_rot, k_rot, dom):
+def tip_bound(q_rot, k_rot, dom, pairs=None):
     half = q_rot.shape[-1] // 2
-    cols = np.concatenate([dom, dom + half])
+    dom = np.asarray(dom)
+    if pairs is None:
+        cols = np.concatenate([dom, dom + half])
+    else:
+        cols = np.concatenate([pairs[0][dom], pairs[1][dom]])
     return np.abs(k_rot[:, cols]) @ np.abs(q_rot[cols])
 
 

@@ -72,3 +72,10 @@ def test_status_strings(fasa):
 def test_create_rejects_bad_arguments(fasa, args, code, msg):
     st, detail = fasa.raw_create(*args)
     assert st == code and msg in detail, (st, detail)
+
+
+@pytest.mark.parametrize("rotary_dim", [0, 3, 66, -2])
+def test_partial_rope_rejects_bad_rotary_dim(fasa, rotary_dim):
+    st, detail = fasa.raw_create(1, 2, 1, 64, 128, 1e4, 1, [[0], [1]], 1, 8,
+                                 rotary_dim=rotary_dim)
+    assert st == -1 and "rotary_dim" in detail, (st, detail)

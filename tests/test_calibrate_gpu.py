@@ -20,6 +20,8 @@ CASES = {
     "c1": (W.get("c1"), 64),
     "c2s": (W.shrink(W.get("c2"), context=5003), 256),
     "c3s": (W.shrink(W.get("c3"), batch=3, context=3001, context_min=1500), 100),
+    # partial RoPE: 32 rotated FCs and 32 pass-through pairs
+    "c6s": (W.shrink(W.get("c6"), context=4001), 128),
 }
 
 
@@ -55,13 +57,13 @@ def test_calibrate_matches_oracle(gpu, name):
         qr = o.query_rot(b, x["q"][0][b])
         for h in range(w.n_q_heads):
             K = o.K[b, h // w.group, :n]
-            want[b, h] = oracle.calibrate.contextual_agreement(qr[h], K, topk)
+            want[b, h] = oracle.calibrate.contextual_agreement(qr[h], K, topk, o.pairs)
             cg = np.rint(got[b, h] * take).astype(np.int64)
             cw = np.rint(want[b, h] * take).astype(np.int64)
             want32[b, h] = cw.astype(np.float32) / np.float32(take)
             bad = np.nonzero(cg != cw)[0]
             if bad.size:
-                s_c = oracle.calibrate.fc_scores(qr[h], K)
+                s_c = oracle.calibrate.fc_scores(qr[h], K, o.pairs)
                 full_tie = near_tie(s_c.sum(axis=0), take)
                 for c in bad:
                     assert full_tie or near_tie(s_c[c], take), (b, h, int(c), cg[c], cw[c])
