@@ -225,6 +225,9 @@ fasa_status fasa_create_partial_rope(fasa_ctx** out, int batch, int n_q_heads, i
     c->plane_off[g + 1] = c->plane_off[g] + slot;
   }
   c->P = c->plane_off[n_kv_heads];
+  c->max_union = 0;
+  for (int g = 0; g < n_kv_heads; ++g)
+    c->max_union = std::max(c->max_union, c->plane_off[g + 1] - c->plane_off[g]);
   // Rotated FCs at theta^(-2c/rotary_dim); pass-through FCs at frequency 0.
   std::vector<double> omega(C, 0.0);
   for (int i = 0; i < c->R; ++i) omega[i] = std::pow(rope_theta, -2.0 * i / rotary_dim);

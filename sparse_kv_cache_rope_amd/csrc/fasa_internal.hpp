@@ -40,6 +40,7 @@ struct WsLayout {
 struct fasa_ctx {
   int batch, hq, hkv, d, C, cap, G, F, max_budget;
   int R;  // rotated FCs: rotary_dim / 2 (C for full RoPE)
+  int max_union;  // largest |U_g| over the KV heads (sidecar planes of one head)
   double theta;
   fasa_dtype dtype;
   int device;

@@ -20,14 +20,31 @@
 // Per-step work that used to be a kernel of its own runs while those loads
 // are in flight: every workgroup rotates its group's queries (fp64 angle, kept
 // in fp32) into LDS weights (q~_c, q~_{c+C}) per plane and head, zero where
-// the FC is not dominant for the head; the tile-0 workgroup also writes the
-// rotated queries for FAC; in decode mode the workgroup whose tile holds the
-// new position n - 1 rotates and stores the step's key (K, V and sidecar) and
-// substitutes the new sidecar pairs into the values its lanes loaded for that
-// position.  Sequence lengths are read, never written, here: another
-// workgroup of the same launch may still be reading them.
+// the FC is not dominant for the head; in decode mode the workgroup whose tile
+// holds the new position n - 1 also rotates the step's key.
+//
+// Order of work, so that every wait counts exactly the loads it needs:
+//   1. the length (scalar), then the query pairs, the tables and the step's
+//      K/V pair (vector) are issued;
+//   2. once the length is in, the sidecar stream is issued, a wave's planes
+//      in order (a workgroup with nothing to read gets empty ranges);
+//   3. the rotations run as soon as the step-1 loads are in (issued before
+//      the stream, with no branch between: the wait is for them alone);
+//      results kept in registers and LDS; only then may a workgroup leave;
+//      one barrier;
+//   4. plane k's FMAs wait for plane k's load only (the compiler counts the
+//      loads issued after it), so the sums proceed as the data arrives;
+//   5. every global store of the launch comes last: scores, the rotated
+//      queries (tile 0), the step's K, V and sidecar pairs (the owner tile),
+//      the length.  A store pending among the loads would make the compiler
+//      wait for all of them.
+// The owner tile's loaded values at n - 1 may predate the step's own pairs:
+// its FMA loop (a copy of the others', under one uniform branch) selects the
+// new pairs into that position's lane instead.
 //
 // HBM-bound: 4 bytes per token and plane (bf16) against 4 G FMAs.
+
+#include <type_traits>
 
 #include "fasa_internal.hpp"
 #include "rope_common.hpp"
@@ -41,8 +58,9 @@ constexpr int kMaxPlanes = 64;         // d/2 FCs at d = 128
 
 // The arguments needed first lead the list: the build preloads the first 16
 // dwords of kernel arguments into registers, which saves a dependent load
-// before the stream starts.
-template <bool BF16, int G, int D>
+// before the stream starts.  PW: sidecar loads per wave, enough for the
+// context's largest union (4 PW >= max_g |U_g|).
+template <bool BF16, int G, int D, int PW>
 __global__ void __launch_bounds__(kTipThreads)
 tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int max_seq_len,
            int cap, int P, int R, int hkv, const void* __restrict__ q,
@@ -53,7 +71,8 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
            float* __restrict__ scores, uint32_t* err, PlaneOffsets po) {
   using T = typename CacheT<BF16>::T;
   constexpr int C = D / 2;
-  constexpr int PW = kMaxPlanes / kTipWaves;  // planes per wave, at most
+  constexpr int kPairBytes = BF16 ? 4 : 8;
+  static_assert(PW * kTipWaves <= kMaxPlanes, "planes per wave");
   const int hq = hkv * G;
   __shared__ float4 red[kTipWaves][G][kWave];
   __shared__ float2 wts[kMaxPlanes][G];
@@ -64,7 +83,6 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int tile0 = tile * kTipTokens;
-  const int j0 = tile0 + lane * 4;
 
   // The length, the plane offsets and the argument pointers used before the
   // stream are independent scalar loads: joining them in one (empty) asm
@@ -73,19 +91,18 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
   int p0 = po.off[g];
   int p1 = po.off[g + 1];
   asm volatile("" : "+s"(v), "+s"(p0), "+s"(p1), "+s"(fc_slot), "+s"(dom_mask), "+s"(k_new),
-               "+s"(nb_out));
+               "+s"(v_new));
   // The asm hides that these point to global memory; say it again so that
   // loads through them stay global (not flat) loads.
   const global_ptr<const int32_t> fc_slot_g = to_global(fc_slot);
   const global_ptr<const uint64_t> dom_mask_g = to_global(dom_mask);
   const global_ptr<const T> k_new_g = to_global(static_cast<const T*>(k_new));
+  const global_ptr<const T> v_new_g = to_global(static_cast<const T*>(v_new));
   const int U = p1 - p0;
   const size_t plane0 = (size_t)b * P + p0;
 
-  // Query elements and tables of this thread's (head, FC) pairs, and the
-  // step's key row: loaded unconditionally (clamped indexes) and before the
-  // sidecar, so that the exact count of loads in flight lets their first use
-  // wait for them alone, not for the stream.
+  // This thread's (head, FC) pairs: query elements and tables; loaded with
+  // clamped indexes so that every thread issues the same loads.
   constexpr int QP = (G * C + kTipThreads - 1) / kTipThreads;
   T qr0[QP], qr1[QP];
   double om[QP];
@@ -102,46 +119,45 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
     slot[r] = fc_slot_g[g * C + c];
     dmask[r] = dom_mask_g[g * G + hh];
   }
-  // Query-only launches have no key row (k_new may be null): they read the
-  // same (unused) indexes of q instead, which holds b * Hq * d >= b * Hkv * d
-  // elements.
+  // The step's key and value pair of FC tid % C.  Query-only launches have no
+  // such row (k_new, v_new may be null): they read the same (unused) indexes
+  // of q instead, which holds b * Hq * d >= b * Hkv * d elements.
+  const bool decode = (mode == kPrologueDecode);
   const size_t kv_src = ((size_t)b * hkv + g) * D;
-  const global_ptr<const T> ksrc =
-      (mode == kPrologueDecode) ? k_new_g : to_global(static_cast<const T*>(q));
-  const T kr0 = ksrc[kv_src + fc_lo(tid % C, R)];
-  const T kr1 = ksrc[kv_src + fc_hi(tid % C, R, C)];
+  const global_ptr<const T> ksrc = decode ? k_new_g : to_global(static_cast<const T*>(q));
+  const global_ptr<const T> vsrc = decode ? v_new_g : to_global(static_cast<const T*>(q));
+  const int c_own = tid % C;
+  const T kr0 = ksrc[kv_src + fc_lo(c_own, R)];
+  const T kr1 = ksrc[kv_src + fc_hi(c_own, R, C)];
+  const T vr0 = vsrc[kv_src + fc_lo(c_own, R)];
+  const T vr1 = vsrc[kv_src + fc_hi(c_own, R, C)];
 
-  const int n = (mode == kPrologueDecode) ? v + 1 : v;
+  // Keep the loads above ahead of the stream.
+  __builtin_amdgcn_sched_barrier(0);
+
+  const int n = decode ? v + 1 : v;
   const bool ok = v >= 0 && n >= 1 && n <= max_seq_len && n <= cap;
   const bool lead = (tile == 0 && g == 0 && tid == 0);
-  if (!ok) {
-    if (lead) {
-      nb_out[b] = 0;
-      if (!(mode == kPrologueQueryOnly && v == 0)) raise_flag(err, FASA_DEVFLAG_SEQ_LEN);
-    }
-    return;
-  }
-  if (lead) nb_out[b] = n;
-  if (tile0 >= n) return;
+  const bool live = ok && tile0 < n;  // this workgroup has tokens to score
   const long pos = n - 1;
-  const bool owner = (mode == kPrologueDecode) && (pos - tile0 < kTipTokens);
+  const bool owner = live && decode && (pos - tile0 < kTipTokens);
 
-  // This wave's sidecar planes, all in flight at once, as buffer loads whose
-  // range ends at the plane's first 4 * ceil(n / 4) tokens: planes past U and
-  // quads past n read zeros without touching memory, so no load is skipped by
-  // a branch.  Each plane gets its own resource (base = the plane).
-  constexpr int kPairBytes = BF16 ? 4 : 8;
-  const int n4 = (n + 3) & ~3;
-  const uint32_t range = (uint32_t)n4 * kPairBytes;
-  const uint32_t voff = (uint32_t)j0 * kPairBytes;
-  const bool live = j0 < n;
+  // 2. This wave's sidecar planes, all in flight at once, as buffer loads
+  // whose resource starts at the tile's first pair and ends at the plane's
+  // first 4 * ceil(n / 4) tokens: planes past U, quads past n and workgroups
+  // with nothing to score read zeros without touching memory, so no load is
+  // skipped by a branch, and the per-lane offset is the only vector operand.
+  const int left = live ? ((n + 3) & ~3) - tile0 : 0;
+  const int range = left * kPairBytes;
+  const uint32_t voff = (uint32_t)lane * 4 * kPairBytes;
   uint4 xa[PW], xb[PW];
 #pragma unroll
   for (int k = 0; k < PW; ++k) {
     const int u = wave + k * kTipWaves;
-    const char* base = static_cast<const char*>(sidecar) + (plane0 + u) * (size_t)cap * kPairBytes;
+    const char* base = static_cast<const char*>(sidecar) +
+                       ((plane0 + u) * (size_t)cap + (size_t)tile0) * kPairBytes;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(base), (short)0, (u < U) ? (int)range : 0, kBufferRsrcWord3);
+        const_cast<char*>(base), (short)0, (u < U) ? range : 0, kBufferRsrcWord3);
     const auto va = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
     xa[k] = make_uint4(va[0], va[1], va[2], va[3]);
     if constexpr (!BF16) {
@@ -150,89 +166,90 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
     }
   }
 
-  // Rotations at position n - 1 while the sidecar streams in.
+  // Every stream load issues before the rotations below wait for anything.
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. Rotations at position n - 1 while the stream is in flight.
+  float qy0[QP], qy1[QP];
+  uint2 own_bits = make_uint2(0u, 0u);
 #pragma unroll
   for (int r = 0; r < QP; ++r) {
-    const int i = tid + r * kTipThreads;
-    if (i < G * C) {
-      const int hh = i / C, c = i % C;
-      const bool dom = (dmask[r] >> c) & 1ull;
-      const int lo = fc_lo(c, R), hi = fc_hi(c, R, C);
-      const bool pass = om[r] == 0.0;  // pass-through FC
-      const double qx0 = to_f64(qr0[r]), qx1 = to_f64(qr1[r]);
-      double sn, cs;
-      sincos((double)pos * om[r], &sn, &cs);
-      const float y0 = (float)(pass ? qx0 : qx0 * cs - qx1 * sn);
-      const float y1 = (float)(pass ? qx1 : qx1 * cs + qx0 * sn);
-      if (tile == 0) {
-        float* qr = qrot + ((size_t)b * hq + g * G + hh) * D;
-        qr[lo] = y0;
-        qr[hi] = y1;
-      }
-      if (slot[r] >= 0) wts[slot[r]][hh] = dom ? make_float2(y0, y1) : make_float2(0.0f, 0.0f);
-      if (owner && i < C) {
-        const size_t dst = (((size_t)b * hkv + g) * cap + pos) * D;
-        const uint2 pair = store_rotated_fc<BF16>(
-            to_f64(kr0), to_f64(kr1), static_cast<const T*>(v_new) + kv_src, static_cast<T*>(k_cache) + dst,
-            static_cast<T*>(v_cache) + dst, sidecar, plane0, slot[r], lo, hi, cap, pos, sn, cs,
-            pass);
-        if (slot[r] >= 0) patch[slot[r]] = pair;
-      }
+    const int i = min(tid + r * kTipThreads, G * C - 1);
+    const int hh = i / C, c = i % C;
+    const bool dom = (dmask[r] >> c) & 1ull;
+    const bool pass = om[r] == 0.0;  // pass-through FC
+    const double qx0 = to_f64(qr0[r]), qx1 = to_f64(qr1[r]);
+    double sn, cs;
+    sincos((double)pos * om[r], &sn, &cs);
+    qy0[r] = (float)(pass ? qx0 : qx0 * cs - qx1 * sn);
+    qy1[r] = (float)(pass ? qx1 : qx1 * cs + qx0 * sn);
+    if (tid + r * kTipThreads < G * C && slot[r] >= 0)
+      wts[slot[r]][hh] = dom ? make_float2(qy0[r], qy1[r]) : make_float2(0.0f, 0.0f);
+    if (r == 0) {
+      // Thread tid < C holds FC tid here (head 0), the FC of its key pair.
+      own_bits = rotate_pair<BF16>(to_f64(kr0), to_f64(kr1), sn, cs, pass);
+      if (owner && tid < C && slot[0] >= 0) patch[slot[0]] = own_bits;
     }
+  }
+  if (!live) {
+    if (lead) {
+      nb_out[b] = ok ? n : 0;
+      if (!ok && !(mode == kPrologueQueryOnly && v == 0)) raise_flag(err, FASA_DEVFLAG_SEQ_LEN);
+    }
+    return;
   }
   __syncthreads();
 
-  // The new position's loaded values may predate its store: use the pairs
-  // just computed instead.
-  if (owner && lane == (int)((pos - tile0) >> 2)) {
-    const int t = (int)(pos & 3);
-#pragma unroll
-    for (int k = 0; k < PW; ++k) {
-      const int u = wave + k * kTipWaves;
-      if (u < U) {
-        const uint2 p = patch[u];
-        if constexpr (BF16) {
-          xa[k].x = (t == 0) ? p.x : xa[k].x;
-          xa[k].y = (t == 1) ? p.x : xa[k].y;
-          xa[k].z = (t == 2) ? p.x : xa[k].z;
-          xa[k].w = (t == 3) ? p.x : xa[k].w;
-        } else {
-          if (t == 0) { xa[k].x = p.x; xa[k].y = p.y; }
-          if (t == 1) { xa[k].z = p.x; xa[k].w = p.y; }
-          if (t == 2) { xb[k].x = p.x; xb[k].y = p.y; }
-          if (t == 3) { xb[k].z = p.x; xb[k].w = p.y; }
-        }
-      }
-    }
-  }
-
+  // 4. Sums over this wave's planes for its 4 tokens and the G heads.
   float acc[G][4];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[hh][t] = 0.0f;
-  if (live) {
+  const bool pos_lane = lane == (int)((pos - tile0) >> 2);
+  const int pos_t = (int)(pos & 3);
+  auto sums = [&](auto own) {
+    constexpr bool OWN = decltype(own)::value;
 #pragma unroll
     for (int k = 0; k < PW; ++k) {
       const int u = wave + k * kTipWaves;
       if (u >= U) break;
+      uint4 da = xa[k], db = xb[k];
+      if constexpr (OWN) {
+        const uint2 p = patch[u];
+        if constexpr (BF16) {
+          da.x = (pos_lane && pos_t == 0) ? p.x : da.x;
+          da.y = (pos_lane && pos_t == 1) ? p.x : da.y;
+          da.z = (pos_lane && pos_t == 2) ? p.x : da.z;
+          da.w = (pos_lane && pos_t == 3) ? p.x : da.w;
+        } else {
+          da.x = (pos_lane && pos_t == 0) ? p.x : da.x;
+          da.y = (pos_lane && pos_t == 0) ? p.y : da.y;
+          da.z = (pos_lane && pos_t == 1) ? p.x : da.z;
+          da.w = (pos_lane && pos_t == 1) ? p.y : da.w;
+          db.x = (pos_lane && pos_t == 2) ? p.x : db.x;
+          db.y = (pos_lane && pos_t == 2) ? p.y : db.y;
+          db.z = (pos_lane && pos_t == 3) ? p.x : db.z;
+          db.w = (pos_lane && pos_t == 3) ? p.y : db.w;
+        }
+      }
       float lo[4], hi[4];
       if constexpr (BF16) {
-        const uint32_t wd[4] = {xa[k].x, xa[k].y, xa[k].z, xa[k].w};
+        const uint32_t wd[4] = {da.x, da.y, da.z, da.w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           lo[t] = bf16_lo(wd[t]);
           hi[t] = bf16_hi(wd[t]);
         }
       } else {
-        lo[0] = __uint_as_float(xa[k].x);
-        hi[0] = __uint_as_float(xa[k].y);
-        lo[1] = __uint_as_float(xa[k].z);
-        hi[1] = __uint_as_float(xa[k].w);
-        lo[2] = __uint_as_float(xb[k].x);
-        hi[2] = __uint_as_float(xb[k].y);
-        lo[3] = __uint_as_float(xb[k].z);
-        hi[3] = __uint_as_float(xb[k].w);
+        lo[0] = __uint_as_float(da.x);
+        hi[0] = __uint_as_float(da.y);
+        lo[1] = __uint_as_float(da.z);
+        hi[1] = __uint_as_float(da.w);
+        lo[2] = __uint_as_float(db.x);
+        hi[2] = __uint_as_float(db.y);
+        lo[3] = __uint_as_float(db.z);
+        hi[3] = __uint_as_float(db.w);
       }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
@@ -241,13 +258,18 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
         for (int t = 0; t < 4; ++t) acc[hh][t] = fmaf(w.y, hi[t], fmaf(w.x, lo[t], acc[hh][t]));
       }
     }
-  }
-
+  };
+  if (owner)
+    sums(std::true_type{});
+  else
+    sums(std::false_type{});
 #pragma unroll
   for (int hh = 0; hh < G; ++hh)
     red[wave][hh][lane] = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
   __syncthreads();
-  // Thread (hh, quad) sums the waves' partials for 4 tokens of head hh.
+
+  // 5. Stores.  Thread (hh, quad) sums the waves' partials for 4 tokens of
+  // head hh.
   for (int i = tid; i < G * kWave; i += kTipThreads) {
     const int hh = i / kWave, qd = i % kWave;
     float4 s = red[0][hh][qd];
@@ -270,16 +292,43 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
         if (j + t < n) dst[t] = vv[t];
     }
   }
+  if (tile == 0) {
+#pragma unroll
+    for (int r = 0; r < QP; ++r) {
+      const int i = tid + r * kTipThreads;
+      if (i < G * C) {
+        const int hh = i / C, c = i % C;
+        float* qr = qrot + ((size_t)b * hq + g * G + hh) * D;
+        qr[fc_lo(c, R)] = qy0[r];
+        qr[fc_hi(c, R, C)] = qy1[r];
+      }
+    }
+  }
+  if (owner && tid < C) {
+    const size_t dst = (((size_t)b * hkv + g) * cap + pos) * D;
+    store_fc_pair<BF16>(own_bits, vr0, vr1, static_cast<T*>(k_cache) + dst,
+                        static_cast<T*>(v_cache) + dst, sidecar, plane0, slot[0],
+                        fc_lo(tid, R), fc_hi(tid, R, C), cap, pos);
+  }
+  if (lead) nb_out[b] = n;
 }
 
 template <bool BF16, int G, int D>
 static void launch_tip_t(dim3 grid, hipStream_t s, int mode, const PlaneOffsets& po,
                          const TipArgs& a, const fasa_ctx* c, int32_t* nb, float* qrot,
                          float* scores, uint32_t* err) {
-  hipLaunchKernelGGL((tip_kernel<BF16, G, D>), grid, dim3(kTipThreads), 0, s, a.seq_lens,
-                     a.sidecar, mode, a.max_seq_len, c->cap, c->P, c->R, c->hkv, a.q,
-                     c->tab.omega, c->tab.fc_slot, c->tab.dom_mask, a.k_new, a.v_new, a.k_cache,
-                     a.v_cache, nb, qrot, scores, err, po);
+#define FASA_TIP(PWV)                                                                          \
+  hipLaunchKernelGGL((tip_kernel<BF16, G, D, PWV>), grid, dim3(kTipThreads), 0, s, a.seq_lens, \
+                     a.sidecar, mode, a.max_seq_len, c->cap, c->P, c->R, c->hkv, a.q,          \
+                     c->tab.omega, c->tab.fc_slot, c->tab.dom_mask, a.k_new, a.v_new,          \
+                     a.k_cache, a.v_cache, nb, qrot, scores, err, po)
+  // Loads per wave: the largest union over the KV heads, 4 planes per step.
+  const int pw = (c->max_union + kTipWaves - 1) / kTipWaves;
+  if (pw <= 4) FASA_TIP(4);
+  else if (pw <= 8) FASA_TIP(8);
+  else if (pw <= 12) FASA_TIP(12);
+  else FASA_TIP(16);
+#undef FASA_TIP
 }
 
 template <int G>
