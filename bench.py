@@ -18,8 +18,9 @@ Printed: one JSON line with the metric (context tokens scanned per second),
 the fraction of HBM peak on the algorithmic bytes, the dominant kernel's
 roofline figure (TIP: sidecar bytes read + score bytes written / its average
 duration from HIP events over back-to-back launches), the in-build dense
-decode comparator, the step with K/V caches in pinned host memory (FASA-M)
-and the CPU oracle baseline on a bounded sample.
+decode comparator, the step with K/V caches in pinned host memory (FASA-M),
+the measured copy bandwidth of the GPU, and the CPU oracle baseline on a
+bounded sample (one core, and all cores up to 16).
 """
 
 import argparse
@@ -335,6 +336,75 @@ def cpu_baseline(w, x, budget_s):
                       f"on one host thread, {spent:.1f} s of step time, prefill excluded"}
 
 
+# Oracle state shared with forked workers (set before the fork).
+_POOL_STATE = {}
+
+
+def _oracle_worker(heads):
+    """Runs the oracle's decode steps for `heads` only (a forked copy of the
+    prefilled state); returns (steps, seconds)."""
+    from threadpoolctl import threadpool_limits
+    st, x, w, n_steps = (_POOL_STATE[k] for k in ("st", "x", "w", "steps"))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for s in range(n_steps):
+            t = s % w.steps
+            st.step(x["q"][t], x["k_new"][t], x["v_new"][t], w.budget, heads=heads)
+        return n_steps, time.perf_counter() - t0
+
+
+def cpu_baseline_all_cores(w, x, budget_s):
+    """The oracle on all host cores this process may use (at most 16): one
+    forked worker per share of the query heads, each running the same
+    consecutive decode steps over its heads.  Must run before the GPU is
+    touched (the workers are forked)."""
+    import multiprocessing as mp
+    import oracle
+    cores = max(1, min(16, len(os.sched_getaffinity(0)), w.n_q_heads))
+    st = oracle.OracleState(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.rope_theta,
+                            w.dtype, x["dom"], w.capacity + 4096)
+    for b in range(w.batch):
+        n0 = int(x["ctx"][b]) - 1
+        st.append(b, x["k_prefill"][b][:, :n0], x["v_prefill"][b][:, :n0])
+    tokens_per_step = int(x["ctx"].sum())
+    # Size the run from one step of one worker's share.
+    share = [list(range(i, w.n_q_heads, cores)) for i in range(cores)]
+    _POOL_STATE.update(st=st, x=x, w=w, steps=1)
+    _, t1 = _oracle_worker(share[0])
+    steps = max(1, int(budget_s / max(t1, 1e-6)))
+    _POOL_STATE["steps"] = steps
+    with mp.get_context("fork").Pool(cores) as pool:
+        res = pool.map(_oracle_worker, share)
+    slowest = max(t for _, t in res)
+    return {"value": steps * tokens_per_step / slowest, "unit": "context tokens/s",
+            "cores": cores, "kind": "oracle",
+            "sample": f"{steps} consecutive decode steps of the same workload, the "
+                      f"{w.n_q_heads} query heads split over {cores} forked processes (one "
+                      f"thread each, append + TIP + top-B + FAC per process), rate from the "
+                      f"slowest process, prefill excluded"}
+
+
+def bw_probe(dev, mib=1024, reps=10):
+    """Measured copy bandwidth of this GPU: a plain device-to-device copy of
+    `mib` MiB, read + write bytes over HIP events."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
 def main():
     args = parse()
     if args.step_only:
@@ -349,14 +419,21 @@ def main():
         copy_probe(args.copy_probe)
         return
 
+    import workloads as W
+
+    w = W.get(args.config)
+    x = W.generate(w)
+    # The CPU legs run first: the all-cores one forks, before any GPU use.
+    cpu = cpu_all = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, x, args.cpu_seconds)
+        cpu_all = cpu_baseline_all_cores(w, x, args.cpu_seconds)
+
     import torch
     import sparse_kv_cache_rope_amd as fasa
-    import workloads as W
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    w = W.get(args.config)
-    x = W.generate(w)
     L = max(1, args.layers)
     td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     to = lambda a, dt=td: torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
@@ -425,6 +502,15 @@ def main():
     use_graph = not args.eager
     ms_step = timed(step, use_graph)
     ms_step_eager = timed(step, False) if use_graph else ms_step
+    # Warm figure, labelled as such: one layer's cache stepped over and over,
+    # so much of it may stay in the 256 MB Infinity Cache.
+    e0w, e1w = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0w.record()
+    for _ in range(K):
+        step(0)
+    e1w.record()
+    torch.cuda.synchronize()
+    ms_step_warm = e0w.elapsed_time(e1w) / K
     assert ctx.check(ws) == 0
     ms_dense = None if args.no_dense else timed(dense, use_graph)
 
@@ -483,6 +569,7 @@ def main():
     tip_s = tip_ms * 1e-3
     achieved = tip_bytes / tip_s / 1e9
     traffic = traffic_from_profile() if args.config == "c2" else None
+    copy_peak = bw_probe(dev)
 
     res = {
         "metric": METRIC,
@@ -505,12 +592,18 @@ def main():
         "hbm_peak_frac": algo_bytes / t_step / (HBM_PEAK_GBS * 1e9),
         "algorithmic_bytes_per_step": algo_bytes,
         "decode_steps_per_s": 1.0 / t_step,
+        "head_tokens_per_s": tokens * w.n_q_heads / t_step,
+        "achieved_gbps_algorithmic": algo_bytes / t_step / 1e9,
+        "measured_copy_peak_gbps": copy_peak,
+        "hbm_measured_peak_frac": algo_bytes / t_step / (copy_peak * 1e9),
+        "ms_per_step_warm_single_cache_eager": ms_step_warm,
         "ms_per_step_eager": ms_step_eager,
         "kernel_avg_ms_with_event_gaps": kernel_ms,
         "roofline": {"bound": "hbm", "kernel": "tip_kernel", "kernel_avg_ms": tip_ms,
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algorithmic_bytes_per_launch": tip_bytes},
+                     "traffic": traffic, "algorithmic_bytes_per_launch": tip_bytes,
+                     "frac_of_measured_copy_peak": achieved / copy_peak},
     }
     if not args.no_calibration:
         res["calibration"] = calibration_timing(ctx, layers[0][0], q, seq_full, msl, w, K)
@@ -526,8 +619,9 @@ def main():
         res["dense"] = {"ms_per_step": ms_dense, "bytes_per_step": dense_bytes,
                         "hbm_gbps": dense_bytes / (ms_dense * 1e-3) / 1e9,
                         "sparse_speedup": ms_dense / ms_step}
-    if args.cpu_seconds > 0:
-        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
+        res["cpu_baseline_all_cores"] = cpu_all
     print(json.dumps(res), flush=True)
 
 
