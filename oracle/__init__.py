@@ -24,6 +24,12 @@ What it computes follows "FASA: Frequency-aware Sparse Attention":
 * ``calibrate.py`` finds each head's dominant FCs offline from the agreement
   of single-FC scores with the full head's (same section, TIP, "Calibracao
   Offline").
+* Partial RoPE (same page, "Contribuicoes": the sparsity holds under
+  Partial-RoPE): ``rope.rope_rotate_partial`` and the FC pair map
+  ``rope.fc_pairs``, used by TIP, calibration and the decode state.
+* Budgets per head (same page, "Variantes de Implementacao": FASA composes
+  with budget allocation across layers): ``select.select_topb_width`` and the
+  ``head_budgets`` argument of ``OracleState.step``.
 
 Readings where the pages are silent (rotate-half pairing, frequencies
 theta^(-2c/d), the query's position, tie order, the softmax scale) are stated
@@ -36,8 +42,8 @@ weights and data that are not part of this project).
 """
 
 from . import rope, tip, select, fac, decode, loops, calibrate  # noqa: F401
-from .rope import inv_freq, rope_rotate, round_to_dtype  # noqa: F401
+from .rope import inv_freq, rope_rotate, rope_rotate_partial, fc_pairs, round_to_dtype  # noqa: F401
 from .tip import tip_scores  # noqa: F401
-from .select import select_topb  # noqa: F401
+from .select import select_topb, select_topb_width  # noqa: F401
 from .fac import attend_subset  # noqa: F401
 from .decode import OracleState  # noqa: F401

@@ -17,7 +17,7 @@
 // 16-byte load (bf16), so a wave reads 1 KiB contiguous per plane, and every
 // wave keeps all its loads in flight at once.
 //
-// Per-step work that used to be a kernel of its own runs while those loads
+// The step's other per-token work is fused here and runs while those loads
 // are in flight: every workgroup rotates its group's queries (fp64 angle, kept
 // in fp32) into LDS weights (q~_c, q~_{c+C}) per plane and head, zero where
 // the FC is not dominant for the head; in decode mode the workgroup whose tile
