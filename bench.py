@@ -80,22 +80,35 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes": n, "copies": 4}), flush=True)
 
 
+def source_code_hash(paths):
+    """sha256 of C/C++ sources with comments and blank space removed, so that
+    only a change of the code itself changes it."""
+    import re
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        for line in text.splitlines():
+            line = " ".join(line.split())
+            if line:
+                h.update(line.encode() + b"\n")
+    return h.hexdigest()
+
+
 def traffic_from_profile():
     """HBM bytes per TIP launch from the committed rocprofv3 --pmc summary, if
-    it was taken on the current kernel sources; else None."""
+    it was taken on the current kernel code (comments aside); else None."""
     path = os.path.join(ROOT, "profiles", "tip_c2_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         prof = json.load(f)
-    h = hashlib.sha256()
-    for rel in prof.get("sources", []):
-        src = os.path.join(ROOT, rel)
-        if not os.path.exists(src):
-            return None
-        with open(src, "rb") as f:
-            h.update(f.read())
-    if prof.get("source_sha256") != h.hexdigest():
+    srcs = [os.path.join(ROOT, rel) for rel in prof.get("sources", [])]
+    if not srcs or not all(os.path.exists(p) for p in srcs):
+        return None
+    if prof.get("source_code_sha256") != source_code_hash(srcs):
         return None
     return prof.get("hbm_bytes_per_launch")
 
