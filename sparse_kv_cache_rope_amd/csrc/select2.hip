@@ -29,6 +29,9 @@ namespace fasa {
 // finish a pass sooner than 16 waves with fewer, and 2 waves per SIMD leave
 // 256 VGPRs each, enough to hold 32 keys or composites without spilling.
 constexpr int kRowThreads = 512;
+// Workgroup size of the selects that hold 16384 scores (the longest chunk,
+// the most candidates): 16 per thread rather than 32, in 1024 threads.
+constexpr int kWideThreads = 1024;
 constexpr int kMaxE = 32;  // scores per thread, at most
 static_assert(kSelectChunk == kRowThreads * kMaxE, "the longest chunk is one workgroup's registers");
 static_assert(kTwoStageMaxCand <= kRowThreads * kMaxE, "candidates fit one workgroup");
@@ -312,32 +315,32 @@ bool select_path_applies(int max_seq_len, int budget) {
   return select_plan(max_seq_len, budget).ok();
 }
 
-template <bool ATT, bool BF, int DD, int E, bool FC>
+template <bool ATT, bool BF, int DD, int E, bool FC, int NT>
 static void launch_row(const fasa_ctx* c, hipStream_t s, const float* scores, const int32_t* nb,
                        int max_seq_len, int budget, const int32_t* hb, const uint64_t* cand,
                        int stride, int chunk, int32_t* idx, const void* k, const void* v,
                        const float* qrot, float* out, int32_t* advance, uint32_t* err) {
-  hipLaunchKernelGGL((row_select_kernel<ATT, BF, DD, E, FC, kRowThreads>),
-                     dim3((unsigned)c->hq, (unsigned)c->batch), dim3(kRowThreads), 0, s, scores,
+  hipLaunchKernelGGL((row_select_kernel<ATT, BF, DD, E, FC, NT>),
+                     dim3((unsigned)c->hq, (unsigned)c->batch), dim3(NT), 0, s, scores,
                      nb, max_seq_len, c->hq, c->cap, budget, hb, cand, stride, chunk, idx, k, v,
                      qrot, c->hkv, c->G, out, advance, err);
 }
 
-template <int E, bool FC>
+template <int E, bool FC, int NT = kRowThreads>
 static void launch_row_e(const fasa_ctx* c, hipStream_t s, const float* scores,
                          const int32_t* nb, int max_seq_len, int budget, const int32_t* hb,
                          const uint64_t* cand, int stride, int chunk, int32_t* idx,
                          const void* k, const void* v, const float* qrot, float* out,
                          int32_t* advance, uint32_t* err) {
   if (out == nullptr) {
-    launch_row<false, true, 128, E, FC>(c, s, scores, nb, max_seq_len, budget, hb, cand, stride,
+    launch_row<false, true, 128, E, FC, NT>(c, s, scores, nb, max_seq_len, budget, hb, cand, stride,
                                         chunk, idx, nullptr, nullptr, nullptr, nullptr, advance,
                                         err);
     return;
   }
   const bool bf = (c->dtype == FASA_BF16);
 #define FASA_ROW(BFV, DV)                                                                       \
-  launch_row<true, BFV, DV, E, FC>(c, s, scores, nb, max_seq_len, budget, hb, cand, stride,   \
+  launch_row<true, BFV, DV, E, FC, NT>(c, s, scores, nb, max_seq_len, budget, hb, cand, stride,   \
                                    chunk, idx, k, v, qrot, out, advance, err)
   if (c->d == 128) {
     if (bf) FASA_ROW(true, 128); else FASA_ROW(false, 128);
@@ -360,12 +363,15 @@ hipError_t launch_select(const fasa_ctx* c, const float* scores, const int32_t* 
 #define FASA_ROWE(EV, FC, CH)                                                                  \
   launch_row_e<EV, FC>(c, s, scores, nb, max_seq_len, budget, head_budget, cand, stride, CH,  \
                        idx, k_cache, v_cache, qrot, out, advance, err)
+#define FASA_ROWW(FC, CH)                                                                      \
+  launch_row_e<16, FC, kWideThreads>(c, s, scores, nb, max_seq_len, budget, head_budget, cand, \
+                                     stride, CH, idx, k_cache, v_cache, qrot, out, advance, err)
   if (p.direct_e) {
     switch (p.direct_e) {
       case 4: FASA_ROWE(4, false, 0); break;
       case 8: FASA_ROWE(8, false, 0); break;
       case 16: FASA_ROWE(16, false, 0); break;
-      default: FASA_ROWE(32, false, 0); break;
+      default: FASA_ROWW(false, 0); break;
     }
     return hipGetLastError();
   }
@@ -379,14 +385,19 @@ hipError_t launch_select(const fasa_ctx* c, const float* scores, const int32_t* 
   switch (p.chunk_e) {
     case 8: FASA_CHUNK(8); break;
     case 16: FASA_CHUNK(16); break;
-    default: FASA_CHUNK(32); break;
+    default:
+      hipLaunchKernelGGL((chunk_select_kernel<16, kWideThreads>), grid, dim3(kWideThreads), 0, s,
+                         scores, nb, max_seq_len, c->hq, c->cap, budget, head_budget, cand,
+                         stride);
+      break;
   }
   if (p.cand_e <= 4) FASA_ROWE(4, true, chunk);
   else if (p.cand_e <= 8) FASA_ROWE(8, true, chunk);
   else if (p.cand_e <= 16) FASA_ROWE(16, true, chunk);
-  else FASA_ROWE(32, true, chunk);
+  else FASA_ROWW(true, chunk);
 #undef FASA_CHUNK
 #undef FASA_ROWE
+#undef FASA_ROWW
   return hipGetLastError();
 }
 
