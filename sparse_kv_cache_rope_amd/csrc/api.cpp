@@ -190,6 +190,15 @@ fasa_status fasa_create_partial_rope(fasa_ctx** out, int batch, int n_q_heads, i
     }
   }
 
+  // FAC runs one workgroup per (sequence, query head, split of the budget) in a
+  // 1-D grid, padded to whole rounds of 8 (b, KV head, split) tuples; a 1-D
+  // launch holds at most 2^32 - 1 work items.
+  const long long fac_tuples =
+      (long long)((max_budget + kFacSplitRows - 1) / kFacSplitRows) * n_kv_heads * batch;
+  if ((fac_tuples + 7) / 8 * 8 * G * kFacThreads > 0xffffffffLL)
+    return fail(FASA_ERR_UNSUPPORTED, "batch %d x heads %d x budget %d exceeds one FAC launch",
+                batch, n_q_heads, max_budget);
+
   fasa_ctx* c = new (std::nothrow) fasa_ctx();
   if (!c) return fail(FASA_ERR_INVALID_ARG, "out of host memory");
   c->batch = batch;

@@ -20,25 +20,34 @@ namespace fasa {
 
 // ---------------------------------------------------------------- FAC ----
 
-constexpr int kFacThreads = 1024;
-
-// grid (splits, Hq, b); split s covers idx entries [s * kFacSplitRows, ...)
-// of the first min(budget, n_b).
+// One workgroup per (b, query head h, split); split s covers idx entries
+// [s * kFacSplitRows, ...) of the first min(budget, n_b).
+//
+// The grid is 1-D.  Workgroups are dealt to the 8 XCDs by linear id mod 8 and
+// each XCD has its own L2.  The G query heads of one KV group gather, at the
+// same split, rows from the same stretch of positions (each head's indices are
+// ascending), and some of the same rows.  So the tuple t = (b, g, split) and
+// its G heads take the ids ((t / 8) * G + h % G) * 8 + t % 8: one XCD, back to
+// back in dispatch order.  Ids whose t is past the last tuple exit.
 template <bool BF16, int D>
 __global__ void __launch_bounds__(kFacThreads)
 fac_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
            const float* __restrict__ qrot, const int32_t* __restrict__ nb, int max_seq_len,
-           const int32_t* __restrict__ idx, int budget, int hq, int hkv, int G, int cap,
-           float* __restrict__ partial, int max_splits, float* __restrict__ out, uint32_t* err) {
+           const int32_t* __restrict__ idx, int budget, int splits, int batch, int hq, int hkv,
+           int G, int cap, float* __restrict__ partial, int max_splits, float* __restrict__ out,
+           uint32_t* err) {
   using Geo = RowGeom<BF16, D>;
   constexpr int LPR = Geo::LPR, EPL = Geo::EPL, RS = Geo::RS, NW = kFacThreads / kWave;
   constexpr int ITERS = kFacSplitRows / (RS * NW);
   static_assert(ITERS >= 1 && ITERS * RS * NW == kFacSplitRows, "split geometry");
   __shared__ float lds[NW * (D + 2 * LPR)];
 
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int id = blockIdx.x, round = id >> 3;
+  const int t = (round / G) * 8 + (id & 7);
+  if (t >= splits * hkv * batch) return;
+  const int split = t % splits, g = (t / splits) % hkv, b = t / (splits * hkv);
+  const int h = g * G + round % G;
   const size_t row = (size_t)b * hq + h;
-  const int g = h / G;
   const int n = checked_len(nb, b, max_seq_len, cap, err, false);
   const int take = n < budget ? n : budget;
   const int nsplit = (take + kFacSplitRows - 1) / kFacSplitRows;
@@ -289,14 +298,16 @@ hipError_t launch_fac(const fasa_ctx* c, const void* k_cache, const void* v_cach
   const int take = budget < max_seq_len ? budget : max_seq_len;
   int splits = (take + kFacSplitRows - 1) / kFacSplitRows;
   if (splits < 1) splits = 1;
-  dim3 grid((unsigned)splits, (unsigned)c->hq, (unsigned)c->batch);
+  // (b, g, split) tuples rounded up to whole rounds of 8 XCDs, G heads each.
+  const long tuples = (long)splits * c->hkv * c->batch;
+  const dim3 grid((unsigned)((tuples + 7) / 8 * 8 * c->G));
   const float* qrot = reinterpret_cast<const float*>(ws + c->ws.qrot);
   float* part = reinterpret_cast<float*>(ws + c->ws.fac);
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
 #define FASA_FAC(BF, DD)                                                                      \
   hipLaunchKernelGGL((fac_kernel<BF, DD>), grid, dim3(kFacThreads), 0, s, k_cache, v_cache, qrot, \
-                     nb, max_seq_len, idx, budget, c->hq, c->hkv, c->G, c->cap, part,          \
-                     c->ws.fac_splits, out, err)
+                     nb, max_seq_len, idx, budget, splits, c->batch, c->hq, c->hkv, c->G,      \
+                     c->cap, part, c->ws.fac_splits, out, err)
   const bool bf = (c->dtype == FASA_BF16);
   if (c->d == 128) {
     if (bf) FASA_FAC(true, 128); else FASA_FAC(false, 128);

@@ -79,6 +79,23 @@ __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
+}
+
+// Lanes 0, 16, 32 and 48 of v: one value of each 16-lane row (wave-uniform).
+// Every lane of the wave must be active.
+struct RowVals {
+  uint32_t r0, r1, r2, r3;
+};
+__device__ __forceinline__ RowVals row_vals(uint32_t v) {
+  return RowVals{(uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                 (uint32_t)__builtin_amdgcn_readlane((int)v, 16),
+                 (uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                 (uint32_t)__builtin_amdgcn_readlane((int)v, 48)};
+}
+
 // Sum over aligned groups of N consecutive lanes (N = 4, 8, 16, 32, 64);
 // every lane of the group gets the sum.
 template <int N>
@@ -91,15 +108,42 @@ __device__ __forceinline__ float group_sum(float v) {
   } else if constexpr (N == 8) {
     v += __shfl_xor(v, 4);
   }
-  if constexpr (N >= 32) v += __shfl_xor(v, 16);
-  if constexpr (N == 64) v += __shfl_xor(v, 32);
+  if constexpr (N >= 32) {
+    // Every lane of a row holds the row's sum; the rows meet through lane
+    // reads (scalar registers), in the order a lane-xor butterfly adds them.
+    const RowVals r = row_vals(__float_as_uint(v));
+    const float h0 = __uint_as_float(r.r0) + __uint_as_float(r.r1);
+    const float h1 = __uint_as_float(r.r2) + __uint_as_float(r.r3);
+    if constexpr (N == 32) v = (threadIdx.x & 32) ? h1 : h0;
+    else v = h0 + h1;
+  }
   return v;
 }
 
+// Wave-wide max (every lane gets it).
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_mov<0x124>(v));  // row_ror:4
+  v = fmaxf(v, dpp_mov<0x128>(v));  // row_ror:8
+  const RowVals r = row_vals(__float_as_uint(v));
+  return fmaxf(fmaxf(__uint_as_float(r.r0), __uint_as_float(r.r1)),
+               fmaxf(__uint_as_float(r.r2), __uint_as_float(r.r3)));
+}
+
+// Wave-wide min of lo and max of hi (wave-uniform results).
+__device__ __forceinline__ void wave_minmax(uint32_t& lo, uint32_t& hi) {
+  lo = min(lo, dpp_u32<0xB1>(lo));
+  hi = max(hi, dpp_u32<0xB1>(hi));
+  lo = min(lo, dpp_u32<0x4E>(lo));
+  hi = max(hi, dpp_u32<0x4E>(hi));
+  lo = min(lo, dpp_u32<0x124>(lo));
+  hi = max(hi, dpp_u32<0x124>(hi));
+  lo = min(lo, dpp_u32<0x128>(lo));
+  hi = max(hi, dpp_u32<0x128>(hi));
+  const RowVals a = row_vals(lo), b = row_vals(hi);
+  lo = min(min(a.r0, a.r1), min(a.r2, a.r3));
+  hi = max(max(b.r0, b.r1), max(b.r2, b.r3));
 }
 
 // Inclusive prefix sum of a uint32 over the 64 lanes of a wave.

@@ -62,6 +62,8 @@ namespace fasa {
 
 // Rows of a FAC split and tokens of a dense split (one workgroup each).
 constexpr int kFacSplitRows = 256;
+// Threads of a FAC workgroup.
+constexpr int kFacThreads = 1024;
 constexpr int kDenseSplitTokens = 512;
 // Largest budget the fused select + FAC kernels keep in LDS.
 constexpr int kFusedMaxBudget = 1024;

@@ -43,8 +43,6 @@ struct RegSelectLds {
   uint32_t wsum[kWaves];
   uint32_t slab_cnt[8][kWaves];
   uint32_t rmin[kWaves], rmax[kWaves];
-  float fmin[kWaves], fmax[kWaves];
-  uint32_t fin[kWaves];
   uint64_t tau;
   uint32_t pick[4];
   uint32_t cand_n;
@@ -109,6 +107,7 @@ __device__ __forceinline__ BinPick fold_and_pick(RegSelectLds<NT, COPIES, CAP>& 
   const uint32_t incl = wave_scan_incl(local);
   const int wave = t / kWave;
   if (lane_id() == kWave - 1) L.wsum[wave] = incl;
+  if (t == 0) L.cand_n = 0;  // for the gather_cand that may follow
   __syncthreads();
   uint32_t before = incl - local;
 #pragma unroll
@@ -133,11 +132,7 @@ __device__ __forceinline__ BinPick fold_and_pick(RegSelectLds<NT, COPIES, CAP>& 
 template <int NT, int COPIES, int CAP>
 __device__ __forceinline__ void block_minmax(uint32_t& lo, uint32_t& hi,
                                              RegSelectLds<NT, COPIES, CAP>& L) {
-#pragma unroll
-  for (int m = kWave / 2; m > 0; m >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, m));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, m));
-  }
+  wave_minmax(lo, hi);
   const int wave = threadIdx.x / kWave;
   if (lane_id() == 0) {
     L.rmin[wave] = lo;
@@ -150,38 +145,6 @@ __device__ __forceinline__ void block_minmax(uint32_t& lo, uint32_t& hi,
   for (int w = 1; w < NT / kWave; ++w) {
     lo = min(lo, L.rmin[w]);
     hi = max(hi, L.rmax[w]);
-  }
-}
-
-// Block-wide key min / max, value min / max and all-finite flag.  One barrier.
-template <int NT, int COPIES, int CAP>
-__device__ __forceinline__ void block_ranges(uint32_t& kmin, uint32_t& kmax, float& vmin,
-                                             float& vmax, uint32_t& fin,
-                                             RegSelectLds<NT, COPIES, CAP>& L) {
-#pragma unroll
-  for (int m = kWave / 2; m > 0; m >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, m));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, m));
-    vmin = fminf(vmin, __shfl_xor(vmin, m));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, m));
-    fin &= (uint32_t)__shfl_xor((int)fin, m);
-  }
-  const int wave = threadIdx.x / kWave;
-  if (lane_id() == 0) {
-    L.rmin[wave] = kmin;
-    L.rmax[wave] = kmax;
-    L.fmin[wave] = vmin;
-    L.fmax[wave] = vmax;
-    L.fin[wave] = fin;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < NT / kWave; ++w) {
-    kmin = min(kmin, L.rmin[w]);
-    kmax = max(kmax, L.rmax[w]);
-    vmin = fminf(vmin, L.fmin[w]);
-    vmax = fmaxf(vmax, L.fmax[w]);
-    fin &= L.fin[w];
   }
 }
 
@@ -198,17 +161,14 @@ __device__ __forceinline__ int range_shift(uint64_t span) {
 
 // Gathers the thread's elements that satisfy `in(e)` into L.cand (one LDS
 // atomic per wave reserves the wave's slots) and returns how many the block
-// gathered (all of them fit: the caller knows the count is <= CAP).  Two
-// barriers.
+// gathered (all of them fit: the caller knows the count is <= CAP).  L.cand_n
+// must be 0 on entry (the fold_and_pick before it clears it).  One barrier.
 template <int NT, int E, int COPIES, int CAP, class Src, class In>
 __device__ __forceinline__ uint32_t gather_cand(const Src& src, In in,
                                                 RegSelectLds<NT, COPIES, CAP>& L) {
-  const int tid = threadIdx.x;
   uint32_t mine = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) mine += in(e) ? 1u : 0u;
-  if (tid == 0) L.cand_n = 0;
-  __syncthreads();
   const uint32_t incl = wave_scan_incl(mine);
   uint32_t base = 0;
   if (lane_id() == kWave - 1 && incl) base = atomicAdd(&L.cand_n, incl);
@@ -326,19 +286,18 @@ template <int NT, int E, int COPIES, int CAP, class Src>
 __device__ __forceinline__ uint64_t adaptive_select(const Src& src, uint32_t need,
                                     RegSelectLds<NT, COPIES, CAP>& L) {
   const int copy = (threadIdx.x / kWave) % COPIES;
-  uint32_t kmin = ~0u, kmax = 0u, fin = 1u;
-  float vmin = INFINITY, vmax = -INFINITY;
+  uint32_t kmin = ~0u, kmax = 0u;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint32_t k = src.key(e);
-    const float v = key_value(k);
     kmin = min(kmin, k ? k : ~0u);
     kmax = max(kmax, k);
-    fin &= (k == 0u || isfinite(v)) ? 1u : 0u;
-    vmin = k ? fminf(vmin, v) : vmin;
-    vmax = k ? fmaxf(vmax, v) : vmax;
   }
-  block_ranges(kmin, kmax, vmin, vmax, fin, L);
+  block_minmax(kmin, kmax, L);
+  // Keys order the scores, so the extreme keys give the extreme scores, and
+  // every score lies between them: all are finite when both ends are.
+  const float vmin = key_value(kmin), vmax = key_value(kmax);
+  const bool fin = isfinite(vmin) && isfinite(vmax);
   const float span = vmax - vmin;
   const float scale = (float)kSelBins / span;
   if (fin && span > 0.0f && isfinite(span) && isfinite(scale)) {

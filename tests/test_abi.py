@@ -68,6 +68,7 @@ def test_status_strings(fasa):
     ((1, 2, 1, 64, 128, 1e4, 1, None, 1, 8), -1, "dom_fc is null"),
     ((1, 129, 129, 64, 128, 1e4, 1, [[0]] * 129, 1, 8), -3, "n_kv_heads"),
     ((1, 2, 1, 64, (1 << 24) + 64, 1e4, 1, [[0], [1]], 1, 8), -2, "capacity"),
+    ((4096, 8, 8, 64, 1 << 20, 1e4, 1, [[0]] * 8, 1, 1 << 20), -3, "one FAC launch"),
 ])
 def test_create_rejects_bad_arguments(fasa, args, code, msg):
     st, detail = fasa.raw_create(*args)
