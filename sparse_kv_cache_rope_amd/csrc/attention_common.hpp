@@ -211,9 +211,15 @@ __device__ __forceinline__ void merge_states_lds(const Soft<EPL>& st, int state,
 
 namespace fasa {
 
-// FAC of query head `row` over the cache rows sel[0 .. take) (sel in LDS),
-// NW waves: softmax(q~ . K[j] / sqrt(d)) weighted sum of V[j].  `scratch`
-// is LDS for the state merge (NW * RS * (D + 3) + 1 + NW * 64 floats).
+// FAC of query head `row` over the cache rows sel[0 .. take) (sel in LDS,
+// take >= 1), NW waves: softmax(q~ . K[j] / sqrt(d)) weighted sum of V[j].
+// `scratch` is LDS for the state merge (NW * RS * (D + 3) + 1 + NW * 64
+// floats).
+//
+// Rows go in batches of PER_BATCH (BATCH per row slot); a 256-row selection
+// is one round of loads.  Slots past the selection load row sel[take - 1]
+// (fetched by another slot, so no new HBM traffic) and count as absent, so
+// every load is issued unconditionally.
 template <bool BF16, int D, int NW>
 __device__ __forceinline__ void attend_rows(const int32_t* sel, int take, const void* __restrict__ k_cache,
                             const void* __restrict__ v_cache, const float* __restrict__ qrot,
@@ -221,8 +227,8 @@ __device__ __forceinline__ void attend_rows(const int32_t* sel, int take, const 
                             float* scratch) {
   using Geo = RowGeom<BF16, D>;
   constexpr int LPR = Geo::LPR, EPL = Geo::EPL, RS = Geo::RS;
-  // Rows per row slot loaded before any is used: enough that a 256-row
-  // selection is one round of loads.
+  // Rows per row slot in a batch: enough that a 256-row selection is one
+  // round of loads.
   constexpr int BATCH = (256 / (RS * NW)) < 4 ? 4 : (256 / (RS * NW)) > 8 ? 8 : (256 / (RS * NW));
   constexpr int PER_BATCH = BATCH * RS * NW;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -233,37 +239,45 @@ __device__ __forceinline__ void attend_rows(const int32_t* sel, int take, const 
   for (int e = 0; e < EPL; ++e) qv[e] = qrot[row * D + sub * EPL + e] * scale;
   const uint4* K = static_cast<const uint4*>(k_cache);
   const uint4* V = static_cast<const uint4*>(v_cache);
-  Soft<EPL> st;
-  st.init();
-  for (int r0 = 0; r0 < take; r0 += PER_BATCH) {
+  const int last = sel[take - 1];
+
+  struct Batch {
     int jr[BATCH];
     uint4 kc[BATCH], vc[BATCH];
+  };
+  auto load = [&](int r0, Batch& x) {
 #pragma unroll
     for (int it = 0; it < BATCH; ++it) {
       const int r = r0 + it * RS * NW + wave * RS + slot;
-      jr[it] = (r < take) ? sel[r] : -1;
-      if (jr[it] >= 0) {
-        const size_t off = (kvbase + jr[it]) * LPR + sub;
-        kc[it] = K[off];
-        vc[it] = V[off];
-      } else {
-        kc[it] = make_uint4(0, 0, 0, 0);
-        vc[it] = make_uint4(0, 0, 0, 0);
-      }
+      const bool in = r < take;
+      const int j = in ? sel[r] : last;
+      x.jr[it] = in ? j : -1;
+      const size_t off = (kvbase + j) * LPR + sub;
+      x.kc[it] = K[off];
+      x.vc[it] = V[off];
     }
+  };
+  Soft<EPL> st;
+  st.init();
+  auto fold = [&](const Batch& x) {
     float z[BATCH], vf[BATCH][EPL];
 #pragma unroll
     for (int it = 0; it < BATCH; ++it) {
       float kf[EPL];
-      unpack<BF16, EPL>(kc[it], kf);
+      unpack<BF16, EPL>(x.kc[it], kf);
       float s = 0.0f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) s = fmaf(qv[e], kf[e], s);
       s = group_sum<LPR>(s);
-      z[it] = jr[it] >= 0 ? s : -INFINITY;
-      unpack<BF16, EPL>(vc[it], vf[it]);
+      z[it] = x.jr[it] >= 0 ? s : -INFINITY;
+      unpack<BF16, EPL>(x.vc[it], vf[it]);
     }
     st.template add_batch<BATCH>(z, vf);
+  };
+  for (int r0 = 0; r0 < take; r0 += PER_BATCH) {
+    Batch a;
+    load(r0, a);
+    fold(a);
   }
   __syncthreads();  // scratch may alias LDS the caller read above
   merge_states_lds<D, LPR, EPL, NW * RS>(st, wave * RS + slot, scratch, out_row);
