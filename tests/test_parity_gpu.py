@@ -29,6 +29,13 @@ SMALL = {
     "c3s": small("c3", batch=3, context=3001, context_min=1500),
     "c4s": small("c4", batch=2, context=2500, budget=473, steps=3),
     "c5s": small("c5", context=9000, budget=300, steps=2),
+    # Query heads per KV head 1, 2 and 8 with budgets of several FAC splits
+    # (256 rows each), ragged batches and a batch that is not a multiple of 8.
+    "g1s": small("c3", batch=3, n_q_heads=8, n_kv_heads=8, context=3001, context_min=1500,
+                 budget=700),
+    "g2s": small("c2", n_q_heads=8, n_kv_heads=4, context=5003, budget=1300),
+    "g8s": small("c3", batch=3, n_q_heads=16, n_kv_heads=2, context=3001, context_min=1500,
+                 budget=700),
 }
 
 
@@ -171,7 +178,7 @@ def test_topk_length_beyond_max_seq_len_flags(gpu):
 
 # ---------------------------------------------------------------- FAC ----
 
-@pytest.mark.parametrize("name", ["c1", "c2s", "c3s"])
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "g1s", "g2s", "g8s"])
 def test_sparse_attn(gpu, name):
     w, x, g, o = _prefilled(gpu, name)
     budget = w.budget
@@ -261,7 +268,7 @@ def _decode_parity(gpu, w, x, steps=None, heads=None, check_steps=None):
     return diffs
 
 
-@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "c4s", "c5s"])
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "c4s", "c5s", "g1s", "g2s", "g8s"])
 def test_decode_step_small(gpu, name):
     w = SMALL[name]
     _decode_parity(gpu, w, W.generate(w))
