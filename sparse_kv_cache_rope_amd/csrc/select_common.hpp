@@ -305,19 +305,21 @@ __device__ __forceinline__ uint64_t adaptive_select(const Src& src, uint32_t nee
       return min(kSelBins - 1, (int)((key_value(k) - vmin) * scale));
     };
     zero_hist(L, COPIES);
+    // Each element's bin, kept for the gather: invalid elements get the
+    // lane's spare word, which is past every bin a pick can return.
     const uint32_t spare = (uint32_t)(kSelBins + lane_id());
+    uint32_t bins[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const uint32_t k = src.key(e);
-      atomicAdd(&L.hist[copy][k ? (uint32_t)bin_of(k) : spare], k ? 1u : 0u);
+      bins[e] = k ? (uint32_t)bin_of(k) : spare;
+      atomicAdd(&L.hist[copy][bins[e]], k ? 1u : 0u);
     }
     __syncthreads();
     const BinPick p = fold_and_pick(L, COPIES, need);
     if (p.count <= (uint32_t)CAP) {
-      const int b = (int)p.bin;
-      const uint32_t M = gather_cand<NT, E>(
-          src, [&](int e) { const uint32_t k = src.key(e); return k != 0u && bin_of(k) == b; },
-          L);
+      const uint32_t M =
+          gather_cand<NT, E>(src, [&](int e) { return bins[e] == p.bin; }, L);
       const uint32_t rest = need - p.above;
       if (M <= kRankMax) return rank_resolve(M, rest, L);
       // Range of the gathered composites, then refinement in LDS.
