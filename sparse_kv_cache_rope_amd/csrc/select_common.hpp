@@ -351,13 +351,19 @@ __device__ __forceinline__ bool is_selected(const Src& src, int e, uint64_t tau)
 // selected elements in slab s.  off[s] receives the output index of the
 // thread's first selected element of slab s; the return value is the total.
 // One barrier.
+//
+// Within a wave, ballots and lane-masked bit counts give each thread its
+// rank.  Across waves, lane s * NW + w of every wave reads wave w's count for
+// slab s and one scan over each slab's NW lanes (DPP shifts, masked at the
+// slab's edge) gives every wave its start in each slab, read out with lane
+// reads.
 template <int NT, int S, int COPIES, int CAP>
 __device__ __forceinline__ uint32_t ordered_offsets(const uint32_t (&sel)[S], uint32_t (&off)[S],
                                                     RegSelectLds<NT, COPIES, CAP>& L) {
   static_assert(S <= 8, "slab table holds 8 slabs");
   constexpr int NW = NT / kWave;
-  const int wave = threadIdx.x / kWave;
-  const uint64_t below = lanes_below();
+  static_assert(S * NW <= kWave && (NW == 8 || NW == 16), "one lane per (slab, wave) count");
+  const int wave = threadIdx.x / kWave, lane = lane_id();
   uint32_t pre[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
@@ -365,25 +371,35 @@ __device__ __forceinline__ uint32_t ordered_offsets(const uint32_t (&sel)[S], ui
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint64_t bal = __ballot((sel[s] >> e) & 1u);
-      p += (uint32_t)__popcll(bal & below);
+      p = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bal, p));
       tot += (uint32_t)__popcll(bal);
     }
     pre[s] = p;
-    if (lane_id() == 0) L.slab_cnt[s][wave] = tot;
+    if (lane == 0) L.slab_cnt[s][wave] = tot;
   }
   __syncthreads();
+  const int lw = lane % NW;
+  uint32_t incl = (lane < S * NW) ? (&L.slab_cnt[0][0])[lane] : 0u;
+  uint32_t t;
+  t = dpp_shr0<0x111>(incl);  // row_shr:1
+  incl += (lw >= 1) ? t : 0u;
+  t = dpp_shr0<0x112>(incl);  // row_shr:2
+  incl += (lw >= 2) ? t : 0u;
+  t = dpp_shr0<0x114>(incl);  // row_shr:4
+  incl += (lw >= 4) ? t : 0u;
+  if constexpr (NW == 16) {
+    t = dpp_shr0<0x118>(incl);  // row_shr:8
+    incl += (lw >= 8) ? t : 0u;
+  }
+  const int w = __builtin_amdgcn_readfirstlane(wave);
   uint32_t base = 0;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    uint32_t before = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const uint32_t v = L.slab_cnt[s][w];
-      before += (w < wave) ? v : 0u;
-      all += v;
-    }
+    const uint32_t before =
+        w > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)incl, s * NW + w - 1) : 0u;
     off[s] = base + before + pre[s];
-    base += all;
+    base += (uint32_t)__builtin_amdgcn_readlane((int)incl, s * NW + NW - 1);
   }
   return base;
 }
