@@ -283,10 +283,12 @@ static int round_e(int per_thread) {
 }
 
 // Short rows go whole to one workgroup (one launch).  Longer rows are cut
-// into the shortest chunks (4096 positions and up) that leave at most 16384
-// candidates and whose chunk is longer than B: more workgroups with fewer
-// scores each finish sooner than one workgroup per row.  Rows where no chunk
-// reduces anything but that fit one workgroup are held whole.
+// into the shortest chunks (4096 positions and up) whose chunk is longer than
+// B and that leave at most 8192 candidates, else at most 16384: more
+// workgroups with fewer scores each finish sooner than one workgroup per row,
+// but the second stage is one workgroup per row, so halving its candidates
+// is worth longer chunks.  Rows where no chunk reduces anything but that fit
+// one workgroup are held whole.
 static SelectPlan select_plan(int max_seq_len, int budget) {
   SelectPlan p;
   if (max_seq_len <= 0 || budget < 1) return p;
@@ -294,16 +296,18 @@ static SelectPlan select_plan(int max_seq_len, int budget) {
     p.direct_e = round_e((max_seq_len + kRowThreads - 1) / kRowThreads);
     return p;
   }
-  for (int e = 8; e <= kMaxE; e *= 2) {
-    const long long chunk = (long long)e * kRowThreads;
-    const long long nch = (max_seq_len + chunk - 1) / chunk;
-    const long long last = max_seq_len - (nch - 1) * chunk;
-    // Candidates of the longest row (no row of the launch has more).
-    const long long cands = (nch - 1) * budget + (last < budget ? last : budget);
-    if (nch > 1 && budget < chunk && cands <= kTwoStageMaxCand) {
-      p.chunk_e = e;
-      p.cand_e = round_e((int)((cands + kRowThreads - 1) / kRowThreads));
-      return p;
+  for (const long long cap : {(long long)kTwoStageMaxCand / 2, (long long)kTwoStageMaxCand}) {
+    for (int e = 8; e <= kMaxE; e *= 2) {
+      const long long chunk = (long long)e * kRowThreads;
+      const long long nch = (max_seq_len + chunk - 1) / chunk;
+      const long long last = max_seq_len - (nch - 1) * chunk;
+      // Candidates of the longest row (no row of the launch has more).
+      const long long cands = (nch - 1) * budget + (last < budget ? last : budget);
+      if (nch > 1 && budget < chunk && cands <= cap) {
+        p.chunk_e = e;
+        p.cand_e = round_e((int)((cands + kRowThreads - 1) / kRowThreads));
+        return p;
+      }
     }
   }
   if (max_seq_len <= kMaxE * kRowThreads)
