@@ -48,6 +48,25 @@ fac_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
   const int split = t % splits, g = (t / splits) % hkv, b = t / (splits * hkv);
   const int h = g * G + round % G;
   const size_t row = (size_t)b * hq + h;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int slot = lane / LPR, sub = lane % LPR;
+
+  // The split's indices and the query are loaded before n_b is known (an idx
+  // row is `budget` wide whatever n_b is), so their round trip overlaps the
+  // length's instead of following it.
+  const int32_t* ids = idx + row * budget + (size_t)split * kFacSplitRows;
+  const int in_row = min(kFacSplitRows, budget - split * kFacSplitRows);
+  int jr[ITERS];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int r = it * RS * NW + wave * RS + slot;
+    jr[it] = (r < in_row) ? ids[r] : -1;
+  }
+  const float scale = logit_scale<D>();
+  float qv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qv[e] = qrot[row * D + sub * EPL + e] * scale;
+
   const int n = checked_len(nb, b, max_seq_len, cap, err, false);
   const int take = n < budget ? n : budget;
   const int nsplit = (take + kFacSplitRows - 1) / kFacSplitRows;
@@ -59,25 +78,16 @@ fac_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
   }
   if (split >= nsplit) return;
 
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int slot = lane / LPR, sub = lane % LPR;
-  const float scale = logit_scale<D>();
-  float qv[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) qv[e] = qrot[row * D + sub * EPL + e] * scale;
-
   const size_t kvbase = ((size_t)b * hkv + g) * cap;
   const uint4* K = static_cast<const uint4*>(k_cache);
   const uint4* V = static_cast<const uint4*>(v_cache);
-  const int32_t* ids = idx + row * budget + (size_t)split * kFacSplitRows;
   const int rows_here = min(kFacSplitRows, take - split * kFacSplitRows);
 
-  int jr[ITERS];
   uint4 kc[ITERS], vc[ITERS];
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     const int r = it * RS * NW + wave * RS + slot;
-    int j = (r < rows_here) ? ids[r] : -1;
+    int j = (r < rows_here) ? jr[it] : -1;
     if (j >= n) {
       if (sub == 0) raise_flag(err, FASA_DEVFLAG_INDEX);
       j = -1;
