@@ -86,38 +86,103 @@ struct CandSrc {
   __device__ __forceinline__ uint32_t low(int e) const { return lo[e]; }
 };
 
-// Loads positions [seg, seg + cn) of a row's scores as E keys per thread with
-// range-limited buffer loads: quads past cn read zeros (and get key 0), so no
-// load waits behind a branch.  Keys of real positions are raised to at least
-// 1, which only merges the two lowest keys (NaN patterns below every number).
-template <int E, int NT>
-__device__ __forceinline__ void load_scores(ScoreSrc<E, NT>& src, const float* row_scores,
-                                            int seg, int cn) {
-  const int t = threadIdx.x;
-  // The resource must be wave-uniform (SGPRs); say so.
-  const uint64_t base = (uint64_t)(row_scores + seg);
-  const uint32_t blo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
-  const uint32_t bhi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
-  const int range = __builtin_amdgcn_readfirstlane(((cn + 3) & ~3) * 4);
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      reinterpret_cast<void*>(((uint64_t)bhi << 32) | blo), (short)0, range, kBufferRsrcWord3);
+// A wave-uniform raw buffer resource over `bytes` bytes from `base`:
+// out-of-range lanes of a load read zeros and fetch nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo),
+                                           (short)0, __builtin_amdgcn_readfirstlane(bytes),
+                                           kBufferRsrcWord3);
+}
+
+// Scores of a row segment as loaded, before the row's length is known.
+template <int E>
+struct RawScores {
   float4 v[E / 4];
+};
+
+// Issues the loads of positions [seg, seg + cn_max) of a row's scores (slab
+// layout of ScoreSrc) with range-limited buffer loads: quads past cn_max read
+// zeros, so no load waits behind a branch.  Nothing here needs the row's own
+// length, so callers issue it before that length arrives.
+template <int E, int NT>
+__device__ __forceinline__ void issue_scores(RawScores<E>& raw, const float* row_scores, int seg,
+                                             int cn_max) {
+  const int t = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(row_scores + seg, ((cn_max + 3) & ~3) * 4);
 #pragma unroll
   for (int g = 0; g < E / 4; ++g) {
     const auto x = __builtin_amdgcn_raw_buffer_load_b128(
         rs, (uint32_t)(4 * (g * NT + t)) * 4u, 0, 0);
-    v[g] = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
-                       __uint_as_float(x[3]));
+    raw.v[g] = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
+                           __uint_as_float(x[3]));
   }
+}
+
+// Keys of positions [seg, seg + cn) from issued loads (cn <= their cn_max):
+// positions past cn get key 0, and keys of real positions are raised to at
+// least 1, which only merges the two lowest keys (NaN patterns below every
+// number).
+template <int E, int NT>
+__device__ __forceinline__ void scores_to_keys(ScoreSrc<E, NT>& src, const RawScores<E>& raw,
+                                               int seg, int cn) {
+  const int t = threadIdx.x;
   src.first = seg + 4 * t;
-  const int lim = cn - 4 * t;  // element e is valid when (e / 4) * 4096 + e % 4 < lim
+  const int lim = cn - 4 * t;  // element e is valid when (e / 4) * 4 NT + e % 4 < lim
 #pragma unroll
   for (int g = 0; g < E / 4; ++g) {
-    const float f[4] = {v[g].x, v[g].y, v[g].z, v[g].w};
+    const float f[4] = {raw.v[g].x, raw.v[g].y, raw.v[g].z, raw.v[g].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t k = score_key(f[e]);
       src.k[4 * g + e] = (g * 4 * NT + e < lim) ? (k ? k : 1u) : 0u;
+    }
+  }
+}
+
+// Candidate composites of a row as loaded, before the row's length is known.
+template <int E>
+struct RawCands {
+  ulonglong2 v[E / 2];
+};
+
+// Issues the loads of a row's candidate slots (slab layout of CandSrc, 4 per
+// thread per slab) with range-limited buffer loads over the row's `stride`
+// slots: slots past it read zeros.
+template <int E, int NT>
+__device__ __forceinline__ void issue_cands(RawCands<E>& raw, const uint64_t* row_cand,
+                                            int stride) {
+  const int t = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(row_cand, stride * 8);
+#pragma unroll
+  for (int g = 0; g < E / 4; ++g) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(
+          rs, (uint32_t)(4 * (g * NT + t) + 2 * half) * 8u, 0, 0);
+      raw.v[2 * g + half] = make_ulonglong2(((uint64_t)x[1] << 32) | x[0],
+                                            ((uint64_t)x[3] << 32) | x[2]);
+    }
+  }
+}
+
+// Candidates [0, M) from issued loads; slots past M get key 0.
+template <int E, int NT>
+__device__ __forceinline__ void cands_to_src(CandSrc<E, NT>& src, const RawCands<E>& raw,
+                                             int M) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int g = 0; g < E / 4; ++g) {
+    const int k0 = 4 * (g * NT + t);
+    const uint64_t c[4] = {raw.v[2 * g].x, raw.v[2 * g].y, raw.v[2 * g + 1].x,
+                           raw.v[2 * g + 1].y};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = k0 + e < M;
+      src.hi[4 * g + e] = in ? (uint32_t)(c[e] >> 32) : 0u;
+      src.lo[4 * g + e] = in ? (uint32_t)c[e] : 0u;
     }
   }
 }
@@ -158,6 +223,11 @@ chunk_select_kernel(const float* __restrict__ scores, const int32_t* __restrict_
   __shared__ RegSelectLds<NT, kHistCopiesSel, kCandCapSel> L;
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t row = (size_t)b * hq + h;
+  const int c0 = chunk * kChunk;
+  // The chunk's loads go out before n_b arrives (bounded by the launch's
+  // longest row; the grid holds no chunk past it).
+  RawScores<E> raw;
+  issue_scores<E, NT>(raw, scores + row * cap, c0, min(kChunk, min(max_seq_len, cap) - c0));
   int n = nb[b];
   if (n < 0 || n > max_seq_len || n > cap) n = 0;
   const int nch = (n + kChunk - 1) / kChunk;
@@ -165,10 +235,9 @@ chunk_select_kernel(const float* __restrict__ scores, const int32_t* __restrict_
   // Rows the second stage takes whole (n <= B, or B = 0) need no candidates;
   // a one-chunk row is a chunk too.
   if (budget == 0 || n <= budget || chunk >= nch) return;
-  const int c0 = chunk * kChunk;
   const int cn = min(kChunk, n - c0);
   ScoreSrc<E, NT> src;
-  load_scores<E, NT>(src, scores + row * cap, c0, cn);
+  scores_to_keys<E, NT>(src, raw, c0, cn);
   // A short last chunk keeps all its positions (need = cn selects them all).
   const uint32_t need = (uint32_t)(cn > budget ? budget : cn);
   const uint64_t tau = adaptive_select<NT, E>(src, need, L);
@@ -201,6 +270,14 @@ row_select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ 
   __shared__ RowLds<NT> L;
   const int h = blockIdx.x, b = blockIdx.y;
   const size_t row = (size_t)b * hq + h;
+  // The row's scores (or candidates) go out before n_b arrives; what lies
+  // past the row's own length is masked once it is known.
+  RawScores<FROM_CAND ? 4 : E> raw_s;
+  RawCands<FROM_CAND ? E : 4> raw_c;
+  if constexpr (FROM_CAND)
+    issue_cands<E, NT>(raw_c, cand + row * cand_stride, cand_stride);
+  else
+    issue_scores<E, NT>(raw_s, scores + row * cap, 0, min(E * NT, min(max_seq_len, cap)));
   const int n = checked_len(nb, b, max_seq_len, cap, err, h == 0 && threadIdx.x == 0);
   if (advance != nullptr && h == 0 && threadIdx.x == 0 && n > 0) advance[b] = n;
   const int t = threadIdx.x;
@@ -216,7 +293,7 @@ row_select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ 
     }
   } else if constexpr (!FROM_CAND) {
     ScoreSrc<E, NT> src;
-    load_scores<E, NT>(src, scores + row * cap, 0, n);
+    scores_to_keys<E, NT>(src, raw_s, 0, n);
     const uint64_t tau = adaptive_select<NT, E>(src, (uint32_t)bh, L.s);
     emit_ordered<E, NT>(src, tau, (uint32_t)bh, L.s, [&](uint32_t r, int e) {
       const int pos = src.pos(e);
@@ -224,30 +301,8 @@ row_select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ 
       if (ATTEND) L.sel[r] = pos;
     });
   } else {
-    const int M = candidates_of(n, bh, chunk);
-    const uint64_t* __restrict__ src_c = cand + row * cand_stride;
     CandSrc<E, NT> src;
-#pragma unroll
-    for (int g = 0; g < E / 4; ++g) {
-      const int k0 = 4 * (g * NT + t);
-      uint64_t c[4];
-      if (k0 + 4 <= M) {
-        const ulonglong2 a = *reinterpret_cast<const ulonglong2*>(src_c + k0);
-        const ulonglong2 c2 = *reinterpret_cast<const ulonglong2*>(src_c + k0 + 2);
-        c[0] = a.x;
-        c[1] = a.y;
-        c[2] = c2.x;
-        c[3] = c2.y;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) c[e] = (k0 + e < M) ? src_c[k0 + e] : 0ull;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        src.hi[4 * g + e] = (uint32_t)(c[e] >> 32);
-        src.lo[4 * g + e] = (uint32_t)c[e];
-      }
-    }
+    cands_to_src<E, NT>(src, raw_c, candidates_of(n, bh, chunk));
     const uint64_t tau = adaptive_select<NT, E>(src, (uint32_t)bh, L.s);
     emit_ordered<E, NT>(src, tau, (uint32_t)bh, L.s, [&](uint32_t r, int e) {
       const int pos = (int)(0xffffffffu - src.lo[e]);
