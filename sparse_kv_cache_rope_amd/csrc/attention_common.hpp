@@ -116,13 +116,31 @@ __device__ __forceinline__ void merge_block(Soft<EPL>& st, float* lds) {
   }
   __syncthreads();
   if (wave == 0 && lane < LPR) {
-    for (int w = 1; w < NW; ++w) {
-      const float* o = lds + w * (D + 2 * LPR);
-      float a2[EPL];
+    // All NW states at once (independent LDS reads, one max, NW weights)
+    // rather than folding them in one after another.
+    float ms[NW];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) a2[e] = o[lane * EPL + e];
-      st.merge(o[D + lane], o[D + LPR + lane], a2);
+    for (int w = 0; w < NW; ++w) ms[w] = lds[w * (D + 2 * LPR) + D + lane];
+    float mx = ms[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, ms[w]);
+    float l = 0.0f, acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float* o = lds + w * (D + 2 * LPR);
+        const float wt = exp2f(ms[w] - mx);  // m = -inf gives 0
+        l = fmaf(o[D + LPR + lane], wt, l);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(o[lane * EPL + e], wt, acc[e]);
+      }
     }
+    st.m = mx;
+    st.l = l;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) st.a[e] = acc[e];
   }
   __syncthreads();
 }
