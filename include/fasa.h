@@ -92,9 +92,9 @@ typedef enum { FASA_F32 = 0, FASA_BF16 = 1 } fasa_dtype;
  * Limits: head_dim 64 or 128; G in {1, 2, 4, 8}; n_kv_heads <= 128
  *   (FASA_ERR_UNSUPPORTED above); capacity a positive multiple of 64, at most
  *   2^24; 1 <= n_dom <= C; 1 <= max_budget <= capacity; batch * n_q_heads *
- *   ceil(max_budget / 256) at most about 4 million (one FAC launch; the
+ *   ceil(max_budget / 256) at most about 8 million (one FAC launch; the
  *   exact bound rounds batch * n_kv_heads * ceil(max_budget / 256) up to a
- *   multiple of 8, times G, times 1024 threads, below 2^32;
+ *   multiple of 8, times G, times 512 threads, below 2^32;
  *   FASA_ERR_UNSUPPORTED above).
  * Allocates the constant tables on the current HIP device (the device every
  * later call must run on).  *out is NULL on failure.

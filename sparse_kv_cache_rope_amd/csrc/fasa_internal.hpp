@@ -62,8 +62,10 @@ namespace fasa {
 
 // Rows of a FAC split and tokens of a dense split (one workgroup each).
 constexpr int kFacSplitRows = 256;
-// Threads of a FAC workgroup.
-constexpr int kFacThreads = 1024;
+// Threads of a FAC workgroup: 8 waves with 8 rows in flight per row slot
+// (80 VGPRs, 3 workgroups per CU) hid the gather's latency chain better than
+// 16 waves with 4 (2 per CU) or 4 waves with 16.
+constexpr int kFacThreads = 512;
 constexpr int kDenseSplitTokens = 512;
 // Largest budget the fused select + FAC kernels keep in LDS.
 constexpr int kFusedMaxBudget = 1024;
