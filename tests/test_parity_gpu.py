@@ -358,8 +358,9 @@ def test_seq_len_beyond_max_flags_and_zeroes(gpu):
     assert g.seq_lens.cpu().numpy()[0] == 299  # not advanced
 
 
-def test_repeat_is_bit_identical(gpu):
-    w = SMALL["c2s"]
+@pytest.mark.parametrize("name", ["c2s", "g2s"])
+def test_repeat_is_bit_identical(gpu, name):
+    w = SMALL[name]
     x = W.generate(w)
     g = GpuSetup(gpu, w, x)
     a_out, a_idx = run_decode(g, 0, w.budget, advance=False)
@@ -368,10 +369,13 @@ def test_repeat_is_bit_identical(gpu):
     assert torch.equal(a_out, b_out)
 
 
-def test_graph_replay_matches_eager(gpu):
+@pytest.mark.parametrize("name", ["c2s", "g2s"])
+def test_graph_replay_matches_eager(gpu, name):
     """The decode step captured in a HIP graph, replayed several times with
-    eager work in between, gives the eager result every time."""
-    w = SMALL["c2s"]
+    eager work in between, gives the eager result every time: the fused
+    select + FAC path (c2s) and the separate select, FAC splits and merge
+    path (g2s, B = 1300)."""
+    w = SMALL[name]
     x = W.generate(w)
     g = GpuSetup(gpu, w, x)
     eager_out, eager_idx = run_decode(g, 0, w.budget, advance=False)
