@@ -7,10 +7,10 @@
 // lower position, listed ascending; exact, by range refinement over 64-bit
 // composites (select_common.hpp).
 //
-// A row of up to 8192 positions (or up to 16384 when chunking cannot reduce
-// it) is held whole in the registers of one 512-thread workgroup (one round
-// of coalesced loads), selected there, and, for B <= 1024, attended in the
-// same workgroup: one launch after TIP.  No workgroup ever waits on another
+// A row of up to 8192 positions is held whole in the registers of one
+// 512-thread workgroup (up to 16384, in 1024 threads, when chunking cannot
+// reduce it), loaded in one round of coalesced loads, selected there, and,
+// for B <= 1024, attended in the same workgroup: one launch after TIP.  No workgroup ever waits on another
 // (device-wide hand-offs are expensive on a multi-die GPU).
 //
 // Longer rows are cut into chunks: chunk_select_kernel writes each chunk's
