@@ -36,6 +36,9 @@ SMALL = {
     "g2s": small("c2", n_q_heads=8, n_kv_heads=4, context=5003, budget=1300),
     "g8s": small("c3", batch=3, n_q_heads=16, n_kv_heads=2, context=3001, context_min=1500,
                  budget=700),
+    # The other two (dtype, head_dim) builds: bf16 at d = 64 and fp32 at d = 128.
+    "h64s": small("c3", batch=2, head_dim=64, context=4003, context_min=2500, budget=300),
+    "f128s": small("c2", dtype="f32", context=3001, budget=1100),
 }
 
 
@@ -47,7 +50,7 @@ def _prefilled(gpu, name):
 
 # ------------------------------------------------------------- append ----
 
-@pytest.mark.parametrize("name", ["c1", "c2s", "c3s"])
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "h64s", "f128s"])
 def test_append_rope_and_sidecar(gpu, name):
     w, x, g, o = _prefilled(gpu, name)
     K = g.k.float().cpu().numpy()
@@ -90,7 +93,7 @@ def test_append_past_capacity_raises_flag(gpu):
 
 # ---------------------------------------------------------------- TIP ----
 
-@pytest.mark.parametrize("name", ["c1", "c2s", "c3s"])
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "h64s", "f128s"])
 def test_tip_scores(gpu, name):
     w, x, g, o = _prefilled(gpu, name)
     # Score the prefilled tokens with the step-0 query at position n0 - 1.
@@ -178,7 +181,7 @@ def test_topk_length_beyond_max_seq_len_flags(gpu):
 
 # ---------------------------------------------------------------- FAC ----
 
-@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "g1s", "g2s", "g8s"])
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "g1s", "g2s", "g8s", "h64s", "f128s"])
 def test_sparse_attn(gpu, name):
     w, x, g, o = _prefilled(gpu, name)
     budget = w.budget
@@ -221,7 +224,7 @@ def test_sparse_attn_bad_index_flags(gpu):
 
 # -------------------------------------------------------------- dense ----
 
-@pytest.mark.parametrize("name", ["c1", "c2s", "c3s"])
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "h64s", "f128s"])
 def test_dense_attn(gpu, name):
     w, x, g, o = _prefilled(gpu, name)
     n = torch.from_numpy((x["ctx"] - 1).astype(np.int32)).cuda()
@@ -268,7 +271,7 @@ def _decode_parity(gpu, w, x, steps=None, heads=None, check_steps=None):
     return diffs
 
 
-@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "c4s", "c5s", "g1s", "g2s", "g8s"])
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "c4s", "c5s", "g1s", "g2s", "g8s", "h64s", "f128s"])
 def test_decode_step_small(gpu, name):
     w = SMALL[name]
     _decode_parity(gpu, w, W.generate(w))
