@@ -215,6 +215,7 @@ fasa_status fasa_create_partial_rope(fasa_ctx** out, int batch, int n_q_heads, i
   c->dtype = dtype;
   c->dom.assign(dom_fc, dom_fc + (size_t)n_q_heads * n_dom);
   c->dev_alloc = nullptr;
+  c->cus = 0;
 
   // Sidecar planes: per KV head, the union of its query heads' dominant FCs.
   std::vector<int32_t> fc_slot((size_t)n_kv_heads * C, -1);
@@ -250,6 +251,7 @@ fasa_status fasa_create_partial_rope(fasa_ctx** out, int batch, int n_q_heads, i
   const size_t b_omega = align256(sizeof(double) * C);
   const size_t bytes = b_off + b_slot + b_mask + b_omega;
   hipError_t e = hipGetDevice(&c->device);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&c->cus, hipDeviceAttributeMultiprocessorCount, c->device);
   if (e == hipSuccess) e = hipMalloc(&c->dev_alloc, bytes);
   if (e != hipSuccess) {
     c->dev_alloc = nullptr;

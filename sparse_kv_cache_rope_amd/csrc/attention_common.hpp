@@ -301,5 +301,85 @@ __device__ __forceinline__ void attend_rows(const int32_t* sel, int take, const 
   merge_states_lds<D, LPR, EPL, NW * RS>(st, wave * RS + slot, scratch, out_row);
 }
 
+// FAC of query head `row` over sel[0 .. take) (sel in LDS, take >= 1), split
+// by output columns over S workgroups; this one (`part`) writes columns
+// [part * D / S, (part + 1) * D / S).  Each of the S workgroups reads every
+// selected row's K (it needs every logit) but only its share of V, so there
+// are no partial states to merge across workgroups and the per-row work of a
+// workgroup drops by about a third at S = 4.
+//
+// A wave step covers S * RS rows.  For K, LPR lanes hold a row, and lane
+// group g (lanes g * LPR ..) scores rows g * S .. g * S + S - 1 in S loads.
+// For V, VL = LPR / S lanes hold a row's slice, and lane L takes row L / VL,
+// which its own K group scored in load (L % LPR) / VL: the logit is already
+// in the lane after the group sum.
+template <bool BF16, int D, int NW, int S>
+__device__ __forceinline__ void attend_rows_split(const int32_t* sel, int take,
+                                                  const void* __restrict__ k_cache,
+                                                  const void* __restrict__ v_cache,
+                                                  const float* __restrict__ qrot, size_t row,
+                                                  size_t kvbase, int part,
+                                                  float* __restrict__ out_row, float* scratch) {
+  using Geo = RowGeom<BF16, D>;
+  constexpr int LPR = Geo::LPR, EPL = Geo::EPL;
+  static_assert(S > 1 && LPR % S == 0, "V slice lanes");
+  constexpr int VL = LPR / S;           // lanes per V slice
+  constexpr int RPS = kWave / VL;       // rows per wave step
+  constexpr int STEPS = 2;              // steps per round of loads
+  constexpr int PER_ROUND = RPS * NW * STEPS;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int kg = lane / LPR, sub = lane % LPR;
+  const int vrow = lane / VL, vsub = lane % VL, mine = (lane % LPR) / VL;
+  const float scale = logit_scale<D>();
+  float qv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qv[e] = qrot[row * D + sub * EPL + e] * scale;
+  const uint4* K = static_cast<const uint4*>(k_cache);
+  const uint4* V = static_cast<const uint4*>(v_cache);
+  const int last = sel[take - 1];
+  Soft<EPL> st;
+  st.init();
+  for (int r0 = 0; r0 < take; r0 += PER_ROUND) {
+    uint4 kc[STEPS][S], vc[STEPS];
+    int jv[STEPS];
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) {
+      const int base = r0 + (t * NW + wave) * RPS;
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        const int r = base + kg * S + i;
+        const int j = r < take ? sel[r] : last;
+        kc[t][i] = K[(kvbase + j) * LPR + sub];
+      }
+      const int rv = base + vrow;
+      const bool in = rv < take;
+      const int j = in ? sel[rv] : last;
+      jv[t] = in ? j : -1;
+      vc[t] = V[(kvbase + j) * LPR + part * VL + vsub];
+    }
+    float z[STEPS], vf[STEPS][EPL];
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) {
+      float zi = 0.0f;
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        float kf[EPL];
+        unpack<BF16, EPL>(kc[t][i], kf);
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s = fmaf(qv[e], kf[e], s);
+        s = group_sum<LPR>(s);
+        zi = (i == mine) ? s : zi;
+      }
+      z[t] = jv[t] >= 0 ? zi : -INFINITY;
+      unpack<BF16, EPL>(vc[t], vf[t]);
+    }
+    st.template add_batch<STEPS>(z, vf);
+  }
+  __syncthreads();  // scratch may alias LDS the caller read above
+  merge_block<D / S, VL, EPL, NW>(st, scratch);
+  write_state<D / S, VL, EPL>(st, true, out_row + part * (D / S), nullptr);
+}
+
 }  // namespace fasa
 

@@ -41,6 +41,7 @@ struct fasa_ctx {
   int batch, hq, hkv, d, C, cap, G, F, max_budget;
   int R;  // rotated FCs: rotary_dim / 2 (C for full RoPE)
   int max_union;  // largest |U_g| over the KV heads (sidecar planes of one head)
+  int cus;        // compute units of the context's device
   double theta;
   fasa_dtype dtype;
   int device;

@@ -255,7 +255,13 @@ chunk_select_kernel(const float* __restrict__ scores, const int32_t* __restrict_
 // row's budget (row_budget); idx rows are `budget` wide, -1 past the set.
 // Also stores n_b into advance[b] (if given): seq_lens may be advanced here
 // since no kernel of this launch reads it.
-template <bool ATTEND, bool BF16, int D, int E, bool FROM_CAND, int NT>
+//
+// With S > 1 (ATTEND only) every row runs on S workgroups (grid x = S * hq;
+// part x / hq, head x % hq, so with hq a multiple of 8 a head's parts share an
+// XCD and its K rows come from that XCD's L2).  Each part makes the same
+// selection and attends over it for D / S output columns (attend_rows_split);
+// part 0 alone writes idx, advance and flags.
+template <bool ATTEND, bool BF16, int D, int E, bool FROM_CAND, int NT, int S = 1>
 __global__ void __launch_bounds__(NT)
 row_select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ nb,
                   int max_seq_len, int hq, int cap, int budget,
@@ -267,8 +273,11 @@ row_select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ 
   static_assert(NT / kWave * RowGeom<BF16, D>::RS * (D + 3) + 1 + NT <=
                     kAttendScratch,
                 "attend_rows scratch");
+  static_assert(S == 1 || ATTEND, "column split is for the fused FAC");
   __shared__ RowLds<NT> L;
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int part = S > 1 ? (int)blockIdx.x / hq : 0;
+  const int h = S > 1 ? (int)blockIdx.x % hq : (int)blockIdx.x, b = blockIdx.y;
+  const bool lead = part == 0;
   const size_t row = (size_t)b * hq + h;
   // The row's scores (or candidates) go out before n_b arrives; what lies
   // past the row's own length is masked once it is known.
@@ -278,11 +287,11 @@ row_select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ 
     issue_cands<E, NT>(raw_c, cand + row * cand_stride, cand_stride);
   else
     issue_scores<E, NT>(raw_s, scores + row * cap, 0, min(E * NT, min(max_seq_len, cap)));
-  const int n = checked_len(nb, b, max_seq_len, cap, err, h == 0 && threadIdx.x == 0);
-  if (advance != nullptr && h == 0 && threadIdx.x == 0 && n > 0) advance[b] = n;
+  const int n = checked_len(nb, b, max_seq_len, cap, err, lead && h == 0 && threadIdx.x == 0);
+  if (advance != nullptr && lead && h == 0 && threadIdx.x == 0 && n > 0) advance[b] = n;
   const int t = threadIdx.x;
-  int32_t* o = idx ? idx + row * budget : nullptr;
-  const int bh = row_budget(head_budget, h, budget, err, b == 0 && t == 0);
+  int32_t* o = (idx && lead) ? idx + row * budget : nullptr;
+  const int bh = row_budget(head_budget, h, budget, err, lead && b == 0 && t == 0);
   const int take = n < bh ? n : bh;
   const bool whole = n <= bh || bh == 0;  // every position, or none
 
@@ -316,12 +325,17 @@ row_select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ 
     __syncthreads();
     float* out_row = out + row * D;
     if (take == 0) {
-      for (int d = t; d < D; d += NT) out_row[d] = 0.0f;
+      if (lead)
+        for (int d = t; d < D; d += NT) out_row[d] = 0.0f;
       return;
     }
     const size_t kvbase = ((size_t)b * hkv + h / G) * cap;
-    attend_rows<BF16, D, NT / kWave>(L.sel, take, k_cache, v_cache, qrot, row, kvbase,
-                                              out_row, L.att);
+    if constexpr (S > 1)
+      attend_rows_split<BF16, D, NT / kWave, S>(L.sel, take, k_cache, v_cache, qrot, row,
+                                                kvbase, part, out_row, L.att);
+    else
+      attend_rows<BF16, D, NT / kWave>(L.sel, take, k_cache, v_cache, qrot, row, kvbase,
+                                       out_row, L.att);
   }
 }
 
@@ -374,16 +388,21 @@ bool select_path_applies(int max_seq_len, int budget) {
   return select_plan(max_seq_len, budget).ok();
 }
 
-template <bool ATT, bool BF, int DD, int E, bool FC, int NT>
+template <bool ATT, bool BF, int DD, int E, bool FC, int NT, int S = 1>
 static void launch_row(const fasa_ctx* c, hipStream_t s, const float* scores, const int32_t* nb,
                        int max_seq_len, int budget, const int32_t* hb, const uint64_t* cand,
                        int stride, int chunk, int32_t* idx, const void* k, const void* v,
                        const float* qrot, float* out, int32_t* advance, uint32_t* err) {
-  hipLaunchKernelGGL((row_select_kernel<ATT, BF, DD, E, FC, NT>),
-                     dim3((unsigned)c->hq, (unsigned)c->batch), dim3(NT), 0, s, scores,
+  hipLaunchKernelGGL((row_select_kernel<ATT, BF, DD, E, FC, NT, S>),
+                     dim3((unsigned)(c->hq * S), (unsigned)c->batch), dim3(NT), 0, s, scores,
                      nb, max_seq_len, c->hq, c->cap, budget, hb, cand, stride, chunk, idx, k, v,
                      qrot, c->hkv, c->G, out, advance, err);
 }
+
+// Column parts of the fused FAC when the rows are few: with S workgroups per
+// row the selection is made S times over, in parallel on otherwise idle CUs,
+// and each part attends for D / S output columns.
+constexpr int kFacColumnParts = 4;
 
 template <int E, bool FC, int NT = kRowThreads>
 static void launch_row_e(const fasa_ctx* c, hipStream_t s, const float* scores,
@@ -398,9 +417,18 @@ static void launch_row_e(const fasa_ctx* c, hipStream_t s, const float* scores,
     return;
   }
   const bool bf = (c->dtype == FASA_BF16);
+  // Split when every part of every row still has a CU of its own.
+  const bool split = (long long)c->batch * c->hq * kFacColumnParts <= c->cus;
 #define FASA_ROW(BFV, DV)                                                                       \
-  launch_row<true, BFV, DV, E, FC, NT>(c, s, scores, nb, max_seq_len, budget, hb, cand, stride,   \
-                                   chunk, idx, k, v, qrot, out, advance, err)
+  do {                                                                                          \
+    if (split)                                                                                  \
+      launch_row<true, BFV, DV, E, FC, NT, kFacColumnParts>(c, s, scores, nb, max_seq_len,       \
+                                                            budget, hb, cand, stride, chunk,    \
+                                                            idx, k, v, qrot, out, advance, err); \
+    else                                                                                        \
+      launch_row<true, BFV, DV, E, FC, NT>(c, s, scores, nb, max_seq_len, budget, hb, cand,     \
+                                           stride, chunk, idx, k, v, qrot, out, advance, err);  \
+  } while (0)
   if (c->d == 128) {
     if (bf) FASA_ROW(true, 128); else FASA_ROW(false, 128);
   } else {
