@@ -39,6 +39,7 @@ SMALL = {
     # The other two (dtype, head_dim) builds: bf16 at d = 64 and fp32 at d = 128.
     "h64s": small("c3", batch=2, head_dim=64, context=4003, context_min=2500, budget=300),
     "f128s": small("c2", dtype="f32", context=3001, budget=1100),
+    "f128f": small("c2", dtype="f32", context=3001),  # fused select + FAC
 }
 
 
@@ -271,7 +272,8 @@ def _decode_parity(gpu, w, x, steps=None, heads=None, check_steps=None):
     return diffs
 
 
-@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "c4s", "c5s", "g1s", "g2s", "g8s", "h64s", "f128s"])
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "c4s", "c5s", "g1s", "g2s", "g8s", "h64s", "f128s",
+                                  "f128f"])
 def test_decode_step_small(gpu, name):
     w = SMALL[name]
     _decode_parity(gpu, w, W.generate(w))
