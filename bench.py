@@ -418,6 +418,29 @@ def bw_probe(dev, mib=1024, reps=10):
     return 2 * n / (ms * 1e-3) / 1e9
 
 
+def read_probe_at(fasa, dev, nbytes, layers=16, reps=160):
+    """GB/s of a plain streaming read (fasa_read_probe) of `nbytes`, back to
+    back over `layers` rotating buffers (more bytes than the Infinity Cache
+    holds), over HIP events: what HBM gives a kernel that only streams that
+    many bytes, the yardstick next to TIP's launch of the same size."""
+    import torch
+    n = (int(nbytes) + 15) // 16 * 16
+    bufs = [torch.zeros(n, dtype=torch.uint8, device=dev) for _ in range(layers)]
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    for i in range(layers):
+        fasa.read_probe(bufs[i], sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fasa.read_probe(bufs[i % layers], sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del bufs
+    return n / (ms * 1e-3) / 1e9, ms
+
+
 def main():
     args = parse()
     if args.step_only:
@@ -583,6 +606,7 @@ def main():
     achieved = tip_bytes / tip_s / 1e9
     traffic = traffic_from_profile() if args.config == "c2" else None
     copy_peak = bw_probe(dev)
+    read_gbps, read_ms = read_probe_at(fasa, dev, tip_bytes)
 
     res = {
         "metric": METRIC,
@@ -616,7 +640,10 @@ def main():
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": tip_bytes,
-                     "frac_of_measured_copy_peak": achieved / copy_peak},
+                     "frac_of_measured_copy_peak": achieved / copy_peak,
+                     "plain_read_same_bytes_ms": read_ms,
+                     "plain_read_same_bytes_gbps": read_gbps,
+                     "frac_of_plain_read_same_bytes": achieved / read_gbps},
     }
     if not args.no_calibration:
         res["calibration"] = calibration_timing(ctx, layers[0][0], q, seq_full, msl, w, K)

@@ -299,6 +299,16 @@ typedef enum { FASA_PTR_UNUSABLE = 0, FASA_PTR_DEVICE = 1, FASA_PTR_HOST_MAPPED 
 fasa_ptr_kind fasa_pointer_kind(const void* ptr);
 
 /*
+ * A plain streaming read (a measurement aid, not part of the decode path):
+ * one pass over `bytes` bytes of device memory at `buf` with 16-byte loads
+ * and no stores (`sink`, one device float, is never written for real data).
+ * Timed next to the TIP kernel, it shows what a kernel that only streams the
+ * same number of bytes gets from HBM.  buf and bytes: non-zero multiples of
+ * 16.  Asynchronous on `stream`.
+ */
+fasa_status fasa_read_probe(const void* buf, size_t bytes, float* sink, hipStream_t stream);
+
+/*
  * Synchronise `stream`, read and clear the workspace's device error flag.
  * *flags (may be NULL) receives the FASA_DEVFLAG_* bits.  Returns
  * FASA_ERR_DEVICE_FLAG when any bit was set.

@@ -54,6 +54,7 @@ _SIGS = {
     "fasa_select_dominant": (_c_int, [ctypes.POINTER(ctypes.c_float), _c_int, _c_int, _c_int,
                                       _c_int, _i32p]),
     "fasa_pointer_kind": (_c_int, [_vp]),
+    "fasa_read_probe": (_c_int, [_vp, _c_size, _vp, _vp]),
     "fasa_check": (_c_int, [_vp, _vp, _vp, ctypes.POINTER(ctypes.c_uint32)]),
     "fasa_timing_enable": (_c_int, [_vp, _c_int]),
     "fasa_timing_collect": (_c_int, [_vp, ctypes.POINTER(ctypes.c_double), _i32p]),
@@ -349,6 +350,16 @@ PTR_UNUSABLE, PTR_DEVICE, PTR_HOST_MAPPED = 0, 1, 2
 def pointer_kind(t):
     """fasa_pointer_kind of a tensor's storage."""
     return int(_lib.fasa_pointer_kind(_vp(t.data_ptr())))
+
+
+def read_probe(buf, sink, stream=None):
+    """fasa_read_probe: one streaming read pass over a device tensor's bytes
+    (a measurement aid); `sink` is a device float tensor of at least one
+    element."""
+    import torch
+    st = stream if stream is not None else torch.cuda.current_stream()
+    _chk(_lib.fasa_read_probe(_vp(buf.data_ptr()), buf.numel() * buf.element_size(),
+                              _vp(sink.data_ptr()), _vp(st.cuda_stream)), "fasa_read_probe")
 
 
 def select_dominant(ca, n_dom):

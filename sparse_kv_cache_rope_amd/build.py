@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libfasa.so")
 ROOT = os.path.dirname(HERE)
 
 SOURCES = ["api.cpp", "rope_append.hip", "tip.hip", "topk.hip", "select2.hip", "attention.hip",
-           "calibrate.hip"]
+           "calibrate.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

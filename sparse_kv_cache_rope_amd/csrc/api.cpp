@@ -605,6 +605,16 @@ fasa_ptr_kind fasa_pointer_kind(const void* ptr) {
   return FASA_PTR_UNUSABLE;
 }
 
+fasa_status fasa_read_probe(const void* buf, size_t bytes, float* sink, hipStream_t stream) {
+  if (buf == nullptr || sink == nullptr) return fail(FASA_ERR_INVALID_ARG, "null pointer");
+  if (bytes == 0 || bytes % 16 || reinterpret_cast<uintptr_t>(buf) % 16)
+    return fail(FASA_ERR_INVALID_ARG, "bytes (%zu) and buf must be non-zero multiples of 16",
+                bytes);
+  if (bytes / 16 > kReadProbeMax16) return fail(FASA_ERR_INVALID_ARG, "buffer too large");
+  FASA_HIP(launch_read_probe(buf, bytes / 16, sink, stream), "fasa_read_probe");
+  return ok();
+}
+
 fasa_status fasa_check(fasa_ctx* c, void* workspace, hipStream_t stream, uint32_t* flags) {
   FASA_TRY(check_ctx(c));
   FASA_NONNULL(workspace);

@@ -120,6 +120,11 @@ hipError_t launch_tip(const fasa_ctx* c, PrologueMode mode, const TipArgs& a, fl
 hipError_t launch_topk(const fasa_ctx* c, const float* scores, const int32_t* nb,
                        int max_seq_len, int budget, int32_t* idx, int32_t* advance, uint8_t* ws,
                        hipStream_t s, const int32_t* head_budget = nullptr);
+// Streams n16 16-byte words from buf with reads only (fasa_read_probe).
+hipError_t launch_read_probe(const void* buf, size_t n16, float* sink, hipStream_t stream);
+// Largest n16 one probe launch takes.
+constexpr size_t kReadProbeMax16 = (size_t)0x7fffffff * 2048;
+
 hipError_t launch_fac(const fasa_ctx* c, const void* k_cache, const void* v_cache,
                       const int32_t* nb, int max_seq_len, const int32_t* idx, int budget,
                       float* out, uint8_t* ws, hipStream_t s);

@@ -80,3 +80,19 @@ def test_partial_rope_rejects_bad_rotary_dim(fasa, rotary_dim):
     st, detail = fasa.raw_create(1, 2, 1, 64, 128, 1e4, 1, [[0], [1]], 1, 8,
                                  rotary_dim=rotary_dim)
     assert st == -1 and "rotary_dim" in detail, (st, detail)
+
+
+@pytest.mark.parametrize("buf,nbytes,sink", [
+    (None, 64, 256),     # null buffer
+    (256, 64, None),     # null sink
+    (256, 0, 256),       # nothing to read
+    (256, 40, 256),      # not a multiple of 16
+    (264, 64, 256),      # misaligned buffer
+])
+def test_read_probe_rejects_bad_arguments(fasa, buf, nbytes, sink):
+    """fasa_read_probe checks its arguments on the host and launches nothing
+    when they are wrong (the addresses here are never dereferenced)."""
+    import ctypes
+    st = fasa._lib.fasa_read_probe(ctypes.c_void_p(buf), nbytes, ctypes.c_void_p(sink), None)
+    assert st == -1, st
+    assert fasa._lib.fasa_last_error().decode()
