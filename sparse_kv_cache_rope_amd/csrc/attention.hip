@@ -128,15 +128,23 @@ fac_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
 // -------------------------------------------------------------- dense ----
 
 constexpr int kDenseThreads = 512;
+// Query heads a dense workgroup holds softmax states for.
+constexpr int kDenseHeads = 2;
 
-// grid (splits, Hkv, b); split s covers tokens [s * kDenseSplitTokens, ...)
-// for all G query heads of KV head g.
-template <bool BF16, int D, int G>
+// One workgroup per (b, KV head g, split, group of HPW of g's query heads);
+// split s covers tokens [s * kDenseSplitTokens, ...).  Fewer heads per
+// workgroup than G keep the per-lane softmax states few enough for two
+// workgroups per CU; the NG = G / HPW workgroups of one (b, g, split) read
+// the same K/V rows, so they take ids on one XCD back to back (the FAC
+// kernel's order: ((t / 8) * NG + head group) * 8 + t % 8 for tuple t) and
+// all but the first find the rows in that XCD's L2.
+template <bool BF16, int D, int HPW>
 __global__ void __launch_bounds__(kDenseThreads)
 dense_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
              const float* __restrict__ qrot, const int32_t* __restrict__ nb, int max_seq_len,
-             int hq, int hkv, int cap, float* __restrict__ partial, int max_splits,
-             float* __restrict__ out, uint32_t* err) {
+             int hq, int hkv, int cap, int splits, int batch, int groups,
+             float* __restrict__ partial, int max_splits, float* __restrict__ out,
+             uint32_t* err) {
   using Geo = RowGeom<BF16, D>;
   constexpr int LPR = Geo::LPR, EPL = Geo::EPL, RS = Geo::RS, NW = kDenseThreads / kWave;
   constexpr int ITERS = kDenseSplitTokens / (RS * NW);
@@ -144,13 +152,16 @@ dense_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
   static_assert(ITERS % BATCH == 0 && ITERS * RS * NW == kDenseSplitTokens, "split geometry");
   __shared__ float lds[NW * (D + 2 * LPR)];
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int id = blockIdx.x, round = id >> 3;
+  const int tt = (round / groups) * 8 + (id & 7);
+  if (tt >= splits * hkv * batch) return;
+  const int split = tt % splits, g = (tt / splits) % hkv, b = tt / (splits * hkv);
   const int n = checked_len(nb, b, max_seq_len, cap, err, false);
   const int nsplit = (n + kDenseSplitTokens - 1) / kDenseSplitTokens;
-  const size_t row0 = (size_t)b * hq + (size_t)g * G;
+  const size_t row0 = (size_t)b * hq + (size_t)g * (HPW * groups) + (size_t)(round % groups) * HPW;
   if (nsplit == 0) {
     if (split == 0)
-      for (int i = threadIdx.x; i < G * D; i += kDenseThreads) out[row0 * D + i] = 0.0f;
+      for (int i = threadIdx.x; i < HPW * D; i += kDenseThreads) out[row0 * D + i] = 0.0f;
     return;
   }
   if (split >= nsplit) return;
@@ -158,9 +169,9 @@ dense_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int slot = lane / LPR, sub = lane % LPR;
   const float scale = logit_scale<D>();
-  float qv[G][EPL];
+  float qv[HPW][EPL];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh)
+  for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qv[hh][e] = qrot[(row0 + hh) * D + sub * EPL + e] * scale;
 
@@ -169,9 +180,9 @@ dense_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
   const uint4* V = static_cast<const uint4*>(v_cache);
   const int t0 = split * kDenseSplitTokens;
 
-  Soft<EPL> st[G];
+  Soft<EPL> st[HPW];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) st[hh].init();
+  for (int hh = 0; hh < HPW; ++hh) st[hh].init();
   // Batches of BATCH rows per row slot, double-buffered: the next batch's
   // loads are issued before the current batch is used, so every workgroup
   // keeps loads in flight while it computes.  Rows past n read row 0 and are
@@ -191,7 +202,7 @@ dense_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
   for (int i0 = 0; i0 < ITERS; i0 += BATCH) {
     const int cur = (i0 / BATCH) & 1;
     if (i0 + BATCH < ITERS) load(i0 + BATCH, kb[cur ^ 1], vb[cur ^ 1]);
-    float z[G][BATCH], vf[BATCH][EPL];
+    float z[HPW][BATCH], vf[BATCH][EPL];
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
       const bool ok = t0 + (i0 + i) * RS * NW + wave * RS + slot < n;
@@ -199,7 +210,7 @@ dense_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
       unpack<BF16, EPL>(kb[cur][i], kf);
       unpack<BF16, EPL>(vb[cur][i], vf[i]);
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
+      for (int hh = 0; hh < HPW; ++hh) {
         float s = 0.0f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) s = fmaf(qv[hh][e], kf[e], s);
@@ -208,10 +219,10 @@ dense_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
       }
     }
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) st[hh].template add_batch<BATCH>(z[hh], vf);
+    for (int hh = 0; hh < HPW; ++hh) st[hh].template add_batch<BATCH>(z[hh], vf);
   }
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
+  for (int hh = 0; hh < HPW; ++hh) {
     merge_block<D, LPR, EPL, NW>(st[hh], lds);
     write_state<D, LPR, EPL>(st[hh], nsplit == 1, out + (row0 + hh) * D,
                              partial + ((row0 + hh) * max_splits + split) * (D + 2));
@@ -331,20 +342,28 @@ hipError_t launch_fac(const fasa_ctx* c, const void* k_cache, const void* v_cach
 }
 
 template <bool BF, int DD>
-static void launch_dense_g(const fasa_ctx* c, dim3 grid, hipStream_t s, const void* k_cache,
+static bool launch_dense_g(const fasa_ctx* c, int splits, hipStream_t s, const void* k_cache,
                            const void* v_cache, const float* qrot, const int32_t* nb,
                            int max_seq_len, float* part, float* out, uint32_t* err) {
+  // Query heads per workgroup: at most kDenseHeads.
+  const int hpw = c->G < kDenseHeads ? c->G : kDenseHeads;
+  const int groups = c->G / hpw;
+  const long tuples = (long)splits * c->hkv * c->batch;
+  const long ids = (tuples + 7) / 8 * 8 * groups;
+  if (ids * kDenseThreads > 0xffffffffL) {
+    (void)hipGetLastError();
+    return false;
+  }
+  const dim3 grid((unsigned)ids);
 #define FASA_DENSE(GG)                                                                          \
   hipLaunchKernelGGL((dense_kernel<BF, DD, GG>), grid, dim3(kDenseThreads), 0, s, k_cache,       \
-                     v_cache, qrot, nb, max_seq_len, c->hq, c->hkv, c->cap, part,                \
-                     c->ws.dense_splits, out, err)
-  switch (c->G) {
-    case 1: FASA_DENSE(1); break;
-    case 2: FASA_DENSE(2); break;
-    case 4: FASA_DENSE(4); break;
-    default: FASA_DENSE(8); break;
-  }
+                     v_cache, qrot, nb, max_seq_len, c->hq, c->hkv, c->cap, splits, c->batch,    \
+                     groups, part, c->ws.dense_splits, out, err)
+  if (hpw == 1) FASA_DENSE(1);
+  else if (hpw == 2) FASA_DENSE(2);
+  else FASA_DENSE(4);
 #undef FASA_DENSE
+  return true;
 }
 
 hipError_t launch_dense(const fasa_ctx* c, const void* k_cache, const void* v_cache,
@@ -352,18 +371,20 @@ hipError_t launch_dense(const fasa_ctx* c, const void* k_cache, const void* v_ca
                         hipStream_t s) {
   int splits = (max_seq_len + kDenseSplitTokens - 1) / kDenseSplitTokens;
   if (splits < 1) splits = 1;
-  dim3 grid((unsigned)splits, (unsigned)c->hkv, (unsigned)c->batch);
   const float* qrot = reinterpret_cast<const float*>(ws + c->ws.qrot);
   float* part = reinterpret_cast<float*>(ws + c->ws.dense);
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
   const bool bf = (c->dtype == FASA_BF16);
+  bool launched;
   if (c->d == 128) {
-    if (bf) launch_dense_g<true, 128>(c, grid, s, k_cache, v_cache, qrot, nb, max_seq_len, part, out, err);
-    else launch_dense_g<false, 128>(c, grid, s, k_cache, v_cache, qrot, nb, max_seq_len, part, out, err);
+    launched = bf ? launch_dense_g<true, 128>(c, splits, s, k_cache, v_cache, qrot, nb, max_seq_len, part, out, err)
+                  : launch_dense_g<false, 128>(c, splits, s, k_cache, v_cache, qrot, nb, max_seq_len, part, out, err);
   } else {
-    if (bf) launch_dense_g<true, 64>(c, grid, s, k_cache, v_cache, qrot, nb, max_seq_len, part, out, err);
-    else launch_dense_g<false, 64>(c, grid, s, k_cache, v_cache, qrot, nb, max_seq_len, part, out, err);
+    launched = bf ? launch_dense_g<true, 64>(c, splits, s, k_cache, v_cache, qrot, nb, max_seq_len, part, out, err)
+                  : launch_dense_g<false, 64>(c, splits, s, k_cache, v_cache, qrot, nb, max_seq_len, part, out, err);
   }
+  // A grid past one 1-D launch (2^32 work items) is refused before launching.
+  if (!launched) return hipErrorInvalidConfiguration;
   if (splits > 1)
     launch_merge(c, part, c->ws.dense_splits, nb, max_seq_len, 0, kDenseSplitTokens, out, s);
   return hipGetLastError();

@@ -225,7 +225,7 @@ def test_sparse_attn_bad_index_flags(gpu):
 
 # -------------------------------------------------------------- dense ----
 
-@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "h64s", "f128s"])
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "h64s", "f128s", "g1s", "g8s"])
 def test_dense_attn(gpu, name):
     w, x, g, o = _prefilled(gpu, name)
     n = torch.from_numpy((x["ctx"] - 1).astype(np.int32)).cuda()
