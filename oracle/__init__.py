@@ -2,7 +2,7 @@
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
 execute this package.  Only the test suite, the smoke check and the CPU
-baseline leg of the benchmark use it, as the yardstick the HIP path is judged
+baseline leg of the benchmark use it, as the yardstick the HIP path is checked
 against.  It shares no code, table or helper with the HIP library and imports
 nothing from it.
 

@@ -10,9 +10,9 @@ Passages ("FASA: Frequency-aware Sparse Attention"): gist.science/pt,
 "Resumo Tecnico" section 2 -- "A Descoberta" (RoPE's 2-D frequency chunks),
 TIP "Previsao Online" (sum of dominant-FC contributions), FAC bullets (select
 T_t, full attention over it, absolute positions kept); the decode setting is
-section 1.  The benchmark spec's own pins: with every FC dominant TIP equals the
-full q.k; with B >= n, FAC equals dense attention; TIP is the sum of per-FC
-rotated 2-D dot products; brute force on tiny contexts.
+section 1.  Among the pins: with every FC dominant TIP equals the full q.k;
+with B >= n, FAC equals dense attention; TIP is the sum of per-FC rotated 2-D
+dot products; brute force on tiny contexts.
 """
 
 import cmath
