@@ -446,7 +446,7 @@ def main():
     if args.step_only:
         args.no_calibration = args.no_per_head = args.no_partial_rope = args.no_fasa_m = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the decode step shards by sequence / KV head with no exchange).",
               file=sys.stderr)
         sys.exit(2)
