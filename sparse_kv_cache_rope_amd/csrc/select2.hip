@@ -9,7 +9,8 @@
 //
 // A row of up to 8192 positions is held whole in the registers of one
 // 512-thread workgroup (up to 16384, in 1024 threads, when chunking cannot
-// reduce it), loaded in one round of coalesced loads, selected there, and,
+// reduce it; up to 40960, 32 or 40 per thread in 1024 threads, when B is
+// past the fused limit and chunks would not cut the row much), loaded in one round of coalesced loads, selected there, and,
 // for B <= 1024, attended in the same workgroup: one launch after TIP.  No workgroup ever waits on another
 // (device-wide hand-offs are expensive on a multi-die GPU).
 //
@@ -32,7 +33,11 @@ constexpr int kRowThreads = 512;
 // Workgroup size of the selects that hold 16384 scores (the longest chunk,
 // the most candidates): 16 per thread rather than 32, in 1024 threads.
 constexpr int kWideThreads = 1024;
-constexpr int kMaxE = 32;  // scores per thread, at most
+constexpr int kMaxE = 32;  // scores per thread, at most (chunk and candidate selects)
+// Scores per thread, at most, of a whole row in kWideThreads when B is past
+// the fused limit (no FAC in the workgroup, so the registers go to scores).
+constexpr int kWideMaxE = 40;
+static_assert(kWideMaxE / 4 <= kMaxSlabs, "slab table");
 static_assert(kSelectChunk == kRowThreads * kMaxE, "the longest chunk is one workgroup's registers");
 static_assert(kTwoStageMaxCand <= kRowThreads * kMaxE, "candidates fit one workgroup");
 constexpr int kHistCopiesSel = 4;
@@ -63,7 +68,7 @@ __device__ __forceinline__ int candidates_of(int n, int budget, int chunk) {
 }
 
 // Scores of one row segment held in registers: element e of thread t is
-// position first + 4 * 1024 * (e / 4) + (e % 4), first = segment + 4 t
+// position first + 4 * NT * (e / 4) + (e % 4), first = segment + 4 t
 // (coalesced float4 slabs).  Only keys are kept (0 for a position past the
 // segment, at least 1 otherwise); positions follow from the indexes.
 template <int E, int NT = kRowThreads>
@@ -248,9 +253,9 @@ chunk_select_kernel(const float* __restrict__ scores, const int32_t* __restrict_
   });
 }
 
-// Selects a row's top B from its raw scores (FROM_CAND = false, n <= E * 1024)
+// Selects a row's top B from its raw scores (FROM_CAND = false, n <= E * NT)
 // or from the chunk stage's candidates (FROM_CAND = true, chunks of `chunk`
-// positions, at most E * 1024 candidates), writes idx
+// positions, at most E * NT candidates), writes idx
 // (if given) and, with ATTEND, runs FAC over the selection in LDS.  B is the
 // row's budget (row_budget); idx rows are `budget` wide, -1 past the set.
 // Also stores n_b into advance[b] (if given): seq_lens may be advanced here
@@ -344,7 +349,8 @@ row_select_kernel(const float* __restrict__ scores, const int32_t* __restrict__ 
 // positions and then their candidates (cand_e per thread).
 struct SelectPlan {
   int direct_e = 0, chunk_e = 0, cand_e = 0;
-  bool ok() const { return direct_e || chunk_e; }
+  int wide_e = 0;  // whole row, wide_e per thread in kWideThreads (no FAC)
+  bool ok() const { return direct_e || chunk_e || wide_e; }
 };
 
 static int round_e(int per_thread) {
@@ -356,8 +362,12 @@ static int round_e(int per_thread) {
 // B and that leave at most 8192 candidates, else at most 16384: more
 // workgroups with fewer scores each finish sooner than one workgroup per row,
 // but the second stage is one workgroup per row, so halving its candidates
-// is worth longer chunks.  Rows where no chunk reduces anything but that fit
-// one workgroup are held whole.
+// is worth longer chunks.  When B is past the fused limit and chunking would
+// leave the second stage more than a quarter of the row (or cannot be
+// planned), a row of up to 40960 positions goes whole to one 1024-thread
+// workgroup instead: that stage would redo most of the first one's work, one
+// workgroup per row anyway.  Other rows where no chunk reduces anything but
+// that fit one workgroup are held whole.
 static SelectPlan select_plan(int max_seq_len, int budget) {
   SelectPlan p;
   if (max_seq_len <= 0 || budget < 1) return p;
@@ -365,21 +375,29 @@ static SelectPlan select_plan(int max_seq_len, int budget) {
     p.direct_e = round_e((max_seq_len + kRowThreads - 1) / kRowThreads);
     return p;
   }
+  long long cands = 0;
   for (const long long cap : {(long long)kTwoStageMaxCand / 2, (long long)kTwoStageMaxCand}) {
-    for (int e = 8; e <= kMaxE; e *= 2) {
+    for (int e = 8; e <= kMaxE && !p.chunk_e; e *= 2) {
       const long long chunk = (long long)e * kRowThreads;
       const long long nch = (max_seq_len + chunk - 1) / chunk;
       const long long last = max_seq_len - (nch - 1) * chunk;
       // Candidates of the longest row (no row of the launch has more).
-      const long long cands = (nch - 1) * budget + (last < budget ? last : budget);
-      if (nch > 1 && budget < chunk && cands <= cap) {
+      const long long c = (nch - 1) * budget + (last < budget ? last : budget);
+      if (nch > 1 && budget < chunk && c <= cap) {
         p.chunk_e = e;
-        p.cand_e = round_e((int)((cands + kRowThreads - 1) / kRowThreads));
-        return p;
+        p.cand_e = round_e((int)((c + kRowThreads - 1) / kRowThreads));
+        cands = c;
       }
     }
+    if (p.chunk_e) break;
   }
-  if (max_seq_len <= kMaxE * kRowThreads)
+  if (budget > kFusedMaxBudget && max_seq_len <= kWideMaxE * kWideThreads &&
+      (!p.chunk_e || 4 * cands > max_seq_len)) {
+    SelectPlan w;
+    w.wide_e = max_seq_len <= 32 * kWideThreads ? 32 : kWideMaxE;
+    return w;
+  }
+  if (!p.chunk_e && max_seq_len <= kMaxE * kRowThreads)
     p.direct_e = round_e((max_seq_len + kRowThreads - 1) / kRowThreads);
   return p;
 }
@@ -453,6 +471,16 @@ hipError_t launch_select(const fasa_ctx* c, const float* scores, const int32_t* 
 #define FASA_ROWW(FC, CH)                                                                      \
   launch_row_e<16, FC, kWideThreads>(c, s, scores, nb, max_seq_len, budget, head_budget, cand, \
                                      stride, CH, idx, k_cache, v_cache, qrot, out, advance, err)
+  if (p.wide_e) {
+#define FASA_WIDE(EV)                                                                          \
+  launch_row<false, true, 128, EV, false, kWideThreads>(c, s, scores, nb, max_seq_len, budget, \
+                                                        head_budget, cand, stride, 0, idx,     \
+                                                        nullptr, nullptr, nullptr, nullptr,    \
+                                                        advance, err)
+    if (p.wide_e == 32) FASA_WIDE(32); else FASA_WIDE(kWideMaxE);
+#undef FASA_WIDE
+    return hipGetLastError();
+  }
   if (p.direct_e) {
     switch (p.direct_e) {
       case 4: FASA_ROWE(4, false, 0); break;

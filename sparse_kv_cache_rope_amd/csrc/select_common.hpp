@@ -32,6 +32,9 @@ struct BinPick {
   uint32_t bin, above, count;
 };
 
+// Slabs of 4 elements per thread a register-resident select holds, at most.
+constexpr int kMaxSlabs = 12;
+
 // Scratch of a register-resident select with NT threads.
 template <int NT, int COPIES, int CAP>
 struct RegSelectLds {
@@ -41,7 +44,7 @@ struct RegSelectLds {
   uint32_t hist[COPIES][kSelBins + kWave];
   uint64_t cand[CAP];
   uint32_t wsum[kWaves];
-  uint32_t slab_cnt[8][kWaves];
+  uint32_t slab_cnt[kMaxSlabs][kWaves];
   uint32_t rmin[kWaves], rmax[kWaves];
   uint64_t tau;
   uint32_t pick[4];
@@ -305,21 +308,28 @@ __device__ __forceinline__ uint64_t adaptive_select(const Src& src, uint32_t nee
       return min(kSelBins - 1, (int)((key_value(k) - vmin) * scale));
     };
     zero_hist(L, COPIES);
-    // Each element's bin, kept for the gather: invalid elements get the
-    // lane's spare word, which is past every bin a pick can return.
+    // Each element's bin, kept for the gather up to 32 elements per thread
+    // (past that, registers are short and the gather computes it again, with
+    // the same operations): invalid elements get the lane's spare word, which
+    // is past every bin a pick can return.
+    constexpr bool kKeepBins = E <= 32;
     const uint32_t spare = (uint32_t)(kSelBins + lane_id());
-    uint32_t bins[E];
+    uint32_t bins[kKeepBins ? E : 1];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const uint32_t k = src.key(e);
-      bins[e] = k ? (uint32_t)bin_of(k) : spare;
-      atomicAdd(&L.hist[copy][bins[e]], k ? 1u : 0u);
+      const uint32_t bn = k ? (uint32_t)bin_of(k) : spare;
+      if constexpr (kKeepBins) bins[e] = bn;
+      atomicAdd(&L.hist[copy][bn], k ? 1u : 0u);
     }
     __syncthreads();
     const BinPick p = fold_and_pick(L, COPIES, need);
     if (p.count <= (uint32_t)CAP) {
-      const uint32_t M =
-          gather_cand<NT, E>(src, [&](int e) { return bins[e] == p.bin; }, L);
+      const uint32_t M = gather_cand<NT, E>(src, [&](int e) {
+        if constexpr (kKeepBins) return bins[e] == p.bin;
+        const uint32_t k = src.key(e);
+        return k != 0u && (uint32_t)bin_of(k) == p.bin;
+      }, L);
       const uint32_t rest = need - p.above;
       if (M <= kRankMax) return rank_resolve(M, rest, L);
       // Range of the gathered composites, then refinement in LDS.
@@ -353,16 +363,19 @@ __device__ __forceinline__ bool is_selected(const Src& src, int e, uint64_t tau)
 // One barrier.
 //
 // Within a wave, ballots and lane-masked bit counts give each thread its
-// rank.  Across waves, lane s * NW + w of every wave reads wave w's count for
-// slab s and one scan over each slab's NW lanes (DPP shifts, masked at the
-// slab's edge) gives every wave its start in each slab, read out with lane
-// reads.
+// rank.  Across waves, the S * NW (slab, wave) counts lie in LDS slab-major;
+// every wave reads them 64 at a time (lane s * NW + w of a group of 64 holds
+// wave w's count for slab s), and one scan over each slab's NW lanes (DPP
+// shifts, masked at the slab's edge) gives every wave its start in each
+// slab, read out with lane reads.
 template <int NT, int S, int COPIES, int CAP>
 __device__ __forceinline__ uint32_t ordered_offsets(const uint32_t (&sel)[S], uint32_t (&off)[S],
                                                     RegSelectLds<NT, COPIES, CAP>& L) {
-  static_assert(S <= 8, "slab table holds 8 slabs");
+  static_assert(S <= kMaxSlabs, "slab table size");
   constexpr int NW = NT / kWave;
-  static_assert(S * NW <= kWave && (NW == 8 || NW == 16), "one lane per (slab, wave) count");
+  static_assert(NW == 8 || NW == 16, "a slab's counts fill part of one 16-lane row or all of it");
+  constexpr int SPG = kWave / NW;           // slabs per group of 64 counts
+  constexpr int NG = (S + SPG - 1) / SPG;   // groups
   const int wave = threadIdx.x / kWave, lane = lane_id();
   uint32_t pre[S];
 #pragma unroll
@@ -380,26 +393,33 @@ __device__ __forceinline__ uint32_t ordered_offsets(const uint32_t (&sel)[S], ui
   }
   __syncthreads();
   const int lw = lane % NW;
-  uint32_t incl = (lane < S * NW) ? (&L.slab_cnt[0][0])[lane] : 0u;
-  uint32_t t;
-  t = dpp_shr0<0x111>(incl);  // row_shr:1
-  incl += (lw >= 1) ? t : 0u;
-  t = dpp_shr0<0x112>(incl);  // row_shr:2
-  incl += (lw >= 2) ? t : 0u;
-  t = dpp_shr0<0x114>(incl);  // row_shr:4
-  incl += (lw >= 4) ? t : 0u;
-  if constexpr (NW == 16) {
-    t = dpp_shr0<0x118>(incl);  // row_shr:8
-    incl += (lw >= 8) ? t : 0u;
+  uint32_t incl[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int i = g * kWave + lane;
+    uint32_t x = (i < S * NW) ? (&L.slab_cnt[0][0])[i] : 0u;
+    uint32_t t;
+    t = dpp_shr0<0x111>(x);  // row_shr:1
+    x += (lw >= 1) ? t : 0u;
+    t = dpp_shr0<0x112>(x);  // row_shr:2
+    x += (lw >= 2) ? t : 0u;
+    t = dpp_shr0<0x114>(x);  // row_shr:4
+    x += (lw >= 4) ? t : 0u;
+    if constexpr (NW == 16) {
+      t = dpp_shr0<0x118>(x);  // row_shr:8
+      x += (lw >= 8) ? t : 0u;
+    }
+    incl[g] = x;
   }
   const int w = __builtin_amdgcn_readfirstlane(wave);
   uint32_t base = 0;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
+    const int g = s / SPG, l0 = (s % SPG) * NW;
     const uint32_t before =
-        w > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)incl, s * NW + w - 1) : 0u;
+        w > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)incl[g], l0 + w - 1) : 0u;
     off[s] = base + before + pre[s];
-    base += (uint32_t)__builtin_amdgcn_readlane((int)incl, s * NW + NW - 1);
+    base += (uint32_t)__builtin_amdgcn_readlane((int)incl[g], l0 + NW - 1);
   }
   return base;
 }

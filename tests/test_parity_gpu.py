@@ -142,6 +142,17 @@ TOPK_CASES = [
     ("normal", 2, 3000, 100, False),
     ("planted", 1, 24000, 8000, False),
     ("ties", 1, 16000, 8500, True),
+    # B past the fused limit on rows of 16k-40k that chunks would not cut by
+    # three quarters: held whole in 1024 threads at 32 per thread (up to
+    # 32768) or 40 (up to 40960).  The shortest such row, a 32k row, ties
+    # with a ragged length, the longest; then one that chunks do cut, and the
+    # first length past the whole-row limit.
+    ("normal", 2, 16385, 1025, False),
+    ("sorted_up", 1, 32768, 15000, False),
+    ("ties", 2, 36000, 3000, True),
+    ("planted", 1, 40960, 12000, False),
+    ("ties", 2, 32768, 2000, True),
+    ("normal", 1, 40961, 6193, False),
 ]
 
 
