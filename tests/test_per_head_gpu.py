@@ -27,7 +27,8 @@ HB_CASES = [
     ("planted", 8, 32768, 256, False, "edges"),    # chunks then candidates
     ("normal", 8, 4096 * 3 + 256, 256, True, "uniform"),
     ("ties", 4, 20000, 1024, False, "edges"),
-    ("planted", 2, 24000, 8000, False, "edges"),
+    ("planted", 2, 24000, 8000, False, "edges"),  # whole row, 1024 threads x 32
+    ("ties", 4, 36000, 3000, True, "edges"),       # whole row, 1024 threads x 40
     ("normal", 4, 131072, 1024, False, "uniform"),
     ("normal", 2, 100000, 3000, False, "edges"),   # one workgroup per row
 ]
