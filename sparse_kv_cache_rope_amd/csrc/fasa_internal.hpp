@@ -139,7 +139,9 @@ hipError_t launch_select_attend(const fasa_ctx* c, const float* scores, const in
                                 hipStream_t s, const int32_t* head_budget = nullptr);
 // Register-resident top-B (when select_path_applies(max_seq_len, budget)):
 // rows up to kSelectChunk positions in one workgroup each, longer rows in
-// chunks of kSelectChunk then their candidates.  Fused with FAC when `out` is
+// chunks of at most kSelectChunk then their candidates, and, for budgets past
+// kFusedMaxBudget, rows up to 40960 positions whole in one 1024-thread
+// workgroup when chunks would not cut them much.  Fused with FAC when `out` is
 // given (then budget <= kFusedMaxBudget and k_cache / v_cache too); idx may be
 // null then.
 bool select_path_applies(int max_seq_len, int budget);
