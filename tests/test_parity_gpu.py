@@ -40,6 +40,12 @@ SMALL = {
     "h64s": small("c3", batch=2, head_dim=64, context=4003, context_min=2500, budget=300),
     "f128s": small("c2", dtype="f32", context=3001, budget=1100),
     "f128f": small("c2", dtype="f32", context=3001),  # fused select + FAC
+    # Fused FAC split over column parts with budgets of several attend
+    # rounds per part (256 rows a round): bf16 at d = 128 and d = 64, fp32
+    # at d = 128.
+    "c2m": small("c2", context=5003, budget=700),
+    "h64m": small("c2", head_dim=64, context=4003, budget=600),
+    "f128m": small("c2", dtype="f32", context=3001, budget=512),
 }
 
 
@@ -284,7 +290,7 @@ def _decode_parity(gpu, w, x, steps=None, heads=None, check_steps=None):
 
 
 @pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "c4s", "c5s", "g1s", "g2s", "g8s", "h64s", "f128s",
-                                  "f128f"])
+                                  "f128f", "c2m", "h64m", "f128m"])
 def test_decode_step_small(gpu, name):
     w = SMALL[name]
     _decode_parity(gpu, w, W.generate(w))
