@@ -187,6 +187,38 @@ def test_topk_exact(gpu, case):
             assert np.array_equal(got[r], want), (r, rep)
 
 
+def _random_topk_cases(per_layout=4, seed=0x70B):
+    """Seeded shapes, per_layout of them in each select layout: rows held whole
+    (n <= 8192), chunks then candidates (B <= 1024), rows held whole in 1024
+    threads at 32 and at 40 per thread (B > 1024, at least a third of n), and
+    the one-workgroup-per-row path (rows past 40960 with B of 9000 and more);
+    kinds, row counts and ragged lengths drawn at random."""
+    r = np.random.Generator(np.random.PCG64(seed))
+    kinds = ["normal", "ties", "wide", "planted", "zeros"]
+    ranges = [  # (n range, B range as a function of n)
+        ((1, 8192), lambda n: (1, n)),
+        ((8193, 70000), lambda n: (1, 1024)),
+        ((16385, 32768), lambda n: (max(1025, n // 3), n)),
+        ((32769, 40960), lambda n: (max(1025, n // 3), n)),
+        ((40961, 70000), lambda n: (9000, 20000)),
+    ]
+    cases = []
+    for (n_lo, n_hi), b_of in ranges:
+        for _ in range(per_layout):
+            n = int(r.integers(n_lo, n_hi + 1))
+            b_lo, b_hi = b_of(n)
+            budget = int(r.integers(b_lo, b_hi + 1))
+            cases.append((kinds[len(cases) % len(kinds)], int(r.integers(1, 4)), n, budget,
+                          bool(r.integers(0, 2)) and n > 40))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_topk_cases(), ids=lambda c: f"{c[0]}-{c[2]}-B{c[3]}")
+def test_topk_random_shapes(gpu, case):
+    """Bit-exact top-B on seeded random shapes, two passes over one workspace."""
+    test_topk_exact(gpu, case)
+
+
 def test_topk_length_beyond_max_seq_len_flags(gpu):
     ctx = gpu.Context(1, 1, 1, 64, 128, 1e4, "f32", np.zeros((1, 1), np.int32), 8)
     ws = ctx.new_workspace()
