@@ -328,6 +328,35 @@ def test_decode_step_small(gpu, name):
     _decode_parity(gpu, w, W.generate(w))
 
 
+def _random_decode_workloads(count=6, seed=0xDEC):
+    """Seeded small workloads: head groupings, head sizes, dtypes, partial
+    RoPE, dominant-FC counts, budgets (B >= n included), ragged contexts and
+    step counts drawn at random."""
+    r = np.random.Generator(np.random.PCG64(seed))
+    groups = [(8, 8), (8, 4), (16, 4), (16, 2), (32, 8)]
+    out = []
+    for i in range(count):
+        hq, hkv = groups[int(r.integers(0, len(groups)))]
+        d = int(r.choice([64, 128]))
+        ctx = int(r.integers(600, 6001))
+        ragged = bool(r.integers(0, 2))
+        steps = int(r.integers(1, 3))
+        budget = int(r.choice([r.integers(1, 300), r.integers(300, 1025), r.integers(1025, 3000)]))
+        cap = (ctx + steps - 1 + 63) // 64 * 64  # the context's capacity bounds max_budget
+        out.append(W.shrink(
+            W.get("c3"), name=f"rand{i}", batch=int(r.integers(1, 4)), n_q_heads=hq,
+            n_kv_heads=hkv, head_dim=d, dtype=str(r.choice(["bf16", "f32"])), context=ctx,
+            context_min=ctx // 2 if ragged else None, budget=min(budget, cap),
+            n_dom=int(r.integers(2, 17)), steps=steps,
+            rotary_dim=(d // 2 if r.integers(0, 3) == 0 else None)))
+    return out
+
+
+@pytest.mark.parametrize("w", _random_decode_workloads(), ids=lambda w: w.name)
+def test_decode_step_random_workloads(gpu, w):
+    _decode_parity(gpu, w, W.generate(w))
+
+
 def test_decode_step_c1_full(gpu):
     w = W.get("c1")
     _decode_parity(gpu, w, W.generate(w))
