@@ -309,6 +309,36 @@ fasa_ptr_kind fasa_pointer_kind(const void* ptr);
 fasa_status fasa_read_probe(const void* buf, size_t bytes, float* sink, hipStream_t stream);
 
 /*
+ * The top-B layout that fasa_topk, fasa_decode_step and their per-head
+ * variants use for rows of up to max_seq_len positions and a budget of
+ * `budget` (the selection of gist.science/pt "Resumo Tecnico" section 2, FAC
+ * first bullet).  A host-side query: no GPU work, no context needed.
+ *   FASA_LAYOUT_WHOLE       each row held whole in one workgroup's registers;
+ *   FASA_LAYOUT_CHUNKED     chunks of *chunk positions keep their own top B,
+ *                           then one workgroup per row selects among those
+ *                           candidates;
+ *   FASA_LAYOUT_WHOLE_WIDE  each row whole in one 1024-thread workgroup
+ *                           (budgets past 1024 on rows that chunks would not
+ *                           cut much);
+ *   FASA_LAYOUT_PER_ROW     one 512-thread workgroup per row reading its
+ *                           scores in passes (rows no layout above fits).
+ * *threads and *per_thread (workgroup size, elements held per thread)
+ * describe the register-resident layouts (for FASA_LAYOUT_CHUNKED, its
+ * candidate stage; 0 for FASA_LAYOUT_PER_ROW) and *chunk the chunk length (0
+ * when the row is not chunked); each may be NULL.  Returns FASA_LAYOUT_NONE (outputs
+ * untouched) for max_seq_len < 1 or budget < 1.
+ */
+typedef enum {
+  FASA_LAYOUT_NONE = 0,
+  FASA_LAYOUT_WHOLE = 1,
+  FASA_LAYOUT_CHUNKED = 2,
+  FASA_LAYOUT_WHOLE_WIDE = 3,
+  FASA_LAYOUT_PER_ROW = 4
+} fasa_select_layout_kind;
+fasa_select_layout_kind fasa_select_layout(int max_seq_len, int budget, int* threads,
+                                           int* per_thread, int* chunk);
+
+/*
  * Synchronise `stream`, read and clear the workspace's device error flag.
  * *flags (may be NULL) receives the FASA_DEVFLAG_* bits.  Returns
  * FASA_ERR_DEVICE_FLAG when any bit was set.

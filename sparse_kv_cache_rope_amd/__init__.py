@@ -55,6 +55,8 @@ _SIGS = {
                                       _c_int, _i32p]),
     "fasa_pointer_kind": (_c_int, [_vp]),
     "fasa_read_probe": (_c_int, [_vp, _c_size, _vp, _vp]),
+    "fasa_select_layout": (_c_int, [_c_int, _c_int, ctypes.POINTER(_c_int),
+                                    ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
     "fasa_check": (_c_int, [_vp, _vp, _vp, ctypes.POINTER(ctypes.c_uint32)]),
     "fasa_timing_enable": (_c_int, [_vp, _c_int]),
     "fasa_timing_collect": (_c_int, [_vp, ctypes.POINTER(ctypes.c_double), _i32p]),
@@ -360,6 +362,18 @@ def read_probe(buf, sink, stream=None):
     st = stream if stream is not None else torch.cuda.current_stream()
     _chk(_lib.fasa_read_probe(_vp(buf.data_ptr()), buf.numel() * buf.element_size(),
                               _vp(sink.data_ptr()), _vp(st.cuda_stream)), "fasa_read_probe")
+
+
+SELECT_LAYOUTS = {0: "none", 1: "whole", 2: "chunked", 3: "whole_wide", 4: "per_row"}
+
+
+def select_layout(max_seq_len, budget):
+    """fasa_select_layout (host only): the top-B layout for rows of up to
+    max_seq_len positions at `budget`, as (name, threads, per_thread, chunk)."""
+    t, e, ch = _c_int(0), _c_int(0), _c_int(0)
+    k = _lib.fasa_select_layout(int(max_seq_len), int(budget), ctypes.byref(t), ctypes.byref(e),
+                                ctypes.byref(ch))
+    return SELECT_LAYOUTS[k], t.value, e.value, ch.value
 
 
 def select_dominant(ca, n_dom):

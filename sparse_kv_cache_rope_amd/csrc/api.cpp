@@ -615,6 +615,16 @@ fasa_status fasa_read_probe(const void* buf, size_t bytes, float* sink, hipStrea
   return ok();
 }
 
+fasa_select_layout_kind fasa_select_layout(int max_seq_len, int budget, int* threads,
+                                           int* per_thread, int* chunk) {
+  if (max_seq_len < 1 || budget < 1) return FASA_LAYOUT_NONE;
+  const SelectLayout l = select_layout(max_seq_len, budget);
+  if (threads) *threads = l.threads;
+  if (per_thread) *per_thread = l.per_thread;
+  if (chunk) *chunk = l.chunk;
+  return static_cast<fasa_select_layout_kind>(l.kind);
+}
+
 fasa_status fasa_check(fasa_ctx* c, void* workspace, hipStream_t stream, uint32_t* flags) {
   FASA_TRY(check_ctx(c));
   FASA_NONNULL(workspace);

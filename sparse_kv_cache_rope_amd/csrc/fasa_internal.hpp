@@ -145,6 +145,12 @@ hipError_t launch_select_attend(const fasa_ctx* c, const float* scores, const in
 // given (then budget <= kFusedMaxBudget and k_cache / v_cache too); idx may be
 // null then.
 bool select_path_applies(int max_seq_len, int budget);
+// The launch plan above as fasa_select_layout reports it (kind 1 whole row,
+// 2 chunked, 3 whole row in 1024 threads, 4 one workgroup per row).
+struct SelectLayout {
+  int kind = 4, threads = 0, per_thread = 0, chunk = 0;
+};
+SelectLayout select_layout(int max_seq_len, int budget);
 hipError_t launch_select(const fasa_ctx* c, const float* scores, const int32_t* nb,
                          int max_seq_len, int budget, int32_t* idx, const void* k_cache,
                          const void* v_cache, float* out, int32_t* advance, uint8_t* ws,

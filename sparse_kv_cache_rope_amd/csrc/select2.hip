@@ -364,10 +364,10 @@ static int round_e(int per_thread) {
 // but the second stage is one workgroup per row, so halving its candidates
 // is worth longer chunks.  When B is past the fused limit and chunking would
 // leave the second stage more than a quarter of the row (or cannot be
-// planned), a row of up to 40960 positions goes whole to one 1024-thread
-// workgroup instead: that stage would redo most of the first one's work, one
-// workgroup per row anyway.  Other rows where no chunk reduces anything but
-// that fit one workgroup are held whole.
+// planned), a row of 16385 to 40960 positions goes whole to one 1024-thread
+// workgroup instead (32 or 40 per thread): that stage would redo most of the
+// first one's work, one workgroup per row anyway.  Other rows where no
+// chunk reduces anything but that fit one workgroup are held whole.
 static SelectPlan select_plan(int max_seq_len, int budget) {
   SelectPlan p;
   if (max_seq_len <= 0 || budget < 1) return p;
@@ -391,8 +391,8 @@ static SelectPlan select_plan(int max_seq_len, int budget) {
     }
     if (p.chunk_e) break;
   }
-  if (budget > kFusedMaxBudget && max_seq_len <= kWideMaxE * kWideThreads &&
-      (!p.chunk_e || 4 * cands > max_seq_len)) {
+  if (budget > kFusedMaxBudget && max_seq_len > kMaxE * kRowThreads &&
+      max_seq_len <= kWideMaxE * kWideThreads && (!p.chunk_e || 4 * cands > max_seq_len)) {
     SelectPlan w;
     w.wide_e = max_seq_len <= 32 * kWideThreads ? 32 : kWideMaxE;
     return w;
@@ -404,6 +404,29 @@ static SelectPlan select_plan(int max_seq_len, int budget) {
 
 bool select_path_applies(int max_seq_len, int budget) {
   return select_plan(max_seq_len, budget).ok();
+}
+
+SelectLayout select_layout(int max_seq_len, int budget) {
+  const SelectPlan p = select_plan(max_seq_len, budget);
+  SelectLayout l;
+  if (p.wide_e) {
+    l.kind = 3;
+    l.threads = kWideThreads;
+    l.per_thread = p.wide_e;
+  } else if (p.direct_e) {
+    // Elements past 16 per thread go to the 1024-thread build (16 each).
+    l.kind = 1;
+    l.threads = p.direct_e > 16 ? kWideThreads : kRowThreads;
+    l.per_thread = p.direct_e > 16 ? 16 : p.direct_e;
+  } else if (p.chunk_e) {
+    l.kind = 2;
+    l.chunk = p.chunk_e * kRowThreads;
+    l.threads = p.cand_e > 16 ? kWideThreads : kRowThreads;  // the candidate stage
+    l.per_thread = p.cand_e > 16 ? 16 : p.cand_e;
+  } else {
+    l.kind = 4;
+  }
+  return l;
 }
 
 template <bool ATT, bool BF, int DD, int E, bool FC, int NT, int S = 1>
