@@ -46,6 +46,9 @@ SMALL = {
     "c2m": small("c2", context=5003, budget=700),
     "h64m": small("c2", head_dim=64, context=4003, budget=600),
     "f128m": small("c2", dtype="f32", context=3001, budget=512),
+    # B past the fused limit on rows chunks would barely cut: each row held
+    # whole in 1024 threads (32 per thread), then the split FAC.
+    "c4w": small("c4", batch=1, context=20000, budget=5000, steps=2),
 }
 
 
@@ -322,7 +325,7 @@ def _decode_parity(gpu, w, x, steps=None, heads=None, check_steps=None):
 
 
 @pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "c4s", "c5s", "g1s", "g2s", "g8s", "h64s", "f128s",
-                                  "f128f", "c2m", "h64m", "f128m"])
+                                  "f128f", "c2m", "h64m", "f128m", "c4w"])
 def test_decode_step_small(gpu, name):
     w = SMALL[name]
     _decode_parity(gpu, w, W.generate(w))
@@ -441,7 +444,7 @@ def test_seq_len_beyond_max_flags_and_zeroes(gpu):
     assert g.seq_lens.cpu().numpy()[0] == 299  # not advanced
 
 
-@pytest.mark.parametrize("name", ["c2s", "g2s"])
+@pytest.mark.parametrize("name", ["c2s", "g2s", "c4w"])
 def test_repeat_is_bit_identical(gpu, name):
     w = SMALL[name]
     x = W.generate(w)
@@ -452,7 +455,7 @@ def test_repeat_is_bit_identical(gpu, name):
     assert torch.equal(a_out, b_out)
 
 
-@pytest.mark.parametrize("name", ["c2s", "g2s"])
+@pytest.mark.parametrize("name", ["c2s", "g2s", "c4w"])
 def test_graph_replay_matches_eager(gpu, name):
     """The decode step captured in a HIP graph, replayed several times with
     eager work in between, gives the eager result every time: the fused
