@@ -16,8 +16,8 @@ HIP graph of L steps; inputs are resident in HBM before timing starts.
 
 Printed: one JSON line with the metric (context tokens scanned per second),
 the fraction of HBM peak on the algorithmic bytes, the dominant kernel's
-roofline figure (TIP: sidecar bytes read + score bytes written / its average
-duration from HIP events over back-to-back launches), the in-build dense
+roofline figure (TIP: sidecar bytes read / its average duration from HIP
+events over back-to-back launches), the in-build dense
 decode comparator, the step with K/V caches in pinned host memory (FASA-M),
 the measured copy bandwidth of the GPU, and the CPU oracle baseline on a
 bounded sample (one core, and all cores up to 16).
@@ -316,7 +316,7 @@ def partial_rope_timing(fasa, dev, L, reps):
     es = 2 if w.dtype == "bf16" else 4
     off, _ = ctx.sidecar_layout()
     n = int(x["ctx"].sum())
-    tip_bytes = (int(off[-1]) * 2 * es + w.n_q_heads * 4) * n
+    tip_bytes = int(off[-1]) * 2 * es * n  # sidecar pairs read
     del layers
     return {"workload": w.name, "rotary_dim": w.rotary_dim, "ms_per_step": ms,
             "value": n / (ms * 1e-3), "unit": "context tokens/s", "tip_kernel_avg_ms": tip_ms,
@@ -505,29 +505,38 @@ def main():
     torch.cuda.synchronize()
     assert ctx.check(ws) == 0
 
-    K = max(L, (args.steps + L - 1) // L * L)
-    reps = K // L
+    # Exactly --steps timed steps, layer i % L for step i: `reps` replays of
+    # a graph over all L layers, then one graph over the first K % L.
+    K = max(1, args.steps)
+    reps, rem = divmod(K, L)
+
+    def capture(fn, count):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(count):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(g):
+            for i in range(count):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        return g
 
     def timed(fn, use_graph):
         if use_graph:
-            g = torch.cuda.CUDAGraph()
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                for i in range(L):
-                    fn(i)
-            torch.cuda.current_stream().wait_stream(side)
-            with torch.cuda.graph(g):
-                for i in range(L):
-                    fn(i)
-            g.replay()
-            torch.cuda.synchronize()
+            g = capture(fn, L) if reps else None
+            g_rem = capture(fn, rem) if rem else None
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
         if use_graph:
             for _ in range(reps):
                 g.replay()
+            if g_rem is not None:
+                g_rem.replay()
         else:
             for i in range(K):
                 fn(i)
@@ -563,13 +572,14 @@ def main():
     for i in range(L):
         tip_only(i)
     torch.cuda.synchronize()
+    tip_n = max(K, 8 * L)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(K):
+    for i in range(tip_n):
         tip_only(i)
     e1.record()
     torch.cuda.synchronize()
-    tip_ms = e0.elapsed_time(e1) / K
+    tip_ms = e0.elapsed_time(e1) / tip_n
     assert ctx.check(ws) == 0
 
     # Per-kernel breakdown of the step: HIP events around every launch, eager,
@@ -590,23 +600,28 @@ def main():
     ctx.timing_enable(False)
     kernel_ms = {f: ms / n for f, (ms, n) in fams.items() if n}
 
-    # Algorithmic bytes: TIP reads the sidecar pairs (P planes x 2 elements per
-    # token) and writes one fp32 score per query head and token; FAC reads
-    # B * 2 * d elements per query head.
+    # Algorithmic bytes of a step: the sidecar pairs TIP reads (P planes x 2
+    # elements per token), the B selected K and V rows FAC reads per query
+    # head (B * 2 * d elements), and the step's appended K, V and sidecar
+    # entries.  Score, candidate and index traffic between the step's kernels
+    # is overhead, reported on its own.
     es = 2 if w.dtype == "bf16" else 4
     off, _ = ctx.sidecar_layout()
     P = int(off[-1])
-    tip_bytes = int(sum((P * 2 * es + w.n_q_heads * 4) * n for n in n_b))
+    sidecar_bytes = int(sum(P * 2 * es * n for n in n_b))
     fac_bytes = int(sum(min(w.budget, n) * 2 * w.head_dim * es * w.n_q_heads for n in n_b))
-    algo_bytes = tip_bytes + fac_bytes
+    append_bytes = w.batch * (w.n_kv_heads * 2 * w.head_dim * es + P * 2 * es)
+    algo_bytes = sidecar_bytes + fac_bytes + append_bytes
+    overhead_bytes = int(sum(w.n_q_heads * 4 * n for n in n_b)) \
+        + w.batch * w.n_q_heads * w.budget * 4
     dense_bytes = int(sum(2 * n * w.head_dim * es * w.n_kv_heads for n in n_b))
     t_step = ms_step * 1e-3
     tokens = int(n_b.sum())
     tip_s = tip_ms * 1e-3
-    achieved = tip_bytes / tip_s / 1e9
+    achieved = sidecar_bytes / tip_s / 1e9
     traffic = traffic_from_profile() if args.config == "c2" else None
     copy_peak = bw_probe(dev)
-    read_gbps, read_ms = read_probe_at(fasa, dev, tip_bytes)
+    read_gbps, read_ms = read_probe_at(fasa, dev, sidecar_bytes)
 
     res = {
         "metric": METRIC,
@@ -628,6 +643,11 @@ def main():
                    "launch": "hipgraph" if use_graph else "eager"},
         "hbm_peak_frac": algo_bytes / t_step / (HBM_PEAK_GBS * 1e9),
         "algorithmic_bytes_per_step": algo_bytes,
+        "algorithmic_bytes_parts": {"sidecar": sidecar_bytes, "fac_rows": fac_bytes,
+                                    "append": append_bytes},
+        "overhead_bytes_per_step": overhead_bytes,
+        "overhead_bytes_what": "fp32 TIP scores written (one per query head and token) "
+                               "and the int32 index rows written; not algorithmic",
         "decode_steps_per_s": 1.0 / t_step,
         "head_tokens_per_s": tokens * w.n_q_heads / t_step,
         "achieved_gbps_algorithmic": algo_bytes / t_step / 1e9,
@@ -637,9 +657,12 @@ def main():
         "ms_per_step_eager": ms_step_eager,
         "kernel_avg_ms_with_event_gaps": kernel_ms,
         "roofline": {"bound": "hbm", "kernel": "tip_kernel", "kernel_avg_ms": tip_ms,
+                     "kernel_launches_timed": tip_n,
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algorithmic_bytes_per_launch": tip_bytes,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": sidecar_bytes,
+                     "algorithmic_bytes_what": "sidecar pairs read; the launch also writes "
+                                               "the fp32 scores (overhead)",
                      "frac_of_measured_copy_peak": achieved / copy_peak,
                      "plain_read_same_bytes_ms": read_ms,
                      "plain_read_same_bytes_gbps": read_gbps,

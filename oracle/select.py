@@ -31,8 +31,15 @@ def select_topb(scores, budget: int) -> np.ndarray:
 
 
 def threshold(scores, budget: int) -> float:
-    """tau: the score of the budget-th ranked token (the smallest kept score)."""
+    """tau: the score of the budget-th ranked token, i.e. the smallest score
+    T_t keeps (with budget >= n every token is kept, so the smallest score of
+    the row).  Raises ValueError for budget < 1 or an empty row, where T_t
+    keeps nothing and no such score exists."""
+    if budget < 1:
+        raise ValueError(f"budget {budget} < 1: T_t is empty and has no threshold")
     s = np.sort(np.asarray(scores, dtype=np.float64))[::-1]
+    if s.shape[0] == 0:
+        raise ValueError("empty row: T_t is empty and has no threshold")
     return float(s[min(budget, s.shape[0]) - 1])
 
 

@@ -6,11 +6,11 @@
 // largest one splits the row exactly: selected <=> composite >= tau.
 //
 // tau is found by range refinement: the composites still in play lie in
-// [lo, hi]; a pass histograms (c - lo) >> s into 2048 LDS bins (s is the
+// [lo, hi]; a pass histograms (c - lo) >> s into 1024 LDS bins (s is the
 // smallest shift that fits the range into them), finds the bin holding the
 // need-th largest and narrows [lo, hi] to that bin.  The first range is the
 // row's own [min, max], so the bins follow the data instead of fixed key
-// digits, and each pass shrinks the range by up to 2048x.  Once the bin's
+// digits, and each pass shrinks the range by up to 1024x (10 bits).  Once the bin's
 // population is small it is gathered into LDS and the passes continue there.
 //
 // With one or two waves per SIMD nothing hides latency, so every step here is

@@ -299,6 +299,54 @@ def pin_select_sets_nest_with_budget():
         prev = cur
 
 
+def pin_threshold_brute_force():
+    """tau is the smallest score of the brute-force best subset of size
+    min(B, n) (T_t's own definition), on tiny integer rows with many ties."""
+    r = _rng(16)
+    for trial in range(80):
+        n = int(r.integers(1, 10))
+        budget = int(r.integers(1, 6))
+        s = r.integers(-3, 4, size=n).astype(np.float64)
+        best = [j for j in _brute_force_topb(s.tolist(), budget) if j >= 0]
+        want = min(s[j] for j in best)
+        got = oracle.select.threshold(s, budget)
+        assert got == want, (s, budget, got, want)
+
+
+def pin_threshold_hand_example():
+    """The hand-ranked fixture: ranking 0 (3), 2 (3), 4 (3), 3 (2), 1 (1),
+    5 (0), so tau is 3, 3, 3, 2 for B = 1..4, and 0 (the smallest score)
+    for B = 8 > n."""
+    with open(os.path.join(GOLDEN, "select_ties.json")) as f:
+        g = json.load(f)
+    expect = {1: 3.0, 2: 3.0, 3: 3.0, 4: 2.0, 8: 0.0}
+    for budget in g["budgets"]:
+        got = oracle.select.threshold(np.array(g["scores"]), budget)
+        assert got == expect[budget], (budget, got)
+
+
+def pin_threshold_vs_partition():
+    """tau equals the B-th largest score from numpy's introselect
+    (np.partition), a routine the oracle does not call."""
+    r = _rng(17)
+    s = np.round(r.standard_normal(5000), 2)
+    for budget in (1, 2, 255, 256, 4999, 5000, 7000):
+        k = min(budget, s.size)
+        want = float(np.partition(s, s.size - k)[s.size - k])
+        assert oracle.select.threshold(s, budget) == want, budget
+
+
+def pin_threshold_rejects_empty_selection():
+    """B = 0 keeps nothing, so there is no threshold: the oracle must refuse
+    rather than return some score."""
+    for budget, row in ((0, [1.0, 2.0]), (-1, [1.0]), (3, [])):
+        try:
+            oracle.select.threshold(np.array(row), budget)
+        except ValueError:
+            continue
+        raise AssertionError(f"threshold accepted budget {budget} on {row}")
+
+
 # ------------------------------------------------------------------ FAC ----
 
 def _sdpa(q, k, v):

@@ -108,6 +108,21 @@ def select_one_short(scores, budget):
     return out
 
 
+def threshold_next_rank(scores, budget):
+    st = np.sort(np.asarray(scores, np.float64))[::-1]
+    return float(st[min(budget, st.shape[0] - 1)])
+
+
+def threshold_ascending(scores, budget):
+    st = np.sort(np.asarray(scores, np.float64))
+    return float(st[min(budget, st.shape[0]) - 1])
+
+
+def threshold_budget_zero_wraps(scores, budget):
+    st = np.sort(np.asarray(scores, np.float64))[::-1]
+    return float(st[min(budget, st.shape[0]) - 1])
+
+
 def attend_no_scale(q, k, v, subset):
     return _attend(np.asarray(q) * np.sqrt(np.asarray(q).shape[-1]), k, v, subset)
 
@@ -206,6 +221,9 @@ MUTATIONS = {
     "select_one_short": (oracle.select, "select_topb", select_one_short),
     "select_width_ignores_budget": (oracle.select, "select_topb_width", width_ignores_budget),
     "select_width_zero_keeps_one": (oracle.select, "select_topb_width", width_zero_keeps_one),
+    "threshold_next_rank": (oracle.select, "threshold", threshold_next_rank),
+    "threshold_ascending_sort": (oracle.select, "threshold", threshold_ascending),
+    "threshold_budget_zero_wraps": (oracle.select, "threshold", threshold_budget_zero_wraps),
     "decode_head_budgets_reversed": (oracle.decode.OracleState, "step", step_budgets_reversed),
     "fac_missing_scale": (oracle.fac, "attend_subset", attend_no_scale),
     "fac_ignores_subset": (oracle.fac, "attend_subset", attend_all_rows),

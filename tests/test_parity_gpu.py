@@ -397,6 +397,14 @@ def test_budget_at_least_context_is_dense(gpu):
     out, idx = run_decode(g, 0, 256)
     got_idx = idx.cpu().numpy()
     assert np.all(got_idx[:, :, :200] == np.arange(200)) and np.all(got_idx[:, :, 200:] == -1)
+    # Against the oracle: its step with B >= n selects every token, and its
+    # output is then dense attention over the whole context.
+    o = oracle_setup(w, x)
+    res = o.step(x["q"][0], x["k_new"][0], x["v_new"][0], 256)
+    assert np.all(res["idx"][:, :, :200] == np.arange(200))
+    for h in range(w.n_q_heads):
+        check_out(out.cpu().numpy()[0, h], res["out"][0, h], w.dtype, f"h{h}")
+    # And against the in-build dense kernel on the same cache.
     dense = torch.empty_like(out)
     n = torch.full((1,), 200, dtype=torch.int32, device="cuda")
     g.ctx.dense_attn(g.k, g.v, to_dev(x["q"][0], g.td), n, 200, dense, g.ws)
