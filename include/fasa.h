@@ -82,6 +82,8 @@ typedef enum { FASA_F32 = 0, FASA_BF16 = 1 } fasa_dtype;
 #define FASA_DEVFLAG_INDEX 2u     /* an index >= its sequence length */
 #define FASA_DEVFLAG_APPEND 4u    /* an append beyond cap */
 #define FASA_DEVFLAG_BUDGET 8u    /* a per-head budget outside [0, budget] (clamped) */
+#define FASA_DEVFLAG_SELECT 16u   /* a filtered selection found its tile lists inconsistent and
+                                     fell back to reading the row (never expected) */
 
 /*
  * Create a context for one attention layer's shapes.
@@ -336,6 +338,27 @@ typedef enum {
   FASA_LAYOUT_PER_ROW = 4
 } fasa_select_layout_kind;
 fasa_select_layout_kind fasa_select_layout(int max_seq_len, int budget, int* threads,
+                                           int* per_thread, int* chunk);
+
+/*
+ * The top-B layout of a decode step (fasa_decode_step and its per-head
+ * variant) for rows of up to max_seq_len positions at `budget`: the same as
+ * fasa_select_layout, except FASA_LAYOUT_GROUP_FILTER where the step filters.
+ * There the TIP launch also writes, per query head, the largest score of
+ * every 8 consecutive tokens, and one launch selects and runs FAC: the B-th
+ * largest group maximum bounds the B-th largest score from below (group
+ * maxima are scores of distinct tokens), so only groups whose maximum
+ * reaches that bound's histogram bin are read again and selected exactly;
+ * rows where those would not fit are selected by streaming passes over their
+ * scores.  The result is the exact T_t either way (gist.science/pt "Resumo
+ * Tecnico" section 2, FAC first bullet).  The step filters when
+ * budget <= 1024 and 8192 < max_seq_len <= 163840.  *threads = 512 there,
+ * *per_thread = group maxima held per thread (8 or 40), *chunk = 8 (the
+ * group); each may be NULL.  Host-side, no context needed.  Returns
+ * FASA_LAYOUT_NONE for max_seq_len < 1 or budget < 1.
+ */
+#define FASA_LAYOUT_GROUP_FILTER ((fasa_select_layout_kind)5)
+fasa_select_layout_kind fasa_decode_layout(int max_seq_len, int budget, int* threads,
                                            int* per_thread, int* chunk);
 
 /*

@@ -57,6 +57,8 @@ _SIGS = {
     "fasa_read_probe": (_c_int, [_vp, _c_size, _vp, _vp]),
     "fasa_select_layout": (_c_int, [_c_int, _c_int, ctypes.POINTER(_c_int),
                                     ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
+    "fasa_decode_layout": (_c_int, [_c_int, _c_int, ctypes.POINTER(_c_int),
+                                    ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
     "fasa_check": (_c_int, [_vp, _vp, _vp, ctypes.POINTER(ctypes.c_uint32)]),
     "fasa_timing_enable": (_c_int, [_vp, _c_int]),
     "fasa_timing_collect": (_c_int, [_vp, ctypes.POINTER(ctypes.c_double), _i32p]),
@@ -75,7 +77,7 @@ EXPORTED = tuple(_SIGS)
 
 F32, BF16 = 0, 1
 ADVANCE_SEQ_LENS = 1
-DEVFLAG_SEQ_LEN, DEVFLAG_INDEX, DEVFLAG_APPEND, DEVFLAG_BUDGET = 1, 2, 4, 8
+DEVFLAG_SEQ_LEN, DEVFLAG_INDEX, DEVFLAG_APPEND, DEVFLAG_BUDGET, DEVFLAG_SELECT = 1, 2, 4, 8, 16
 _DTYPES = {"f32": (F32, torch.float32), "bf16": (BF16, torch.bfloat16)}
 
 
@@ -364,7 +366,8 @@ def read_probe(buf, sink, stream=None):
                               _vp(sink.data_ptr()), _vp(st.cuda_stream)), "fasa_read_probe")
 
 
-SELECT_LAYOUTS = {0: "none", 1: "whole", 2: "chunked", 3: "whole_wide", 4: "per_row"}
+SELECT_LAYOUTS = {0: "none", 1: "whole", 2: "chunked", 3: "whole_wide", 4: "per_row",
+                  5: "group_filter"}
 
 
 def select_layout(max_seq_len, budget):
@@ -372,6 +375,16 @@ def select_layout(max_seq_len, budget):
     max_seq_len positions at `budget`, as (name, threads, per_thread, chunk)."""
     t, e, ch = _c_int(0), _c_int(0), _c_int(0)
     k = _lib.fasa_select_layout(int(max_seq_len), int(budget), ctypes.byref(t), ctypes.byref(e),
+                                ctypes.byref(ch))
+    return SELECT_LAYOUTS[k], t.value, e.value, ch.value
+
+
+def decode_layout(max_seq_len, budget):
+    """fasa_decode_layout (host only): the top-B layout of a decode step, as
+    (name, threads, per_thread, chunk); "group_filter" where the step selects
+    through TIP's group maxima."""
+    t, e, ch = _c_int(0), _c_int(0), _c_int(0)
+    k = _lib.fasa_decode_layout(int(max_seq_len), int(budget), ctypes.byref(t), ctypes.byref(e),
                                 ctypes.byref(ch))
     return SELECT_LAYOUTS[k], t.value, e.value, ch.value
 

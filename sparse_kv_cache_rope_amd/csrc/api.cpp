@@ -69,6 +69,8 @@ void build_layout(fasa_ctx* c) {
     w.cand_stride = (need + 3) & ~3;  // rows start 32-byte aligned
     w.cand = take(sizeof(uint64_t) * rows * w.cand_stride);
   }
+  w.gstride = (c->cap + kGroupTokens - 1) / kGroupTokens;
+  w.gmax = take(sizeof(uint32_t) * rows * w.gstride);
   w.fac = take(sizeof(float) * rows * w.fac_splits * (c->d + 2));
   w.dense = take(sizeof(float) * rows * w.dense_splits * (c->d + 2));
   w.total = off;
@@ -446,10 +448,22 @@ static fasa_status decode_impl(fasa_ctx* c, void* k_cache, void* v_cache, void* 
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + c->ws.idx);
   int32_t* advance = (flags & FASA_ADVANCE_SEQ_LENS) ? seq_lens : nullptr;
   TipArgs a{sidecar, q, k_new, v_new, k_cache, v_cache, seq_lens, max_seq_len};
+  // Long rows with a fused budget: TIP also writes each token group's largest
+  // score, and one launch selects from those and attends.
+  const bool filtered = filter_path_applies(max_seq_len, budget);
   {
     // Append, query rotation and TIP in one launch.
     Timed t(c, FASA_K_TIP, stream);
-    FASA_HIP(launch_tip(c, kPrologueDecode, a, scores, ws, stream), "fasa_decode_step: tip");
+    FASA_HIP(launch_tip(c, kPrologueDecode, a, scores, ws, stream,
+                        filtered ? reinterpret_cast<uint32_t*>(ws + c->ws.gmax) : nullptr),
+             "fasa_decode_step: tip");
+  }
+  if (filtered) {
+    Timed t(c, FASA_K_SELECT_FAC, stream);
+    FASA_HIP(launch_filter_select(c, scores, nb, max_seq_len, budget, idx_out, k_cache, v_cache,
+                                  out, advance, ws, stream, head_budget),
+             "fasa_decode_step: filtered select+fac");
+    return ok();
   }
   if (select_path_applies(max_seq_len, budget)) {
     if (budget <= kFusedMaxBudget) {
@@ -623,6 +637,17 @@ fasa_select_layout_kind fasa_select_layout(int max_seq_len, int budget, int* thr
   if (per_thread) *per_thread = l.per_thread;
   if (chunk) *chunk = l.chunk;
   return static_cast<fasa_select_layout_kind>(l.kind);
+}
+
+fasa_select_layout_kind fasa_decode_layout(int max_seq_len, int budget, int* threads,
+                                           int* per_thread, int* chunk) {
+  if (max_seq_len < 1 || budget < 1) return FASA_LAYOUT_NONE;
+  if (!filter_path_applies(max_seq_len, budget))
+    return fasa_select_layout(max_seq_len, budget, threads, per_thread, chunk);
+  if (threads) *threads = kFilterSelectThreads;
+  if (per_thread) *per_thread = filter_group_slots(max_seq_len);
+  if (chunk) *chunk = kGroupTokens;
+  return FASA_LAYOUT_GROUP_FILTER;
 }
 
 fasa_status fasa_check(fasa_ctx* c, void* workspace, hipStream_t stream, uint32_t* flags) {

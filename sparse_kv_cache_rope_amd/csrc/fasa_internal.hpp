@@ -27,12 +27,14 @@ struct WsLayout {
   size_t scores = 0;    // float [b][Hq][cap]
   size_t idx = 0;       // int32 [b][Hq][max_budget]
   size_t cand = 0;      // uint64 [b*Hq][cand_stride]: two-stage top-B candidates
+  size_t gmax = 0;      // uint32 [b*Hq][gstride]: TIP's largest score key per token group
   size_t fac = 0;       // float [b*Hq][fac_splits][d + 2]
   size_t dense = 0;     // float [b*Hq][dense_splits][d + 2]
   size_t total = 0;
   int fac_splits = 0;
   int dense_splits = 0;
   int cand_stride = 0;
+  int gstride = 0;  // token groups per row of gmax: ceil(cap / kGroupTokens)
 };
 
 }  // namespace fasa
@@ -75,6 +77,12 @@ constexpr int kFusedMaxBudget = 1024;
 constexpr int kSelectChunk = 16384;
 constexpr int kTwoStageMaxCand = 16384;
 
+// Token groups: in a decode step whose selection is filtered
+// (filter_path_applies) the TIP launch also writes, per query head, the
+// largest score key (select_common.hpp order) of every kGroupTokens
+// consecutive tokens; 0 for a group past the row.
+constexpr int kGroupTokens = 8;
+
 // How a launch reads seq_lens.
 enum PrologueMode : int {
   kPrologueQueryOnly = 0,  // seq_lens = n_b; rotate q at n_b - 1
@@ -110,8 +118,10 @@ hipError_t launch_prologue(const fasa_ctx* c, const void* q, const int32_t* seq_
 // TIP scores with the step's prologue fused in: writes ws.nb, ws.qrot and
 // scores; in decode mode also appends the step's token.  Never writes
 // seq_lens (see `advance` below).
+// With group_max (decode mode only), also writes every group's largest score
+// key there (ws.gmax layout).
 hipError_t launch_tip(const fasa_ctx* c, PrologueMode mode, const TipArgs& a, float* scores,
-                      uint8_t* ws, hipStream_t s);
+                      uint8_t* ws, hipStream_t s, uint32_t* group_max = nullptr);
 // The launchers below that take `advance` (may be null) store n_b into
 // advance[b] from a kernel that reads only ws.nb, so it can be seq_lens.
 // Those that take `head_budget` (device int32 [Hq], may be null) give query
@@ -156,6 +166,24 @@ hipError_t launch_select(const fasa_ctx* c, const float* scores, const int32_t* 
                          const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
                          hipStream_t s, const int32_t* head_budget = nullptr);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+// Filtered top-B + FAC of a decode step (filter.hip): one histogram pass over
+// TIP's group maxima bounds the row's threshold from below; only the groups
+// whose maximum clears that bound are read from the scores and selected
+// exactly (streaming passes over the row where that would not fit).  Applies
+// to fused budgets on rows longer than one whole-row select holds, up to
+// kFilterMaxGroups groups.
+constexpr int kFilterSelectThreads = 512;
+constexpr int kFilterMaxGroups = kFilterSelectThreads * 40;
+bool filter_path_applies(int max_seq_len, int budget);
+// Group-maximum keys per thread of the filter select's first pass (8 or 40),
+// and survivor slots per thread of its second (8 or 24).
+int filter_group_slots(int max_seq_len);
+int filter_survivor_slots(int budget);
+hipError_t launch_filter_select(const fasa_ctx* c, const float* scores, const int32_t* nb,
+                                int max_seq_len, int budget, int32_t* idx, const void* k_cache,
+                                const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
+                                hipStream_t s, const int32_t* head_budget = nullptr);
 
 // Calibration (calibrate.hip): its workspace regions (err, nb, qrot, scores
 // [b][Hq (C + 1)][cap], idx [b][Hq (C + 1)][topk], cand), and the launcher.

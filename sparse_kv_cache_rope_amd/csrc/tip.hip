@@ -42,6 +42,10 @@
 // its FMA loop (a copy of the others', under one uniform branch) selects the
 // new pairs into that position's lane instead.
 //
+// In a decode step whose selection is filtered, the launch also writes the
+// largest score key of every 8-token group, after the scores: the B-th
+// largest group maximum bounds the row's threshold from below (filter.hip).
+//
 // HBM-bound: 4 bytes per token and plane (bf16) against 4 G FMAs.
 
 #include <type_traits>
@@ -55,6 +59,7 @@ constexpr int kTipWaves = 4;
 constexpr int kTipThreads = kTipWaves * kWave;
 constexpr int kTipTokens = kWave * 4;  // tokens per workgroup
 constexpr int kMaxPlanes = 64;         // d/2 FCs at d = 128
+static_assert(kGroupTokens == 8, "a group is the 4 tokens of two neighbouring lanes");
 
 // The arguments needed first lead the list: the build preloads the first 16
 // dwords of kernel arguments into registers, which saves a dependent load
@@ -68,7 +73,8 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
            const uint64_t* __restrict__ dom_mask, const void* __restrict__ k_new,
            const void* __restrict__ v_new, void* __restrict__ k_cache,
            void* __restrict__ v_cache, int32_t* __restrict__ nb_out, float* __restrict__ qrot,
-           float* __restrict__ scores, uint32_t* err, PlaneOffsets po) {
+           float* __restrict__ scores, uint32_t* err, PlaneOffsets po,
+           uint32_t* __restrict__ gmax, int gstride) {
   using T = typename CacheT<BF16>::T;
   constexpr int C = D / 2;
   constexpr int kPairBytes = BF16 ? 4 : 8;
@@ -291,6 +297,22 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
       for (int t = 0; t < 4; ++t)
         if (j + t < n) dst[t] = vv[t];
     }
+    if (gmax != nullptr) {
+      // The largest score key of each kGroupTokens-token group: this lane's
+      // 4 tokens and its neighbour's (key 0 past n, >= 1 otherwise).
+      const float vv[4] = {s.x, s.y, s.z, s.w};
+      uint32_t km = 0u;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t kk = score_key(vv[t]);
+        km = max(km, (j + t < n) ? (kk ? kk : 1u) : 0u);
+      }
+      km = max(km, dpp_u32<0xB1>(km));  // quad_perm [1,0,3,2]: the neighbour lane
+      // Only groups holding a token of the row: the row's gstride groups
+      // end at the capacity, which a last tile may reach past.
+      if ((qd & 1) == 0 && j < n)
+        gmax[((size_t)b * hq + (size_t)g * G + hh) * gstride + (size_t)(j / kGroupTokens)] = km;
+    }
   }
   if (tile == 0) {
 #pragma unroll
@@ -316,12 +338,12 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
 template <bool BF16, int G, int D>
 static void launch_tip_t(dim3 grid, hipStream_t s, int mode, const PlaneOffsets& po,
                          const TipArgs& a, const fasa_ctx* c, int32_t* nb, float* qrot,
-                         float* scores, uint32_t* err) {
+                         float* scores, uint32_t* err, uint32_t* gmax) {
 #define FASA_TIP(PWV)                                                                          \
   hipLaunchKernelGGL((tip_kernel<BF16, G, D, PWV>), grid, dim3(kTipThreads), 0, s, a.seq_lens, \
                      a.sidecar, mode, a.max_seq_len, c->cap, c->P, c->R, c->hkv, a.q,          \
                      c->tab.omega, c->tab.fc_slot, c->tab.dom_mask, a.k_new, a.v_new,          \
-                     a.k_cache, a.v_cache, nb, qrot, scores, err, po)
+                     a.k_cache, a.v_cache, nb, qrot, scores, err, po, gmax, c->ws.gstride)
   // Loads per wave: the largest union over the KV heads, 4 planes per step.
   const int pw = (c->max_union + kTipWaves - 1) / kTipWaves;
   if (pw <= 4) FASA_TIP(4);
@@ -334,19 +356,19 @@ static void launch_tip_t(dim3 grid, hipStream_t s, int mode, const PlaneOffsets&
 template <int G>
 static void launch_tip_g(dim3 grid, hipStream_t s, int mode, const PlaneOffsets& po,
                          const TipArgs& a, const fasa_ctx* c, int32_t* nb, float* qrot,
-                         float* scores, uint32_t* err) {
+                         float* scores, uint32_t* err, uint32_t* tc) {
   const bool bf = (c->dtype == FASA_BF16);
   if (c->d == 128) {
-    if (bf) launch_tip_t<true, G, 128>(grid, s, mode, po, a, c, nb, qrot, scores, err);
-    else launch_tip_t<false, G, 128>(grid, s, mode, po, a, c, nb, qrot, scores, err);
+    if (bf) launch_tip_t<true, G, 128>(grid, s, mode, po, a, c, nb, qrot, scores, err, tc);
+    else launch_tip_t<false, G, 128>(grid, s, mode, po, a, c, nb, qrot, scores, err, tc);
   } else {
-    if (bf) launch_tip_t<true, G, 64>(grid, s, mode, po, a, c, nb, qrot, scores, err);
-    else launch_tip_t<false, G, 64>(grid, s, mode, po, a, c, nb, qrot, scores, err);
+    if (bf) launch_tip_t<true, G, 64>(grid, s, mode, po, a, c, nb, qrot, scores, err, tc);
+    else launch_tip_t<false, G, 64>(grid, s, mode, po, a, c, nb, qrot, scores, err, tc);
   }
 }
 
 hipError_t launch_tip(const fasa_ctx* c, PrologueMode mode, const TipArgs& a, float* scores,
-                      uint8_t* ws, hipStream_t s) {
+                      uint8_t* ws, hipStream_t s, uint32_t* group_max) {
   if (c->hkv > kArgKvHeads || c->d / 2 > kMaxPlanes) return hipErrorInvalidValue;
   PlaneOffsets po;
   for (int g = 0; g <= c->hkv; ++g) po.off[g] = c->plane_off[g];
@@ -357,10 +379,10 @@ hipError_t launch_tip(const fasa_ctx* c, PrologueMode mode, const TipArgs& a, fl
   float* qrot = reinterpret_cast<float*>(ws + c->ws.qrot);
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
   switch (c->G) {
-    case 1: launch_tip_g<1>(grid, s, (int)mode, po, a, c, nb, qrot, scores, err); break;
-    case 2: launch_tip_g<2>(grid, s, (int)mode, po, a, c, nb, qrot, scores, err); break;
-    case 4: launch_tip_g<4>(grid, s, (int)mode, po, a, c, nb, qrot, scores, err); break;
-    case 8: launch_tip_g<8>(grid, s, (int)mode, po, a, c, nb, qrot, scores, err); break;
+    case 1: launch_tip_g<1>(grid, s, (int)mode, po, a, c, nb, qrot, scores, err, group_max); break;
+    case 2: launch_tip_g<2>(grid, s, (int)mode, po, a, c, nb, qrot, scores, err, group_max); break;
+    case 4: launch_tip_g<4>(grid, s, (int)mode, po, a, c, nb, qrot, scores, err, group_max); break;
+    case 8: launch_tip_g<8>(grid, s, (int)mode, po, a, c, nb, qrot, scores, err, group_max); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
