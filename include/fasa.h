@@ -241,6 +241,29 @@ fasa_status fasa_decode_step_per_head(fasa_ctx* ctx, void* k_cache, void* v_cach
                                       hipStream_t stream);
 
 /*
+ * fasa_decode_step for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and results as fasa_decode_step (no head budgets), except that
+ * the workspace is a file-scope device array of the library, 64 MiB per GPU
+ * (FASA_STATIC_SCRATCH_BYTES), held until the process ends: a context whose
+ * fasa_workspace_bytes exceeds it is refused with FASA_ERR_CAPACITY before
+ * anything is enqueued.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); its first call on a device looks the array's
+ * device address up once, with the context's device current.  Every call on
+ * a GPU shares that GPU's array, which keeps the last call's contents: the
+ * call clears the device error flag word first, so calls that overlap on one
+ * GPU (other streams, other host threads) race and must be ordered by the
+ * caller.  dev_flags: device uint32 (may be NULL) that receives the call's
+ * FASA_DEVFLAG_* bits (fasa_check cannot reach the array).
+ */
+#define FASA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+fasa_status fasa_decode_step_static(fasa_ctx* ctx, void* k_cache, void* v_cache, void* sidecar,
+                                    const void* q, const void* k_new, const void* v_new,
+                                    int32_t* seq_lens, int max_seq_len, int budget, float* out,
+                                    int32_t* idx_out, uint32_t* dev_flags, unsigned flags,
+                                    hipStream_t stream);
+
+/*
  * Dense full-KV decode attention over all n_b cached tokens (the comparator
  * the pages measure FASA against: full KV, gist.science/pt, "Resumo Tecnico"
  * section 4).  seq_lens[b] = n_b; out: float [b][Hq][d].

@@ -48,6 +48,8 @@ _SIGS = {
                                   _vp, _vp, _vp, ctypes.c_uint, _vp]),
     "fasa_decode_step_per_head": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _vp,
                                            _c_int, _vp, _vp, _vp, ctypes.c_uint, _vp]),
+    "fasa_decode_step_static": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int,
+                                         _vp, _vp, _vp, ctypes.c_uint, _vp]),
     "fasa_dense_attn": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp]),
     "fasa_calibrate_workspace_bytes": (_c_size, [_vp, _c_int]),
     "fasa_calibrate": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp]),
@@ -77,6 +79,7 @@ EXPORTED = tuple(_SIGS)
 
 F32, BF16 = 0, 1
 ADVANCE_SEQ_LENS = 1
+STATIC_SCRATCH_BYTES = 64 << 20  # FASA_STATIC_SCRATCH_BYTES
 DEVFLAG_SEQ_LEN, DEVFLAG_INDEX, DEVFLAG_APPEND, DEVFLAG_BUDGET, DEVFLAG_SELECT = 1, 2, 4, 8, 16
 _DTYPES = {"f32": (F32, torch.float32), "bf16": (BF16, torch.bfloat16)}
 
@@ -298,6 +301,29 @@ class Context:
                                    int(max_seq_len), int(budget), _ptr(out), _ptr(idx_out),
                                    _ptr(workspace), ADVANCE_SEQ_LENS if advance else 0,
                                    self._stream(stream)), "fasa_decode_step")
+
+    def decode_step_static(self, k_cache, v_cache, sidecar, q, k_new, v_new, seq_lens,
+                           max_seq_len, budget, out, idx_out=None, dev_flags=None,
+                           advance=False, stream=None):
+        """fasa_decode_step_static: one decode step whose workspace is the
+        library's own per-GPU array (no workspace argument, nothing
+        allocated).  dev_flags: optional device uint32 [1] that receives the
+        step's device flag bits."""
+        b, hq, hkv, d = self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim
+        self._want(q, "q", self.torch_dtype, (b, hq, d))
+        self._want(k_new, "k_new", self.torch_dtype, (b, hkv, d))
+        self._want(v_new, "v_new", self.torch_dtype, (b, hkv, d))
+        self._want(seq_lens, "seq_lens", torch.int32, (b,))
+        self._want(out, "out", torch.float32, (b, hq, d))
+        if idx_out is not None:
+            self._want(idx_out, "idx_out", torch.int32, (b, hq, budget))
+        if dev_flags is not None:
+            self._want(dev_flags, "dev_flags", torch.int32, (1,))
+        _chk(_lib.fasa_decode_step_static(
+            self._h, self._cache(k_cache, 'k_cache'), self._cache(v_cache, 'v_cache'),
+            _ptr(sidecar), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(seq_lens), int(max_seq_len),
+            int(budget), _ptr(out), _ptr(idx_out), _ptr(dev_flags),
+            ADVANCE_SEQ_LENS if advance else 0, self._stream(stream)), "fasa_decode_step_static")
 
     def dense_attn(self, k_cache, v_cache, q, seq_lens, max_seq_len, out, workspace,
                    stream=None):

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -528,6 +529,68 @@ fasa_status fasa_decode_step_per_head(fasa_ctx* c, void* k_cache, void* v_cache,
   FASA_NONNULL(head_budget);
   return decode_impl(c, k_cache, v_cache, sidecar, q, k_new, v_new, seq_lens, max_seq_len,
                      head_budget, budget, out, idx_out, workspace, flags, stream);
+}
+
+}  // extern "C"
+
+// The workspace of fasa_decode_step_static: one array per GPU the library
+// runs on, zero at load, held until the process ends.  Host code never uses
+// its name as an address: the device address comes from hipGetSymbolAddress,
+// once per device.
+static __device__ __align__(256) uint8_t scratch[FASA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kScratchDevices] = {};
+
+// The device address of `scratch` on `device`, looked up on first use with
+// that device current.
+fasa_status scratch_on(int device, uint8_t** out) {
+  if (device < 0 || device >= kScratchDevices)
+    return fail(FASA_ERR_UNSUPPORTED, "device %d outside [0, %d)", device, kScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device] == nullptr) {
+    int cur = -1;
+    FASA_HIP(hipGetDevice(&cur), "fasa_decode_step_static: current device");
+    if (cur != device) FASA_HIP(hipSetDevice(device), "fasa_decode_step_static: set device");
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != device) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return hip_fail(e, "fasa_decode_step_static: scratch address");
+    if (p == nullptr) return fail(FASA_ERR_HIP, "fasa_decode_step_static: null scratch address");
+    g_scratch_ptr[device] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_ptr[device];
+  return FASA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fasa_status fasa_decode_step_static(fasa_ctx* c, void* k_cache, void* v_cache, void* sidecar,
+                                    const void* q, const void* k_new, const void* v_new,
+                                    int32_t* seq_lens, int max_seq_len, int budget, float* out,
+                                    int32_t* idx_out, uint32_t* dev_flags, unsigned flags,
+                                    hipStream_t stream) {
+  FASA_TRY(check_ctx(c));
+  if (c->ws.total > FASA_STATIC_SCRATCH_BYTES)
+    return fail(FASA_ERR_CAPACITY,
+                "fasa_decode_step_static: the context needs a %zu-byte workspace, above the "
+                "%zu-byte static scratch", c->ws.total, (size_t)FASA_STATIC_SCRATCH_BYTES);
+  uint8_t* ws = nullptr;
+  FASA_TRY(scratch_on(c->device, &ws));
+  // Only the flag word must start at zero: every other region is written
+  // before it is read within one step.
+  FASA_HIP(launch_fill_zero(ws + c->ws.err, 16, stream), "fasa_decode_step_static: flags");
+  FASA_TRY(decode_impl(c, k_cache, v_cache, sidecar, q, k_new, v_new, seq_lens, max_seq_len,
+                       nullptr, budget, out, idx_out, ws, flags, stream));
+  if (dev_flags != nullptr)
+    FASA_HIP(launch_copy_u32(reinterpret_cast<const uint32_t*>(ws + c->ws.err), dev_flags, stream),
+             "fasa_decode_step_static: flags out");
+  return ok();
 }
 
 fasa_status fasa_dense_attn(fasa_ctx* c, const void* k_cache, const void* v_cache,

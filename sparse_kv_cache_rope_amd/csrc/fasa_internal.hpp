@@ -166,6 +166,8 @@ hipError_t launch_select(const fasa_ctx* c, const float* scores, const int32_t* 
                          const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
                          hipStream_t s, const int32_t* head_budget = nullptr);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// *dst = *src (one device word, a one-thread kernel).
+hipError_t launch_copy_u32(const uint32_t* src, uint32_t* dst, hipStream_t s);
 
 // Filtered top-B + FAC of a decode step (filter.hip): one histogram pass over
 // TIP's group maxima bounds the row's threshold from below; only the groups

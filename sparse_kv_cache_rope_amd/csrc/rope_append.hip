@@ -106,6 +106,15 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
+__global__ void copy_u32_kernel(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst) {
+  *dst = *src;
+}
+
+hipError_t launch_copy_u32(const uint32_t* src, uint32_t* dst, hipStream_t s) {
+  hipLaunchKernelGGL(copy_u32_kernel, dim3(1), dim3(1), 0, s, src, dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_append(const fasa_ctx* c, void* k_cache, void* v_cache, void* sidecar,
                          const void* k_new, const void* v_new, const int32_t* start_pos,
                          int n_new, uint8_t* ws, hipStream_t s) {
