@@ -371,20 +371,65 @@ def test_decode_step_c2_full(gpu):
     _decode_parity(gpu, w, W.generate(w))
 
 
+def _full_parity(gpu, w, x, check_steps=None, threads=16):
+    """Every (sequence, query head) row of the checked steps against the
+    oracle, at the workload's full size, through the launch configuration
+    bench.py times.  The GPU runs every step; the oracle appends every
+    step's token and checks the chosen steps' rows in a thread pool (NumPy
+    releases the GIL in its heavy calls)."""
+    from concurrent.futures import ThreadPoolExecutor
+    g = GpuSetup(gpu, w, x)
+    o = oracle_setup(w, x)
+    check = set(range(w.steps)) if check_steps is None else set(check_steps)
+    rows = [(b, h) for b in range(w.batch) for h in range(w.n_q_heads)]
+    diffs, worst = 0, 0.0
+    with ThreadPoolExecutor(threads) as pool:
+        for t in range(w.steps):
+            out, idx = run_decode(g, t, w.budget)
+            o.step(x["q"][t], x["k_new"][t], x["v_new"][t], w.budget, heads=[])  # append only
+            if t not in check:
+                continue
+            got_idx, got_out = idx.cpu().numpy(), out.cpu().numpy()
+            qrs = [o.query_rot(b, x["q"][t][b]) for b in range(w.batch)]
+
+            def one(bh):
+                b, h = bh
+                n = int(o.lens[b])
+                where = f"step {t} b{b} h{h}"
+                s = o.head_scores(b, h, qrs[b][h])
+                d = check_index_set(got_idx[b, h], s, w.budget, n, where)
+                want = o.attend(b, h, qrs[b][h], got_idx[b, h])
+                return d, check_out(got_out[b, h], want, w.dtype, where)
+
+            for d, r in pool.map(one, rows):
+                diffs += d
+                worst = max(worst, r)
+    assert g.ctx.check(g.ws) == 0
+    assert np.array_equal(g.seq_lens.cpu().numpy(), (x["ctx"] - 1 + w.steps).astype(np.int32))
+    return diffs, worst
+
+
+@pytest.mark.timeout(600)
 def test_decode_step_c3_full(gpu):
+    """16 ragged sequences of 4k-8k tokens: every head of every sequence."""
     w = W.get("c3")
-    _decode_parity(gpu, w, W.generate(w), heads=[0, 5, 17, 31])
+    _full_parity(gpu, w, W.generate(w))
 
 
+@pytest.mark.timeout(900)
 def test_decode_step_c4_full(gpu):
-    """64 steps with append; the oracle checks a sample of steps and heads."""
+    """64 steps with append at 4 x 32k tokens, B = 6193: every head of every
+    sequence at every step."""
     w = W.get("c4")
-    _decode_parity(gpu, w, W.generate(w), heads=[0, 13, 31], check_steps={0, 1, 32, 63})
+    _full_parity(gpu, w, W.generate(w))
 
 
+@pytest.mark.timeout(900)
 def test_decode_step_c5_full(gpu):
+    """32 steps with append at 128k tokens, B = 1024: every head at every
+    step."""
     w = W.get("c5")
-    _decode_parity(gpu, w, W.generate(w), heads=[0, 7, 30], check_steps={0, 15, 31})
+    _full_parity(gpu, w, W.generate(w))
 
 
 # -------------------------------------------------------- edge cases ----
