@@ -368,7 +368,7 @@ fasa_select_layout_kind fasa_select_layout(int max_seq_len, int budget, int* thr
  * variant) for rows of up to max_seq_len positions at `budget`: the same as
  * fasa_select_layout, except FASA_LAYOUT_GROUP_FILTER where the step filters.
  * There the TIP launch also writes, per query head, the largest score of
- * every 8 consecutive tokens, and one launch selects and runs FAC: the B-th
+ * every 16 consecutive tokens, and one launch selects and runs FAC: the B-th
  * largest group maximum bounds the B-th largest score from below (group
  * maxima are scores of distinct tokens), so only groups whose maximum
  * reaches that bound's histogram bin are read again and selected exactly;
@@ -376,7 +376,7 @@ fasa_select_layout_kind fasa_select_layout(int max_seq_len, int budget, int* thr
  * scores.  The result is the exact T_t either way (gist.science/pt "Resumo
  * Tecnico" section 2, FAC first bullet).  The step filters when
  * budget <= 1024 and 8192 < max_seq_len <= 163840.  *threads = 512 there,
- * *per_thread = group maxima held per thread (8 or 40), *chunk = 8 (the
+ * *per_thread = group maxima held per thread (4 or 20), *chunk = 16 (the
  * group); each may be NULL.  Host-side, no context needed.  Returns
  * FASA_LAYOUT_NONE for max_seq_len < 1 or budget < 1.
  */

@@ -81,7 +81,7 @@ constexpr int kTwoStageMaxCand = 16384;
 // (filter_path_applies) the TIP launch also writes, per query head, the
 // largest score key (select_common.hpp order) of every kGroupTokens
 // consecutive tokens; 0 for a group past the row.
-constexpr int kGroupTokens = 8;
+constexpr int kGroupTokens = 16;
 
 // How a launch reads seq_lens.
 enum PrologueMode : int {
@@ -176,10 +176,10 @@ hipError_t launch_copy_u32(const uint32_t* src, uint32_t* dst, hipStream_t s);
 // to fused budgets on rows longer than one whole-row select holds, up to
 // kFilterMaxGroups groups.
 constexpr int kFilterSelectThreads = 512;
-constexpr int kFilterMaxGroups = kFilterSelectThreads * 40;
+constexpr int kFilterMaxGroups = kFilterSelectThreads * 20;
 bool filter_path_applies(int max_seq_len, int budget);
-// Group-maximum keys per thread of the filter select's first pass (8 or 40),
-// and survivor slots per thread of its second (8 or 24).
+// Group-maximum keys per thread of the filter select's first pass (4 or 20),
+// and survivor slots per thread of its second (12 or 40).
 int filter_group_slots(int max_seq_len);
 int filter_survivor_slots(int budget);
 hipError_t launch_filter_select(const fasa_ctx* c, const float* scores, const int32_t* nb,

@@ -8,24 +8,33 @@
 // select_common.hpp: selected <=> composite >= tau, tau the B-th largest.
 //
 // In a filtered decode step the TIP launch has also written the largest
-// score key of every 8-token group of each row.  Group maxima are scores of
+// score key of every 16-token group of each row.  Group maxima are scores of
 // distinct tokens, so the B-th largest of them is at most tau, and every
 // token >= tau lies in a group whose maximum is >= it.  Here:
 //   1. one histogram pass over the row's group maxima (bins linear in the
 //      score between their min and max) finds the bin P holding the B-th
 //      largest; every group whose maximum falls in bin P or above survives
-//      (about B groups);
-//   2. the survivors' scores (8 each, 32 contiguous bytes) are gathered, those
-//      below bin P dropped, and tau is the B-th largest of the rest, exactly;
-//      T_t is emitted in position order (groups ascending, then positions);
-//   3. rows where that would not fit (ties spread over too many groups, or a
-//      degenerate score range) are selected by streaming range refinement
-//      over their scores and an ordered streaming emit.
-// Rows of at most B groups skip step 1 (every group survives).
+//      (about B groups), and kp, the smallest surviving maximum, is at most
+//      tau;
+//   2. the survivors' scores (16 each, 64 contiguous bytes) are gathered;
+//      those >= kp are "in play" and listed in position order in LDS, and a
+//      second histogram (keys from kp) counts them;
+//   3. the K and V rows of the in-play tokens are requested right away, so
+//      the gather overlaps the rest of the selection: the bin of the B-th
+//      largest in-play key gives tau at once when the whole bin is taken,
+//      else its few elements are ranked;
+//   4. FAC over the list, unselected entries masked: logits of every listed
+//      row, then the softmax max and denominator, then the weighted sum of
+//      V (two passes over LDS logits instead of an online merge);
+//   5. rows this does not fit (fewer groups than B, one score value, more
+//      survivors or in-play tokens than the slots hold, a crowded pivot bin)
+//      are selected by streaming range refinement over their scores and an
+//      ordered streaming emit, then attended the same way.
 //
-// One 512-thread workgroup per row, or S per row for the fused FAC's column
-// split (each part makes the same selection); part 0 writes idx, the advanced
-// length and flags.  No workgroup waits on another.
+// One 512-thread workgroup per row, or S per row for the FAC's column split
+// (each part makes the same selection and writes D / S output columns);
+// part 0 writes idx, the advanced length and flags.  No workgroup waits on
+// another.
 
 #include "attention_common.hpp"
 #include "budget.hpp"
@@ -37,29 +46,42 @@ namespace fasa {
 
 constexpr int kFilterThreads = kFilterSelectThreads;
 constexpr int kFilterWaves = kFilterThreads / kWave;
+// Streaming route: histogram copies and LDS candidates.
 constexpr int kFilterHistCopies = 4;
 constexpr int kFilterCandCap = 4096;
-// Most surviving groups: 24 survivor slots per thread, 8 per group.
-constexpr int kFilterMaxSurvivors = kFilterThreads * 24 / kGroupTokens;
-static_assert(kGroupTokens == 8 && kFilterThreads % 2 == 0, "two threads per group");
-// LDS the fused FAC needs for its state merge, worst case over the head
-// sizes and dtypes built (bf16, d = 64: 128 states of 64 dims).
-constexpr int kFilterAttendScratch = 9728;
+// In-play tokens listed in LDS, and pivot-bin elements ranked by one wave.
+constexpr int kPlayCap = 2048;
+constexpr int kPivotCap = kWave;
+// Threads per surviving group (a 16-byte score load each).
+constexpr int kGroupThreads = kGroupTokens / 4;
+// Most surviving groups: 40 survivor slots per thread.
+constexpr int kFilterMaxSurvivors = kFilterThreads * 40 / kGroupTokens;
+// FAC partial sums: up to 4 row slots per wave of D / S floats each.
+constexpr int kFacRedFloats = kFilterWaves * 4 * 128;
+static_assert(kPlayCap % kFilterThreads == 0, "emit chunks");
 
 using FilterSelLds = RegSelectLds<kFilterThreads, kFilterHistCopies, kFilterCandCap>;
 
 struct FilterLds {
   union {
-    FilterSelLds s;  // streaming passes, LDS refinement, pivot-bin gather, ordered emits
-    float att[kFilterAttendScratch];
+    FilterSelLds s;             // streaming route; block_minmax's wave extremes
+    float red[kFacRedFloats];   // FAC partial sums (after every select)
   };
-  // Histograms of the group maxima and of the survivors, cleared at the
+  // Histograms of the group maxima and of the in-play keys, cleared at the
   // kernel's start (a spare word per lane past the bins, as in RegSelectLds).
   alignas(16) uint32_t hist1[kSelBins + kWave];
   alignas(16) uint32_t hist2[kSelBins + kWave];
-  int32_t sel[kFusedMaxBudget];
   int32_t grp[kFilterMaxSurvivors];  // surviving groups, ascending
-  uint32_t kpmin[kFilterWaves];      // per-wave smallest surviving group maximum
+  // The list FAC reads: positions ascending, their keys, their logits.
+  int32_t pos[kPlayCap];
+  uint32_t key[kPlayCap];
+  float z[kPlayCap];
+  uint64_t pivot[kPivotCap];
+  uint32_t pivot_n;
+  uint32_t kpmin[kFilterWaves];  // per-wave smallest surviving group maximum
+  uint32_t slab_g[kMaxSlabs * kFilterWaves];
+  uint32_t slab_p[kMaxSlabs * kFilterWaves];
+  uint32_t emit_cnt[kPlayCap / kWave];
 };
 
 struct WavePick {
@@ -122,21 +144,6 @@ __device__ __forceinline__ uint64_t wave_rank(const uint64_t* cand, uint32_t M, 
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(c >> 32), src);
   return ((uint64_t)hi << 32) | lo;
 }
-
-// The surviving groups' scores held for the exact select: slot e of thread t
-// is virtual element 4 (s NT + t) + e % 4 (s = e / 4), i.e. list entry
-// (s NT + t) / 2 and offset 4 (t % 2) + e % 4 in its group, so (slab, thread,
-// e) order is position order.  Key 0 marks no element.
-template <int E>
-struct SurvivorSrc {
-  uint32_t k[E];
-  int g[E / 4];  // group of slab s (any value where the slab holds none)
-  __device__ __forceinline__ int pos(int e) const {
-    return g[e / 4] * kGroupTokens + 4 * (int)(threadIdx.x & 1) + (e & 3);
-  }
-  __device__ __forceinline__ uint32_t key(int e) const { return k[e]; }
-  __device__ __forceinline__ uint32_t low(int e) const { return 0xffffffffu - (uint32_t)pos(e); }
-};
 
 // Streaming passes over a row's n scores (8192 per round: 4 float4 slabs per
 // thread, slab layout), for rows whose saturated tiles do not fit registers.
@@ -282,10 +289,221 @@ __device__ __forceinline__ void stream_emit(const float* row, int n, uint64_t ta
   }
 }
 
+// ---- FAC over the in-play list ---------------------------------------------
+//
+// Rows r < np of the list (L.pos, L.key); a row takes part iff its composite
+// is >= tau.  Each of the S parts computes every logit (the softmax needs
+// them all) and the weighted V sum of its D / S columns.
+//
+// K: LPR lanes hold a row (RS rows per wave step); V: VL = LPR / S lanes hold
+// a row's column slice (RV rows per wave step).  A round of loads covers RK
+// rows of K and RVR rows of V; list slots past np load the list's last row
+// (fetched anyway) and count as absent.
+template <bool BF16, int D, int S>
+struct PlayFac {
+  using Geo = RowGeom<BF16, D>;
+  static constexpr int LPR = Geo::LPR, EPL = Geo::EPL, RS = Geo::RS;
+  static constexpr int NW = kFilterWaves;
+  static_assert(LPR % S == 0, "V slice lanes");
+  static constexpr int VL = LPR / S;
+  static constexpr int RV = kWave / VL;
+  static constexpr int cl(int x) { return x < 1 ? 1 : (x > 10 ? 10 : x); }
+  static constexpr int KST = cl(320 / (RS * NW));
+  static constexpr int VST = cl((320 + RV * NW - 1) / (RV * NW));
+  static constexpr int RK = RS * NW * KST;
+  static constexpr int RVR = RV * NW * VST;
+  // Row slots of a wave after the in-row V sums, and the floats they hold.
+  static constexpr int SLOTS = VL < 16 ? 4 : kWave / VL;
+  static constexpr int W = D / S;
+  static_assert(NW * SLOTS * W <= kFacRedFloats, "partial sums");
+  uint4 k[KST], v[VST];
+};
+
+template <class F>
+__device__ __forceinline__ void fac_issue_k(F& f, int r0, int np, const int32_t* pos,
+                                            const uint4* __restrict__ K, size_t kvbase) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int last = np - 1;
+#pragma unroll
+  for (int s = 0; s < F::KST; ++s) {
+    const int r = r0 + (s * F::NW + wave) * F::RS + lane / F::LPR;
+    const int j = pos[r < np ? r : last];
+    f.k[s] = K[(kvbase + (size_t)j) * F::LPR + lane % F::LPR];
+  }
+}
+
+template <class F>
+__device__ __forceinline__ void fac_issue_v(F& f, int r0, int np, const int32_t* pos,
+                                            const uint4* __restrict__ V, size_t kvbase, int part) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int last = np - 1;
+#pragma unroll
+  for (int s = 0; s < F::VST; ++s) {
+    const int r = r0 + (s * F::NW + wave) * F::RV + lane / F::VL;
+    const int j = pos[r < np ? r : last];
+    f.v[s] = V[(kvbase + (size_t)j) * F::LPR + part * F::VL + lane % F::VL];
+  }
+}
+
+// bf16 pair of a float, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+typedef __bf16 fasa_bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(fasa_bf16x2, a),
+                                         __builtin_bit_cast(fasa_bf16x2, b), c, false);
+}
+
+template <int SH>
+__device__ __forceinline__ float row_shr_add(float v) {
+  // Lanes with no source SH lanes below in their 16-lane row add 0.
+  return v + __int_as_float(
+                 __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + SH, 0xf, 0xf, true));
+}
+
+// The query's part of a logit: q~ scaled to log2 units; for bf16 rows split
+// into a high and a low bf16 pair per two dims (q = hi + lo to about 2^-16),
+// so that each 16-byte K load takes EPL dot2 steps and no unpacking.
+template <bool BF16, int EPL>
+struct FacQuery {
+  float q[EPL];
+  uint32_t hi[EPL / 2], lo[EPL / 2];
+};
+
+template <class F, class Q>
+__device__ __forceinline__ void fac_logits(const F& f, const Q& qq, int r0, int np, uint64_t tau,
+                                           FilterLds& L) {
+  using Geo = typename F::Geo;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int s = 0; s < F::KST; ++s) {
+    const uint4 x = f.k[s];
+    float dot = 0.0f;
+    if constexpr (Geo::ES == 2) {
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dot = dot2_bf16(w[i], qq.hi[i], dot);
+        dot = dot2_bf16(w[i], qq.lo[i], dot);
+      }
+    } else {
+      const float kf[4] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
+                           __uint_as_float(x.w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dot = fmaf(qq.q[e], kf[e], dot);
+    }
+    dot = group_sum<F::LPR>(dot);
+    const int r = r0 + (s * F::NW + wave) * F::RS + lane / F::LPR;
+    if (lane % F::LPR == 0 && r < np) {
+      const bool in = composite(L.key[r], (uint32_t)L.pos[r]) >= tau;
+      L.z[r] = in ? dot : -INFINITY;
+    }
+  }
+}
+
+// FAC over the list (loads of the first round already issued in f), this
+// part's columns written to out_row.  Two barriers; reads L.pos, L.key.
+template <bool BF16, int D, int S>
+__device__ __forceinline__ void fac_play(PlayFac<BF16, D, S>& f, int np, uint64_t tau,
+                                         const uint4* __restrict__ K, const uint4* __restrict__ V,
+                                         size_t kvbase, int part, const float* __restrict__ qrow,
+                                         float* __restrict__ out_row, FilterLds& L) {
+  using F = PlayFac<BF16, D, S>;
+  constexpr int LPR = F::LPR, EPL = F::EPL, VL = F::VL;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  FacQuery<BF16, EPL> qq;
+  {
+    const float scale = logit_scale<D>();
+    const int sub = lane % LPR;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qq.q[e] = qrow[sub * EPL + e] * scale;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < EPL / 2; ++i) {
+        const uint32_t h0 = f32_to_bf16_bits(qq.q[2 * i]), h1 = f32_to_bf16_bits(qq.q[2 * i + 1]);
+        const uint32_t l0 = f32_to_bf16_bits(qq.q[2 * i] - __uint_as_float(h0 << 16));
+        const uint32_t l1 = f32_to_bf16_bits(qq.q[2 * i + 1] - __uint_as_float(h1 << 16));
+        qq.hi[i] = h0 | (h1 << 16);
+        qq.lo[i] = l0 | (l1 << 16);
+      }
+    }
+  }
+  // Logits, round by round (the first round's K is in flight already).
+  fac_logits(f, qq, 0, np, tau, L);
+  for (int r0 = F::RK; r0 < np; r0 += F::RK) {
+    fac_issue_k(f, r0, np, L.pos, K, kvbase);
+    fac_logits(f, qq, r0, np, tau, L);
+  }
+  __syncthreads();
+  // Softmax max and denominator over the list, every wave on its own.
+  float m = -INFINITY;
+  for (int i = lane; i < np; i += kWave) m = fmaxf(m, L.z[i]);
+  m = wave_max(m);
+  float l = 0.0f;
+  for (int i = lane; i < np; i += kWave) l += exp2f(L.z[i] - m);  // -inf gives 0
+  l = group_sum<kWave>(l);
+  // Weighted V sum of this part's columns.
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+  for (int r0 = 0; r0 < np; r0 += F::RVR) {
+    if (r0 > 0) fac_issue_v(f, r0, np, L.pos, V, kvbase, part);
+#pragma unroll
+    for (int s = 0; s < F::VST; ++s) {
+      const int r = r0 + (s * F::NW + wave) * F::RV + lane / VL;
+      const float p = r < np ? exp2f(L.z[r] - m) : 0.0f;
+      float vf[EPL];
+      unpack<BF16, EPL>(f.v[s], vf);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
+    }
+  }
+  // Sum over the row slots holding the same slice: within 16-lane rows by
+  // DPP, then the waves' rows through LDS.
+  if constexpr (VL < 16) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      if constexpr (VL <= 1) acc[e] = row_shr_add<1>(acc[e]);
+      if constexpr (VL <= 2) acc[e] = row_shr_add<2>(acc[e]);
+      if constexpr (VL <= 4) acc[e] = row_shr_add<4>(acc[e]);
+      acc[e] = row_shr_add<8>(acc[e]);
+    }
+  }
+  const bool holder = VL < 16 ? (lane & 15) >= 16 - VL : true;
+  const int slot = VL < 16 ? lane >> 4 : lane / VL;
+  if (holder) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      L.red[(wave * F::SLOTS + slot) * F::W + (lane % VL) * EPL + e] = acc[e];
+  }
+  __syncthreads();
+  if (t < F::W) {
+    float sum = 0.0f;
+#pragma unroll 8
+    for (int st = 0; st < F::NW * F::SLOTS; ++st) sum += L.red[st * F::W + t];
+    out_row[part * F::W + t] = l > 0.0f ? sum / l : 0.0f;
+  }
+}
+
+// Smallest shift that fits [0, sp] into the histogram's bins.
+__device__ __forceinline__ int bin_shift(uint32_t sp) {
+  return sp < (uint32_t)kSelBins ? 0 : 32 - (int)__clz(sp) - kSelBits;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  uint32_t unused = 0u;
+  wave_minmax(v, unused);
+  return v;
+}
+
 // T_t of row (b, h) from the group maxima (see the file comment), written to
-// idx (part 0, if given) and attended (fused FAC) by every part for its
-// columns.  E1 group maxima per thread (E1 NT >= the row's groups), E2
-// survivor slots per thread (E2 NT / 8 groups).
+// idx (part 0, if given) and attended (FAC) by every part for its columns.
+// E1 group maxima per thread (E1 NT >= the row's groups), E2 survivor slots
+// per thread (E2 NT / 16 groups).
 template <bool BF16, int D, int E1, int E2, int S>
 __global__ void __launch_bounds__(kFilterThreads)
 filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
@@ -299,16 +517,15 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
   constexpr int NW = kFilterWaves;
   constexpr int kCapGroups = E2 * NT / kGroupTokens;
   static_assert(kCapGroups <= kFilterMaxSurvivors, "survivor list");
-  static_assert(NW * RowGeom<BF16, D>::RS * (D + 3) + 1 + NT <= kFilterAttendScratch,
-                "attend_rows scratch");
   static_assert(E1 % 4 == 0 && E1 / 4 <= kMaxSlabs && E2 % 4 == 0 && E2 / 4 <= kMaxSlabs,
                 "slabs");
+  using F = PlayFac<BF16, D, S>;
   __shared__ FilterLds L;
   const int part = S > 1 ? (int)blockIdx.x / hq : 0;
   const int h = S > 1 ? (int)blockIdx.x % hq : (int)blockIdx.x, b = blockIdx.y;
   const bool lead = part == 0;
   const size_t row = (size_t)b * hq + h;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
 
   // The row's group maxima go out before n_b arrives (bounded by the
   // launch's longest row); groups past the row's own length are masked once
@@ -324,8 +541,8 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
       graw[g] = make_uint4(x[0], x[1], x[2], x[3]);
     }
   }
-  // Both histograms and the pivot gather's counter are cleared while the
-  // loads fly (the first barrier below orders that before any count).
+  // Both histograms and the pivot counter are cleared while the loads fly
+  // (the first barrier below orders that before any count).
   {
     uint4* h1 = reinterpret_cast<uint4*>(L.hist1);
     uint4* h2 = reinterpret_cast<uint4*>(L.hist2);
@@ -333,7 +550,7 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
       h1[i] = make_uint4(0, 0, 0, 0);
       h2[i] = make_uint4(0, 0, 0, 0);
     }
-    if (t == 0) L.s.cand_n = 0u;
+    if (t == 0) L.pivot_n = 0u;
   }
   const int n = checked_len(nb, b, max_seq_len, cap, err, lead && h == 0 && t == 0);
   if (advance != nullptr && lead && h == 0 && t == 0 && n > 0) advance[b] = n;
@@ -341,195 +558,222 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
   const int bh = row_budget(head_budget, h, budget, err, lead && b == 0 && t == 0);
   const int take = n < bh ? n : bh;
   const bool whole = n <= bh || bh == 0;  // every position, or none
+  const float* row_scores = scores + row * cap;
+  const size_t kvbase = ((size_t)b * hkv + h / G) * cap;
+  const uint4* K = static_cast<const uint4*>(k_cache);
+  const uint4* V = static_cast<const uint4*>(v_cache);
 
-  // Every slot FAC may read starts at position 0 (always a token), so no
-  // selection outcome can send its gather out of the row.
-  for (int j = t; j < take; j += NT) L.sel[j] = 0;
+  int np = take;      // entries of the list FAC reads
+  uint64_t tau = 0;   // an entry takes part <=> its composite >= tau
+  F fac;
+  bool issued = false;  // the first round of FAC loads is in flight
+  bool cold = false;    // the streaming route selects this row
+
   if (whole) {
-    for (int j = t; j < budget; j += NT) {
-      if (o) o[j] = (j < take) ? j : -1;
-      if (j < kFusedMaxBudget) L.sel[j] = j;
+    for (int j = t; j < take; j += NT) {
+      L.pos[j] = j;
+      L.key[j] = 1u;
     }
+    if (o)
+      for (int j = t; j < budget; j += NT) o[j] = (j < take) ? j : -1;
   } else {
-    const float* row_scores = scores + row * cap;
     const int ng = (n + kGroupTokens - 1) / kGroupTokens;
-    const uint32_t spare = (uint32_t)(kSelBins + lane_id());
-    uint32_t gk[E1];
+    cold = ng <= bh;  // every group would survive
+    if (!cold) {
+      // 1. Bin P of the bh-th largest group maximum (1024 bins linear in the
+      // score over the maxima's range); groups at bin P or above survive.
+      uint32_t gk[E1];
 #pragma unroll
-    for (int g = 0; g < E1 / 4; ++g) {
-      const uint32_t w4[4] = {graw[g].x, graw[g].y, graw[g].z, graw[g].w};
+      for (int g = 0; g < E1 / 4; ++g) {
+        const uint32_t w4[4] = {graw[g].x, graw[g].y, graw[g].z, graw[g].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) gk[4 * g + e] = (4 * (g * NT + t) + e < ng) ? w4[e] : 0u;
-    }
-
-    // 1. Bin P of the bh-th largest group maximum (1024 bins linear in the
-    // score over the maxima's range); groups at bin P or above survive.
-    // Rows of at most bh groups keep every group.
-    bool stream = false;
-    const bool filter = ng > bh;
-    uint32_t kmin = ~0u, kmax = 0u;
+        for (int e = 0; e < 4; ++e) gk[4 * g + e] = (4 * (g * NT + t) + e < ng) ? w4[e] : 0u;
+      }
+      uint32_t kmin = ~0u, kmax = 0u;
 #pragma unroll
-    for (int e = 0; e < E1; ++e) {
-      kmin = min(kmin, gk[e] ? gk[e] : ~0u);
-      kmax = max(kmax, gk[e]);
-    }
-    block_minmax(kmin, kmax, L.s);  // barrier 1
-    const float vmin = key_value(kmin), vmax = key_value(kmax);
-    const float span = vmax - vmin;
-    const float scale = (float)kSelBins / span;
-    uint32_t pbin = 0;
-    if (filter) {
-      if (isfinite(vmin) && isfinite(vmax) && span > 0.0f && isfinite(span) && isfinite(scale)) {
+      for (int e = 0; e < E1; ++e) {
+        kmin = min(kmin, gk[e] ? gk[e] : ~0u);
+        kmax = max(kmax, gk[e]);
+      }
+      block_minmax(kmin, kmax, L.s);  // barrier
+      const float vmin = key_value(kmin), vmax = key_value(kmax);
+      const float span = vmax - vmin;
+      const float scale = (float)kSelBins / span;
+      cold = !(isfinite(vmin) && isfinite(vmax) && span > 0.0f && isfinite(span) &&
+               isfinite(scale));
+      WavePick p{0u, 0u, 0u, false};
+      uint32_t bn[E1];
+      if (!cold) {
 #pragma unroll
         for (int e = 0; e < E1; ++e) {
           const uint32_t k = gk[e];
-          const uint32_t bn = (uint32_t)min(kSelBins - 1, (int)((key_value(k) - vmin) * scale));
-          atomicAdd(&L.hist1[k ? bn : spare], 1u);
-        }
-        __syncthreads();  // barrier 2
-        const WavePick p = wave_pick(L.hist1, (uint32_t)bh);
-        pbin = p.bin;
-        stream = !p.ok || p.above + p.count > (uint32_t)kCapGroups;
-      } else {
-        stream = true;  // one score value, or non-finite ones
-      }
-    } else {
-      stream = ng > kCapGroups;
-    }
-    if (!stream) {
-      // The surviving groups, ascending, into L.grp (barriers 3, 4).
-      // kp: the smallest surviving group maximum (its wave minima ride along
-      // with the compaction's barriers).  Every token >= tau has a key >= kp.
-      uint32_t m4[E1 / 4], off[E1 / 4];
-      uint32_t kmine = ~0u;
-#pragma unroll
-      for (int g = 0; g < E1 / 4; ++g) {
-        m4[g] = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t k = gk[4 * g + e];
-          const bool in =
-              k != 0u && (!filter || min(kSelBins - 1, (int)((key_value(k) - vmin) * scale)) >=
-                                         (int)pbin);
-          m4[g] |= (in ? 1u : 0u) << e;
-          kmine = in ? min(kmine, k) : kmine;
-        }
-      }
-      {
-        uint32_t unused = 0u;
-        wave_minmax(kmine, unused);
-        if (lane_id() == 0) L.kpmin[t / kWave] = kmine;
-      }
-      const uint32_t ns = ordered_offsets<NT>(m4, off, L.s);
-#pragma unroll
-      for (int g = 0; g < E1 / 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if ((m4[g] >> e) & 1u) {
-            if (off[g] < (uint32_t)kCapGroups) L.grp[off[g]] = 4 * (g * NT + t) + e;
-            ++off[g];
-          }
-      __syncthreads();
-      uint32_t kp = 1u;  // rows kept whole: every token in play
-      if (filter) {
-        kp = ~0u;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) kp = min(kp, L.kpmin[w]);
-      }
-
-      // 2. The survivors' scores: thread t holds half of list entry
-      // (s NT + t) / 2 in slab s.  Keys below kp are out of play.
-      SurvivorSrc<E2> src;
-      {
-        const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(row_scores, ((n + 3) & ~3) * 4);
-        float4 sv[E2 / 4];
-#pragma unroll
-        for (int s = 0; s < E2 / 4; ++s) {
-          const uint32_t li = (uint32_t)(s * NT + t) / 2;
-          const int g = li < ns ? L.grp[li] : 0;
-          src.g[s] = g;
-          const uint32_t at = li < ns ? (uint32_t)(g * kGroupTokens + 4 * (t & 1)) * 4u
-                                      : 0xfffffff0u;  // past the range: reads zeros
-          const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, at, 0, 0);
-          sv[s] = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]),
-                              __uint_as_float(x[2]), __uint_as_float(x[3]));
-        }
-#pragma unroll
-        for (int s = 0; s < E2 / 4; ++s) {
-          const bool slab = (uint32_t)(s * NT + t) / 2 < ns;
-          const int p0 = src.g[s] * kGroupTokens + 4 * (t & 1);
-          const float f[4] = {sv[s].x, sv[s].y, sv[s].z, sv[s].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t k0 = score_key(f[e]);
-            const uint32_t k = k0 ? k0 : 1u;
-            src.k[4 * s + e] = (slab && p0 + e < n && k >= kp) ? k : 0u;
-          }
-        }
-      }
-      // Exact tau among the keys in play (all in [kp, kmax], a narrow range
-      // near the top of the row): 1024 bins of 2^sh2 keys from kp
-      // (barrier 5), each wave picks the pivot bin, its elements are
-      // gathered (barrier 6) and ranked by each wave (or refined in LDS when
-      // there are many).  Rows kept whole take the score-linear select.
-      auto shift_for = [](uint32_t sp) {  // smallest shift fitting sp into the bins
-        return sp < (uint32_t)kSelBins ? 0 : 32 - (int)__clz(sp) - kSelBits;
-      };
-      const int sh2 = shift_for(kmax - kp);
-      WavePick p2{0u, 0u, 0u, false};
-      if (filter) {
-#pragma unroll
-        for (int e = 0; e < E2; ++e) {
-          const uint32_t k = src.k[e];
-          atomicAdd(&L.hist2[k ? (k - kp) >> sh2 : spare], 1u);
+          bn[e] = (uint32_t)min(kSelBins - 1, (int)((key_value(k) - vmin) * scale));
+          if (k) atomicAdd(&L.hist1[bn[e]], 1u);
         }
         __syncthreads();
-        p2 = wave_pick(L.hist2, (uint32_t)bh);
+        p = wave_pick(L.hist1, (uint32_t)bh);
+        cold = !p.ok || p.above + p.count > (uint32_t)kCapGroups;
       }
-      uint64_t tau = 0;
-      if (!filter) {
-        tau = adaptive_select<NT, E2>(src, (uint32_t)bh, L.s);
-        emit_ordered<E2, NT>(src, tau, (uint32_t)bh, L.s, [&](uint32_t r, int e) {
-          const int pos = src.pos(e);
-          if (o) o[r] = pos;
-          L.sel[r] = pos;
-        });
-      } else if (!p2.ok) {
-        // Fewer in play than bh: never with consistent group maxima.
-        if (t == 0) raise_flag(err, FASA_DEVFLAG_SELECT);
-        stream = true;
-      } else {
-        const uint32_t need = (uint32_t)bh - p2.above;
-        const uint32_t blo = kp + (p2.bin << sh2);
-        const uint32_t bhi = blo + ((1u << sh2) - 1u);  // same bin <=> key in [blo, bhi]
-        const uint64_t clo = (uint64_t)blo << 32, chi = ((uint64_t)bhi << 32) | 0xffffffffull;
-        if (p2.count <= (uint32_t)kFilterCandCap) {
-          const uint32_t M = gather_cand<NT, E2>(src, [&](int e) {
-            return src.k[e] >= blo && src.k[e] <= bhi;
-          }, L.s);
-          tau = M <= (uint32_t)kWave ? wave_rank(L.s.cand, M, need)
-                                     : refine<NT, E2>(src, need, clo, chi, true, M, L.s);
-        } else {
-          // A pivot bin larger than the LDS gather (ties, or short rows kept
-          // whole): refinement passes over the registers.
-          tau = refine<NT, E2>(src, need, clo, chi, false, 0u, L.s);
+      if (!cold) {
+        // The surviving groups, ascending, into L.grp; kp, the smallest
+        // surviving maximum (its wave minima ride along with the barriers).
+        uint32_t m4[E1 / 4], off[E1 / 4];
+        uint32_t kmine = ~0u;
+#pragma unroll
+        for (int g = 0; g < E1 / 4; ++g) {
+          m4[g] = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool in = gk[4 * g + e] != 0u && bn[4 * g + e] >= p.bin;
+            m4[g] |= (in ? 1u : 0u) << e;
+            kmine = in ? min(kmine, gk[4 * g + e]) : kmine;
+          }
         }
-        emit_ordered<E2, NT>(src, tau, (uint32_t)bh, L.s, [&](uint32_t r, int e) {
-          const int pos = src.pos(e);
-          if (o) o[r] = pos;
-          L.sel[r] = pos;
-        });
+        kmine = wave_min_u32(kmine);
+        if (lane == 0) L.kpmin[wave] = kmine;
+        const uint32_t ns = ordered_offsets_tab<NT>(m4, off, L.slab_g);
+#pragma unroll
+        for (int g = 0; g < E1 / 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if ((m4[g] >> e) & 1u) L.grp[off[g]++] = 4 * (g * NT + t) + e;
+        __syncthreads();
+        uint32_t kp = ~0u;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) kp = min(kp, L.kpmin[w]);
+
+        // 2. The survivors' scores: slab s of thread t holds the quarter
+        // t % 4 of list entry (s NT + t) / 4, so (slab, thread, element)
+        // order is position order.  Keys below kp are out of play.
+        uint32_t kk[E2];
+        int p0[E2 / 4];
+        {
+          const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(row_scores, ((n + 3) & ~3) * 4);
+          float4 sv[E2 / 4];
+#pragma unroll
+          for (int s = 0; s < E2 / 4; ++s) {
+            const uint32_t li = (uint32_t)(s * NT + t) / kGroupThreads;
+            const int g = li < ns ? L.grp[li] : 0;
+            p0[s] = g * kGroupTokens + 4 * (t % kGroupThreads);
+            const uint32_t at = li < ns ? (uint32_t)p0[s] * 4u : 0xfffffff0u;  // past: zeros
+            const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, at, 0, 0);
+            sv[s] = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]),
+                                __uint_as_float(x[2]), __uint_as_float(x[3]));
+          }
+#pragma unroll
+          for (int s = 0; s < E2 / 4; ++s) {
+            const bool slab = (uint32_t)(s * NT + t) / kGroupThreads < ns;
+            const float fv[4] = {sv[s].x, sv[s].y, sv[s].z, sv[s].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t k0 = score_key(fv[e]);
+              const uint32_t k = k0 ? k0 : 1u;
+              kk[4 * s + e] = (slab && p0[s] + e < n && k >= kp) ? k : 0u;
+            }
+          }
+        }
+        // The in-play tokens, in position order, into the list; their keys
+        // counted in 1024 bins of 2^sh2 keys from kp.
+        const int sh2 = bin_shift(kmax - kp);
+        uint32_t mp[E2 / 4], offp[E2 / 4];
+#pragma unroll
+        for (int s = 0; s < E2 / 4; ++s) {
+          mp[s] = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t k = kk[4 * s + e];
+            mp[s] |= (k ? 1u : 0u) << e;
+            if (k) atomicAdd(&L.hist2[(k - kp) >> sh2], 1u);
+          }
+        }
+        np = (int)ordered_offsets_tab<NT>(mp, offp, L.slab_p);  // barrier (hist2 complete)
+        cold = np > kPlayCap;
+        if (!cold) {
+#pragma unroll
+          for (int s = 0; s < E2 / 4; ++s)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if ((mp[s] >> e) & 1u) {
+                L.pos[offp[s]] = p0[s] + e;
+                L.key[offp[s]] = kk[4 * s + e];
+                ++offp[s];
+              }
+          __syncthreads();
+          // 3. The rows FAC will read go out now.
+          fac_issue_k(fac, 0, np, L.pos, K, kvbase);
+          fac_issue_v(fac, 0, np, L.pos, V, kvbase, part);
+          issued = true;
+          const WavePick p2 = wave_pick(L.hist2, (uint32_t)bh);
+          if (!p2.ok) {
+            // Fewer in play than bh: never with consistent group maxima.
+            if (t == 0) raise_flag(err, FASA_DEVFLAG_SELECT);
+            cold = true;
+          } else {
+            const uint32_t need = (uint32_t)bh - p2.above;
+            const uint32_t blo = kp + (p2.bin << sh2);
+            const uint64_t bend = (uint64_t)blo + ((1ull << sh2) - 1ull);
+            const uint32_t bhi = bend > 0xffffffffull ? 0xffffffffu : (uint32_t)bend;
+            if (p2.count == need) {
+              tau = (uint64_t)blo << 32;  // the whole pivot bin is taken
+            } else {
+              // The pivot bin's few elements, ranked by each wave.
+              for (int i = t; i < np; i += NT) {
+                const uint32_t k = L.key[i];
+                if (k >= blo && k <= bhi) {
+                  const uint32_t at = atomicAdd(&L.pivot_n, 1u);
+                  if (at < (uint32_t)kPivotCap) L.pivot[at] = composite(k, (uint32_t)L.pos[i]);
+                }
+              }
+              __syncthreads();
+              const uint32_t M = L.pivot_n;
+              if (M > (uint32_t)kPivotCap) cold = true;
+              else tau = wave_rank(L.pivot, M, need);
+            }
+          }
+        }
       }
     }
-    if (stream) {
-      // 3. Streaming passes over all of the row's composites.
+    if (cold) {
+      // 5. Streaming passes over all of the row's composites.
       __syncthreads();  // LDS of the steps above is reused
-      const uint64_t tau =
+      const uint64_t ts =
           stream_select(row_scores, n, (uint32_t)bh, 1ull << 32, ~0ull, L.s, err);
-      stream_emit(row_scores, n, tau, (uint32_t)bh, L.s, [&](uint32_t r, int pos) {
+      stream_emit(row_scores, n, ts, (uint32_t)bh, L.s, [&](uint32_t r, int pos) {
         if (o) o[r] = pos;
-        L.sel[r] = pos;
+        L.pos[r] = pos;
+        L.key[r] = 1u;
       });
+      np = take;
+      tau = 0;
+      issued = false;
+    } else if (o != nullptr) {
+      // idx: each listed entry's rank among the selected ones (the list is
+      // in position order); one barrier.
+      constexpr int CH = kPlayCap / NT;
+      uint32_t pre[CH];
+      bool sel[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int i = c * NT + t;
+        sel[c] = i < np && composite(L.key[i], (uint32_t)L.pos[i]) >= tau;
+        const uint64_t bal = __ballot(sel[c]);
+        pre[c] = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+        if (lane == 0) L.emit_cnt[c * NW + wave] = (uint32_t)__popcll(bal);
+      }
+      __syncthreads();
+      uint32_t before = 0;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        uint32_t mine = before;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const uint32_t cnt = L.emit_cnt[c * NW + w];
+          mine += w < wave ? cnt : 0u;
+          before += cnt;
+        }
+        if (sel[c] && mine + pre[c] < (uint32_t)bh) o[mine + pre[c]] = L.pos[c * NT + t];
+      }
     }
     if (o != nullptr)
       for (int j = bh + t; j < budget; j += NT) o[j] = -1;
@@ -541,12 +785,12 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
       for (int d = t; d < D; d += NT) out_row[d] = 0.0f;
     return;
   }
-  const size_t kvbase = ((size_t)b * hkv + h / G) * cap;
-  if constexpr (S > 1)
-    attend_rows_split<BF16, D, NW, S>(L.sel, take, k_cache, v_cache, qrot, row, kvbase, part,
-                                      out_row, L.att);
-  else
-    attend_rows<BF16, D, NW>(L.sel, take, k_cache, v_cache, qrot, row, kvbase, out_row, L.att);
+  // 4. FAC over the list.
+  if (!issued) {
+    fac_issue_k(fac, 0, np, L.pos, K, kvbase);
+    fac_issue_v(fac, 0, np, L.pos, V, kvbase, part);
+  }
+  fac_play<BF16, D, S>(fac, np, tau, K, V, kvbase, part, qrot + row * D, out_row, L);
 }
 
 bool filter_path_applies(int max_seq_len, int budget) {
@@ -559,11 +803,11 @@ bool filter_path_applies(int max_seq_len, int budget) {
 
 int filter_group_slots(int max_seq_len) {
   const int groups = (max_seq_len + kGroupTokens - 1) / kGroupTokens;
-  return groups <= 8 * kFilterThreads ? 8 : 40;
+  return groups <= 4 * kFilterThreads ? 4 : 20;
 }
 
 // Survivors are about B groups; the slots leave room for those in bin P.
-int filter_survivor_slots(int budget) { return budget <= 384 ? 8 : 24; }
+int filter_survivor_slots(int budget) { return budget <= 320 ? 12 : 40; }
 
 // Column parts of the fused FAC when the rows are few (as in select2.hip).
 constexpr int kFilterColumnParts = 4;
@@ -595,12 +839,12 @@ static void launch_filter_d(const fasa_ctx* c, hipStream_t s, const uint32_t* gm
 #define FASA_FILTER(E1V, E2V)                                                                 \
   launch_filter_t<BF16, D, E1V, E2V>(c, s, gm, scores, nb, max_seq_len, budget, hb, idx, k, v, \
                                      qrot, out, advance, err)
-  const bool short_rows = filter_group_slots(max_seq_len) == 8;
-  const bool few = filter_survivor_slots(budget) == 8;
+  const bool short_rows = filter_group_slots(max_seq_len) == 4;
+  const bool few = filter_survivor_slots(budget) == 12;
   if (short_rows) {
-    if (few) FASA_FILTER(8, 8); else FASA_FILTER(8, 24);
+    if (few) FASA_FILTER(4, 12); else FASA_FILTER(4, 40);
   } else {
-    if (few) FASA_FILTER(40, 8); else FASA_FILTER(40, 24);
+    if (few) FASA_FILTER(20, 12); else FASA_FILTER(20, 40);
   }
 #undef FASA_FILTER
 }

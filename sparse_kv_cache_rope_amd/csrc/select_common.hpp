@@ -368,9 +368,11 @@ __device__ __forceinline__ bool is_selected(const Src& src, int e, uint64_t tau)
 // wave w's count for slab s), and one scan over each slab's NW lanes (DPP
 // shifts, masked at the slab's edge) gives every wave its start in each
 // slab, read out with lane reads.
-template <int NT, int S, int COPIES, int CAP>
-__device__ __forceinline__ uint32_t ordered_offsets(const uint32_t (&sel)[S], uint32_t (&off)[S],
-                                                    RegSelectLds<NT, COPIES, CAP>& L) {
+//
+// `tab` is LDS of S * NT / 64 words (the (slab, wave) counts, slab-major).
+template <int NT, int S>
+__device__ __forceinline__ uint32_t ordered_offsets_tab(const uint32_t (&sel)[S],
+                                                        uint32_t (&off)[S], uint32_t* tab) {
   static_assert(S <= kMaxSlabs, "slab table size");
   constexpr int NW = NT / kWave;
   static_assert(NW == 8 || NW == 16, "a slab's counts fill part of one 16-lane row or all of it");
@@ -389,7 +391,7 @@ __device__ __forceinline__ uint32_t ordered_offsets(const uint32_t (&sel)[S], ui
       tot += (uint32_t)__popcll(bal);
     }
     pre[s] = p;
-    if (lane == 0) L.slab_cnt[s][wave] = tot;
+    if (lane == 0) tab[s * NW + wave] = tot;
   }
   __syncthreads();
   const int lw = lane % NW;
@@ -397,7 +399,7 @@ __device__ __forceinline__ uint32_t ordered_offsets(const uint32_t (&sel)[S], ui
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     const int i = g * kWave + lane;
-    uint32_t x = (i < S * NW) ? (&L.slab_cnt[0][0])[i] : 0u;
+    uint32_t x = (i < S * NW) ? tab[i] : 0u;
     uint32_t t;
     t = dpp_shr0<0x111>(x);  // row_shr:1
     x += (lw >= 1) ? t : 0u;
@@ -422,6 +424,13 @@ __device__ __forceinline__ uint32_t ordered_offsets(const uint32_t (&sel)[S], ui
     base += (uint32_t)__builtin_amdgcn_readlane((int)incl[g], l0 + NW - 1);
   }
   return base;
+}
+
+// ordered_offsets_tab with the scratch's slab table.
+template <int NT, int S, int COPIES, int CAP>
+__device__ __forceinline__ uint32_t ordered_offsets(const uint32_t (&sel)[S], uint32_t (&off)[S],
+                                                    RegSelectLds<NT, COPIES, CAP>& L) {
+  return ordered_offsets_tab<NT, S>(sel, off, &L.slab_cnt[0][0]);
 }
 
 }  // namespace fasa

@@ -43,7 +43,7 @@
 // new pairs into that position's lane instead.
 //
 // In a decode step whose selection is filtered, the launch also writes the
-// largest score key of every 8-token group, after the scores: the B-th
+// largest score key of every 16-token group, after the scores: the B-th
 // largest group maximum bounds the row's threshold from below (filter.hip).
 //
 // HBM-bound: 4 bytes per token and plane (bf16) against 4 G FMAs.
@@ -59,7 +59,7 @@ constexpr int kTipWaves = 4;
 constexpr int kTipThreads = kTipWaves * kWave;
 constexpr int kTipTokens = kWave * 4;  // tokens per workgroup
 constexpr int kMaxPlanes = 64;         // d/2 FCs at d = 128
-static_assert(kGroupTokens == 8, "a group is the 4 tokens of two neighbouring lanes");
+static_assert(kGroupTokens == 16, "a group is the 4 tokens of each lane of a quad");
 
 // The arguments needed first lead the list: the build preloads the first 16
 // dwords of kernel arguments into registers, which saves a dependent load
@@ -298,8 +298,8 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
         if (j + t < n) dst[t] = vv[t];
     }
     if (gmax != nullptr) {
-      // The largest score key of each kGroupTokens-token group: this lane's
-      // 4 tokens and its neighbour's (key 0 past n, >= 1 otherwise).
+      // The largest score key of each kGroupTokens-token group: the 4
+      // tokens of each lane of the quad (key 0 past n, >= 1 otherwise).
       const float vv[4] = {s.x, s.y, s.z, s.w};
       uint32_t km = 0u;
 #pragma unroll
@@ -307,10 +307,11 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
         const uint32_t kk = score_key(vv[t]);
         km = max(km, (j + t < n) ? (kk ? kk : 1u) : 0u);
       }
-      km = max(km, dpp_u32<0xB1>(km));  // quad_perm [1,0,3,2]: the neighbour lane
+      km = max(km, dpp_u32<0xB1>(km));  // quad_perm [1,0,3,2]
+      km = max(km, dpp_u32<0x4E>(km));  // quad_perm [2,3,0,1]: the quad's maximum
       // Only groups holding a token of the row: the row's gstride groups
       // end at the capacity, which a last tile may reach past.
-      if ((qd & 1) == 0 && j < n)
+      if ((qd & 3) == 0 && j < n)
         gmax[((size_t)b * hq + (size_t)g * G + hh) * gstride + (size_t)(j / kGroupTokens)] = km;
     }
   }

@@ -3,15 +3,18 @@ group maxima (gist.science/pt, "Resumo Tecnico" section 2, FAC first
 bullet: the critical subset is chosen from the TIP scores).
 
 On long rows with a fused budget, the TIP launch also writes the largest
-score of every 8 consecutive tokens, and one launch selects T_t and attends.
-The selection takes one of three routes, decided on the device per row:
-  "all"     rows of at most B groups keep every group, then select exactly;
-  "filter"  a histogram of the group maxima gives the bin of the B-th largest,
-            groups from that bin up are read again and selected exactly;
-  "stream"  when those would not fit (or every score is equal): streaming
-            passes over the row's scores.
-Each case names the routes it is meant to reach, and the test checks that
-with a host copy of the route decision on the GPU's own scores.
+score of every 16 consecutive tokens, and one launch selects T_t and attends.
+The selection takes one of two routes, decided on the device per row:
+  "filter"  a histogram of the group maxima gives the bin of the B-th largest;
+            groups from that bin up are read again, their tokens at or above
+            the smallest surviving maximum are listed, and a second histogram
+            of those (plus a rank of its pivot bin) gives T_t exactly;
+  "stream"  when those would not fit (at most B groups, every score equal,
+            too many survivors or listed tokens, a crowded pivot bin):
+            streaming passes over the row's scores.
+Rows of at most B tokens ("whole") keep every position.  Each case names the
+routes it is meant to reach, and the test checks that with a host copy of the
+route decision on the GPU's own scores.
 
 Checks per (sequence, query head):
 * index work, bit-exact: the step's T_t equals the oracle's selection rule
@@ -31,39 +34,76 @@ from fasa_harness import GpuSetup, check_index_set, check_out, oracle_setup, run
 
 pytestmark = pytest.mark.gpu
 
-GROUP = 8
+GROUP = 16
+PLAY_CAP = 2048   # in-play tokens the list holds
+PIVOT_CAP = 64    # pivot-bin elements one wave ranks
 
 
 def small(name, **kw):
     return W.shrink(W.get(name), **kw)
 
 
+def _keys(s):
+    """Order-preserving keys of fp32 scores as the kernels form them (-0 folded
+    onto +0; a key of 0, from NaN only, taken as 1)."""
+    u = np.asarray(s, np.float32).view(np.uint32).astype(np.uint64)
+    u = np.where((u << 1) & 0xFFFFFFFF == 0, 0, u)
+    k = np.where(u & 0x80000000, (~u) & 0xFFFFFFFF, u | 0x80000000)
+    return np.where(k == 0, 1, k).astype(np.uint64)
+
+
+def _key_value(k):
+    k = np.asarray(k, np.uint64)
+    bits = np.where(k & 0x80000000, k & 0x7FFFFFFF, (~k) & 0xFFFFFFFF)
+    return bits.astype(np.uint32).view(np.float32)
+
+
+def _pick(bins, nbins, budget):
+    """(bin, count above it, its count) of the budget-th largest, from the top."""
+    counts = np.bincount(bins, minlength=nbins)[::-1]
+    cum = counts.cumsum()
+    r = int(np.searchsorted(cum, budget))
+    return nbins - 1 - r, int(cum[r] - counts[r]), int(counts[r])
+
+
 def route(scores, budget):
     """The device's route for one row of fp32 scores at budget B (the
     decision described in the module docstring, in fp32 like the kernel):
-    "whole", "all", "filter" or "stream"."""
+    "whole", "filter" or "stream"."""
     s = np.asarray(scores, np.float32)
     n = s.size
     if n <= budget:
         return "whole"
     ng = -(-n // GROUP)
-    cap = 512 if budget <= 384 else 1536  # groups the survivor slots hold
     if ng <= budget:
-        return "all" if ng <= cap else "stream"
-    pad = np.full(ng * GROUP, -np.inf, np.float32)
-    pad[:n] = s
-    gm = pad.reshape(ng, GROUP).max(axis=1)
-    vmin, vmax = gm.min(), gm.max()
+        return "stream"
+    cap = 384 if budget <= 320 else 1280  # groups the survivor slots hold
+    k = np.zeros(ng * GROUP, np.uint64)
+    k[:n] = _keys(s)
+    gk = k.reshape(ng, GROUP).max(axis=1)
+    vmin, vmax = _key_value(gk.min()), _key_value(gk.max())
     span = np.float32(vmax - vmin)
-    if not (np.isfinite(span) and span > 0):
+    if not (np.isfinite(vmin) and np.isfinite(vmax) and np.isfinite(span) and span > 0):
         return "stream"
     scale = np.float32(1024) / span
     if not np.isfinite(scale):
         return "stream"
-    bins = np.minimum(1023, ((gm - vmin).astype(np.float32) * scale).astype(np.int64))
-    counts = np.bincount(bins, minlength=1024)[::-1].cumsum()
-    pbin = 1023 - int(np.searchsorted(counts, budget))
-    return "filter" if (bins >= pbin).sum() <= cap else "stream"
+    bins = np.minimum(1023, ((_key_value(gk) - vmin) * scale).astype(np.int64))
+    pbin, above, count = _pick(bins, 1024, budget)
+    surv = bins >= pbin
+    if above + count > cap:
+        return "stream"
+    kp = gk[surv].min()
+    play = k.reshape(ng, GROUP)[surv].ravel()
+    play = play[play >= kp]
+    if play.size > PLAY_CAP:
+        return "stream"
+    span2 = int(gk.max() - kp)
+    sh2 = 0 if span2 < 1024 else span2.bit_length() - 10
+    b2 = ((play - kp) >> np.uint64(sh2)).astype(np.int64)
+    _, above2, count2 = _pick(b2, 1024, budget)
+    need = budget - above2
+    return "filter" if count2 == need or count2 <= PIVOT_CAP else "stream"
 
 
 CASES = {
@@ -76,11 +116,10 @@ CASES = {
     "c5_70k": (small("c5", n_q_heads=8, n_kv_heads=2, context=70000), {"filter"}),
     # Ragged batch with short rows (at most B groups: every group kept).
     "ragged": (small("c3", batch=4, context=16000, context_min=900, budget=200),
-               {"filter", "all"}),
-    # Short ragged rows at B = 1000: rows of at most B groups keep every
-    # group, so the exact select sees thousands of keys in few bins.
+               {"filter", "stream"}),
+    # Ragged rows at B = 1000, all of at most B groups: streamed.
     "ragged_b1000": (small("c3", batch=3, context=16000, context_min=2500, budget=1000),
-                     {"filter", "all"}),
+                     {"filter", "stream"}),
     # One query head per KV head, and eight.
     "g1": (small("c3", batch=2, n_q_heads=8, n_kv_heads=8, context=12000, budget=150),
            {"filter"}),

@@ -83,17 +83,17 @@ def test_workload_layouts(n, budget, want):
 
 def test_decode_layout_filters_long_rows_with_fused_budgets():
     """A decode step selects through TIP's group maxima exactly when B <= 1024
-    and 8192 < n <= 163840 (at most 20480 groups of 8, 40 per thread of 512);
+    and 8192 < n <= 163840 (at most 10240 groups of 16, 20 per thread of 512);
     otherwise it uses the top-B layout fasa_select_layout reports."""
     # The 32k Llama-3-shaped layer and the 128k workload.
-    assert fasa.decode_layout(32768, 256) == ("group_filter", 512, 8, 8)
-    assert fasa.decode_layout(131072 + 31, 1024) == ("group_filter", 512, 40, 8)
+    assert fasa.decode_layout(32768, 256) == ("group_filter", 512, 4, 16)
+    assert fasa.decode_layout(131072 + 31, 1024) == ("group_filter", 512, 20, 16)
     for n, budget in [(8192, 256), (32768, 1025), (163841, 16), (8193, 0), (6000, 100),
                       (200000, 1024)]:
         assert fasa.decode_layout(n, budget) == fasa.select_layout(n, budget), (n, budget)
     for n in (8193, 9000, 20000, 32768, 32769, 65536, 131103, 163840):
         for budget in (1, 256, 1024):
             kind, threads, per, chunk = fasa.decode_layout(n, budget)
-            assert (kind, threads, chunk) == ("group_filter", 512, 8), (n, budget)
-            assert per == (8 if -(-n // 8) <= 4096 else 40)
-            assert threads * per >= -(-n // 8)
+            assert (kind, threads, chunk) == ("group_filter", 512, 16), (n, budget)
+            assert per == (4 if -(-n // 16) <= 2048 else 20)
+            assert threads * per >= -(-n // 16)
