@@ -16,20 +16,25 @@
 //      largest; every group whose maximum falls in bin P or above survives
 //      (about B groups), and kp, the smallest surviving maximum, is at most
 //      tau;
-//   2. the survivors' scores (16 each, 64 contiguous bytes) are gathered;
-//      those >= kp are "in play" and listed in position order in LDS, and a
-//      second histogram (keys from kp) counts them;
-//   3. the K and V rows of the in-play tokens are requested right away, so
-//      the gather overlaps the rest of the selection: the bin of the B-th
-//      largest in-play key gives tau at once when the whole bin is taken,
-//      else its few elements are ranked;
-//   4. FAC over the list, unselected entries masked: logits of every listed
-//      row, then the softmax max and denominator, then the weighted sum of
-//      V (two passes over LDS logits instead of an online merge);
+//   2. each wave reads the scores of the surviving groups it holds (group g
+//      belongs to thread g mod 512, so a run of groups spreads over all
+//      waves) and lists its tokens >= kp, "in play", in position order in
+//      its own part of LDS, with no barrier;
+//   3. each wave requests the K and V rows of its listed tokens at once, so
+//      the gathers overlap the rest of the selection, and counts the listed
+//      keys in a shared histogram (bins of keys from kp): the bin of the
+//      B-th largest in-play key gives tau at once when the whole bin is
+//      taken, else its few elements are ranked;
+//   4. FAC, each wave over its own list (entries below tau masked): logits,
+//      the wave's softmax max and sum, its weighted V sum, then one merge of
+//      the waves' states through LDS;
 //   5. rows this does not fit (fewer groups than B, one score value, more
 //      survivors or in-play tokens than the slots hold, a crowded pivot bin)
 //      are selected by streaming range refinement over their scores and an
-//      ordered streaming emit, then attended the same way.
+//      ordered streaming emit, then attended the same way (the list split
+//      evenly over the waves).
+// With idx requested, part 0 also ranks the selected entries of the waves'
+// sorted lists against each other to write T_t in position order.
 //
 // One 512-thread workgroup per row, or S per row for the FAC's column split
 // (each part makes the same selection and writes D / S output columns);
@@ -49,39 +54,41 @@ constexpr int kFilterWaves = kFilterThreads / kWave;
 // Streaming route: histogram copies and LDS candidates.
 constexpr int kFilterHistCopies = 4;
 constexpr int kFilterCandCap = 4096;
-// In-play tokens listed in LDS, and pivot-bin elements ranked by one wave.
-constexpr int kPlayCap = 2048;
+// In-play tokens a wave lists, and pivot-bin elements ranked by one wave.
+constexpr int kWavePlayCap = 512;
 constexpr int kPivotCap = kWave;
-// Threads per surviving group (a 16-byte score load each).
-constexpr int kGroupThreads = kGroupTokens / 4;
-// Most surviving groups: 40 survivor slots per thread.
-constexpr int kFilterMaxSurvivors = kFilterThreads * 40 / kGroupTokens;
-// FAC partial sums: up to 4 row slots per wave of D / S floats each.
-constexpr int kFacRedFloats = kFilterWaves * 4 * 128;
-static_assert(kPlayCap % kFilterThreads == 0, "emit chunks");
+// Lanes per surviving group (a 16-byte score load each).
+constexpr int kGroupLanes = kGroupTokens / 4;
+// Surviving groups a wave holds: 40 survivor slots per lane at most.
+constexpr int kWaveMaxSurvivors = kWave * 40 / kGroupTokens;
+// FAC partial sums: one state of D / S floats per wave.
+constexpr int kFacRedFloats = kFilterWaves * 128;
+static_assert(kFusedMaxBudget <= kFilterWaves * kWavePlayCap, "a streamed T_t fits the lists");
 
 using FilterSelLds = RegSelectLds<kFilterThreads, kFilterHistCopies, kFilterCandCap>;
 
 struct FilterLds {
   union {
-    FilterSelLds s;             // streaming route; block_minmax's wave extremes
-    float red[kFacRedFloats];   // FAC partial sums (after every select)
+    FilterSelLds s;           // streaming route; block_minmax's wave extremes
+    int32_t emit[kFilterWaves][kWavePlayCap];  // idx: each wave's selected positions
   };
   // Histograms of the group maxima and of the in-play keys, cleared at the
   // kernel's start (a spare word per lane past the bins, as in RegSelectLds).
   alignas(16) uint32_t hist1[kSelBins + kWave];
   alignas(16) uint32_t hist2[kSelBins + kWave];
-  int32_t grp[kFilterMaxSurvivors];  // surviving groups, ascending
-  // The list FAC reads: positions ascending, their keys, their logits.
-  int32_t pos[kPlayCap];
-  uint32_t key[kPlayCap];
-  float z[kPlayCap];
+  // Each wave's surviving groups and in-play list (positions ascending, their
+  // keys); a streamed or whole T_t lies flat over pos.
+  int32_t grp[kFilterWaves][kWaveMaxSurvivors];
+  int32_t pos[kFilterWaves * kWavePlayCap];
+  uint32_t key[kFilterWaves * kWavePlayCap];
+  float red[kFacRedFloats];  // FAC: the waves' partial sums
+  float zw[kFilterWaves][64];  // FAC: a wave's logits of one round
+  float mw[kFilterWaves], lw[kFilterWaves];
   uint64_t pivot[kPivotCap];
   uint32_t pivot_n;
-  uint32_t kpmin[kFilterWaves];  // per-wave smallest surviving group maximum
-  uint32_t slab_g[kMaxSlabs * kFilterWaves];
-  uint32_t slab_p[kMaxSlabs * kFilterWaves];
-  uint32_t emit_cnt[kPlayCap / kWave];
+  uint32_t kpmin[kFilterWaves];   // per-wave smallest surviving group maximum
+  uint32_t overflow;              // a wave's survivors or list did not fit
+  uint32_t emit_n[kFilterWaves];  // idx: each wave's selected count
 };
 
 struct WavePick {
@@ -289,63 +296,54 @@ __device__ __forceinline__ void stream_emit(const float* row, int n, uint64_t ta
   }
 }
 
-// ---- FAC over the in-play list ---------------------------------------------
+// ---- FAC over a wave's list ------------------------------------------------
 //
-// Rows r < np of the list (L.pos, L.key); a row takes part iff its composite
-// is >= tau.  Each of the S parts computes every logit (the softmax needs
-// them all) and the weighted V sum of its D / S columns.
-//
-// K: LPR lanes hold a row (RS rows per wave step); V: VL = LPR / S lanes hold
-// a row's column slice (RV rows per wave step).  A round of loads covers RK
-// rows of K and RVR rows of V; list slots past np load the list's last row
-// (fetched anyway) and count as absent.
+// A wave attends over its own list entries r < cnt (positions pos[r], keys
+// key[r]); an entry takes part iff its composite is >= tau.  K: LPR lanes
+// hold a row (RS rows per step); V: VL = LPR / S lanes hold the row's column
+// slice of this part (RV rows per step).  A round covers RR entries: their
+// logits (through the wave's LDS slot), the round's max, a rescale of the
+// wave's running state, and the weighted V sum.  Entries past cnt load the
+// list's last row (fetched anyway) and count as absent.
 template <bool BF16, int D, int S>
-struct PlayFac {
+struct WaveFac {
   using Geo = RowGeom<BF16, D>;
   static constexpr int LPR = Geo::LPR, EPL = Geo::EPL, RS = Geo::RS;
-  static constexpr int NW = kFilterWaves;
   static_assert(LPR % S == 0, "V slice lanes");
   static constexpr int VL = LPR / S;
   static constexpr int RV = kWave / VL;
-  static constexpr int cl(int x) { return x < 1 ? 1 : (x > 10 ? 10 : x); }
-  static constexpr int KST = cl(320 / (RS * NW));
-  static constexpr int VST = cl((320 + RV * NW - 1) / (RV * NW));
-  static constexpr int RK = RS * NW * KST;
-  static constexpr int RVR = RV * NW * VST;
-  // Row slots of a wave after the in-row V sums, and the floats they hold.
-  static constexpr int SLOTS = VL < 16 ? 4 : kWave / VL;
+  static constexpr int KST = (64 / RS) > 16 ? 16 : (64 / RS) < 1 ? 1 : (64 / RS);
+  static constexpr int RR = RS * KST;
+  static constexpr int VST = (RR + RV - 1) / RV;
+  static_assert(RR <= 64, "a round's logits fit the wave's LDS slot");
+  // Floats of a wave's state (this part's columns).
   static constexpr int W = D / S;
-  static_assert(NW * SLOTS * W <= kFacRedFloats, "partial sums");
+  static_assert(VL <= 32 && kFilterWaves * W <= kFacRedFloats, "partial sums");
   uint4 k[KST], v[VST];
 };
 
+// Issues round r0's K and V loads (cnt >= 1).
 template <class F>
-__device__ __forceinline__ void fac_issue_k(F& f, int r0, int np, const int32_t* pos,
-                                            const uint4* __restrict__ K, size_t kvbase) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int last = np - 1;
+__device__ __forceinline__ void fac_issue(F& f, int r0, int cnt, const int32_t* pos,
+                                          const uint4* __restrict__ K, const uint4* __restrict__ V,
+                                          size_t kvbase, int part) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int last = cnt - 1;
 #pragma unroll
   for (int s = 0; s < F::KST; ++s) {
-    const int r = r0 + (s * F::NW + wave) * F::RS + lane / F::LPR;
-    const int j = pos[r < np ? r : last];
+    const int r = r0 + s * F::RS + lane / F::LPR;
+    const int j = pos[r < cnt ? r : last];
     f.k[s] = K[(kvbase + (size_t)j) * F::LPR + lane % F::LPR];
   }
-}
-
-template <class F>
-__device__ __forceinline__ void fac_issue_v(F& f, int r0, int np, const int32_t* pos,
-                                            const uint4* __restrict__ V, size_t kvbase, int part) {
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int last = np - 1;
 #pragma unroll
   for (int s = 0; s < F::VST; ++s) {
-    const int r = r0 + (s * F::NW + wave) * F::RV + lane / F::VL;
-    const int j = pos[r < np ? r : last];
+    const int r = r0 + s * F::RV + lane / F::VL;
+    const int j = pos[r < cnt ? r : last];
     f.v[s] = V[(kvbase + (size_t)j) * F::LPR + part * F::VL + lane % F::VL];
   }
 }
 
-// bf16 pair of a float, round to nearest even (finite inputs).
+// bf16 bits of a float, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   const uint32_t u = __float_as_uint(x);
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
@@ -365,128 +363,200 @@ __device__ __forceinline__ float row_shr_add(float v) {
                  __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + SH, 0xf, 0xf, true));
 }
 
-// The query's part of a logit: q~ scaled to log2 units; for bf16 rows split
-// into a high and a low bf16 pair per two dims (q = hi + lo to about 2^-16),
-// so that each 16-byte K load takes EPL dot2 steps and no unpacking.
-template <bool BF16, int EPL>
+// The query's part of a logit: q~ scaled to log2 units; for bf16 rows also
+// split into a high and a low bf16 pair per two dims (q = hi + lo to about
+// 2^-16), so a 16-byte K load takes EPL dot2 steps and no unpacking.
+template <int EPL>
 struct FacQuery {
   float q[EPL];
   uint32_t hi[EPL / 2], lo[EPL / 2];
 };
 
+// This lane's EPL query values (its 16-byte column chunk of a K row), loaded
+// at the kernel's start so that FAC never waits for them.
+template <bool BF16, int D>
+struct QueryRaw {
+  float4 v[RowGeom<BF16, D>::EPL / 4];
+};
+
+template <bool BF16, int D>
+__device__ __forceinline__ QueryRaw<BF16, D> load_query(const float* __restrict__ qrow) {
+  constexpr int LPR = RowGeom<BF16, D>::LPR, EPL = RowGeom<BF16, D>::EPL;
+  QueryRaw<BF16, D> r;
+  const int sub = (threadIdx.x & (kWave - 1)) % LPR;
+  const float4* q4 = reinterpret_cast<const float4*>(qrow + sub * EPL);
+#pragma unroll
+  for (int i = 0; i < EPL / 4; ++i) r.v[i] = q4[i];
+  return r;
+}
+
+template <bool BF16, int D>
+__device__ __forceinline__ FacQuery<RowGeom<BF16, D>::EPL> fac_query(const QueryRaw<BF16, D>& raw) {
+  constexpr int EPL = RowGeom<BF16, D>::EPL;
+  FacQuery<EPL> qq;
+  const float scale = logit_scale<D>();
+#pragma unroll
+  for (int i = 0; i < EPL / 4; ++i) {
+    qq.q[4 * i] = raw.v[i].x * scale;
+    qq.q[4 * i + 1] = raw.v[i].y * scale;
+    qq.q[4 * i + 2] = raw.v[i].z * scale;
+    qq.q[4 * i + 3] = raw.v[i].w * scale;
+  }
+  if constexpr (BF16) {
+#pragma unroll
+    for (int i = 0; i < EPL / 2; ++i) {
+      const uint32_t h0 = f32_to_bf16_bits(qq.q[2 * i]), h1 = f32_to_bf16_bits(qq.q[2 * i + 1]);
+      const uint32_t l0 = f32_to_bf16_bits(qq.q[2 * i] - __uint_as_float(h0 << 16));
+      const uint32_t l1 = f32_to_bf16_bits(qq.q[2 * i + 1] - __uint_as_float(h1 << 16));
+      qq.hi[i] = h0 | (h1 << 16);
+      qq.lo[i] = l0 | (l1 << 16);
+    }
+  }
+  return qq;
+}
+
+// The wave's online-softmax state over its list.
+template <int EPL>
+struct WaveSoft {
+  float m, l, acc[EPL];
+};
+
+// One round: logits of entries r0 .. r0 + RR - 1, then their weighted V.
+// The KST dot products are independent chains (so they interleave), their
+// group sums likewise; lane i then masks entry r0 + i (past cnt, or below
+// tau) and the masked logits go back through the wave's LDS slot.
 template <class F, class Q>
-__device__ __forceinline__ void fac_logits(const F& f, const Q& qq, int r0, int np, uint64_t tau,
-                                           FilterLds& L) {
-  using Geo = typename F::Geo;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+__device__ __forceinline__ void fac_round(const F& f, const Q& qq, int r0, int cnt,
+                                          const int32_t* pos, const uint32_t* key, uint64_t tau,
+                                          float* zw, WaveSoft<F::EPL>& st) {
+  constexpr int LPR = F::LPR, EPL = F::EPL, VL = F::VL;
+  const int lane = threadIdx.x & (kWave - 1);
+  float d[F::KST];
 #pragma unroll
   for (int s = 0; s < F::KST; ++s) {
     const uint4 x = f.k[s];
-    float dot = 0.0f;
-    if constexpr (Geo::ES == 2) {
+    if constexpr (F::Geo::ES == 2) {
       const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+      float a = 0.0f, c = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        dot = dot2_bf16(w[i], qq.hi[i], dot);
-        dot = dot2_bf16(w[i], qq.lo[i], dot);
+        a = dot2_bf16(w[i], qq.hi[i], a);
+        c = dot2_bf16(w[i], qq.lo[i], c);
       }
+      d[s] = a + c;
     } else {
-      const float kf[4] = {__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
-                           __uint_as_float(x.w)};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dot = fmaf(qq.q[e], kf[e], dot);
-    }
-    dot = group_sum<F::LPR>(dot);
-    const int r = r0 + (s * F::NW + wave) * F::RS + lane / F::LPR;
-    if (lane % F::LPR == 0 && r < np) {
-      const bool in = composite(L.key[r], (uint32_t)L.pos[r]) >= tau;
-      L.z[r] = in ? dot : -INFINITY;
+      d[s] = fmaf(qq.q[0], __uint_as_float(x.x), qq.q[1] * __uint_as_float(x.y)) +
+             fmaf(qq.q[2], __uint_as_float(x.z), qq.q[3] * __uint_as_float(x.w));
     }
   }
+#pragma unroll
+  for (int s = 0; s < F::KST; ++s) d[s] = group_sum<LPR>(d[s]);
+  if (lane % LPR == 0) {
+#pragma unroll
+    for (int s = 0; s < F::KST; ++s) zw[s * F::RS + lane / LPR] = d[s];
+  }
+  // The wave reads back what its own lanes wrote (LDS keeps a wave's
+  // accesses in order); the barrier only stops the compiler moving them.
+  __builtin_amdgcn_wave_barrier();
+  float zl = -INFINITY;
+  {
+    const int r = r0 + lane;
+    if (lane < F::RR && r < cnt && composite(key[r], (uint32_t)pos[r]) >= tau) zl = zw[lane];
+  }
+  const float mr = wave_max(zl);
+  const float mn = fmaxf(st.m, mr);
+  if (mn == -INFINITY) return;  // nothing selected yet (wave-uniform)
+  __builtin_amdgcn_wave_barrier();
+  if (lane < F::RR) zw[lane] = zl;
+  __builtin_amdgcn_wave_barrier();
+  const float sc = exp2f(st.m - mn);  // m = -inf gives 0
+  st.l *= sc;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) st.acc[e] *= sc;
+  st.m = mn;
+#pragma unroll
+  for (int s = 0; s < F::VST; ++s) {
+    const int rr = s * F::RV + lane / VL;
+    const float z = rr < F::RR ? zw[rr < F::RR ? rr : 0] : -INFINITY;
+    const float p = exp2f(z - mn);  // -inf gives 0
+    float vf[EPL];
+    unpack<F::Geo::ES == 2, EPL>(f.v[s], vf);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) st.acc[e] = fmaf(p, vf[e], st.acc[e]);
+    if (lane % VL == 0) st.l += p;
+  }
+  __builtin_amdgcn_wave_barrier();  // zw is rewritten next round
 }
 
-// FAC over the list (loads of the first round already issued in f), this
-// part's columns written to out_row.  Two barriers; reads L.pos, L.key.
+// FAC of a wave over its list (the first round's loads already in f when
+// `issued`), its state left in L.red / L.mw / L.lw for fac_merge.
 template <bool BF16, int D, int S>
-__device__ __forceinline__ void fac_play(PlayFac<BF16, D, S>& f, int np, uint64_t tau,
+__device__ __forceinline__ void fac_wave(WaveFac<BF16, D, S>& f, bool issued, int cnt,
+                                         const int32_t* pos, const uint32_t* key, uint64_t tau,
                                          const uint4* __restrict__ K, const uint4* __restrict__ V,
-                                         size_t kvbase, int part, const float* __restrict__ qrow,
-                                         float* __restrict__ out_row, FilterLds& L) {
-  using F = PlayFac<BF16, D, S>;
-  constexpr int LPR = F::LPR, EPL = F::EPL, VL = F::VL;
-  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
-  FacQuery<BF16, EPL> qq;
-  {
-    const float scale = logit_scale<D>();
-    const int sub = lane % LPR;
+                                         size_t kvbase, int part,
+                                         const QueryRaw<BF16, D>& qraw, FilterLds& L) {
+  using F = WaveFac<BF16, D, S>;
+  constexpr int EPL = F::EPL, VL = F::VL;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const auto qq = fac_query<BF16, D>(qraw);
+  WaveSoft<EPL> st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qq.q[e] = qrow[sub * EPL + e] * scale;
-    if constexpr (BF16) {
-#pragma unroll
-      for (int i = 0; i < EPL / 2; ++i) {
-        const uint32_t h0 = f32_to_bf16_bits(qq.q[2 * i]), h1 = f32_to_bf16_bits(qq.q[2 * i + 1]);
-        const uint32_t l0 = f32_to_bf16_bits(qq.q[2 * i] - __uint_as_float(h0 << 16));
-        const uint32_t l1 = f32_to_bf16_bits(qq.q[2 * i + 1] - __uint_as_float(h1 << 16));
-        qq.hi[i] = h0 | (h1 << 16);
-        qq.lo[i] = l0 | (l1 << 16);
-      }
-    }
-  }
-  // Logits, round by round (the first round's K is in flight already).
-  fac_logits(f, qq, 0, np, tau, L);
-  for (int r0 = F::RK; r0 < np; r0 += F::RK) {
-    fac_issue_k(f, r0, np, L.pos, K, kvbase);
-    fac_logits(f, qq, r0, np, tau, L);
-  }
-  __syncthreads();
-  // Softmax max and denominator over the list, every wave on its own.
-  float m = -INFINITY;
-  for (int i = lane; i < np; i += kWave) m = fmaxf(m, L.z[i]);
-  m = wave_max(m);
-  float l = 0.0f;
-  for (int i = lane; i < np; i += kWave) l += exp2f(L.z[i] - m);  // -inf gives 0
-  l = group_sum<kWave>(l);
-  // Weighted V sum of this part's columns.
-  float acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-  for (int r0 = 0; r0 < np; r0 += F::RVR) {
-    if (r0 > 0) fac_issue_v(f, r0, np, L.pos, V, kvbase, part);
-#pragma unroll
-    for (int s = 0; s < F::VST; ++s) {
-      const int r = r0 + (s * F::NW + wave) * F::RV + lane / VL;
-      const float p = r < np ? exp2f(L.z[r] - m) : 0.0f;
-      float vf[EPL];
-      unpack<BF16, EPL>(f.v[s], vf);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
-    }
+  for (int e = 0; e < EPL; ++e) st.acc[e] = 0.0f;
+  float* zw = L.zw[wave];
+  for (int r0 = 0; r0 < cnt; r0 += F::RR) {
+    if (r0 > 0 || !issued) fac_issue(f, r0, cnt, pos, K, V, kvbase, part);
+    fac_round(f, qq, r0, cnt, pos, key, tau, zw, st);
   }
   // Sum over the row slots holding the same slice: within 16-lane rows by
-  // DPP, then the waves' rows through LDS.
+  // DPP, the rows and waves through LDS.
   if constexpr (VL < 16) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      if constexpr (VL <= 1) acc[e] = row_shr_add<1>(acc[e]);
-      if constexpr (VL <= 2) acc[e] = row_shr_add<2>(acc[e]);
-      if constexpr (VL <= 4) acc[e] = row_shr_add<4>(acc[e]);
-      acc[e] = row_shr_add<8>(acc[e]);
+      if constexpr (VL <= 1) st.acc[e] = row_shr_add<1>(st.acc[e]);
+      if constexpr (VL <= 2) st.acc[e] = row_shr_add<2>(st.acc[e]);
+      if constexpr (VL <= 4) st.acc[e] = row_shr_add<4>(st.acc[e]);
+      st.acc[e] = row_shr_add<8>(st.acc[e]);
     }
   }
-  const bool holder = VL < 16 ? (lane & 15) >= 16 - VL : true;
-  const int slot = VL < 16 ? lane >> 4 : lane / VL;
-  if (holder) {
+  // Then across the wave's rows of 16 lanes (lane l meets l ^ 16, l ^ 32):
+  // lanes 48 .. 63 end with the wave's sums, slice l % VL in lane l.
 #pragma unroll
-    for (int e = 0; e < EPL; ++e)
-      L.red[(wave * F::SLOTS + slot) * F::W + (lane % VL) * EPL + e] = acc[e];
+  for (int e = 0; e < EPL; ++e) st.acc[e] += __shfl_xor(st.acc[e], 32);
+  if constexpr (VL <= 16) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) st.acc[e] += __shfl_xor(st.acc[e], 16);
   }
-  __syncthreads();
-  if (t < F::W) {
-    float sum = 0.0f;
-#pragma unroll 8
-    for (int st = 0; st < F::NW * F::SLOTS; ++st) sum += L.red[st * F::W + t];
-    out_row[part * F::W + t] = l > 0.0f ? sum / l : 0.0f;
+  if (lane >= kWave - VL) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) L.red[wave * F::W + (lane % VL) * EPL + e] = st.acc[e];
   }
+  const float l = group_sum<kWave>(st.l);
+  if (lane == 0) {
+    L.mw[wave] = st.m;
+    L.lw[wave] = l;
+  }
+}
+
+// The waves' states merged (after a barrier): this part's columns.
+template <bool BF16, int D, int S>
+__device__ __forceinline__ void fac_merge(float* __restrict__ out_row, int part, FilterLds& L) {
+  using F = WaveFac<BF16, D, S>;
+  const int t = threadIdx.x;
+  if (t >= F::W) return;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kFilterWaves; ++w) mx = fmaxf(mx, L.mw[w]);
+  float lsum = 0.0f, sum = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kFilterWaves; ++w) {
+    const float wt = mx == -INFINITY ? 0.0f : exp2f(L.mw[w] - mx);  // m = -inf gives 0
+    sum = fmaf(L.red[w * F::W + t], wt, sum);
+    lsum = fmaf(L.lw[w], wt, lsum);
+  }
+  out_row[part * F::W + t] = lsum > 0.0f ? sum / lsum : 0.0f;
 }
 
 // Smallest shift that fits [0, sp] into the histogram's bins.
@@ -500,10 +570,26 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return v;
 }
 
+__device__ __forceinline__ uint32_t lanes_below_count(uint64_t bal) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+}
+
+// Entries of a sorted list a[0 .. n) below v.
+__device__ __forceinline__ uint32_t lower_bound_lds(const int32_t* a, uint32_t n, int32_t v) {
+  uint32_t lo = 0, hi = n;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (a[mid] < v) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
 // T_t of row (b, h) from the group maxima (see the file comment), written to
 // idx (part 0, if given) and attended (FAC) by every part for its columns.
 // E1 group maxima per thread (E1 NT >= the row's groups), E2 survivor slots
-// per thread (E2 NT / 16 groups).
+// per lane (a wave holds E2 * 64 / 16 surviving groups).
 template <bool BF16, int D, int E1, int E2, int S>
 __global__ void __launch_bounds__(kFilterThreads)
 filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
@@ -515,11 +601,9 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
                      int32_t* __restrict__ advance, uint32_t* err) {
   constexpr int NT = kFilterThreads;
   constexpr int NW = kFilterWaves;
-  constexpr int kCapGroups = E2 * NT / kGroupTokens;
-  static_assert(kCapGroups <= kFilterMaxSurvivors, "survivor list");
-  static_assert(E1 % 4 == 0 && E1 / 4 <= kMaxSlabs && E2 % 4 == 0 && E2 / 4 <= kMaxSlabs,
-                "slabs");
-  using F = PlayFac<BF16, D, S>;
+  constexpr int kCapW = E2 * kWave / kGroupTokens;  // surviving groups a wave holds
+  static_assert(kCapW <= kWaveMaxSurvivors && E2 % 4 == 0, "survivor slots");
+  using F = WaveFac<BF16, D, S>;
   __shared__ FilterLds L;
   const int part = S > 1 ? (int)blockIdx.x / hq : 0;
   const int h = S > 1 ? (int)blockIdx.x % hq : (int)blockIdx.x, b = blockIdx.y;
@@ -527,22 +611,21 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
   const size_t row = (size_t)b * hq + h;
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
 
-  // The row's group maxima go out before n_b arrives (bounded by the
-  // launch's longest row); groups past the row's own length are masked once
-  // it is known.
+  // The row's group maxima (group g at thread g % NT, slot g / NT) go out
+  // before n_b arrives (bounded by the launch's longest row); groups past the
+  // row's own length are masked once it is known.
   const int groups_max = (min(max_seq_len, cap) + kGroupTokens - 1) / kGroupTokens;
-  uint4 graw[E1 / 4];
+  uint32_t graw[E1];
   {
     const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(gmax + row * (size_t)gstride, groups_max * 4);
 #pragma unroll
-    for (int g = 0; g < E1 / 4; ++g) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(4 * (g * NT + t)) * 4u,
-                                                           0, 0);
-      graw[g] = make_uint4(x[0], x[1], x[2], x[3]);
-    }
+    for (int e = 0; e < E1; ++e)
+      graw[e] = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(e * NT + t) * 4u, 0, 0);
   }
-  // Both histograms and the pivot counter are cleared while the loads fly
-  // (the first barrier below orders that before any count).
+  // This lane's query values for FAC (written by TIP for this row).
+  const QueryRaw<BF16, D> qraw = load_query<BF16, D>(qrot + row * D);
+  // Both histograms and the counters are cleared while the loads fly (the
+  // first barrier below orders that before any count).
   {
     uint4* h1 = reinterpret_cast<uint4*>(L.hist1);
     uint4* h2 = reinterpret_cast<uint4*>(L.hist2);
@@ -550,7 +633,10 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
       h1[i] = make_uint4(0, 0, 0, 0);
       h2[i] = make_uint4(0, 0, 0, 0);
     }
-    if (t == 0) L.pivot_n = 0u;
+    if (t == 0) {
+      L.pivot_n = 0u;
+      L.overflow = 0u;
+    }
   }
   const int n = checked_len(nb, b, max_seq_len, cap, err, lead && h == 0 && t == 0);
   if (advance != nullptr && lead && h == 0 && t == 0 && n > 0) advance[b] = n;
@@ -563,10 +649,14 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
   const uint4* K = static_cast<const uint4*>(k_cache);
   const uint4* V = static_cast<const uint4*>(v_cache);
 
-  int np = take;      // entries of the list FAC reads
-  uint64_t tau = 0;   // an entry takes part <=> its composite >= tau
+  // This wave's list for FAC: cnt entries at lpos / lkey.
+  const int32_t* lpos = &L.pos[wave * kWavePlayCap];
+  const uint32_t* lkey = &L.key[wave * kWavePlayCap];
+  int cnt = 0;
+  uint64_t tau = 0;     // an entry takes part <=> its composite >= tau
   F fac;
   bool issued = false;  // the first round of FAC loads is in flight
+  bool listed = false;  // the waves' own lists hold the row's in-play tokens
   bool cold = false;    // the streaming route selects this row
 
   if (whole) {
@@ -584,11 +674,7 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
       // score over the maxima's range); groups at bin P or above survive.
       uint32_t gk[E1];
 #pragma unroll
-      for (int g = 0; g < E1 / 4; ++g) {
-        const uint32_t w4[4] = {graw[g].x, graw[g].y, graw[g].z, graw[g].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) gk[4 * g + e] = (4 * (g * NT + t) + e < ng) ? w4[e] : 0u;
-      }
+      for (int e = 0; e < E1; ++e) gk[e] = (e * NT + t < ng) ? graw[e] : 0u;
       uint32_t kmin = ~0u, kmax = 0u;
 #pragma unroll
       for (int e = 0; e < E1; ++e) {
@@ -612,97 +698,96 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
         }
         __syncthreads();
         p = wave_pick(L.hist1, (uint32_t)bh);
-        cold = !p.ok || p.above + p.count > (uint32_t)kCapGroups;
+        cold = !p.ok || p.above + p.count > (uint32_t)(NW * kCapW);
       }
       if (!cold) {
-        // The surviving groups, ascending, into L.grp; kp, the smallest
-        // surviving maximum (its wave minima ride along with the barriers).
-        uint32_t m4[E1 / 4], off[E1 / 4];
-        uint32_t kmine = ~0u;
+        // 2. This wave's surviving groups, ascending (slot-major, then
+        // lane), and the smallest surviving maximum of the wave.
+        uint32_t ns = 0, kmine = ~0u;
 #pragma unroll
-        for (int g = 0; g < E1 / 4; ++g) {
-          m4[g] = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bool in = gk[4 * g + e] != 0u && bn[4 * g + e] >= p.bin;
-            m4[g] |= (in ? 1u : 0u) << e;
-            kmine = in ? min(kmine, gk[4 * g + e]) : kmine;
-          }
+        for (int e = 0; e < E1; ++e) {
+          const bool in = gk[e] != 0u && bn[e] >= p.bin;
+          const uint64_t bal = __ballot(in);
+          const uint32_t at = ns + lanes_below_count(bal);
+          if (in && at < (uint32_t)kCapW) L.grp[wave][at] = e * NT + t;
+          ns += (uint32_t)__popcll(bal);
+          kmine = in ? min(kmine, gk[e]) : kmine;
         }
         kmine = wave_min_u32(kmine);
         if (lane == 0) L.kpmin[wave] = kmine;
-        const uint32_t ns = ordered_offsets_tab<NT>(m4, off, L.slab_g);
-#pragma unroll
-        for (int g = 0; g < E1 / 4; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if ((m4[g] >> e) & 1u) L.grp[off[g]++] = 4 * (g * NT + t) + e;
-        __syncthreads();
-        uint32_t kp = ~0u;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) kp = min(kp, L.kpmin[w]);
-
-        // 2. The survivors' scores: slab s of thread t holds the quarter
-        // t % 4 of list entry (s NT + t) / 4, so (slab, thread, element)
-        // order is position order.  Keys below kp are out of play.
-        uint32_t kk[E2];
+        bool ovf = ns > (uint32_t)kCapW;
+        const uint32_t nsw = ovf ? (uint32_t)kCapW : ns;
+        __builtin_amdgcn_wave_barrier();  // the wave reads back its own L.grp
+        // Their scores: slab s holds the wave's survivors 16 s .. 16 s + 15,
+        // 4 lanes each, so (slab, lane, element) order is position order.
+        float4 sv[E2 / 4];
         int p0[E2 / 4];
         {
           const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(row_scores, ((n + 3) & ~3) * 4);
-          float4 sv[E2 / 4];
 #pragma unroll
           for (int s = 0; s < E2 / 4; ++s) {
-            const uint32_t li = (uint32_t)(s * NT + t) / kGroupThreads;
-            const int g = li < ns ? L.grp[li] : 0;
-            p0[s] = g * kGroupTokens + 4 * (t % kGroupThreads);
-            const uint32_t at = li < ns ? (uint32_t)p0[s] * 4u : 0xfffffff0u;  // past: zeros
+            const uint32_t li = (uint32_t)(s * kWave + lane) / kGroupLanes;
+            const int g = li < nsw ? L.grp[wave][li] : 0;
+            p0[s] = li < nsw ? g * kGroupTokens + 4 * (lane % kGroupLanes) : -kGroupTokens;
+            const uint32_t at = li < nsw ? (uint32_t)p0[s] * 4u : 0xfffffff0u;  // past: zeros
             const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, at, 0, 0);
             sv[s] = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]),
                                 __uint_as_float(x[2]), __uint_as_float(x[3]));
           }
-#pragma unroll
-          for (int s = 0; s < E2 / 4; ++s) {
-            const bool slab = (uint32_t)(s * NT + t) / kGroupThreads < ns;
-            const float fv[4] = {sv[s].x, sv[s].y, sv[s].z, sv[s].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t k0 = score_key(fv[e]);
-              const uint32_t k = k0 ? k0 : 1u;
-              kk[4 * s + e] = (slab && p0[s] + e < n && k >= kp) ? k : 0u;
-            }
-          }
         }
-        // The in-play tokens, in position order, into the list; their keys
-        // counted in 1024 bins of 2^sh2 keys from kp.
+        __syncthreads();  // every wave's smallest surviving maximum
+        uint32_t kp = ~0u;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) kp = min(kp, L.kpmin[w]);
+        // The wave's tokens >= kp into its list, in position order; their
+        // keys counted in 1024 bins of 2^sh2 keys from kp.
         const int sh2 = bin_shift(kmax - kp);
-        uint32_t mp[E2 / 4], offp[E2 / 4];
+        int32_t* wpos = &L.pos[wave * kWavePlayCap];
+        uint32_t* wkey = &L.key[wave * kWavePlayCap];
 #pragma unroll
         for (int s = 0; s < E2 / 4; ++s) {
-          mp[s] = 0;
+          const float fv[4] = {sv[s].x, sv[s].y, sv[s].z, sv[s].w};
+          uint32_t kk[4];
+          uint64_t bal[4];
+          uint32_t below = 0, tot = 0;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t k = kk[4 * s + e];
-            mp[s] |= (k ? 1u : 0u) << e;
-            if (k) atomicAdd(&L.hist2[(k - kp) >> sh2], 1u);
+            const uint32_t k0 = score_key(fv[e]);
+            const uint32_t k = k0 ? k0 : 1u;
+            kk[e] = (p0[s] >= 0 && p0[s] + e < n && k >= kp) ? k : 0u;
+            bal[e] = __ballot(kk[e] != 0u);
+            below += lanes_below_count(bal[e]);  // this slab's entries of lower lanes
+            tot += (uint32_t)__popcll(bal[e]);
           }
-        }
-        np = (int)ordered_offsets_tab<NT>(mp, offp, L.slab_p);  // barrier (hist2 complete)
-        cold = np > kPlayCap;
-        if (!cold) {
+          // (slab, lane, element) order: lower lanes first, then this lane's
+          // elements in order.
+          uint32_t at = (uint32_t)cnt + below;
 #pragma unroll
-          for (int s = 0; s < E2 / 4; ++s)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if ((mp[s] >> e) & 1u) {
-                L.pos[offp[s]] = p0[s] + e;
-                L.key[offp[s]] = kk[4 * s + e];
-                ++offp[s];
+          for (int e = 0; e < 4; ++e)
+            if (kk[e]) {
+              if (at < (uint32_t)kWavePlayCap) {
+                wpos[at] = p0[s] + e;
+                wkey[at] = kk[e];
               }
-          __syncthreads();
-          // 3. The rows FAC will read go out now.
-          fac_issue_k(fac, 0, np, L.pos, K, kvbase);
-          fac_issue_v(fac, 0, np, L.pos, V, kvbase, part);
+              ++at;
+            }
+          cnt += (int)tot;
+        }
+        ovf = ovf || cnt > kWavePlayCap;
+        if (ovf && lane == 0) L.overflow = 1u;
+        // 3. The rows FAC will read go out now; then the list's keys are
+        // counted (one atomic per listed token).
+        __builtin_amdgcn_wave_barrier();  // the wave reads back its own list
+        if (!ovf && cnt > 0) {
+          fac_issue(fac, 0, cnt, wpos, K, V, kvbase, part);
           issued = true;
+        }
+        const int listed_n = min(cnt, kWavePlayCap);
+        for (int i = lane; i < listed_n; i += kWave)
+          atomicAdd(&L.hist2[(wkey[i] - kp) >> sh2], 1u);
+        __syncthreads();  // the histogram and the overflow flag are complete
+        cold = L.overflow != 0u;
+        if (!cold) {
           const WavePick p2 = wave_pick(L.hist2, (uint32_t)bh);
           if (!p2.ok) {
             // Fewer in play than bh: never with consistent group maxima.
@@ -717,11 +802,11 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
               tau = (uint64_t)blo << 32;  // the whole pivot bin is taken
             } else {
               // The pivot bin's few elements, ranked by each wave.
-              for (int i = t; i < np; i += NT) {
-                const uint32_t k = L.key[i];
+              for (int i = lane; i < cnt; i += kWave) {
+                const uint32_t k = wkey[i];
                 if (k >= blo && k <= bhi) {
                   const uint32_t at = atomicAdd(&L.pivot_n, 1u);
-                  if (at < (uint32_t)kPivotCap) L.pivot[at] = composite(k, (uint32_t)L.pos[i]);
+                  if (at < (uint32_t)kPivotCap) L.pivot[at] = composite(k, (uint32_t)wpos[i]);
                 }
               }
               __syncthreads();
@@ -731,10 +816,12 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
             }
           }
         }
+        listed = !cold;
       }
     }
     if (cold) {
-      // 5. Streaming passes over all of the row's composites.
+      // 5. Streaming passes over all of the row's composites; T_t lies flat
+      // over L.pos.
       __syncthreads();  // LDS of the steps above is reused
       const uint64_t ts =
           stream_select(row_scores, n, (uint32_t)bh, 1ull << 32, ~0ull, L.s, err);
@@ -743,54 +830,54 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
         L.pos[r] = pos;
         L.key[r] = 1u;
       });
-      np = take;
       tau = 0;
       issued = false;
-    } else if (o != nullptr) {
-      // idx: each listed entry's rank among the selected ones (the list is
-      // in position order); one barrier.
-      constexpr int CH = kPlayCap / NT;
-      uint32_t pre[CH];
-      bool sel[CH];
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int i = c * NT + t;
-        sel[c] = i < np && composite(L.key[i], (uint32_t)L.pos[i]) >= tau;
-        const uint64_t bal = __ballot(sel[c]);
-        pre[c] = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-        if (lane == 0) L.emit_cnt[c * NW + wave] = (uint32_t)__popcll(bal);
-      }
-      __syncthreads();
-      uint32_t before = 0;
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        uint32_t mine = before;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          const uint32_t cnt = L.emit_cnt[c * NW + w];
-          mine += w < wave ? cnt : 0u;
-          before += cnt;
-        }
-        if (sel[c] && mine + pre[c] < (uint32_t)bh) o[mine + pre[c]] = L.pos[c * NT + t];
-      }
     }
     if (o != nullptr)
       for (int j = bh + t; j < budget; j += NT) o[j] = -1;
   }
-  __syncthreads();
   float* out_row = out + row * D;
   if (take == 0) {
     if (lead)
       for (int d = t; d < D; d += NT) out_row[d] = 0.0f;
     return;
   }
-  // 4. FAC over the list.
-  if (!issued) {
-    fac_issue_k(fac, 0, np, L.pos, K, kvbase);
-    fac_issue_v(fac, 0, np, L.pos, V, kvbase, part);
+  if (!listed) {
+    // A whole or streamed T_t: wave w takes the w-th share of the flat list.
+    __syncthreads();
+    const int share = (take + NW - 1) / NW;
+    const int lo = wave * share;
+    cnt = max(0, min(take - lo, share));
+    lpos = &L.pos[lo];
+    lkey = &L.key[lo];
   }
-  fac_play<BF16, D, S>(fac, np, tau, K, V, kvbase, part, qrot + row * D, out_row, L);
+  // 4. FAC.
+  fac_wave<BF16, D, S>(fac, issued, cnt, lpos, lkey, tau, K, V, kvbase, part, qraw, L);
+  __syncthreads();
+  fac_merge<BF16, D, S>(out_row, part, L);
+
+  if (listed && o != nullptr) {
+    // idx: each wave's selected entries in its (sorted) list order, ranked
+    // against the other waves' by binary search.
+    uint32_t mine = 0;
+    for (int i0 = 0; i0 < cnt; i0 += kWave) {
+      const int i = i0 + lane;
+      const bool sel = i < cnt && composite(lkey[i], (uint32_t)lpos[i]) >= tau;
+      const uint64_t bal = __ballot(sel);
+      if (sel) L.emit[wave][mine + lanes_below_count(bal)] = lpos[i];
+      mine += (uint32_t)__popcll(bal);
+    }
+    if (lane == 0) L.emit_n[wave] = mine;
+    __syncthreads();
+    for (uint32_t i = lane; i < mine; i += kWave) {
+      const int32_t v = L.emit[wave][i];
+      uint32_t r = i;
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        if (w != wave) r += lower_bound_lds(L.emit[w], L.emit_n[w], v);
+      if (r < (uint32_t)bh) o[r] = v;
+    }
+  }
 }
 
 bool filter_path_applies(int max_seq_len, int budget) {
@@ -806,8 +893,9 @@ int filter_group_slots(int max_seq_len) {
   return groups <= 4 * kFilterThreads ? 4 : 20;
 }
 
-// Survivors are about B groups; the slots leave room for those in bin P.
-int filter_survivor_slots(int budget) { return budget <= 320 ? 12 : 40; }
+// Survivors are about B groups, about B / 8 per wave; the slots leave room for
+// those in bin P and for uneven waves.
+int filter_survivor_slots(int budget) { return budget <= 320 ? 16 : 40; }
 
 // Column parts of the fused FAC when the rows are few (as in select2.hip).
 constexpr int kFilterColumnParts = 4;
@@ -840,11 +928,11 @@ static void launch_filter_d(const fasa_ctx* c, hipStream_t s, const uint32_t* gm
   launch_filter_t<BF16, D, E1V, E2V>(c, s, gm, scores, nb, max_seq_len, budget, hb, idx, k, v, \
                                      qrot, out, advance, err)
   const bool short_rows = filter_group_slots(max_seq_len) == 4;
-  const bool few = filter_survivor_slots(budget) == 12;
+  const bool few = filter_survivor_slots(budget) == 16;
   if (short_rows) {
-    if (few) FASA_FILTER(4, 12); else FASA_FILTER(4, 40);
+    if (few) FASA_FILTER(4, 16); else FASA_FILTER(4, 40);
   } else {
-    if (few) FASA_FILTER(20, 12); else FASA_FILTER(20, 40);
+    if (few) FASA_FILTER(20, 16); else FASA_FILTER(20, 40);
   }
 #undef FASA_FILTER
 }

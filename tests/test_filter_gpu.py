@@ -35,8 +35,9 @@ from fasa_harness import GpuSetup, check_index_set, check_out, oracle_setup, run
 pytestmark = pytest.mark.gpu
 
 GROUP = 16
-PLAY_CAP = 2048   # in-play tokens the list holds
-PIVOT_CAP = 64    # pivot-bin elements one wave ranks
+THREADS, WAVES = 512, 8
+WAVE_PLAY_CAP = 512  # in-play tokens a wave lists
+PIVOT_CAP = 64       # pivot-bin elements one wave ranks
 
 
 def small(name, **kw):
@@ -77,7 +78,7 @@ def route(scores, budget):
     ng = -(-n // GROUP)
     if ng <= budget:
         return "stream"
-    cap = 384 if budget <= 320 else 1280  # groups the survivor slots hold
+    cap_w = 64 if budget <= 320 else 160  # surviving groups a wave holds
     k = np.zeros(ng * GROUP, np.uint64)
     k[:n] = _keys(s)
     gk = k.reshape(ng, GROUP).max(axis=1)
@@ -91,13 +92,18 @@ def route(scores, budget):
     bins = np.minimum(1023, ((_key_value(gk) - vmin) * scale).astype(np.int64))
     pbin, above, count = _pick(bins, 1024, budget)
     surv = bins >= pbin
-    if above + count > cap:
+    if above + count > WAVES * cap_w:
+        return "stream"
+    # Group g belongs to thread g % 512, so to wave (g % 512) // 64.
+    wave = (np.arange(ng) % THREADS) // (THREADS // WAVES)
+    if np.bincount(wave[surv], minlength=WAVES).max() > cap_w:
         return "stream"
     kp = gk[surv].min()
-    play = k.reshape(ng, GROUP)[surv].ravel()
-    play = play[play >= kp]
-    if play.size > PLAY_CAP:
+    tok = k.reshape(ng, GROUP)
+    in_play = (tok >= kp) & surv[:, None]
+    if np.bincount(wave, weights=in_play.sum(axis=1), minlength=WAVES).max() > WAVE_PLAY_CAP:
         return "stream"
+    play = tok[in_play]
     span2 = int(gk.max() - kp)
     sh2 = 0 if span2 < 1024 else span2.bit_length() - 10
     b2 = ((play - kp) >> np.uint64(sh2)).astype(np.int64)
@@ -110,11 +116,11 @@ CASES = {
     # 32k-layer shapes at 9k-20k tokens.
     "c2_20k": (small("c2", context=20000), {"filter"}),
     "c2_9k_b100": (small("c2", context=9000, budget=100), {"filter"}),
-    # Clustered planting (64-token spans), and rows past 4096 groups (40
-    # group maxima per thread), with B past 384 (the larger survivor slots).
+    # Clustered planting (64-token spans), and rows past 2048 groups (20
+    # group maxima per thread), with B past 320 (the larger survivor slots).
     "c5_40k": (small("c5", context=40000, budget=512, steps=2), {"filter"}),
     "c5_70k": (small("c5", n_q_heads=8, n_kv_heads=2, context=70000), {"filter"}),
-    # Ragged batch with short rows (at most B groups: every group kept).
+    # Ragged batch with short rows (at most B groups: streamed).
     "ragged": (small("c3", batch=4, context=16000, context_min=900, budget=200),
                {"filter", "stream"}),
     # Ragged rows at B = 1000, all of at most B groups: streamed.
@@ -128,6 +134,10 @@ CASES = {
     # bf16 at d = 64 and fp32 at d = 128.
     "d64": (small("c2", head_dim=64, context=20000, budget=256), {"filter"}),
     "f32": (small("c2", dtype="f32", context=10000, budget=128), {"filter"}),
+    # A 1024-token span of planted keys: about 64 surviving groups fall to
+    # one or two waves, past their slots, so the row is streamed.
+    "wave_crowd": (small("c5", n_q_heads=8, n_kv_heads=2, context=30000, budget=256,
+                         spans=(1, 1024), planted_count=1000), {"stream"}),
     # One 12288-token span of planted keys holding all of T_t.
     "one_span": (small("c5", n_q_heads=8, n_kv_heads=2, context=30000, budget=400,
                        spans=(1, 12288), planted_count=11000), {"filter"}),
