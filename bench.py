@@ -189,6 +189,17 @@ def fasa_m_timing(ctx, w, x, q, kn, vn, seq, seq_full, msl, reps, with_dense):
            "device_bytes_per_layer_fasa_c": ctx.sidecar_bytes + kv_bytes,
            "device_kv_compression": (ctx.sidecar_bytes + kv_bytes) / ctx.sidecar_bytes,
            "host_bytes_per_layer": kv_bytes}
+    # The link's yardstick: one streaming read pass over the host-resident K
+    # cache (large contiguous reads), next to the step's gather of scattered
+    # rows over the same link.
+    import sparse_kv_cache_rope_amd as fasa_lib
+    sink = torch.zeros(1, device=dev)
+    probe_ms = run(lambda: fasa_lib.read_probe(k, sink), 4)
+    k_bytes = k.numel() * es
+    res["host_link_read_probe_gbps"] = k_bytes / (probe_ms * 1e-3) / 1e9
+    res["host_link_read_probe_bytes"] = k_bytes
+    res["host_link_gather_frac_of_read_probe"] = (res["host_link_gbps"]
+                                                  / res["host_link_read_probe_gbps"])
     if with_dense:
         dense_out = torch.empty_like(out)
         res["dense_from_host_ms"] = run(

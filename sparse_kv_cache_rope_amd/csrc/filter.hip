@@ -33,8 +33,9 @@
 //      are selected by streaming range refinement over their scores and an
 //      ordered streaming emit, then attended the same way (the list split
 //      evenly over the waves).
-// With idx requested, part 0 also ranks the selected entries of the waves'
-// sorted lists against each other to write T_t in position order.
+// With idx requested, part 0 also writes T_t in position order: the waves'
+// runs of positions interleave in a fixed pattern, so per-(block, wave)
+// counts of the selected entries give every entry its rank.
 //
 // One 512-thread workgroup per row, or S per row for the FAC's column split
 // (each part makes the same selection and writes D / S output columns);
@@ -88,7 +89,10 @@ struct FilterLds {
   uint32_t pivot_n;
   uint32_t kpmin[kFilterWaves];   // per-wave smallest surviving group maximum
   uint32_t overflow;              // a wave's survivors or list did not fit
-  uint32_t emit_n[kFilterWaves];  // idx: each wave's selected count
+  // idx: selected tokens per (block of 512 groups, wave), then each one's
+  // first rank.
+  alignas(16) uint32_t emit_cnt[kFilterMaxGroups / kFilterThreads][kFilterWaves];
+  uint32_t emit_base[kFilterMaxGroups / kFilterThreads][kFilterWaves];
 };
 
 struct WavePick {
@@ -575,17 +579,6 @@ __device__ __forceinline__ uint32_t lanes_below_count(uint64_t bal) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
 }
 
-// Entries of a sorted list a[0 .. n) below v.
-__device__ __forceinline__ uint32_t lower_bound_lds(const int32_t* a, uint32_t n, int32_t v) {
-  uint32_t lo = 0, hi = n;
-  while (lo < hi) {
-    const uint32_t mid = (lo + hi) >> 1;
-    if (a[mid] < v) lo = mid + 1;
-    else hi = mid;
-  }
-  return lo;
-}
-
 // T_t of row (b, h) from the group maxima (see the file comment), written to
 // idx (part 0, if given) and attended (FAC) by every part for its columns.
 // E1 group maxima per thread (E1 NT >= the row's groups), E2 survivor slots
@@ -637,6 +630,8 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
       L.pivot_n = 0u;
       L.overflow = 0u;
     }
+    for (int i = t; i < kFilterMaxGroups / kFilterThreads * kFilterWaves; i += NT)
+      (&L.emit_cnt[0][0])[i] = 0u;
   }
   const int n = checked_len(nb, b, max_seq_len, cap, err, lead && h == 0 && t == 0);
   if (advance != nullptr && lead && h == 0 && t == 0 && n > 0) advance[b] = n;
@@ -857,26 +852,55 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
   fac_merge<BF16, D, S>(out_row, part, L);
 
   if (listed && o != nullptr) {
-    // idx: each wave's selected entries in its (sorted) list order, ranked
-    // against the other waves' by binary search.
+    // idx in position order.  Block k of 512 groups (8192 positions) holds,
+    // for wave w, the 1024 positions 8192 k + 1024 w ..: so T_t in position
+    // order is by (block, wave, position), and each wave's sorted list holds
+    // its blocks' entries one after another.  Count the selected entries per
+    // (block, wave), take first ranks from the counts, and rank each entry
+    // by its place among its wave's selected ones.
+    constexpr int NB = kFilterMaxGroups / kFilterThreads;
+    constexpr int kBlockPos = kFilterThreads * kGroupTokens;
+    constexpr int kWavePos = kWave * kGroupTokens;
     uint32_t mine = 0;
     for (int i0 = 0; i0 < cnt; i0 += kWave) {
       const int i = i0 + lane;
       const bool sel = i < cnt && composite(lkey[i], (uint32_t)lpos[i]) >= tau;
       const uint64_t bal = __ballot(sel);
-      if (sel) L.emit[wave][mine + lanes_below_count(bal)] = lpos[i];
+      if (sel) {
+        L.emit[wave][mine + lanes_below_count(bal)] = lpos[i];
+        atomicAdd(&L.emit_cnt[lpos[i] / kBlockPos][wave], 1u);
+      }
       mine += (uint32_t)__popcll(bal);
     }
-    if (lane == 0) L.emit_n[wave] = mine;
     __syncthreads();
+    {
+      // This wave's first rank in block k (lane k): the entries of earlier
+      // blocks not its own, plus those of lower waves in block k.
+      uint32_t x = 0, below = 0;
+      if (lane < NB) {
+        const uint4* c4 = reinterpret_cast<const uint4*>(L.emit_cnt[lane]);
+        const uint4 a = c4[0], c = c4[1];
+        const uint32_t cw[kFilterWaves] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+        uint32_t tot = 0, own = 0;
+#pragma unroll
+        for (int w = 0; w < kFilterWaves; ++w) {
+          tot += cw[w];
+          own = w == wave ? cw[w] : own;
+          below += w < wave ? cw[w] : 0u;
+        }
+        x = tot - own;
+      }
+      const uint32_t incl = wave_scan_incl(x);
+      if (lane < NB) L.emit_base[lane][wave] = incl - x + below;
+    }
+    __builtin_amdgcn_wave_barrier();  // the wave reads back its own bases
     for (uint32_t i = lane; i < mine; i += kWave) {
       const int32_t v = L.emit[wave][i];
-      uint32_t r = i;
-#pragma unroll
-      for (int w = 0; w < NW; ++w)
-        if (w != wave) r += lower_bound_lds(L.emit[w], L.emit_n[w], v);
+      const uint32_t r = L.emit_base[v / kBlockPos][wave] + i;
       if (r < (uint32_t)bh) o[r] = v;
     }
+    static_assert(kBlockPos == kFilterWaves * kWavePos && NB <= kWave && kFilterWaves == 8,
+                  "blocks of the waves' runs");
   }
 }
 
