@@ -217,10 +217,11 @@ static int round_e(int per_thread) {
 // but the second stage is one workgroup per row, so halving its candidates
 // is worth longer chunks.  When B is past the fused limit and chunking would
 // leave the second stage more than a quarter of the row (or cannot be
-// planned), a row of 16385 to 40960 positions goes whole to one 1024-thread
-// workgroup instead (32 or 40 per thread): that stage would redo most of the
-// first one's work, one workgroup per row anyway.  Other rows where no
-// chunk reduces anything but that fit one workgroup are held whole.
+// planned), the row goes whole to one 1024-thread workgroup instead: 16 per
+// thread up to 16384 positions, 32 or 40 per thread up to 40960.  That stage
+// would redo most of the first one's work, one workgroup per row anyway.
+// Other rows where no chunk reduces anything but that fit one workgroup are
+// held whole.
 static SelectPlan select_plan(int max_seq_len, int budget) {
   SelectPlan p;
   if (max_seq_len <= 0 || budget < 1) return p;
@@ -244,10 +245,13 @@ static SelectPlan select_plan(int max_seq_len, int budget) {
     }
     if (p.chunk_e) break;
   }
-  if (budget > kFusedMaxBudget && max_seq_len > kMaxE * kRowThreads &&
-      max_seq_len <= kWideMaxE * kWideThreads && (!p.chunk_e || 4 * cands > max_seq_len)) {
+  if (budget > kFusedMaxBudget && max_seq_len <= kWideMaxE * kWideThreads &&
+      (!p.chunk_e || 4 * cands > max_seq_len)) {
     SelectPlan w;
-    w.wide_e = max_seq_len <= 32 * kWideThreads ? 32 : kWideMaxE;
+    if (max_seq_len <= kMaxE * kRowThreads)
+      w.direct_e = round_e((max_seq_len + kRowThreads - 1) / kRowThreads);  // 1024 x 16
+    else
+      w.wide_e = max_seq_len <= 32 * kWideThreads ? 32 : kWideMaxE;
     return w;
   }
   if (!p.chunk_e && max_seq_len <= kMaxE * kRowThreads)

@@ -63,6 +63,17 @@ def test_large_budgets_on_rows_chunks_barely_cut_are_held_whole():
     assert fasa.select_layout(32768, 2000)[0] == "chunked"
 
 
+def test_large_budgets_on_rows_up_to_16384_are_held_whole_16_per_thread():
+    # Rows of 8193-16384 positions with B past the fused limit, where chunks
+    # would leave more than a quarter of the row as candidates: one
+    # 1024-thread workgroup holds the row whole, 16 scores per thread.
+    for n, budget in [(9000, 2000), (12000, 2000), (16000, 8500), (16384, 4096),
+                      (16384, 1025)]:
+        assert fasa.select_layout(n, budget) == ("whole", 1024, 16, 0), (n, budget)
+    # Budgets within the fused limit keep their chunks there.
+    assert fasa.select_layout(12000, 1024)[0] == "chunked"
+
+
 def test_invalid_arguments():
     assert fasa.select_layout(0, 10)[0] == "none"
     assert fasa.select_layout(10, 0)[0] == "none"
