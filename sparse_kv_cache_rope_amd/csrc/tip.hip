@@ -18,8 +18,8 @@
 // wave keeps all its loads in flight at once.
 //
 // The step's other per-token work is fused here and runs while those loads
-// are in flight: every workgroup rotates its group's queries (fp64 angle, kept
-// in fp32) into LDS weights (q~_c, q~_{c+C}) per plane and head, zero where
+// are in flight: every workgroup rotates its group's queries (angle reduced
+// in fp64, sine and cosine in fp32, kept in fp32) into LDS weights (q~_c, q~_{c+C}) per plane and head, zero where
 // the FC is not dominant for the head; in decode mode the workgroup whose tile
 // holds the new position n - 1 also rotates the step's key.
 //
@@ -185,16 +185,27 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
     const bool dom = (dmask[r] >> c) & 1ull;
     const bool pass = om[r] == 0.0;  // pass-through FC
     const double qx0 = to_f64(qr0[r]), qx1 = to_f64(qr1[r]);
-    double sn, cs;
-    sincos((double)pos * om[r], &sn, &cs);
-    qy0[r] = (float)(pass ? qx0 : qx0 * cs - qx1 * sn);
-    qy1[r] = (float)(pass ? qx1 : qx1 * cs + qx0 * sn);
+    // The query's angle, reduced to [-pi, pi] in fp64 (pos < 2^24, so the
+    // reduction keeps about 1e-8 rad), then its sine and cosine in fp32:
+    // q~ is kept in fp32 anyway.
+    const double ang = (double)pos * om[r];
+    const double rev = ang * 0.15915494309189533577;  // 1 / (2 pi)
+    const float red = (float)((rev - rint(rev)) * 6.28318530717958647693);
+    float sf, cf;
+    sincosf(red, &sf, &cf);
+    qy0[r] = (float)(pass ? qx0 : qx0 * (double)cf - qx1 * (double)sf);
+    qy1[r] = (float)(pass ? qx1 : qx1 * (double)cf + qx0 * (double)sf);
     if (tid + r * kTipThreads < G * C && slot[r] >= 0)
       wts[slot[r]][hh] = dom ? make_float2(qy0[r], qy1[r]) : make_float2(0.0f, 0.0f);
-    if (r == 0) {
-      // Thread tid < C holds FC tid here (head 0), the FC of its key pair.
+    if (r == 0 && owner) {
+      // The tile holding the step's position also rotates the step's key, in
+      // fp64 like the bulk append (the cache keeps its bf16 rounding of the
+      // exact rotation).  Thread tid < C holds FC tid here (head 0), the FC
+      // of its key pair.
+      double sn, cs;
+      sincos(ang, &sn, &cs);
       own_bits = rotate_pair<BF16>(to_f64(kr0), to_f64(kr1), sn, cs, pass);
-      if (owner && tid < C && slot[0] >= 0) patch[slot[0]] = own_bits;
+      if (tid < C && slot[0] >= 0) patch[slot[0]] = own_bits;
     }
   }
   if (!live) {
