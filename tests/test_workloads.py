@@ -77,3 +77,21 @@ def test_planted_positions_rank_high():
     pl = set(x["planted"][0].tolist())
     sel = set(r["idx"][0, 0][r["idx"][0, 0] >= 0].tolist())
     assert pl <= sel
+
+
+@pytest.mark.parametrize("head_dim,rotary_dim,theta", [(128, 128, 5e5), (64, 64, 1e4),
+                                                       (128, 64, 1e4), (64, 16, 1e4)])
+def test_planting_ladder_matches_the_oracle(head_dim, rotary_dim, theta):
+    """The planting's own frequency and FC-pair tables (workloads keep none
+    of the method's arithmetic for the kernels; planting needs these to align
+    keys with the query) equal the oracle's."""
+    from workloads.generate import plant_ladder
+    w = W.shrink(W.get("c2"), head_dim=head_dim, rotary_dim=rotary_dim, rope_theta=theta)
+    omega, lo, hi = plant_ladder(w)
+    R = rotary_dim // 2
+    want_w = np.zeros(head_dim // 2)
+    want_w[:R] = oracle.rope.inv_freq(rotary_dim, theta)
+    np.testing.assert_array_equal(omega, want_w)
+    olo, ohi = oracle.rope.fc_pairs(head_dim, rotary_dim)
+    np.testing.assert_array_equal(lo, olo)
+    np.testing.assert_array_equal(hi, ohi)

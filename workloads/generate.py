@@ -81,6 +81,21 @@ def _plant_positions(w: Workload, rng_plant, rng_span, ctx: int):
     return np.sort(rng_plant.choice(slots, size=count, replace=False))
 
 
+def plant_ladder(w):
+    """The frequency of every FC and its dimension pair (lo, hi), as the
+    planting aligns keys with the query: frequencies theta^(-2c/r) for the r
+    rotated dims' FCs and 0 for pass-through FCs; pairs (c, c + R) for
+    c < R = r/2, else the pass-through dims paired in order.  Only the
+    planting uses it; tests hold it against the oracle's own tables."""
+    d, r_dim = w.head_dim, w.rotated
+    half, R = d // 2, r_dim // 2
+    ci = np.arange(half)
+    omega = np.where(ci < R, np.power(float(w.rope_theta), -2.0 * np.minimum(ci, R) / r_dim), 0.0)
+    lo_d = np.where(ci < R, ci, r_dim + ci - R)
+    hi_d = np.where(ci < R, ci + R, r_dim + ci - R + (d - r_dim) // 2)
+    return omega, lo_d, hi_d
+
+
 def generate(w: Workload, seed: int = 0xFA5A, with_prefill: bool = True):
     """Draw every input of workload ``w``.
 
@@ -125,12 +140,7 @@ def generate(w: Workload, seed: int = 0xFA5A, with_prefill: bool = True):
     v = _normal(_rng(seed, cid, S_V), (b, hkv, L, d), w.dtype)
 
     # Planting (see module docstring).
-    r_dim = w.rotated
-    R = r_dim // 2
-    ci = np.arange(half)
-    omega = np.where(ci < R, np.power(float(w.rope_theta), -2.0 * np.minimum(ci, R) / r_dim), 0.0)
-    lo_d = np.where(ci < R, ci, r_dim + ci - R)
-    hi_d = np.where(ci < R, ci + R, r_dim + ci - R + (d - r_dim) // 2)
+    omega, lo_d, hi_d = plant_ladder(w)
     for i in range(b):
         pos = planted[i]
         if pos.size == 0:
