@@ -605,6 +605,12 @@ fasa_status fasa_dense_attn(fasa_ctx* c, const void* k_cache, const void* v_cach
   FASA_NONNULL(out);
   FASA_NONNULL(workspace);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (c->dtype == FASA_BF16 && c->d == 128) {
+    Timed t(c, FASA_K_DENSE, stream);
+    FASA_HIP(launch_dense_fused(c, k_cache, v_cache, q, seq_lens, max_seq_len, out, ws, stream),
+             "fasa_dense_attn");
+    return ok();
+  }
   {
     Timed t(c, FASA_K_PROLOGUE, stream);
     FASA_HIP(launch_prologue(c, q, seq_lens, max_seq_len, ws, stream), "fasa_dense_attn: prologue");

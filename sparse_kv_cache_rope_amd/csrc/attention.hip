@@ -229,6 +229,247 @@ dense_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
   }
 }
 
+// ------------------------------------------------------- dense (MFMA) ----
+
+// bf16 caches at d = 128: the dense comparator's q . K is a real contraction
+// (the G <= 4 query heads of a workgroup against every key of its split), so
+// it runs on the matrix cores: per 16-token tile, D / 32 steps of
+// v_mfma_f32_16x16x32_bf16 with the K tile as the A operand (a lane's 16-byte
+// load of a K row is its A fragment) and the queries as B: columns h < HPW
+// hold head h's scaled q~ rounded to bf16, columns HPW + h the rest of it
+// (q~ - hi, rounded again), so a logit is two columns' sum and keeps about
+// 2^-16 relative precision.  The softmax weights and P . V stay on VALU.
+//
+// A wave takes 32 consecutive tokens (2 tiles) of the workgroup's 256-token
+// split: all its K and V loads go out first (113 VGPRs, so two workgroups
+// share a CU and one streams while the other computes); the logits of its
+// tiles give the wave's
+// maximum and sum per head; V rows are read 4 per load, lane l holding row
+// l % 4 and dims 8 (l / 4) .. 8 (l / 4) + 7, so the sum over a load's rows is
+// a quad reduction.  The 8 waves' states merge once through LDS.
+typedef __bf16 fasa_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float fasa_f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kDenseMfmaTiles = 2;  // 16-token tiles per wave
+
+__device__ __forceinline__ uint32_t f32_bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
+template <int HPW>
+__global__ void __launch_bounds__(kDenseThreads)
+dense_mfma_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
+                  const uint16_t* __restrict__ q, const int32_t* __restrict__ seq_lens,
+                  const double* __restrict__ omega, int R, int max_seq_len, int hq, int hkv,
+                  int cap, int splits, int batch, int groups, float* __restrict__ partial,
+                  int max_splits, float* __restrict__ out, int32_t* __restrict__ nb_out,
+                  uint32_t* err) {
+  constexpr int D = 128;
+  constexpr int KK = D / 32;                 // MFMA steps over the head dim
+  constexpr int NW = kDenseThreads / kWave;  // 8
+  constexpr int T = kDenseMfmaTiles;
+  static_assert(NW * T * 16 == kDenseSplitTokens, "a split is 8 waves x T tiles of 16 tokens");
+  static_assert(2 * HPW <= 16, "hi and lo columns of the B operand");
+  __shared__ float pl[NW][T * 16][4];   // a wave's softmax weights, [token][head]
+  __shared__ float red[NW][HPW][D];     // the waves' weighted V sums
+  __shared__ float mw[NW][HPW], lw[NW][HPW];
+  __shared__ float qs[HPW][D];          // the workgroup's rotated queries
+
+  const int id = blockIdx.x, round = id >> 3;
+  const int tt = (round / groups) * 8 + (id & 7);
+  if (tt >= splits * hkv * batch) return;
+  const int split = tt % splits, g = (tt / splits) % hkv, b = tt / (splits * hkv);
+  // The length, validated here (one workgroup per sequence records it for
+  // the merge and raises the flag): 1 <= n_b <= min(max_seq_len, cap), and
+  // n_b = 0 gives a zero output without a flag.
+  const int n_in = seq_lens[b];
+  const bool len_ok = n_in >= 1 && n_in <= max_seq_len && n_in <= cap;
+  const int n = len_ok ? n_in : 0;
+  if (split == 0 && g == 0 && round % groups == 0 && threadIdx.x == 0) {
+    nb_out[b] = n;
+    if (!len_ok && n_in != 0) raise_flag(err, FASA_DEVFLAG_SEQ_LEN);
+  }
+  const int nsplit = (n + kDenseSplitTokens - 1) / kDenseSplitTokens;
+  const size_t row0 = (size_t)b * hq + (size_t)g * (HPW * groups) + (size_t)(round % groups) * HPW;
+  if (nsplit == 0) {
+    if (split == 0)
+      for (int i = threadIdx.x; i < HPW * D; i += kDenseThreads) out[row0 * D + i] = 0.0f;
+    return;
+  }
+  if (split >= nsplit) return;
+
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const size_t kvbase = ((size_t)b * hkv + g) * cap;
+  const uint4* K = static_cast<const uint4*>(k_cache);
+  const uint4* V = static_cast<const uint4*>(v_cache);
+  const int tw = split * kDenseSplitTokens + wave * (T * 16);  // the wave's first token
+
+  // Every K and V load of the wave first (tokens past n read row 0, masked).
+  uint4 kr[T][KK], vr[T][4];
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    const int tk = tw + 16 * j + lane % 16;
+    const size_t kb = (kvbase + (size_t)(tk < n ? tk : 0)) * (D / 8) + lane / 16;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) kr[j][kk] = K[kb + 4 * kk];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int tv = tw + 16 * j + 4 * s4 + lane % 4;
+      vr[j][s4] = V[(kvbase + (size_t)(tv < n ? tv : 0)) * (D / 8) + lane / 4];
+    }
+  }
+
+  // The queries, rotated to position n - 1 while the loads fly: one FC pair
+  // per thread (angle reduced in fp64, sine and cosine in fp32, as TIP does).
+  if (threadIdx.x < HPW * (D / 2)) {
+    const int hh = threadIdx.x / (D / 2), cf = threadIdx.x % (D / 2);
+    const int lo = fc_lo(cf, R), hi = fc_hi(cf, R, D / 2);
+    const uint16_t* qh = q + (row0 + hh) * D;
+    const float x0 = bf16_bits_to_f32(qh[lo]), x1 = bf16_bits_to_f32(qh[hi]);
+    const double w = omega[cf];
+    const double rev = (double)(n - 1) * w * 0.15915494309189533577;  // turns
+    float sf, cf2;
+    sincosf((float)((rev - rint(rev)) * 6.28318530717958647693), &sf, &cf2);
+    const bool pass = w == 0.0;
+    qs[hh][lo] = pass ? x0 : (float)((double)x0 * cf2 - (double)x1 * sf);
+    qs[hh][hi] = pass ? x1 : (float)((double)x1 * cf2 + (double)x0 * sf);
+  }
+  __syncthreads();
+
+  // B operands: lane l holds column c = l % 16, dims 32 kk + 8 (l / 16) ..
+  const int c = lane % 16;
+  fasa_bf16x8 qb[KK];
+  {
+    const bool hi_col = c < HPW, lo_col = c >= HPW && c < 2 * HPW;
+    const int hh = hi_col ? c : (lo_col ? c - HPW : 0);
+    const float scale = logit_scale<D>();
+    const float4* q4 = reinterpret_cast<const float4*>(qs[hh]);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int d0 = 32 * kk + 8 * (lane / 16);
+      const float4 a = q4[d0 / 4], bq = q4[d0 / 4 + 1];
+      const float qv[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = qv[i] * scale;
+        const uint32_t h16 = f32_bf16_rne_bits(x);
+        const uint32_t l16 = f32_bf16_rne_bits(x - __uint_as_float(h16 << 16));
+        const uint16_t bits = hi_col ? (uint16_t)h16 : (lo_col ? (uint16_t)l16 : (uint16_t)0);
+        qb[kk][i] = __builtin_bit_cast(__bf16, bits);
+      }
+    }
+  }
+
+  // Logits: tile j's D fragment holds tokens 16 j + 4 (l / 16) + i of column
+  // c; head c's logit is column c plus column c + HPW (lane l + HPW).
+  float z[T][4];
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    fasa_f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(fasa_bf16x8, kr[j][kk]),
+                                                    qb[kk], acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = acc[i] + dpp_f<0x100 + HPW>(acc[i]);  // row_shl: lane l + HPW
+      const int tk = tw + 16 * j + 4 * (lane / 16) + i;
+      z[j][i] = (c < HPW && tk < n) ? v : -INFINITY;
+      m = fmaxf(m, z[j][i]);
+    }
+  }
+  // The wave's max and sum per head (lanes c < HPW; l, l ^ 16, l ^ 32 hold
+  // the same head).
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  float lsum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < T; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = m == -INFINITY ? 0.0f : exp2f(z[j][i] - m);  // -inf gives 0
+      lsum += p;
+      if (c < HPW) pl[wave][16 * j + 4 * (lane / 16) + i][c] = p;
+    }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (lane < HPW) {
+    mw[wave][lane] = m;
+    lw[wave][lane] = lsum;
+  }
+  // The wave reads back what its own lanes wrote (LDS keeps a wave's
+  // accesses in order); the barrier only stops the compiler moving them.
+  __builtin_amdgcn_wave_barrier();
+
+  // Weighted V: lane l adds rows 16 j + 4 s + l % 4, dims 8 (l / 4) ...
+  float acc_o[HPW][8];
+#pragma unroll
+  for (int h = 0; h < HPW; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc_o[h][e] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < T; ++j)
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const float4 p4 = *reinterpret_cast<const float4*>(pl[wave][16 * j + 4 * s4 + lane % 4]);
+      const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+      float vf[8];
+      unpack<true, 8>(vr[j][s4], vf);
+#pragma unroll
+      for (int h = 0; h < HPW; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc_o[h][e] = fmaf(pv[h], vf[e], acc_o[h][e]);
+    }
+#pragma unroll
+  for (int h = 0; h < HPW; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc_o[h][e];
+      v += dpp_f<0xB1>(v);  // quad_perm [1,0,3,2]
+      v += dpp_f<0x4E>(v);  // quad_perm [2,3,0,1]
+      acc_o[h][e] = v;
+    }
+  if (lane % 4 == 0) {
+#pragma unroll
+    for (int h = 0; h < HPW; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[wave][h][8 * (lane / 4) + e] = acc_o[h][e];
+  }
+  __syncthreads();
+
+  // The 8 wave states of each head merged: thread (h, d).
+  for (int t = threadIdx.x; t < HPW * D; t += kDenseThreads) {
+    const int h = t / D, d = t % D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, mw[w][h]);
+    float L = 0.0f, S = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float wt = mx == -INFINITY ? 0.0f : exp2f(mw[w][h] - mx);  // -inf gives 0
+      L = fmaf(lw[w][h], wt, L);
+      S = fmaf(red[w][h][d], wt, S);
+    }
+    if (nsplit == 1) {
+      out[(row0 + h) * D + d] = L > 0.0f ? S / L : 0.0f;
+    } else {
+      float* part = partial + ((row0 + h) * max_splits + split) * (D + 2);
+      if (d == 0) {
+        part[0] = mx;
+        part[1] = L;
+      }
+      part[2 + d] = S;
+    }
+  }
+}
+
 // -------------------------------------------------------------- merge ----
 
 // One 1024-thread workgroup per (h, b) combines the per-split partials
@@ -338,6 +579,38 @@ hipError_t launch_fac(const fasa_ctx* c, const void* k_cache, const void* v_cach
 #undef FASA_FAC
   if (splits > 1)
     launch_merge(c, part, c->ws.fac_splits, nb, max_seq_len, budget, kFacSplitRows, out, s);
+  return hipGetLastError();
+}
+
+// The dense call on bf16 caches at d = 128: one launch that validates the
+// lengths and rotates the queries itself, then the merge of its splits.
+hipError_t launch_dense_fused(const fasa_ctx* c, const void* k_cache, const void* v_cache,
+                              const void* q, const int32_t* seq_lens, int max_seq_len,
+                              float* out, uint8_t* ws, hipStream_t s) {
+  if (c->dtype != FASA_BF16 || c->d != 128) return hipErrorInvalidValue;
+  int splits = (max_seq_len + kDenseSplitTokens - 1) / kDenseSplitTokens;
+  if (splits < 1) splits = 1;
+  float* part = reinterpret_cast<float*>(ws + c->ws.dense);
+  int32_t* nb = reinterpret_cast<int32_t*>(ws + c->ws.nb);
+  uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
+  // Query heads per workgroup: all of the group's, at most 4.
+  const int hpw = c->G < 4 ? c->G : 4;
+  const int groups = c->G / hpw;
+  const long tuples = (long)splits * c->hkv * c->batch;
+  const long ids = (tuples + 7) / 8 * 8 * groups;
+  if (ids * kDenseThreads > 0xffffffffL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)ids);
+  const uint16_t* qb = static_cast<const uint16_t*>(q);
+#define FASA_DENSE_MFMA(GG)                                                                   \
+  hipLaunchKernelGGL((dense_mfma_kernel<GG>), grid, dim3(kDenseThreads), 0, s, k_cache, v_cache, \
+                     qb, seq_lens, c->tab.omega, c->R, max_seq_len, c->hq, c->hkv, c->cap,       \
+                     splits, c->batch, groups, part, c->ws.dense_splits, out, nb, err)
+  if (hpw == 1) FASA_DENSE_MFMA(1);
+  else if (hpw == 2) FASA_DENSE_MFMA(2);
+  else FASA_DENSE_MFMA(4);
+#undef FASA_DENSE_MFMA
+  if (splits > 1)
+    launch_merge(c, part, c->ws.dense_splits, nb, max_seq_len, 0, kDenseSplitTokens, out, s);
   return hipGetLastError();
 }
 

@@ -69,7 +69,7 @@ constexpr int kFacSplitRows = 256;
 // (80 VGPRs, 3 workgroups per CU) hid the gather's latency chain better than
 // 16 waves with 4 (2 per CU) or 4 waves with 16.
 constexpr int kFacThreads = 512;
-constexpr int kDenseSplitTokens = 512;
+constexpr int kDenseSplitTokens = 256;
 // Largest budget the fused select + FAC kernels keep in LDS.
 constexpr int kFusedMaxBudget = 1024;
 // Row select (select2.hip): positions per chunk of a long row (at most), and
@@ -141,6 +141,11 @@ hipError_t launch_fac(const fasa_ctx* c, const void* k_cache, const void* v_cach
 hipError_t launch_dense(const fasa_ctx* c, const void* k_cache, const void* v_cache,
                         const int32_t* nb, int max_seq_len, float* out, uint8_t* ws,
                         hipStream_t s);
+// bf16 caches at d = 128: validation, query rotation and dense decode in one
+// launch (matrix cores for q . K), then the merge (attention.hip).
+hipError_t launch_dense_fused(const fasa_ctx* c, const void* k_cache, const void* v_cache,
+                              const void* q, const int32_t* seq_lens, int max_seq_len,
+                              float* out, uint8_t* ws, hipStream_t s);
 // Top-B selection fused with FAC (budget <= kFusedMaxBudget): one workgroup
 // per (h, b) selects and attends; idx may be null.
 hipError_t launch_select_attend(const fasa_ctx* c, const float* scores, const int32_t* nb,

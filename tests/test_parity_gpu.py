@@ -449,11 +449,12 @@ def test_budget_at_least_context_is_dense(gpu):
     assert np.all(res["idx"][:, :, :200] == np.arange(200))
     for h in range(w.n_q_heads):
         check_out(out.cpu().numpy()[0, h], res["out"][0, h], w.dtype, f"h{h}")
-    # And against the in-build dense kernel on the same cache.
+    # The in-build dense kernel on the same cache meets the same oracle.
     dense = torch.empty_like(out)
     n = torch.full((1,), 200, dtype=torch.int32, device="cuda")
     g.ctx.dense_attn(g.k, g.v, to_dev(x["q"][0], g.td), n, 200, dense, g.ws)
-    assert torch.allclose(out, dense, rtol=1e-5, atol=1e-6)
+    for h in range(w.n_q_heads):
+        check_out(dense.cpu().numpy()[0, h], res["out"][0, h], w.dtype, f"dense h{h}")
 
 
 def test_single_token_context(gpu):
