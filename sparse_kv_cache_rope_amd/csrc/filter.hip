@@ -307,8 +307,10 @@ __device__ __forceinline__ void stream_emit(const float* row, int n, uint64_t ta
 // hold a row (RS rows per step); V: VL = LPR / S lanes hold the row's column
 // slice of this part (RV rows per step).  A round covers RR entries: their
 // logits (through the wave's LDS slot), the round's max, a rescale of the
-// wave's running state, and the weighted V sum.  Entries past cnt load the
-// list's last row (fetched anyway) and count as absent.
+// wave's running state, and the weighted V sum.  Two register sets hold
+// consecutive rounds, so round r + 1's rows fly while round r is computed.
+// Entries past cnt load the list's last row (fetched anyway) and count as
+// absent.
 template <bool BF16, int D, int S>
 struct WaveFac {
   using Geo = RowGeom<BF16, D>;
@@ -316,10 +318,10 @@ struct WaveFac {
   static_assert(LPR % S == 0, "V slice lanes");
   static constexpr int VL = LPR / S;
   static constexpr int RV = kWave / VL;
-  static constexpr int KST = (64 / RS) > 16 ? 16 : (64 / RS) < 1 ? 1 : (64 / RS);
+  static constexpr int KST = (32 / RS) > 8 ? 8 : (32 / RS) < 1 ? 1 : (32 / RS);
   static constexpr int RR = RS * KST;
   static constexpr int VST = (RR + RV - 1) / RV;
-  static_assert(RR <= 64, "a round's logits fit the wave's LDS slot");
+  static_assert(2 * RR <= 64, "two rounds' logits fit the wave's LDS slot");
   // Floats of a wave's state (this part's columns).
   static constexpr int W = D / S;
   static_assert(VL <= 32 && kFilterWaves * W <= kFacRedFloats, "partial sums");
@@ -425,20 +427,23 @@ struct WaveSoft {
   float m, l, acc[EPL];
 };
 
-// One round: logits of entries r0 .. r0 + RR - 1, then their weighted V.
-// The KST dot products are independent chains (so they interleave), their
-// group sums likewise; lane i then masks entry r0 + i (past cnt, or below
-// tau) and the masked logits go back through the wave's LDS slot.
-template <class F, class Q>
-__device__ __forceinline__ void fac_round(const F& f, const Q& qq, int r0, int cnt,
+// One round: logits of the entries r0 .. in the register sets given (one
+// set: RR entries; both: 2 RR, f0's then f1's), then their weighted V.  The
+// dot products are independent chains (so they interleave), their group sums
+// likewise; lane i then masks entry r0 + i (past cnt, or below tau) and the
+// masked logits go back through the wave's LDS slot.
+template <int NSETS, class F, class Q>
+__device__ __forceinline__ void fac_round(const F& f0, const F& f1, const Q& qq, int r0, int cnt,
                                           const int32_t* pos, const uint32_t* key, uint64_t tau,
                                           float* zw, WaveSoft<F::EPL>& st) {
   constexpr int LPR = F::LPR, EPL = F::EPL, VL = F::VL;
+  constexpr int KS = F::KST * NSETS, VS = F::VST * NSETS, RN = F::RR * NSETS;
+  static_assert(RN <= kWave, "a round's logits fit the wave's LDS slot");
   const int lane = threadIdx.x & (kWave - 1);
-  float d[F::KST];
+  float d[KS];
 #pragma unroll
-  for (int s = 0; s < F::KST; ++s) {
-    const uint4 x = f.k[s];
+  for (int s = 0; s < KS; ++s) {
+    const uint4 x = s < F::KST ? f0.k[s % F::KST] : f1.k[s % F::KST];
     if constexpr (F::Geo::ES == 2) {
       const uint32_t w[4] = {x.x, x.y, x.z, x.w};
       float a = 0.0f, c = 0.0f;
@@ -454,10 +459,12 @@ __device__ __forceinline__ void fac_round(const F& f, const Q& qq, int r0, int c
     }
   }
 #pragma unroll
-  for (int s = 0; s < F::KST; ++s) d[s] = group_sum<LPR>(d[s]);
+  for (int s = 0; s < KS; ++s) d[s] = group_sum<LPR>(d[s]);
   if (lane % LPR == 0) {
+    // Set k's step s covers round entries k RR + s RS + lane / LPR.
 #pragma unroll
-    for (int s = 0; s < F::KST; ++s) zw[s * F::RS + lane / LPR] = d[s];
+    for (int s = 0; s < KS; ++s)
+      zw[(s / F::KST) * F::RR + (s % F::KST) * F::RS + lane / LPR] = d[s];
   }
   // The wave reads back what its own lanes wrote (LDS keeps a wave's
   // accesses in order); the barrier only stops the compiler moving them.
@@ -465,13 +472,13 @@ __device__ __forceinline__ void fac_round(const F& f, const Q& qq, int r0, int c
   float zl = -INFINITY;
   {
     const int r = r0 + lane;
-    if (lane < F::RR && r < cnt && composite(key[r], (uint32_t)pos[r]) >= tau) zl = zw[lane];
+    if (lane < RN && r < cnt && composite(key[r], (uint32_t)pos[r]) >= tau) zl = zw[lane];
   }
   const float mr = wave_max(zl);
   const float mn = fmaxf(st.m, mr);
   if (mn == -INFINITY) return;  // nothing selected yet (wave-uniform)
   __builtin_amdgcn_wave_barrier();
-  if (lane < F::RR) zw[lane] = zl;
+  if (lane < RN) zw[lane] = zl;
   __builtin_amdgcn_wave_barrier();
   const float sc = exp2f(st.m - mn);  // m = -inf gives 0
   st.l *= sc;
@@ -479,12 +486,13 @@ __device__ __forceinline__ void fac_round(const F& f, const Q& qq, int r0, int c
   for (int e = 0; e < EPL; ++e) st.acc[e] *= sc;
   st.m = mn;
 #pragma unroll
-  for (int s = 0; s < F::VST; ++s) {
-    const int rr = s * F::RV + lane / VL;
-    const float z = rr < F::RR ? zw[rr < F::RR ? rr : 0] : -INFINITY;
+  for (int s = 0; s < VS; ++s) {
+    const int rr = (s / F::VST) * F::RR + (s % F::VST) * F::RV + lane / VL;
+    const bool in_set = (s % F::VST) * F::RV + lane / VL < F::RR;
+    const float z = in_set ? zw[in_set ? rr : 0] : -INFINITY;
     const float p = exp2f(z - mn);  // -inf gives 0
     float vf[EPL];
-    unpack<F::Geo::ES == 2, EPL>(f.v[s], vf);
+    unpack<F::Geo::ES == 2, EPL>(s < F::VST ? f0.v[s % F::VST] : f1.v[s % F::VST], vf);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) st.acc[e] = fmaf(p, vf[e], st.acc[e]);
     if (lane % VL == 0) st.l += p;
@@ -492,11 +500,13 @@ __device__ __forceinline__ void fac_round(const F& f, const Q& qq, int r0, int c
   __builtin_amdgcn_wave_barrier();  // zw is rewritten next round
 }
 
-// FAC of a wave over its list (the first round's loads already in f when
-// `issued`), its state left in L.red / L.mw / L.lw for fac_merge.
+// FAC of a wave over its list (rounds 0 and 1 already in flight in f0 / f1
+// when `issued` says so), its state left in L.red / L.mw / L.lw for
+// fac_merge.
 template <bool BF16, int D, int S>
-__device__ __forceinline__ void fac_wave(WaveFac<BF16, D, S>& f, bool issued, int cnt,
-                                         const int32_t* pos, const uint32_t* key, uint64_t tau,
+__device__ __forceinline__ void fac_wave(WaveFac<BF16, D, S>& f0, WaveFac<BF16, D, S>& f1,
+                                         int issued, int cnt, const int32_t* pos,
+                                         const uint32_t* key, uint64_t tau,
                                          const uint4* __restrict__ K, const uint4* __restrict__ V,
                                          size_t kvbase, int part,
                                          const QueryRaw<BF16, D>& qraw, FilterLds& L) {
@@ -510,9 +520,23 @@ __device__ __forceinline__ void fac_wave(WaveFac<BF16, D, S>& f, bool issued, in
 #pragma unroll
   for (int e = 0; e < EPL; ++e) st.acc[e] = 0.0f;
   float* zw = L.zw[wave];
-  for (int r0 = 0; r0 < cnt; r0 += F::RR) {
-    if (r0 > 0 || !issued) fac_issue(f, r0, cnt, pos, K, V, kvbase, part);
-    fac_round(f, qq, r0, cnt, pos, key, tau, zw, st);
+  const int nr = (cnt + F::RR - 1) / F::RR;
+  if (nr > 0 && issued < 1) fac_issue(f0, 0, cnt, pos, K, V, kvbase, part);
+  if (nr > 1 && issued < 2) fac_issue(f1, F::RR, cnt, pos, K, V, kvbase, part);
+  if (nr <= 2) {
+    // Both sets as one round: one max, one rescale.
+    if (nr == 2) fac_round<2>(f0, f1, qq, 0, cnt, pos, key, tau, zw, st);
+    else if (nr == 1) fac_round<1>(f0, f1, qq, 0, cnt, pos, key, tau, zw, st);
+  } else {
+    // Longer lists: round r computed while round r + 1 flies.
+    for (int r = 0; r < nr; r += 2) {
+      fac_round<1>(f0, f0, qq, r * F::RR, cnt, pos, key, tau, zw, st);
+      if (r + 2 < nr) fac_issue(f0, (r + 2) * F::RR, cnt, pos, K, V, kvbase, part);
+      if (r + 1 < nr) {
+        fac_round<1>(f1, f1, qq, (r + 1) * F::RR, cnt, pos, key, tau, zw, st);
+        if (r + 3 < nr) fac_issue(f1, (r + 3) * F::RR, cnt, pos, K, V, kvbase, part);
+      }
+    }
   }
   // Sum over the row slots holding the same slice: within 16-lane rows by
   // DPP, the rows and waves through LDS.
@@ -649,8 +673,8 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
   const uint32_t* lkey = &L.key[wave * kWavePlayCap];
   int cnt = 0;
   uint64_t tau = 0;     // an entry takes part <=> its composite >= tau
-  F fac;
-  bool issued = false;  // the first round of FAC loads is in flight
+  F fac0, fac1;
+  int issued = 0;       // FAC rounds whose loads are in flight (0, 1 or 2)
   bool listed = false;  // the waves' own lists hold the row's in-play tokens
   bool cold = false;    // the streaming route selects this row
 
@@ -774,8 +798,12 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
         // counted (one atomic per listed token).
         __builtin_amdgcn_wave_barrier();  // the wave reads back its own list
         if (!ovf && cnt > 0) {
-          fac_issue(fac, 0, cnt, wpos, K, V, kvbase, part);
-          issued = true;
+          fac_issue(fac0, 0, cnt, wpos, K, V, kvbase, part);
+          issued = 1;
+          if (cnt > F::RR) {
+            fac_issue(fac1, F::RR, cnt, wpos, K, V, kvbase, part);
+            issued = 2;
+          }
         }
         const int listed_n = min(cnt, kWavePlayCap);
         for (int i = lane; i < listed_n; i += kWave)
@@ -826,7 +854,7 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
         L.key[r] = 1u;
       });
       tau = 0;
-      issued = false;
+      issued = 0;
     }
     if (o != nullptr)
       for (int j = bh + t; j < budget; j += NT) o[j] = -1;
@@ -846,8 +874,31 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
     lpos = &L.pos[lo];
     lkey = &L.key[lo];
   }
+  if (listed && cnt > 2 * F::RR) {
+    // Past the two rounds already in flight, keep only the selected entries
+    // (in place, in order: a chunk is read before any of it is written, and
+    // writes never pass the entries still to read).
+    int32_t* wp = &L.pos[wave * kWavePlayCap];
+    uint32_t* wk = &L.key[wave * kWavePlayCap];
+    uint32_t at = 2 * F::RR;
+    for (int i0 = 2 * F::RR; i0 < cnt; i0 += kWave) {
+      const int i = i0 + lane;
+      const int32_t pv = i < cnt ? wp[i] : 0;
+      const uint32_t kv = i < cnt ? wk[i] : 0u;
+      const bool sel = i < cnt && composite(kv, (uint32_t)pv) >= tau;
+      const uint64_t bal = __ballot(sel);
+      __builtin_amdgcn_wave_barrier();
+      if (sel) {
+        wp[at + lanes_below_count(bal)] = pv;
+        wk[at + lanes_below_count(bal)] = kv;
+      }
+      at += (uint32_t)__popcll(bal);
+    }
+    cnt = (int)at;
+    __builtin_amdgcn_wave_barrier();  // the wave reads back its own list
+  }
   // 4. FAC.
-  fac_wave<BF16, D, S>(fac, issued, cnt, lpos, lkey, tau, K, V, kvbase, part, qraw, L);
+  fac_wave<BF16, D, S>(fac0, fac1, issued, cnt, lpos, lkey, tau, K, V, kvbase, part, qraw, L);
   __syncthreads();
   fac_merge<BF16, D, S>(out_row, part, L);
 
