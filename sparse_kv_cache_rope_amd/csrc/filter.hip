@@ -27,7 +27,9 @@
 //      taken, else its few elements are ranked;
 //   4. FAC, each wave over its own list (entries below tau masked): logits,
 //      the wave's softmax max and sum, its weighted V sum, then one merge of
-//      the waves' states through LDS;
+//      the waves' states through LDS; when some wave's list is long (tokens
+//      clustered in few waves' groups), T_t is first laid out flat and split
+//      evenly over the waves;
 //   5. rows this does not fit (fewer groups than B, one score value, more
 //      survivors or in-play tokens than the slots hold, a crowded pivot bin)
 //      are selected by streaming range refinement over their scores and an
@@ -89,6 +91,8 @@ struct FilterLds {
   uint32_t pivot_n;
   uint32_t kpmin[kFilterWaves];   // per-wave smallest surviving group maximum
   uint32_t overflow;              // a wave's survivors or list did not fit
+  int32_t wcnt[kFilterWaves];     // each wave's list length
+  uint32_t selcnt[kFilterWaves];  // each wave's selected entries (FAC rebalance)
   // idx: selected tokens per (block of 512 groups, wave), then each one's
   // first rank.
   alignas(16) uint32_t emit_cnt[kFilterMaxGroups / kFilterThreads][kFilterWaves];
@@ -808,7 +812,8 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
         const int listed_n = min(cnt, kWavePlayCap);
         for (int i = lane; i < listed_n; i += kWave)
           atomicAdd(&L.hist2[(wkey[i] - kp) >> sh2], 1u);
-        __syncthreads();  // the histogram and the overflow flag are complete
+        if (lane == 0) L.wcnt[wave] = cnt;
+        __syncthreads();  // the histogram, the overflow flag and the list lengths are complete
         cold = L.overflow != 0u;
         if (!cold) {
           const WavePick p2 = wave_pick(L.hist2, (uint32_t)bh);
@@ -874,31 +879,53 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
     lpos = &L.pos[lo];
     lkey = &L.key[lo];
   }
-  if (listed && cnt > 2 * F::RR) {
-    // Past the two rounds already in flight, keep only the selected entries
-    // (in place, in order: a chunk is read before any of it is written, and
-    // writes never pass the entries still to read).
-    int32_t* wp = &L.pos[wave * kWavePlayCap];
-    uint32_t* wk = &L.key[wave * kWavePlayCap];
-    uint32_t at = 2 * F::RR;
-    for (int i0 = 2 * F::RR; i0 < cnt; i0 += kWave) {
-      const int i = i0 + lane;
-      const int32_t pv = i < cnt ? wp[i] : 0;
-      const uint32_t kv = i < cnt ? wk[i] : 0u;
-      const bool sel = i < cnt && composite(kv, (uint32_t)pv) >= tau;
-      const uint64_t bal = __ballot(sel);
-      __builtin_amdgcn_wave_barrier();
-      if (sel) {
-        wp[at + lanes_below_count(bal)] = pv;
-        wk[at + lanes_below_count(bal)] = kv;
+  // FAC reads fcnt entries at fpos / fkey (selected <=> composite >= ftau).
+  int fcnt = cnt;
+  const int32_t* fpos = lpos;
+  const uint32_t* fkey = lkey;
+  uint64_t ftau = tau;
+  if (listed) {
+    int maxcnt = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) maxcnt = max(maxcnt, L.wcnt[w]);
+    if (maxcnt > 2 * F::RR) {
+      // Some wave's list runs past the two rounds in flight (clustered
+      // tokens land in few waves): T_t is laid out flat, the waves' selected
+      // entries one after another, and each wave attends an even share.
+      uint32_t mine = 0;
+      for (int i0 = 0; i0 < cnt; i0 += kWave) {
+        const int i = i0 + lane;
+        mine += (uint32_t)__popcll(
+            __ballot(i < cnt && composite(lkey[i], (uint32_t)lpos[i]) >= tau));
       }
-      at += (uint32_t)__popcll(bal);
+      if (lane == 0) L.selcnt[wave] = mine;
+      __syncthreads();
+      uint32_t base = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        base += w < wave ? L.selcnt[w] : 0u;
+        total += L.selcnt[w];
+      }
+      int32_t* flat = &L.emit[0][0];
+      for (int i0 = 0; i0 < cnt; i0 += kWave) {
+        const int i = i0 + lane;
+        const bool sel = i < cnt && composite(lkey[i], (uint32_t)lpos[i]) >= tau;
+        const uint64_t bal = __ballot(sel);
+        if (sel) flat[base + lanes_below_count(bal)] = lpos[i];
+        base += (uint32_t)__popcll(bal);
+      }
+      __syncthreads();
+      const int share = ((int)total + NW - 1) / NW;
+      const int lo = wave * share;
+      fcnt = max(0, min((int)total - lo, share));
+      fpos = flat + lo;
+      fkey = reinterpret_cast<const uint32_t*>(fpos);  // with ftau = 0 every entry is in
+      ftau = 0;
+      issued = 0;
     }
-    cnt = (int)at;
-    __builtin_amdgcn_wave_barrier();  // the wave reads back its own list
   }
   // 4. FAC.
-  fac_wave<BF16, D, S>(fac0, fac1, issued, cnt, lpos, lkey, tau, K, V, kvbase, part, qraw, L);
+  fac_wave<BF16, D, S>(fac0, fac1, issued, fcnt, fpos, fkey, ftau, K, V, kvbase, part, qraw, L);
   __syncthreads();
   fac_merge<BF16, D, S>(out_row, part, L);
 
