@@ -472,25 +472,42 @@ dense_mfma_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_c
 
 // -------------------------------------------------------------- merge ----
 
-// One 1024-thread workgroup per (h, b) combines the per-split partials
-// (m, l, acc) of a row whose work spanned more than one split.  `unit` is the
-// rows (FAC: of min(budget, n)) or tokens (dense: of n) per split.  Every
-// split's partial is loaded at once (thread = split x 16 dims) and summed
-// through LDS, so the merge costs one memory round trip per 1024/(D/16)
-// splits instead of one per split.
+// One 1024-thread workgroup per (h, b, 16-dim slice) combines the per-split
+// partials (m, l, acc) of a row whose work spanned more than one split.
+// `unit` is the rows (FAC: of min(budget, n)) or tokens (dense: of n) per
+// split.  Thread t takes dim t % 16 of the slice for splits t / 16,
+// t / 16 + 64, ..: sixteen threads read one split's 64 contiguous bytes, and
+// a thread's loads are independent.  Each thread folds its splits into an
+// (m, l, acc) state of its own and the states are merged across lanes and
+// waves, so a row of hundreds of splits costs one memory round trip.
 constexpr int kMergeThreads = 1024;
+constexpr int kMergeDims = 16;
+
+struct MergeState {
+  float m, l, a;
+};
+
+// The merge of two softmax states; a state with m = -inf is empty.
+__device__ __forceinline__ MergeState merge_states(MergeState x, MergeState y) {
+  const float mn = fmaxf(x.m, y.m);
+  if (mn == -INFINITY) return x;
+  const float wx = exp2f(x.m - mn), wy = exp2f(y.m - mn);  // -inf gives 0
+  return {mn, fmaf(x.l, wx, y.l * wy), fmaf(x.a, wx, y.a * wy)};
+}
+
+__device__ __forceinline__ MergeState shfl_xor_state(MergeState x, int k) {
+  return {__shfl_xor(x.m, k), __shfl_xor(x.l, k), __shfl_xor(x.a, k)};
+}
 
 template <int D>
 __global__ void __launch_bounds__(kMergeThreads)
 merge_kernel(const float* __restrict__ partial, int max_splits, const int32_t* __restrict__ nb,
              int max_seq_len, int cap, int budget, int unit, int hq, float* __restrict__ out) {
-  constexpr int DPT = 16;                      // dims per thread
-  constexpr int TPS = D / DPT;                 // threads per split
-  constexpr int SPB = kMergeThreads / TPS;     // splits per pass
-  __shared__ float red[SPB][D + 1];
-  __shared__ float lred[SPB];
-  __shared__ float wmax[kMergeThreads / kWave];
-  const int h = blockIdx.x, b = blockIdx.y;
+  constexpr int SL = kMergeThreads / kMergeDims;  // split lanes
+  constexpr int NWV = kMergeThreads / kWave;
+  constexpr int U = 8;  // splits per thread in flight
+  __shared__ MergeState ws[NWV][kMergeDims];
+  const int h = blockIdx.x, b = blockIdx.y, d0 = blockIdx.z * kMergeDims;
   const size_t row = (size_t)b * hq + h;
   int n = nb[b];
   if (n < 0 || n > max_seq_len || n > cap) n = 0;
@@ -498,54 +515,55 @@ merge_kernel(const float* __restrict__ partial, int max_splits, const int32_t* _
   const int nsplit = (work + unit - 1) / unit;
   if (nsplit <= 1) return;  // written directly by the split kernel
   const float* p = partial + row * max_splits * (D + 2);
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  const int dd = t % kMergeDims;
 
-  float m = -INFINITY;
-  for (int s = t; s < nsplit; s += kMergeThreads) m = fmaxf(m, p[(size_t)s * (D + 2)]);
-  m = wave_max(m);
-  if ((t & (kWave - 1)) == 0) wmax[t / kWave] = m;
-  __syncthreads();
-  float M = -INFINITY;
+  MergeState st = {-INFINITY, 0.0f, 0.0f};
+  for (int s0 = t / kMergeDims; s0 < nsplit; s0 += U * SL) {
+    // Up to U splits at once: their loads go out together.
+    float mv[U], lv[U], av[U];
 #pragma unroll
-  for (int w = 0; w < kMergeThreads / kWave; ++w) M = fmaxf(M, wmax[w]);
-
-  float A = 0.0f, L = 0.0f;
-  const int sl = t / TPS, dd = (t % TPS) * DPT;
-  for (int c0 = 0; c0 < nsplit; c0 += SPB) {
-    const int s = c0 + sl;
-    float v[DPT];
-    float l = 0.0f;
-    if (s < nsplit && M != -INFINITY) {
-      const float* q = p + (size_t)s * (D + 2);
-      const float w = exp2f(q[0] - M);
-      l = q[1] * w;
-#pragma unroll
-      for (int i = 0; i < DPT; ++i) v[i] = q[2 + dd + i] * w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < DPT; ++i) v[i] = 0.0f;
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * SL;
+      const float* q = p + (size_t)(s < nsplit ? s : s0) * (D + 2);
+      mv[u] = s < nsplit ? q[0] : -INFINITY;
+      lv[u] = q[1];
+      av[u] = q[2 + d0 + dd];
     }
+    float mx = st.m;
 #pragma unroll
-    for (int i = 0; i < DPT; ++i) red[sl][dd + i] = v[i];
-    if (dd == 0) lred[sl] = l;
-    __syncthreads();
-    if (t < D) {
-      const int lim = min(SPB, nsplit - c0);
-      for (int r = 0; r < lim; ++r) {
-        A += red[r][t];
-        L += lred[r];
+    for (int u = 0; u < U; ++u) mx = fmaxf(mx, mv[u]);
+    if (mx != -INFINITY) {
+      const float sc = exp2f(st.m - mx);  // -inf gives 0
+      st.l *= sc;
+      st.a *= sc;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float w = exp2f(mv[u] - mx);  // -inf gives 0
+        st.l = fmaf(lv[u], w, st.l);
+        st.a = fmaf(av[u], w, st.a);
       }
+      st.m = mx;
     }
-    __syncthreads();
   }
-  if (t < D) out[row * D + t] = (L > 0.0f) ? A / L : 0.0f;
+  // Lanes dd, dd + 16, dd + 32, dd + 48 of a wave, then the waves.
+  st = merge_states(st, shfl_xor_state(st, 16));
+  st = merge_states(st, shfl_xor_state(st, 32));
+  if (lane < kMergeDims) ws[wave][lane] = st;
+  __syncthreads();
+  if (t < kMergeDims) {
+    MergeState r = ws[0][t];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) r = merge_states(r, ws[w][t]);
+    out[row * D + d0 + t] = (r.l > 0.0f) ? r.a / r.l : 0.0f;
+  }
 }
 
 // ------------------------------------------------------------ launchers --
 
 static void launch_merge(const fasa_ctx* c, const float* part, int max_splits, const int32_t* nb,
                          int max_seq_len, int budget, int unit, float* out, hipStream_t s) {
-  dim3 grid((unsigned)c->hq, (unsigned)c->batch);
+  dim3 grid((unsigned)c->hq, (unsigned)c->batch, (unsigned)(c->d / kMergeDims));
   if (c->d == 128)
     hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, s, part, max_splits, nb,
                        max_seq_len, c->cap, budget, unit, c->hq, out);
