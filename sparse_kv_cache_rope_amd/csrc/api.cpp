@@ -252,7 +252,18 @@ fasa_status fasa_create_partial_rope(fasa_ctx** out, int batch, int n_q_heads, i
   const size_t b_slot = align256(sizeof(int32_t) * fc_slot.size());
   const size_t b_mask = align256(sizeof(uint64_t) * mask.size());
   const size_t b_omega = align256(sizeof(double) * C);
-  const size_t bytes = b_off + b_slot + b_mask + b_omega;
+  // Per query head, its dominant FCs ascending with their planes (the first
+  // 16; TIP's per-head layout is used only when a head has at most 16).
+  constexpr int kHeadFcSlots = 16;
+  std::vector<int2> head_fc((size_t)n_q_heads * kHeadFcSlots, make_int2(-1, -1));
+  for (int h = 0; h < n_q_heads; ++h) {
+    int k = 0;
+    for (int fc = 0; fc < C && k < kHeadFcSlots; ++fc)
+      if (mask[h] >> fc & 1ull)
+        head_fc[(size_t)h * kHeadFcSlots + k++] = make_int2(fc, fc_slot[(size_t)(h / G) * C + fc]);
+  }
+  const size_t b_head = align256(sizeof(int2) * head_fc.size());
+  const size_t bytes = b_off + b_slot + b_mask + b_omega + b_head;
   hipError_t e = hipGetDevice(&c->device);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&c->cus, hipDeviceAttributeMultiprocessorCount, c->device);
   if (e == hipSuccess) e = hipMalloc(&c->dev_alloc, bytes);
@@ -266,6 +277,7 @@ fasa_status fasa_create_partial_rope(fasa_ctx** out, int batch, int n_q_heads, i
   c->tab.fc_slot = reinterpret_cast<int32_t*>(base + b_off);
   c->tab.dom_mask = reinterpret_cast<uint64_t*>(base + b_off + b_slot);
   c->tab.omega = reinterpret_cast<double*>(base + b_off + b_slot + b_mask);
+  c->tab.head_fc = reinterpret_cast<int2*>(base + b_off + b_slot + b_mask + b_omega);
   e = hipMemcpy(c->tab.plane_off, c->plane_off.data(), sizeof(int32_t) * c->plane_off.size(),
                 hipMemcpyHostToDevice);
   if (e == hipSuccess)
@@ -276,6 +288,9 @@ fasa_status fasa_create_partial_rope(fasa_ctx** out, int batch, int n_q_heads, i
                   hipMemcpyHostToDevice);
   if (e == hipSuccess)
     e = hipMemcpy(c->tab.omega, omega.data(), sizeof(double) * C, hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(c->tab.head_fc, head_fc.data(), sizeof(int2) * head_fc.size(),
+                  hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     fasa_destroy(c);
     return hip_fail(e, "fasa_create: uploading tables");

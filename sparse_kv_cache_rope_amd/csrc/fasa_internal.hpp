@@ -17,6 +17,7 @@ struct DeviceTables {
   int32_t* fc_slot;    // [Hkv][C]: plane index within the KV head, or -1
   uint64_t* dom_mask;  // [Hq]: bit c set when FC c is dominant for head h
   double* omega;       // [C]: theta^(-2c/d), fp64
+  int2* head_fc;       // [Hq][16]: head h's dominant FCs ascending, (FC, plane); (-1, -1) past them
 };
 
 // Byte offsets of the workspace regions (each 256-byte aligned).

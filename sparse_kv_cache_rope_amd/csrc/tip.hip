@@ -347,6 +347,236 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
   if (lead) nb_out[b] = n;
 }
 
+// TIP with one wave per query head (G = 4 or 8 heads per KV head, at most
+// kHeadPlanes dominant FCs per head).  The workgroup again covers 256 tokens
+// of one (sequence, KV head), but wave w streams only the planes of query
+// head g G + w's own dominant FCs (a plane dominant for several heads is read
+// by each of their waves; the copies meet in the cache) and sums them for its
+// 4 tokens per lane: no FMA is spent on a plane whose weight for the head is
+// zero (about 2/3 of them for G = 4 in the union layout above), and no sum
+// across waves is needed.  Every lane rotates FC lane % C of its head; the
+// dominant FCs' rotated pairs are read across the wave.  The order of work,
+// the owner tile's append and the stores follow tip_kernel.
+constexpr int kHeadPlanes = 16;
+
+template <bool BF16, int G, int D, int PW>
+__global__ void __launch_bounds__(G * kWave)
+tip_head_kernel(const int32_t* __restrict__ seq_lens, void* sidecar,
+                const int2* __restrict__ head_fc, int mode, int max_seq_len, int cap, int P,
+                int R, int hkv, const void* __restrict__ q, const double* __restrict__ omega,
+                const int32_t* __restrict__ fc_slot, const void* __restrict__ k_new,
+                const void* __restrict__ v_new, void* __restrict__ k_cache,
+                void* __restrict__ v_cache, int32_t* __restrict__ nb_out, float* __restrict__ qrot,
+                float* __restrict__ scores, uint32_t* err, PlaneOffsets po,
+                uint32_t* __restrict__ gmax, int gstride) {
+  using T = typename CacheT<BF16>::T;
+  constexpr int C = D / 2;
+  constexpr int kPairBytes = BF16 ? 4 : 8;
+  static_assert(PW <= kHeadPlanes && C <= kWave, "planes per head, FCs per lane");
+  const int hq = hkv * G;
+  __shared__ uint2 patch[kMaxPlanes];
+
+  const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int tile0 = tile * kTipTokens;
+  const int h = g * G + wave;  // this wave's query head within the KV head's group
+
+  // Scalar loads first, issued together (see tip_kernel): the head's (FC,
+  // plane) list, the length and the KV head's plane offset (the first three
+  // arguments arrive preloaded).
+  int2 hf[PW];
+#pragma unroll
+  for (int k = 0; k < PW; ++k) hf[k] = head_fc[(size_t)h * kHeadPlanes + k];
+  int v = seq_lens[b];
+  int p0 = po.off[g];
+  asm volatile("" : "+s"(v), "+s"(p0), "+s"(fc_slot), "+s"(k_new), "+s"(v_new));
+  const global_ptr<const int32_t> fc_slot_g = to_global(fc_slot);
+  const global_ptr<const T> k_new_g = to_global(static_cast<const T*>(k_new));
+  const global_ptr<const T> v_new_g = to_global(static_cast<const T*>(v_new));
+  const size_t plane0 = (size_t)b * P + p0;
+
+  // This lane's FC c = lane % C of head h: query pair and frequency; and the
+  // step's key and value pair of FC c (query-only launches read q instead,
+  // as in tip_kernel).
+  const int c = lane % C;
+  const T* qs = static_cast<const T*>(q) + ((size_t)b * hq + h) * D;
+  const T qr0 = qs[fc_lo(c, R)];
+  const T qr1 = qs[fc_hi(c, R, C)];
+  const double om = omega[c];
+  const int slot_c = fc_slot_g[g * C + c];
+  const bool decode = (mode == kPrologueDecode);
+  const size_t kv_src = ((size_t)b * hkv + g) * D;
+  const global_ptr<const T> ksrc = decode ? k_new_g : to_global(static_cast<const T*>(q));
+  const global_ptr<const T> vsrc = decode ? v_new_g : to_global(static_cast<const T*>(q));
+  const T kr0 = ksrc[kv_src + fc_lo(c, R)];
+  const T kr1 = ksrc[kv_src + fc_hi(c, R, C)];
+  const T vr0 = vsrc[kv_src + fc_lo(c, R)];
+  const T vr1 = vsrc[kv_src + fc_hi(c, R, C)];
+
+  __builtin_amdgcn_sched_barrier(0);
+
+  const int n = decode ? v + 1 : v;
+  const bool ok = v >= 0 && n >= 1 && n <= max_seq_len && n <= cap;
+  const bool lead = (tile == 0 && g == 0 && tid == 0);
+  const bool live = ok && tile0 < n;
+  const long pos = n - 1;
+  const bool owner = live && decode && (pos - tile0 < kTipTokens);
+
+  // The head's planes, all in flight (empty ranges past its list, past n,
+  // and for a workgroup with nothing to score).
+  const int left = live ? ((n + 3) & ~3) - tile0 : 0;
+  const int range = left * kPairBytes;
+  const uint32_t voff = (uint32_t)lane * 4 * kPairBytes;
+  // The tile's first pair in plane 0 of the KV head; plane sl is sl planes
+  // further (a 32-bit offset: the launcher checks that it fits).
+  const char* kvb = static_cast<const char*>(sidecar) +
+                    (plane0 * (size_t)cap + (size_t)tile0) * kPairBytes;
+  const uint32_t plane_bytes = (uint32_t)cap * kPairBytes;
+  uint4 xa[PW], xb[PW];
+#pragma unroll
+  for (int k = 0; k < PW; ++k) {
+    const int sl = hf[k].y;
+    const bool valid = sl >= 0;
+    const char* base = kvb + (valid ? (uint32_t)sl * plane_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(base), (short)0, valid ? range : 0, kBufferRsrcWord3);
+    const auto va = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
+    xa[k] = make_uint4(va[0], va[1], va[2], va[3]);
+    if constexpr (!BF16) {
+      const auto vb = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16, 0, 0);
+      xb[k] = make_uint4(vb[0], vb[1], vb[2], vb[3]);
+    }
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Rotation of FC c at position n - 1 (angle reduced in fp64, sine and
+  // cosine in fp32, as in tip_kernel).
+  const bool pass = om == 0.0;
+  const double qx0 = to_f64(qr0), qx1 = to_f64(qr1);
+  const double ang = (double)pos * om;
+  const double rev = ang * 0.15915494309189533577;  // 1 / (2 pi)
+  const float red = (float)((rev - rint(rev)) * 6.28318530717958647693);
+  float sf, cf;
+  sincosf(red, &sf, &cf);
+  const float qy0 = (float)(pass ? qx0 : qx0 * (double)cf - qx1 * (double)sf);
+  const float qy1 = (float)(pass ? qx1 : qx1 * (double)cf + qx0 * (double)sf);
+  uint2 own_bits = make_uint2(0u, 0u);
+  if (owner && wave == 0 && lane < C) {
+    // The tile holding the step's position rotates the step's key in fp64.
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    own_bits = rotate_pair<BF16>(to_f64(kr0), to_f64(kr1), sn, cs, pass);
+    if (slot_c >= 0) patch[slot_c] = own_bits;
+  }
+  if (!live) {
+    if (lead) {
+      nb_out[b] = ok ? n : 0;
+      if (!ok && !(mode == kPrologueQueryOnly && v == 0)) raise_flag(err, FASA_DEVFLAG_SEQ_LEN);
+    }
+    return;
+  }
+  if (owner) __syncthreads();  // the patch is written (owner is uniform per workgroup)
+
+  // The head's weights: the rotated pair of its k-th dominant FC, read from
+  // that FC's lane.
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const bool pos_lane = lane == (int)((pos - tile0) >> 2);
+  const int pos_t = (int)(pos & 3);
+  auto sums = [&](auto own) {
+    constexpr bool OWN = decltype(own)::value;
+#pragma unroll
+    for (int k = 0; k < PW; ++k) {
+      const int fc = hf[k].x, sl = hf[k].y;
+      if (sl < 0) break;
+      const float wx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qy0), fc));
+      const float wy = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qy1), fc));
+      uint4 da = xa[k], db = xb[k];
+      if constexpr (OWN) {
+        const uint2 p = patch[sl];
+        if constexpr (BF16) {
+          da.x = (pos_lane && pos_t == 0) ? p.x : da.x;
+          da.y = (pos_lane && pos_t == 1) ? p.x : da.y;
+          da.z = (pos_lane && pos_t == 2) ? p.x : da.z;
+          da.w = (pos_lane && pos_t == 3) ? p.x : da.w;
+        } else {
+          da.x = (pos_lane && pos_t == 0) ? p.x : da.x;
+          da.y = (pos_lane && pos_t == 0) ? p.y : da.y;
+          da.z = (pos_lane && pos_t == 1) ? p.x : da.z;
+          da.w = (pos_lane && pos_t == 1) ? p.y : da.w;
+          db.x = (pos_lane && pos_t == 2) ? p.x : db.x;
+          db.y = (pos_lane && pos_t == 2) ? p.y : db.y;
+          db.z = (pos_lane && pos_t == 3) ? p.x : db.z;
+          db.w = (pos_lane && pos_t == 3) ? p.y : db.w;
+        }
+      }
+      float lo[4], hi[4];
+      if constexpr (BF16) {
+        const uint32_t wd[4] = {da.x, da.y, da.z, da.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          lo[t] = bf16_lo(wd[t]);
+          hi[t] = bf16_hi(wd[t]);
+        }
+      } else {
+        lo[0] = __uint_as_float(da.x);
+        hi[0] = __uint_as_float(da.y);
+        lo[1] = __uint_as_float(da.z);
+        hi[1] = __uint_as_float(da.w);
+        lo[2] = __uint_as_float(db.x);
+        hi[2] = __uint_as_float(db.y);
+        lo[3] = __uint_as_float(db.z);
+        hi[3] = __uint_as_float(db.w);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t] = fmaf(wy, hi[t], fmaf(wx, lo[t], acc[t]));
+    }
+  };
+  if (owner)
+    sums(std::true_type{});
+  else
+    sums(std::false_type{});
+
+  // Stores: the lane's 4 scores, the group maxima, the rotated query (tile 0),
+  // the step's K, V and sidecar pairs (owner tile), the length.
+  const int j = tile0 + lane * 4;
+  float* dst = scores + ((size_t)b * hq + h) * cap + j;
+  const float4 s4 = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  if (j + 4 <= n) {
+    *reinterpret_cast<float4*>(dst) = s4;
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (j + t < n) dst[t] = acc[t];
+  }
+  if (gmax != nullptr) {
+    uint32_t km = 0u;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t kk = score_key(acc[t]);
+      km = max(km, (j + t < n) ? (kk ? kk : 1u) : 0u);
+    }
+    km = max(km, dpp_u32<0xB1>(km));  // quad_perm [1,0,3,2]
+    km = max(km, dpp_u32<0x4E>(km));  // quad_perm [2,3,0,1]: the quad's maximum
+    if ((lane & 3) == 0 && j < n)
+      gmax[((size_t)b * hq + h) * gstride + (size_t)(j / kGroupTokens)] = km;
+  }
+  if (tile == 0 && lane < C) {
+    float* qr = qrot + ((size_t)b * hq + h) * D;
+    qr[fc_lo(c, R)] = qy0;
+    qr[fc_hi(c, R, C)] = qy1;
+  }
+  if (owner && wave == 0 && lane < C) {
+    const size_t dst_kv = (((size_t)b * hkv + g) * cap + pos) * D;
+    store_fc_pair<BF16>(own_bits, vr0, vr1, static_cast<T*>(k_cache) + dst_kv,
+                        static_cast<T*>(v_cache) + dst_kv, sidecar, plane0, slot_c,
+                        fc_lo(c, R), fc_hi(c, R, C), cap, pos);
+  }
+  if (lead) nb_out[b] = n;
+}
+
 template <bool BF16, int G, int D>
 static void launch_tip_t(dim3 grid, hipStream_t s, int mode, const PlaneOffsets& po,
                          const TipArgs& a, const fasa_ctx* c, int32_t* nb, float* qrot,
@@ -356,6 +586,23 @@ static void launch_tip_t(dim3 grid, hipStream_t s, int mode, const PlaneOffsets&
                      a.sidecar, mode, a.max_seq_len, c->cap, c->P, c->R, c->hkv, a.q,          \
                      c->tab.omega, c->tab.fc_slot, c->tab.dom_mask, a.k_new, a.v_new,          \
                      a.k_cache, a.v_cache, nb, qrot, scores, err, po, gmax, c->ws.gstride)
+  if constexpr (G == 4 || G == 8) {
+    if (c->F <= kHeadPlanes &&
+        (unsigned long long)c->max_union * (unsigned long long)c->cap * (BF16 ? 4u : 8u) <
+            (1ull << 32)) {
+#define FASA_TIP_HEAD(PWV)                                                                   \
+  hipLaunchKernelGGL((tip_head_kernel<BF16, G, D, PWV>), grid, dim3(G * kWave), 0, s,        \
+                     a.seq_lens, a.sidecar, c->tab.head_fc, mode, a.max_seq_len, c->cap, c->P, \
+                     c->R, c->hkv, a.q, c->tab.omega, c->tab.fc_slot, a.k_new, a.v_new,        \
+                     a.k_cache, a.v_cache, nb, qrot, scores, err, po, gmax, c->ws.gstride)
+      if (c->F <= 4) FASA_TIP_HEAD(4);
+      else if (c->F <= 8) FASA_TIP_HEAD(8);
+      else if (c->F <= 12) FASA_TIP_HEAD(12);
+      else FASA_TIP_HEAD(16);
+#undef FASA_TIP_HEAD
+      return;
+    }
+  }
   // Loads per wave: the largest union over the KV heads, 4 planes per step.
   const int pw = (c->max_union + kTipWaves - 1) / kTipWaves;
   if (pw <= 4) FASA_TIP(4);

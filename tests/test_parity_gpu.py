@@ -103,7 +103,7 @@ def test_append_past_capacity_raises_flag(gpu):
 
 # ---------------------------------------------------------------- TIP ----
 
-@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "h64s", "f128s"])
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "h64s", "f128s", "g1s", "g2s", "g8s"])
 def test_tip_scores(gpu, name):
     w, x, g, o = _prefilled(gpu, name)
     # Score the prefilled tokens with the step-0 query at position n0 - 1.
