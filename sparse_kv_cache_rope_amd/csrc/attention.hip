@@ -240,13 +240,17 @@ dense_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
 // (q~ - hi, rounded again), so a logit is two columns' sum and keeps about
 // 2^-16 relative precision.  The softmax weights and P . V stay on VALU.
 //
-// A wave takes 32 consecutive tokens (2 tiles) of the workgroup's 256-token
-// split: all its K and V loads go out first (113 VGPRs, so two workgroups
-// share a CU and one streams while the other computes); the logits of its
-// tiles give the wave's
-// maximum and sum per head; V rows are read 4 per load, lane l holding row
-// l % 4 and dims 8 (l / 4) .. 8 (l / 4) + 7, so the sum over a load's rows is
-// a quad reduction.  The 8 waves' states merge once through LDS.
+// A wave takes 32 consecutive tokens (2 tiles) of each 256-token chunk of
+// the workgroup's split.  With one chunk per workgroup (MULTI false) all its
+// K and V loads go out first (113 VGPRs, so two workgroups share a CU and one
+// streams while the other computes).  When the grid would not fit the device
+// at once, a workgroup walks several chunks (MULTI) with the next chunk's K
+// loads issued as soon as this chunk's logits are done and its V loads as
+// soon as the weighted V sum is, an online softmax state carried across
+// chunks (about 210 VGPRs, one workgroup per CU, one round of workgroups).
+// V rows are read 4 per load, lane l holding row l % 4 and dims
+// 8 (l / 4) .. 8 (l / 4) + 7, so the sum over a load's rows is a quad
+// reduction.  The 8 waves' states merge once through LDS.
 typedef __bf16 fasa_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float fasa_f32x4 __attribute__((ext_vector_type(4)));
 
@@ -262,12 +266,12 @@ __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
 }
 
-template <int HPW>
+template <int HPW, bool MULTI>
 __global__ void __launch_bounds__(kDenseThreads)
 dense_mfma_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_cache,
                   const uint16_t* __restrict__ q, const int32_t* __restrict__ seq_lens,
                   const double* __restrict__ omega, int R, int max_seq_len, int hq, int hkv,
-                  int cap, int splits, int batch, int groups, float* __restrict__ partial,
+                  int cap, int splits, int cpw, int batch, int groups, float* __restrict__ partial,
                   int max_splits, float* __restrict__ out, int32_t* __restrict__ nb_out,
                   uint32_t* err) {
   constexpr int D = 128;
@@ -295,35 +299,56 @@ dense_mfma_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_c
     nb_out[b] = n;
     if (!len_ok && n_in != 0) raise_flag(err, FASA_DEVFLAG_SEQ_LEN);
   }
-  const int nsplit = (n + kDenseSplitTokens - 1) / kDenseSplitTokens;
+  const int span = kDenseSplitTokens * cpw;  // tokens of one split: cpw chunks
+  const int nsplit = (n + span - 1) / span;
   const size_t row0 = (size_t)b * hq + (size_t)g * (HPW * groups) + (size_t)(round % groups) * HPW;
-  if (nsplit == 0) {
-    if (split == 0)
+  // With several splits in the launch every split writes a partial state
+  // (an empty one past the row's tokens) and the merge, which then needs no
+  // lengths, writes the output.
+  if (split >= nsplit) {
+    if (splits > 1) {
+      for (int i = threadIdx.x; i < HPW * (D + 2); i += kDenseThreads) {
+        const int h = i / (D + 2), e = i % (D + 2);
+        partial[((row0 + h) * max_splits + split) * (D + 2) + e] = e == 0 ? -INFINITY : 0.0f;
+      }
+    } else {
       for (int i = threadIdx.x; i < HPW * D; i += kDenseThreads) out[row0 * D + i] = 0.0f;
+    }
     return;
   }
-  if (split >= nsplit) return;
 
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const size_t kvbase = ((size_t)b * hkv + g) * cap;
   const uint4* K = static_cast<const uint4*>(k_cache);
   const uint4* V = static_cast<const uint4*>(v_cache);
-  const int tw = split * kDenseSplitTokens + wave * (T * 16);  // the wave's first token
+  const int t_split = split * span;
+  // Chunks of this split that hold tokens (one without MULTI).
+  const int nch = MULTI ? min(cpw, (n - t_split + kDenseSplitTokens - 1) / kDenseSplitTokens) : 1;
 
-  // Every K and V load of the wave first (tokens past n read row 0, masked).
+  // A chunk's K and V loads for this wave (tokens past n read row 0, masked).
   uint4 kr[T][KK], vr[T][4];
+  auto issue_k = [&](int ch) {
+    const int tw = t_split + ch * kDenseSplitTokens + wave * (T * 16);
 #pragma unroll
-  for (int j = 0; j < T; ++j) {
-    const int tk = tw + 16 * j + lane % 16;
-    const size_t kb = (kvbase + (size_t)(tk < n ? tk : 0)) * (D / 8) + lane / 16;
+    for (int j = 0; j < T; ++j) {
+      const int tk = tw + 16 * j + lane % 16;
+      const size_t kb = (kvbase + (size_t)(tk < n ? tk : 0)) * (D / 8) + lane / 16;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kr[j][kk] = K[kb + 4 * kk];
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int tv = tw + 16 * j + 4 * s4 + lane % 4;
-      vr[j][s4] = V[(kvbase + (size_t)(tv < n ? tv : 0)) * (D / 8) + lane / 4];
+      for (int kk = 0; kk < KK; ++kk) kr[j][kk] = K[kb + 4 * kk];
     }
-  }
+  };
+  auto issue_v = [&](int ch) {
+    const int tw = t_split + ch * kDenseSplitTokens + wave * (T * 16);
+#pragma unroll
+    for (int j = 0; j < T; ++j)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int tv = tw + 16 * j + 4 * s4 + lane % 4;
+        vr[j][s4] = V[(kvbase + (size_t)(tv < n ? tv : 0)) * (D / 8) + lane / 4];
+      }
+  };
+  issue_k(0);
+  issue_v(0);
 
   // The queries, rotated to position n - 1 while the loads fly: one FC pair
   // per thread (angle reduced in fp64, sine and cosine in fp32, as TIP does).
@@ -366,67 +391,87 @@ dense_mfma_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_c
     }
   }
 
-  // Logits: tile j's D fragment holds tokens 16 j + 4 (l / 16) + i of column
-  // c; head c's logit is column c plus column c + HPW (lane l + HPW).
-  float z[T][4];
-  float m = -INFINITY;
+  // The wave's running state: max m per head (lanes c < HPW; l, l ^ 16,
+  // l ^ 32 hold the same head), sum of weights per lane, and the weighted V
+  // sums of every head for the lane's dims.
+  float m = -INFINITY, lsum = 0.0f;
+  float acc_o[HPW][8];
 #pragma unroll
-  for (int j = 0; j < T; ++j) {
-    fasa_f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int h = 0; h < HPW; ++h)
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(fasa_bf16x8, kr[j][kk]),
-                                                    qb[kk], acc, 0, 0, 0);
+    for (int e = 0; e < 8; ++e) acc_o[h][e] = 0.0f;
+  for (int ch = 0; ch < nch; ++ch) {
+    const int tw = t_split + ch * kDenseSplitTokens + wave * (T * 16);  // the wave's first token
+    // Logits: tile j's D fragment holds tokens 16 j + 4 (l / 16) + i of
+    // column c; head c's logit is column c plus column c + HPW (lane l + HPW).
+    float z[T][4];
+    float mc = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float v = acc[i] + dpp_f<0x100 + HPW>(acc[i]);  // row_shl: lane l + HPW
-      const int tk = tw + 16 * j + 4 * (lane / 16) + i;
-      z[j][i] = (c < HPW && tk < n) ? v : -INFINITY;
-      m = fmaxf(m, z[j][i]);
+    for (int j = 0; j < T; ++j) {
+      fasa_f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(fasa_bf16x8, kr[j][kk]),
+                                                      qb[kk], acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = acc[i] + dpp_f<0x100 + HPW>(acc[i]);  // row_shl: lane l + HPW
+        const int tk = tw + 16 * j + 4 * (lane / 16) + i;
+        z[j][i] = (c < HPW && tk < n) ? v : -INFINITY;
+        mc = fmaxf(mc, z[j][i]);
+      }
     }
+    if (MULTI && ch + 1 < nch) issue_k(ch + 1);  // the K registers are free again
+    mc = fmaxf(mc, __shfl_xor(mc, 16));
+    mc = fmaxf(mc, __shfl_xor(mc, 32));
+    const float mn = fmaxf(m, mc);
+    // The rescale of the state so far (m = -inf gives 0; nothing yet if the
+    // new max is -inf too).
+    const float own_sc = mn == -INFINITY ? 1.0f : exp2f(m - mn);
+    m = mn;
+    lsum *= own_sc;
+#pragma unroll
+    for (int j = 0; j < T; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = mn == -INFINITY ? 0.0f : exp2f(z[j][i] - mn);  // -inf gives 0
+        lsum += p;
+        if (c < HPW) pl[wave][16 * j + 4 * (lane / 16) + i][c] = p;
+      }
+    // The wave reads back what its own lanes wrote (LDS keeps a wave's
+    // accesses in order); the barrier only stops the compiler moving them.
+    __builtin_amdgcn_wave_barrier();
+    if (MULTI) {
+#pragma unroll
+      for (int h = 0; h < HPW; ++h) {
+        const float sc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(own_sc), h));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc_o[h][e] *= sc;
+      }
+    }
+    // Weighted V: lane l adds rows 16 j + 4 s + l % 4, dims 8 (l / 4) ...
+#pragma unroll
+    for (int j = 0; j < T; ++j)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const float4 p4 = *reinterpret_cast<const float4*>(pl[wave][16 * j + 4 * s4 + lane % 4]);
+        const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+        float vf[8];
+        unpack<true, 8>(vr[j][s4], vf);
+#pragma unroll
+        for (int h = 0; h < HPW; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc_o[h][e] = fmaf(pv[h], vf[e], acc_o[h][e]);
+      }
+    if (MULTI && ch + 1 < nch) issue_v(ch + 1);  // the V registers are free again
+    __builtin_amdgcn_wave_barrier();              // pl is rewritten by the next chunk
   }
-  // The wave's max and sum per head (lanes c < HPW; l, l ^ 16, l ^ 32 hold
-  // the same head).
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
-  float lsum = 0.0f;
-#pragma unroll
-  for (int j = 0; j < T; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = m == -INFINITY ? 0.0f : exp2f(z[j][i] - m);  // -inf gives 0
-      lsum += p;
-      if (c < HPW) pl[wave][16 * j + 4 * (lane / 16) + i][c] = p;
-    }
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
   if (lane < HPW) {
     mw[wave][lane] = m;
     lw[wave][lane] = lsum;
   }
-  // The wave reads back what its own lanes wrote (LDS keeps a wave's
-  // accesses in order); the barrier only stops the compiler moving them.
-  __builtin_amdgcn_wave_barrier();
-
-  // Weighted V: lane l adds rows 16 j + 4 s + l % 4, dims 8 (l / 4) ...
-  float acc_o[HPW][8];
-#pragma unroll
-  for (int h = 0; h < HPW; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc_o[h][e] = 0.0f;
-#pragma unroll
-  for (int j = 0; j < T; ++j)
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const float4 p4 = *reinterpret_cast<const float4*>(pl[wave][16 * j + 4 * s4 + lane % 4]);
-      const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
-      float vf[8];
-      unpack<true, 8>(vr[j][s4], vf);
-#pragma unroll
-      for (int h = 0; h < HPW; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc_o[h][e] = fmaf(pv[h], vf[e], acc_o[h][e]);
-    }
 #pragma unroll
   for (int h = 0; h < HPW; ++h)
 #pragma unroll
@@ -457,7 +502,7 @@ dense_mfma_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_c
       L = fmaf(lw[w][h], wt, L);
       S = fmaf(red[w][h][d], wt, S);
     }
-    if (nsplit == 1) {
+    if (splits == 1) {
       out[(row0 + h) * D + d] = L > 0.0f ? S / L : 0.0f;
     } else {
       float* part = partial + ((row0 + h) * max_splits + split) * (D + 2);
@@ -502,18 +547,22 @@ __device__ __forceinline__ MergeState shfl_xor_state(MergeState x, int k) {
 template <int D>
 __global__ void __launch_bounds__(kMergeThreads)
 merge_kernel(const float* __restrict__ partial, int max_splits, const int32_t* __restrict__ nb,
-             int max_seq_len, int cap, int budget, int unit, int hq, float* __restrict__ out) {
+             int max_seq_len, int cap, int budget, int unit, int hq, int fixed_splits,
+             float* __restrict__ out) {
   constexpr int SL = kMergeThreads / kMergeDims;  // split lanes
   constexpr int NWV = kMergeThreads / kWave;
   constexpr int U = 8;  // splits per thread in flight
   __shared__ MergeState ws[NWV][kMergeDims];
   const int h = blockIdx.x, b = blockIdx.y, d0 = blockIdx.z * kMergeDims;
   const size_t row = (size_t)b * hq + h;
-  int n = nb[b];
-  if (n < 0 || n > max_seq_len || n > cap) n = 0;
-  const int work = (budget > 0 && budget < n) ? budget : n;
-  const int nsplit = (work + unit - 1) / unit;
-  if (nsplit <= 1) return;  // written directly by the split kernel
+  int nsplit = fixed_splits;  // every split wrote a state (the dense launch)
+  if (fixed_splits == 0) {
+    int n = nb[b];
+    if (n < 0 || n > max_seq_len || n > cap) n = 0;
+    const int work = (budget > 0 && budget < n) ? budget : n;
+    nsplit = (work + unit - 1) / unit;
+    if (nsplit <= 1) return;  // written directly by the split kernel
+  }
   const float* p = partial + row * max_splits * (D + 2);
   const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
   const int dd = t % kMergeDims;
@@ -562,14 +611,15 @@ merge_kernel(const float* __restrict__ partial, int max_splits, const int32_t* _
 // ------------------------------------------------------------ launchers --
 
 static void launch_merge(const fasa_ctx* c, const float* part, int max_splits, const int32_t* nb,
-                         int max_seq_len, int budget, int unit, float* out, hipStream_t s) {
+                         int max_seq_len, int budget, int unit, float* out, hipStream_t s,
+                         int fixed_splits = 0) {
   dim3 grid((unsigned)c->hq, (unsigned)c->batch, (unsigned)(c->d / kMergeDims));
   if (c->d == 128)
     hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, s, part, max_splits, nb,
-                       max_seq_len, c->cap, budget, unit, c->hq, out);
+                       max_seq_len, c->cap, budget, unit, c->hq, fixed_splits, out);
   else
     hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeThreads), 0, s, part, max_splits, nb,
-                       max_seq_len, c->cap, budget, unit, c->hq, out);
+                       max_seq_len, c->cap, budget, unit, c->hq, fixed_splits, out);
 }
 
 hipError_t launch_fac(const fasa_ctx* c, const void* k_cache, const void* v_cache,
@@ -606,29 +656,46 @@ hipError_t launch_dense_fused(const fasa_ctx* c, const void* k_cache, const void
                               const void* q, const int32_t* seq_lens, int max_seq_len,
                               float* out, uint8_t* ws, hipStream_t s) {
   if (c->dtype != FASA_BF16 || c->d != 128) return hipErrorInvalidValue;
-  int splits = (max_seq_len + kDenseSplitTokens - 1) / kDenseSplitTokens;
-  if (splits < 1) splits = 1;
-  float* part = reinterpret_cast<float*>(ws + c->ws.dense);
-  int32_t* nb = reinterpret_cast<int32_t*>(ws + c->ws.nb);
-  uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
   // Query heads per workgroup: all of the group's, at most 4.
   const int hpw = c->G < 4 ? c->G : 4;
   const int groups = c->G / hpw;
+  // 256-token chunks per workgroup: one while the grid fits two workgroups
+  // per CU at once; else enough that it fits one per CU (a workgroup that
+  // walks several chunks keeps the next chunk's loads in flight and holds
+  // about 210 VGPRs).
+  const int chunks = max(1, (max_seq_len + kDenseSplitTokens - 1) / kDenseSplitTokens);
+  const long per_split = (long)c->hkv * c->batch * groups;
+  const long cus = c->cus > 0 ? c->cus : 256;
+  int cpw = 1;
+  if ((long)chunks * per_split > 2 * cus)
+    cpw = (int)std::min<long>(chunks, ((long)chunks * per_split + cus - 1) / cus);
+  const int splits = (chunks + cpw - 1) / cpw;
+  float* part = reinterpret_cast<float*>(ws + c->ws.dense);
+  int32_t* nb = reinterpret_cast<int32_t*>(ws + c->ws.nb);
+  uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
   const long tuples = (long)splits * c->hkv * c->batch;
   const long ids = (tuples + 7) / 8 * 8 * groups;
   if (ids * kDenseThreads > 0xffffffffL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)ids);
   const uint16_t* qb = static_cast<const uint16_t*>(q);
-#define FASA_DENSE_MFMA(GG)                                                                   \
-  hipLaunchKernelGGL((dense_mfma_kernel<GG>), grid, dim3(kDenseThreads), 0, s, k_cache, v_cache, \
-                     qb, seq_lens, c->tab.omega, c->R, max_seq_len, c->hq, c->hkv, c->cap,       \
-                     splits, c->batch, groups, part, c->ws.dense_splits, out, nb, err)
-  if (hpw == 1) FASA_DENSE_MFMA(1);
-  else if (hpw == 2) FASA_DENSE_MFMA(2);
-  else FASA_DENSE_MFMA(4);
+#define FASA_DENSE_MFMA(GG, MM)                                                             \
+  hipLaunchKernelGGL((dense_mfma_kernel<GG, MM>), grid, dim3(kDenseThreads), 0, s, k_cache,    \
+                     v_cache, qb, seq_lens, c->tab.omega, c->R, max_seq_len, c->hq, c->hkv,    \
+                     c->cap, splits, cpw, c->batch, groups, part, c->ws.dense_splits, out, nb, \
+                     err)
+  if (cpw == 1) {
+    if (hpw == 1) FASA_DENSE_MFMA(1, false);
+    else if (hpw == 2) FASA_DENSE_MFMA(2, false);
+    else FASA_DENSE_MFMA(4, false);
+  } else {
+    if (hpw == 1) FASA_DENSE_MFMA(1, true);
+    else if (hpw == 2) FASA_DENSE_MFMA(2, true);
+    else FASA_DENSE_MFMA(4, true);
+  }
 #undef FASA_DENSE_MFMA
   if (splits > 1)
-    launch_merge(c, part, c->ws.dense_splits, nb, max_seq_len, 0, kDenseSplitTokens, out, s);
+    launch_merge(c, part, c->ws.dense_splits, nb, max_seq_len, 0, kDenseSplitTokens * cpw, out,
+                 s, splits);
   return hipGetLastError();
 }
 

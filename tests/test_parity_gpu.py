@@ -49,6 +49,12 @@ SMALL = {
     # B past the fused limit on rows chunks would barely cut: each row held
     # whole in 1024 threads (32 per thread), then the split FAC.
     "c4w": small("c4", batch=1, context=20000, budget=5000, steps=2),
+    # Dense grids past two workgroups per CU, so each workgroup walks several
+    # 256-token chunks: 1, 2, 4 (ragged) and 8 query heads per KV head.
+    "dm1": small("c3", batch=4, n_q_heads=8, n_kv_heads=8, context=6001, context_min=3000),
+    "dm2": small("c2", n_q_heads=16, n_kv_heads=8, context=20000),
+    "dm4": small("c3", batch=6, context=8192, context_min=4096),
+    "dm8": small("c3", batch=3, n_q_heads=16, n_kv_heads=2, context=30001, context_min=15000),
 }
 
 
@@ -277,7 +283,8 @@ def test_sparse_attn_bad_index_flags(gpu):
 
 # -------------------------------------------------------------- dense ----
 
-@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "h64s", "f128s", "g1s", "g8s"])
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "h64s", "f128s", "g1s", "g8s",
+                                  "dm1", "dm2", "dm4", "dm8"])
 def test_dense_attn(gpu, name):
     w, x, g, o = _prefilled(gpu, name)
     n = torch.from_numpy((x["ctx"] - 1).astype(np.int32)).cuda()
