@@ -49,6 +49,13 @@
  *   only the device can see (a sequence length beyond max_seq_len or cap, an
  *   index >= its sequence length) set a sticky flag in the workspace; the
  *   affected rows produce zeros / -1 and fasa_check() reports the flag.
+ * - Tracing (host side, off by default, read once per process): with
+ *   FASA_LOG=1 every call below (getters aside) writes one line to stderr,
+ *   "fasa: <call>(<arguments that shape its launches>)", and one more,
+ *   "fasa: <call>: error <status>: <message>", when it refuses its
+ *   arguments; with FASA_ROCTX=1 every such call is a roctx range (loaded from
+ *   the ROCm marker library on first use; rocprofv3 --marker-trace records
+ *   them around the call's kernels).
  */
 #ifndef FASA_H
 #define FASA_H

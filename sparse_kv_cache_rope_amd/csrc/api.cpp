@@ -3,10 +3,13 @@
 
 #include <hip/hip_runtime.h>
 
+#include <dlfcn.h>
+
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -22,6 +25,76 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// Host-side call log and trace ranges (no GPU work, off by default):
+//   FASA_LOG=1    one line per C-ABI call on stderr (the call and the
+//                 arguments that shape its launches), and one per error it
+//                 returns;
+//   FASA_ROCTX=1  a roctx range around each call (rocprofv3 --marker-trace
+//                 shows them next to the kernels), through the ROCm marker
+//                 library, loaded on first use.
+bool env_on(const char* name) {
+  const char* v = std::getenv(name);
+  return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
+}
+
+bool log_on() {
+  static const bool on = env_on("FASA_LOG");
+  return on;
+}
+
+struct Roctx {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+
+const Roctx& roctx() {
+  static const Roctx r = [] {
+    Roctx x;
+    if (!env_on("FASA_ROCTX")) return x;
+    void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+    if (h == nullptr) {
+      std::fprintf(stderr, "fasa: FASA_ROCTX set but the roctx library did not load: %s\n",
+                   dlerror());
+      return x;
+    }
+    x.push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+    x.pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+    if (x.push == nullptr || x.pop == nullptr) x = Roctx{};
+    return x;
+  }();
+  return r;
+}
+
+thread_local const char* g_call = nullptr;  // the C-ABI call in progress (for the log)
+
+// One per C-ABI call: logs the call, opens and closes its roctx range.
+class ApiScope {
+ public:
+  ApiScope(const char* name, const char* fmt, ...) : outer_(g_call) {
+    g_call = name;
+    if (log_on()) {
+      char buf[384];
+      va_list ap;
+      va_start(ap, fmt);
+      std::vsnprintf(buf, sizeof buf, fmt, ap);
+      va_end(ap);
+      std::fprintf(stderr, "fasa: %s(%s)\n", name, buf);
+    }
+    if (roctx().push) roctx().push(name);
+  }
+  ~ApiScope() {
+    if (roctx().pop) roctx().pop();
+    g_call = outer_;
+  }
+  ApiScope(const ApiScope&) = delete;
+  ApiScope& operator=(const ApiScope&) = delete;
+
+ private:
+  const char* outer_;
+};
+
+#define FASA_API(...) ApiScope api_scope_(__func__, __VA_ARGS__)
+
 fasa_status fail(fasa_status st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -29,6 +102,7 @@ fasa_status fail(fasa_status st, const char* fmt, ...) {
   std::vsnprintf(buf, sizeof buf, fmt, ap);
   va_end(ap);
   g_last_error = buf;
+  if (log_on()) std::fprintf(stderr, "fasa: %s: error %d: %s\n", g_call ? g_call : "?", (int)st, buf);
   return st;
 }
 
@@ -149,6 +223,7 @@ fasa_status fasa_create_partial_rope(fasa_ctx** out, int batch, int n_q_heads, i
                                      int head_dim, int rotary_dim, int capacity,
                                      double rope_theta, fasa_dtype dtype, const int32_t* dom_fc,
                                      int n_dom, int max_budget) {
+  FASA_API("batch=%d hq=%d hkv=%d d=%d r=%d cap=%d theta=%g dtype=%d n_dom=%d max_budget=%d", batch, n_q_heads, n_kv_heads, head_dim, rotary_dim, capacity, rope_theta, (int)dtype, n_dom, max_budget);
   if (out == nullptr) return fail(FASA_ERR_INVALID_ARG, "out is null");
   *out = nullptr;
   if (batch < 1) return fail(FASA_ERR_INVALID_ARG, "batch %d < 1", batch);
@@ -300,6 +375,7 @@ fasa_status fasa_create_partial_rope(fasa_ctx** out, int batch, int n_q_heads, i
 }
 
 void fasa_destroy(fasa_ctx* ctx) {
+  FASA_API("ctx=%p", (void*)ctx);
   if (!ctx) return;
   for (hipEvent_t e : ctx->ev) (void)hipEventDestroy(e);
   if (ctx->dev_alloc) (void)hipFree(ctx->dev_alloc);
@@ -326,6 +402,7 @@ int fasa_sidecar_layout(const fasa_ctx* c, int32_t* plane_offset, int32_t* plane
 }
 
 fasa_status fasa_workspace_init(fasa_ctx* c, void* workspace, hipStream_t stream) {
+  FASA_API("ctx=%p ws=%p", (void*)c, workspace);
   FASA_TRY(check_ctx(c));
   FASA_NONNULL(workspace);
   FASA_HIP(launch_fill_zero(workspace, c->ws.total, stream), "fasa_workspace_init");
@@ -335,6 +412,7 @@ fasa_status fasa_workspace_init(fasa_ctx* c, void* workspace, hipStream_t stream
 fasa_status fasa_append_kv(fasa_ctx* c, void* k_cache, void* v_cache, void* sidecar,
                            const void* k_new, const void* v_new, const int32_t* start_pos,
                            int n_new, void* workspace, hipStream_t stream) {
+  FASA_API("ctx=%p n_new=%d ws=%p stream=%p", (void*)c, n_new, workspace, (void*)stream);
   FASA_TRY(check_ctx(c));
   if (n_new < 0) return fail(FASA_ERR_INVALID_ARG, "n_new %d < 0", n_new);
   if (n_new > c->cap) return fail(FASA_ERR_CAPACITY, "n_new %d exceeds capacity", n_new);
@@ -358,6 +436,7 @@ fasa_status fasa_append_kv(fasa_ctx* c, void* k_cache, void* v_cache, void* side
 fasa_status fasa_tip_scores(fasa_ctx* c, const void* sidecar, const void* q,
                             const int32_t* seq_lens, int max_seq_len, float* scores,
                             void* workspace, hipStream_t stream) {
+  FASA_API("ctx=%p max_seq_len=%d ws=%p stream=%p", (void*)c, max_seq_len, workspace, (void*)stream);
   FASA_TRY(check_ctx(c));
   FASA_TRY(check_len(c, max_seq_len));
   FASA_NONNULL(sidecar);
@@ -403,12 +482,14 @@ static fasa_status topk_impl(fasa_ctx* c, const float* scores, const int32_t* se
 fasa_status fasa_topk(fasa_ctx* c, const float* scores, const int32_t* seq_lens,
                       int max_seq_len, int budget, int32_t* idx, void* workspace,
                       hipStream_t stream) {
+  FASA_API("ctx=%p max_seq_len=%d budget=%d ws=%p stream=%p", (void*)c, max_seq_len, budget, workspace, (void*)stream);
   return topk_impl(c, scores, seq_lens, max_seq_len, nullptr, budget, idx, workspace, stream);
 }
 
 fasa_status fasa_topk_per_head(fasa_ctx* c, const float* scores, const int32_t* seq_lens,
                                int max_seq_len, const int32_t* head_budget, int budget,
                                int32_t* idx, void* workspace, hipStream_t stream) {
+  FASA_API("ctx=%p max_seq_len=%d budget=%d head_budget=%p ws=%p stream=%p", (void*)c, max_seq_len, budget, (const void*)head_budget, workspace, (void*)stream);
   FASA_NONNULL(head_budget);
   return topk_impl(c, scores, seq_lens, max_seq_len, head_budget, budget, idx, workspace,
                    stream);
@@ -417,6 +498,7 @@ fasa_status fasa_topk_per_head(fasa_ctx* c, const float* scores, const int32_t* 
 fasa_status fasa_sparse_attn(fasa_ctx* c, const void* k_cache, const void* v_cache,
                              const void* q, const int32_t* seq_lens, const int32_t* idx,
                              int budget, float* out, void* workspace, hipStream_t stream) {
+  FASA_API("ctx=%p budget=%d ws=%p stream=%p", (void*)c, budget, workspace, (void*)stream);
   FASA_TRY(check_ctx(c));
   FASA_TRY(check_budget(c, budget));
   FASA_NONNULL(k_cache);
@@ -531,6 +613,7 @@ fasa_status fasa_decode_step(fasa_ctx* c, void* k_cache, void* v_cache, void* si
                              int32_t* seq_lens, int max_seq_len, int budget, float* out,
                              int32_t* idx_out, void* workspace, unsigned flags,
                              hipStream_t stream) {
+  FASA_API("ctx=%p max_seq_len=%d budget=%d idx=%p flags=%u ws=%p stream=%p", (void*)c, max_seq_len, budget, (void*)idx_out, flags, workspace, (void*)stream);
   return decode_impl(c, k_cache, v_cache, sidecar, q, k_new, v_new, seq_lens, max_seq_len,
                      nullptr, budget, out, idx_out, workspace, flags, stream);
 }
@@ -541,6 +624,7 @@ fasa_status fasa_decode_step_per_head(fasa_ctx* c, void* k_cache, void* v_cache,
                                       const int32_t* head_budget, int budget, float* out,
                                       int32_t* idx_out, void* workspace, unsigned flags,
                                       hipStream_t stream) {
+  FASA_API("ctx=%p max_seq_len=%d budget=%d head_budget=%p idx=%p flags=%u ws=%p stream=%p", (void*)c, max_seq_len, budget, (const void*)head_budget, (void*)idx_out, flags, workspace, (void*)stream);
   FASA_NONNULL(head_budget);
   return decode_impl(c, k_cache, v_cache, sidecar, q, k_new, v_new, seq_lens, max_seq_len,
                      head_budget, budget, out, idx_out, workspace, flags, stream);
@@ -590,6 +674,7 @@ fasa_status fasa_decode_step_static(fasa_ctx* c, void* k_cache, void* v_cache, v
                                     int32_t* seq_lens, int max_seq_len, int budget, float* out,
                                     int32_t* idx_out, uint32_t* dev_flags, unsigned flags,
                                     hipStream_t stream) {
+  FASA_API("ctx=%p max_seq_len=%d budget=%d idx=%p flags=%u stream=%p", (void*)c, max_seq_len, budget, (void*)idx_out, flags, (void*)stream);
   FASA_TRY(check_ctx(c));
   if (c->ws.total > FASA_STATIC_SCRATCH_BYTES)
     return fail(FASA_ERR_CAPACITY,
@@ -611,6 +696,7 @@ fasa_status fasa_decode_step_static(fasa_ctx* c, void* k_cache, void* v_cache, v
 fasa_status fasa_dense_attn(fasa_ctx* c, const void* k_cache, const void* v_cache,
                             const void* q, const int32_t* seq_lens, int max_seq_len,
                             float* out, void* workspace, hipStream_t stream) {
+  FASA_API("ctx=%p max_seq_len=%d ws=%p stream=%p", (void*)c, max_seq_len, workspace, (void*)stream);
   FASA_TRY(check_ctx(c));
   FASA_TRY(check_len(c, max_seq_len));
   FASA_NONNULL(k_cache);
@@ -647,6 +733,7 @@ size_t fasa_calibrate_workspace_bytes(const fasa_ctx* c, int topk) {
 fasa_status fasa_calibrate(fasa_ctx* c, const void* k_cache, const void* q,
                            const int32_t* seq_lens, int max_seq_len, int topk, float* ca,
                            void* workspace, hipStream_t stream) {
+  FASA_API("ctx=%p max_seq_len=%d topk=%d ws=%p stream=%p", (void*)c, max_seq_len, topk, workspace, (void*)stream);
   FASA_TRY(check_ctx(c));
   FASA_TRY(check_len(c, max_seq_len));
   if (topk < 1 || topk > c->cap || topk > kCalibMaxTopk)
@@ -668,6 +755,7 @@ fasa_status fasa_calibrate(fasa_ctx* c, const void* k_cache, const void* q,
 
 fasa_status fasa_select_dominant(const float* ca, int samples, int n_q_heads, int n_fc,
                                  int n_dom, int32_t* dom_out) {
+  FASA_API("samples=%d hq=%d n_fc=%d n_dom=%d", samples, n_q_heads, n_fc, n_dom);
   if (!ca || !dom_out) return fail(FASA_ERR_INVALID_ARG, "null pointer");
   if (samples < 1 || n_q_heads < 1 || n_fc < 1 || n_dom < 1 || n_dom > n_fc)
     return fail(FASA_ERR_INVALID_ARG, "sizes out of range (samples %d, heads %d, fc %d, dom %d)",
@@ -704,6 +792,7 @@ fasa_ptr_kind fasa_pointer_kind(const void* ptr) {
 }
 
 fasa_status fasa_read_probe(const void* buf, size_t bytes, float* sink, hipStream_t stream) {
+  FASA_API("bytes=%zu stream=%p", bytes, (void*)stream);
   if (buf == nullptr || sink == nullptr) return fail(FASA_ERR_INVALID_ARG, "null pointer");
   if (bytes == 0 || bytes % 16 || reinterpret_cast<uintptr_t>(buf) % 16)
     return fail(FASA_ERR_INVALID_ARG, "bytes (%zu) and buf must be non-zero multiples of 16",
@@ -735,6 +824,7 @@ fasa_select_layout_kind fasa_decode_layout(int max_seq_len, int budget, int* thr
 }
 
 fasa_status fasa_check(fasa_ctx* c, void* workspace, hipStream_t stream, uint32_t* flags) {
+  FASA_API("ctx=%p ws=%p stream=%p", (void*)c, workspace, (void*)stream);
   FASA_TRY(check_ctx(c));
   FASA_NONNULL(workspace);
   if (flags) *flags = 0;
@@ -753,6 +843,7 @@ fasa_status fasa_check(fasa_ctx* c, void* workspace, hipStream_t stream, uint32_
 }
 
 fasa_status fasa_timing_enable(fasa_ctx* c, int enable) {
+  FASA_API("ctx=%p enable=%d", (void*)c, enable);
   FASA_TRY(check_ctx(c));
   if (enable && c->ev.empty()) {
     c->ev.assign(2 * kTimingPairs, nullptr);
@@ -764,6 +855,7 @@ fasa_status fasa_timing_enable(fasa_ctx* c, int enable) {
 }
 
 fasa_status fasa_timing_collect(fasa_ctx* c, double* total_ms, int32_t* launches) {
+  FASA_API("ctx=%p", (void*)c);
   FASA_TRY(check_ctx(c));
   if (total_ms)
     for (int k = 0; k < FASA_K_COUNT; ++k) total_ms[k] = 0.0;

@@ -96,3 +96,35 @@ def test_read_probe_rejects_bad_arguments(fasa, buf, nbytes, sink):
     st = fasa._lib.fasa_read_probe(ctypes.c_void_p(buf), nbytes, ctypes.c_void_p(sink), None)
     assert st == -1, st
     assert fasa._lib.fasa_last_error().decode()
+
+
+def _run_host_calls(env_extra):
+    """A child process makes two host-only calls (one valid, one refused)."""
+    code = ("import numpy as np, sparse_kv_cache_rope_amd as f\n"
+            "ca = np.linspace(0, 1, 64, dtype=np.float32).reshape(2, 4, 8)\n"
+            "f.select_dominant(ca, 2)\n"
+            "try:\n    f.select_dominant(ca, 9)\nexcept Exception:\n    pass\n")
+    env = dict(os.environ, **env_extra)
+    return subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                          text=True, check=True)
+
+
+def test_call_log_off_by_default(fasa):
+    r = _run_host_calls({"FASA_LOG": "0"})
+    assert "fasa:" not in r.stderr
+
+
+def test_call_log_lines(fasa):
+    r = _run_host_calls({"FASA_LOG": "1"})
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("fasa:")]
+    assert lines[0] == "fasa: fasa_select_dominant(samples=2 hq=4 n_fc=8 n_dom=2)"
+    assert lines[1] == "fasa: fasa_select_dominant(samples=2 hq=4 n_fc=8 n_dom=9)"
+    assert lines[2].startswith("fasa: fasa_select_dominant: error -1: sizes out of range")
+    assert len(lines) == 3
+
+
+def test_roctx_ranges_load_quietly(fasa):
+    # The marker library loads on first use; a call with ranges on behaves
+    # like one without.
+    r = _run_host_calls({"FASA_ROCTX": "1", "FASA_LOG": "0"})
+    assert "did not load" not in r.stderr
