@@ -97,6 +97,14 @@ def source_code_hash(paths):
     return h.hexdigest()
 
 
+def tip_kernel_name(w):
+    """The TIP kernel the library launches for this shape: one wave per query
+    head when a KV head serves 4 or 8 of them and each has at most 16
+    dominant FCs, else the union kernel."""
+    g = w.n_q_heads // w.n_kv_heads
+    return "tip_head_kernel" if g in (4, 8) and w.n_dom <= 16 else "tip_kernel"
+
+
 def traffic_from_profile():
     """HBM bytes per TIP launch from the committed rocprofv3 --pmc summary, if
     it was taken on the current kernel code (comments aside); else None."""
@@ -667,7 +675,7 @@ def main():
         "ms_per_step_warm_single_cache_eager": ms_step_warm,
         "ms_per_step_eager": ms_step_eager,
         "kernel_avg_ms_with_event_gaps": kernel_ms,
-        "roofline": {"bound": "hbm", "kernel": "tip_kernel", "kernel_avg_ms": tip_ms,
+        "roofline": {"bound": "hbm", "kernel": tip_kernel_name(w), "kernel_avg_ms": tip_ms,
                      "kernel_launches_timed": tip_n,
                      "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
