@@ -558,8 +558,16 @@ static fasa_status decode_impl(fasa_ctx* c, void* k_cache, void* v_cache, void* 
   }
   if (filtered) {
     Timed t(c, FASA_K_SELECT_FAC, stream);
+    // K and V in host memory: one workgroup per row, so each selected row
+    // crosses the host link once (column parts would each fetch its K row).
+    if (c->kv_kind.ptr.load(std::memory_order_relaxed) != k_cache) {
+      c->kv_kind.host.store(fasa_pointer_kind(k_cache) == FASA_PTR_HOST_MAPPED,
+                            std::memory_order_relaxed);
+      c->kv_kind.ptr.store(k_cache, std::memory_order_relaxed);
+    }
     FASA_HIP(launch_filter_select(c, scores, nb, max_seq_len, budget, idx_out, k_cache, v_cache,
-                                  out, advance, ws, stream, head_budget),
+                                  out, advance, ws, stream, head_budget,
+                                  c->kv_kind.host.load(std::memory_order_relaxed)),
              "fasa_decode_step: filtered select+fac");
     return ok();
   }

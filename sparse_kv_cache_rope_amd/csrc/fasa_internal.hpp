@@ -5,11 +5,27 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <vector>
 
 #include "../../include/fasa.h"
 
 namespace fasa {
+
+// A pointer and whether it is host memory mapped into the device, read and
+// written from any thread (copyable, so a context can be copied).
+struct KvKindHint {
+  std::atomic<const void*> ptr{nullptr};
+  std::atomic<bool> host{false};
+  KvKindHint() = default;
+  KvKindHint(const KvKindHint& o)
+      : ptr(o.ptr.load(std::memory_order_relaxed)), host(o.host.load(std::memory_order_relaxed)) {}
+  KvKindHint& operator=(const KvKindHint& o) {
+    ptr.store(o.ptr.load(std::memory_order_relaxed), std::memory_order_relaxed);
+    host.store(o.host.load(std::memory_order_relaxed), std::memory_order_relaxed);
+    return *this;
+  }
+};
 
 // Device-resident constant tables, one allocation.
 struct DeviceTables {
@@ -60,6 +76,10 @@ struct fasa_ctx {
   std::vector<hipEvent_t> ev;     // pairs: ev[2i] start, ev[2i+1] stop
   std::vector<int> ev_family;     // family of each recorded pair
   int ev_used = 0;
+  // The last K cache pointer a decode step saw and whether it is host memory
+  // mapped into the device (a launch-shape hint only: both shapes give the
+  // same results).
+  fasa::KvKindHint kv_kind;
 };
 
 namespace fasa {
@@ -188,10 +208,14 @@ bool filter_path_applies(int max_seq_len, int budget);
 // and survivor slots per thread of its second (12 or 40).
 int filter_group_slots(int max_seq_len);
 int filter_survivor_slots(int budget);
+// whole_rows: one workgroup per row even when the rows are few (K and V in
+// host memory: each row crosses the host link once instead of once per
+// column part).
 hipError_t launch_filter_select(const fasa_ctx* c, const float* scores, const int32_t* nb,
                                 int max_seq_len, int budget, int32_t* idx, const void* k_cache,
                                 const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
-                                hipStream_t s, const int32_t* head_budget = nullptr);
+                                hipStream_t s, const int32_t* head_budget = nullptr,
+                                bool whole_rows = false);
 
 // Calibration (calibrate.hip): its workspace regions (err, nb, qrot, scores
 // [b][Hq (C + 1)][cap], idx [b][Hq (C + 1)][topk], cand), and the launcher.

@@ -1006,8 +1006,9 @@ template <bool BF16, int D, int E1, int E2>
 static void launch_filter_t(const fasa_ctx* c, hipStream_t s, const uint32_t* gm,
                             const float* scores, const int32_t* nb, int max_seq_len, int budget,
                             const int32_t* hb, int32_t* idx, const void* k, const void* v,
-                            const float* qrot, float* out, int32_t* advance, uint32_t* err) {
-  const bool split = (long long)c->batch * c->hq * kFilterColumnParts <= c->cus;
+                            const float* qrot, float* out, int32_t* advance, uint32_t* err,
+                            bool whole_rows) {
+  const bool split = !whole_rows && (long long)c->batch * c->hq * kFilterColumnParts <= c->cus;
   if (split)
     hipLaunchKernelGGL((filter_select_kernel<BF16, D, E1, E2, kFilterColumnParts>),
                        dim3((unsigned)(c->hq * kFilterColumnParts), (unsigned)c->batch),
@@ -1025,10 +1026,11 @@ template <bool BF16, int D>
 static void launch_filter_d(const fasa_ctx* c, hipStream_t s, const uint32_t* gm,
                             const float* scores, const int32_t* nb, int max_seq_len, int budget,
                             const int32_t* hb, int32_t* idx, const void* k, const void* v,
-                            const float* qrot, float* out, int32_t* advance, uint32_t* err) {
+                            const float* qrot, float* out, int32_t* advance, uint32_t* err,
+                            bool whole_rows) {
 #define FASA_FILTER(E1V, E2V)                                                                 \
   launch_filter_t<BF16, D, E1V, E2V>(c, s, gm, scores, nb, max_seq_len, budget, hb, idx, k, v, \
-                                     qrot, out, advance, err)
+                                     qrot, out, advance, err, whole_rows)
   const bool short_rows = filter_group_slots(max_seq_len) == 4;
   const bool few = filter_survivor_slots(budget) == 16;
   if (short_rows) {
@@ -1042,7 +1044,7 @@ static void launch_filter_d(const fasa_ctx* c, hipStream_t s, const uint32_t* gm
 hipError_t launch_filter_select(const fasa_ctx* c, const float* scores, const int32_t* nb,
                                 int max_seq_len, int budget, int32_t* idx, const void* k_cache,
                                 const void* v_cache, float* out, int32_t* advance, uint8_t* ws,
-                                hipStream_t s, const int32_t* head_budget) {
+                                hipStream_t s, const int32_t* head_budget, bool whole_rows) {
   if (!filter_path_applies(max_seq_len, budget) || out == nullptr) return hipErrorInvalidValue;
   uint32_t* err = reinterpret_cast<uint32_t*>(ws + c->ws.err);
   const float* qrot = reinterpret_cast<const float*>(ws + c->ws.qrot);
@@ -1051,17 +1053,17 @@ hipError_t launch_filter_select(const fasa_ctx* c, const float* scores, const in
   if (c->d == 128) {
     if (bf)
       launch_filter_d<true, 128>(c, s, gm, scores, nb, max_seq_len, budget, head_budget, idx,
-                                 k_cache, v_cache, qrot, out, advance, err);
+                                 k_cache, v_cache, qrot, out, advance, err, whole_rows);
     else
       launch_filter_d<false, 128>(c, s, gm, scores, nb, max_seq_len, budget, head_budget, idx,
-                                  k_cache, v_cache, qrot, out, advance, err);
+                                  k_cache, v_cache, qrot, out, advance, err, whole_rows);
   } else {
     if (bf)
       launch_filter_d<true, 64>(c, s, gm, scores, nb, max_seq_len, budget, head_budget, idx,
-                                k_cache, v_cache, qrot, out, advance, err);
+                                k_cache, v_cache, qrot, out, advance, err, whole_rows);
     else
       launch_filter_d<false, 64>(c, s, gm, scores, nb, max_seq_len, budget, head_budget, idx,
-                                 k_cache, v_cache, qrot, out, advance, err);
+                                 k_cache, v_cache, qrot, out, advance, err, whole_rows);
   }
   return hipGetLastError();
 }

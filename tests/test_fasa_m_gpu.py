@@ -2,8 +2,13 @@
 (gist.science/pt, "Resumo Tecnico" section 2, "Variantes de Implementacao").
 
 The kernels are the same ones, reading and writing the caches over the host
-link, so every result must be bit-identical to the device-resident run, and
-the decode step must pass the oracle's checks as before.
+link, so the caches, the indices and (with one launch shape) the outputs must
+be bit-identical to the device-resident run, and the decode step must pass the
+oracle's checks as before.  One launch shape differs on purpose: with K and V
+on the host, the filtered select + FAC takes one workgroup per row where the
+device run splits a row's columns over 4 workgroups when rows are few, so
+that each selected row crosses the link once.  The two shapes sum the same
+products in a different order, so there the outputs agree to fp32 rounding.
 """
 
 import numpy as np
@@ -48,9 +53,21 @@ def test_host_kv_matches_device_kv_and_oracle(gpu, name):
     assert torch.equal(gd.k.cpu(), gh.k), "K caches differ"
     assert torch.equal(gd.v.cpu(), gh.v), "V caches differ"
     assert torch.equal(gd.side, gh.side), "sidecars differ"
+    msl = int(x["ctx"].max()) + w.steps - 1  # as run_decode passes it
+    filtered = gpu.decode_layout(msl, w.budget)[0] == "group_filter"
+    vmax = float(gd.v.float().abs().max())
+    split = w.batch * w.n_q_heads * 4 <= torch.cuda.get_device_properties(0).multi_processor_count
     for t in range(w.steps):
         assert np.array_equal(idx_d[t], idx_h[t]), f"step {t}: indices differ"
-        assert np.array_equal(out_d[t], out_h[t]), f"step {t}: outputs differ"
+        if filtered and split:
+            # An output is sum(p v) / sum(p) over at most B rows, each sum in
+            # fp32 in some order: either order is within B * 2^-24 of the
+            # exact sums relative to sum(p |v|) and sum(p), so two orders
+            # differ by at most about 4 B 2^-24 max|v|.
+            bound = 4 * w.budget * 2.0 ** -24 * vmax
+            assert np.all(np.abs(out_d[t] - out_h[t]) <= bound), f"step {t}: outputs differ"
+        else:
+            assert np.array_equal(out_d[t], out_h[t]), f"step {t}: outputs differ"
     assert np.array_equal(gh.seq_lens.cpu().numpy(), (x["ctx"] - 1 + w.steps).astype(np.int32))
 
     o = oracle_setup(w, x)
