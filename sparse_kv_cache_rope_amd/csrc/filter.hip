@@ -572,23 +572,31 @@ __device__ __forceinline__ void fac_wave(WaveFac<BF16, D, S>& f0, WaveFac<BF16, 
   }
 }
 
-// The waves' states merged (after a barrier): this part's columns.
+// The waves' states merged (after a barrier): this part's columns.  Thread t
+// takes wave t % 8's term of column t / 8 (and of every further column
+// 64 apart), and the 8 lanes holding one column's terms sum them.
 template <bool BF16, int D, int S>
 __device__ __forceinline__ void fac_merge(float* __restrict__ out_row, int part, FilterLds& L) {
   using F = WaveFac<BF16, D, S>;
-  const int t = threadIdx.x;
-  if (t >= F::W) return;
+  constexpr int NW = kFilterWaves;
+  static_assert(NW == 8, "a column's terms are 8 consecutive lanes");
+  const int t = threadIdx.x, w = t % NW;
+  if (t / NW >= F::W) return;  // whole waves (W is a multiple of 8)
   float mx = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kFilterWaves; ++w) mx = fmaxf(mx, L.mw[w]);
-  float lsum = 0.0f, sum = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kFilterWaves; ++w) {
-    const float wt = mx == -INFINITY ? 0.0f : exp2f(L.mw[w] - mx);  // m = -inf gives 0
-    sum = fmaf(L.red[w * F::W + t], wt, sum);
-    lsum = fmaf(L.lw[w], wt, lsum);
+  for (int i = 0; i < NW; ++i) mx = fmaxf(mx, L.mw[i]);
+  const float wt = mx == -INFINITY ? 0.0f : exp2f(L.mw[w] - mx);  // m = -inf gives 0
+  float lsum = L.lw[w] * wt;
+  lsum += __shfl_xor(lsum, 1);
+  lsum += __shfl_xor(lsum, 2);
+  lsum += __shfl_xor(lsum, 4);
+  for (int col = t / NW; col < F::W; col += kFilterThreads / NW) {
+    float v = L.red[w * F::W + col] * wt;
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    if (w == 0) out_row[part * F::W + col] = lsum > 0.0f ? v / lsum : 0.0f;
   }
-  out_row[part * F::W + t] = lsum > 0.0f ? sum / lsum : 0.0f;
 }
 
 // Smallest shift that fits [0, sp] into the histogram's bins.
