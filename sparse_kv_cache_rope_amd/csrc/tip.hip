@@ -10,12 +10,15 @@
 // newest token).  Under partial RoPE FC c is the dim pair fc_lo / fc_hi name
 // (R rotated FCs; R = C is full RoPE).
 //
-// One workgroup (4 waves) covers 256 consecutive tokens of one (sequence, KV
-// head) and all G query heads of that KV head.  The KV head's sidecar planes
-// (one per FC of the union U_g of the group's dominant FCs) are dealt out to
-// the 4 waves; a lane loads 4 consecutive token pairs of a plane with one
-// 16-byte load (bf16), so a wave reads 1 KiB contiguous per plane, and every
-// wave keeps all its loads in flight at once.
+// Two kernels share the layout below.  tip_kernel: one workgroup (4 waves)
+// covers 256 consecutive tokens of one (sequence, KV head) and all G query
+// heads of that KV head.  tip_head_kernel (G = 4 or 8, at most 16 dominant FCs
+// per head): the same tile, one wave per query head over that head's own
+// planes (its comment has the details).  In tip_kernel the KV head's sidecar
+// planes (one per FC of the union U_g of the group's dominant FCs) are dealt
+// out to the 4 waves.  In both, a lane loads 4 consecutive token pairs of a
+// plane with one 16-byte load (bf16), so a wave reads 1 KiB contiguous per
+// plane, and every wave keeps all its loads in flight at once.
 //
 // The step's other per-token work is fused here and runs while those loads
 // are in flight: every workgroup rotates its group's queries (angle reduced
