@@ -254,3 +254,27 @@ def test_filtered_repeat_and_graph_replay(gpu):
         assert torch.equal(idx, a_idx), rep
         assert torch.equal(out, a_out), rep
         _ = run_decode(g, 0, w.budget, advance=False)
+
+
+@pytest.mark.parametrize("kv_on_host", [False, True])
+def test_filtered_step_captured_before_any_eager_call(gpu, kv_on_host):
+    """A context's first decode step captured in a HIP graph (the step asks
+    the runtime once whether K lives in host memory, here inside the capture)
+    replays to exactly what the same step gives eagerly afterwards."""
+    w = small("c5", context=12000, budget=512)
+    x = W.generate(w)
+    g = GpuSetup(gpu, w, x, kv_on_host=kv_on_host)
+    q, kn, vn = (to_dev(x[k][0], g.td) for k in ("q", "k_new", "v_new"))
+    msl = int(x["ctx"].max())
+    out = torch.zeros(w.batch, w.n_q_heads, w.head_dim, dtype=torch.float32, device="cuda")
+    idx = torch.zeros(w.batch, w.n_q_heads, w.budget, dtype=torch.int32, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.ctx.decode_step(g.k, g.v, g.side, q, kn, vn, g.seq_lens, msl, w.budget, out, g.ws,
+                          idx_out=idx)
+    graph.replay()
+    torch.cuda.synchronize()
+    assert g.ctx.check(g.ws) == 0
+    e_out, e_idx = run_decode(g, 0, w.budget, advance=False, max_seq_len=msl)
+    assert torch.equal(idx, e_idx)
+    assert torch.equal(out, e_out)
