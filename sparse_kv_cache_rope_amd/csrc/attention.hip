@@ -517,15 +517,20 @@ dense_mfma_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_c
 
 // -------------------------------------------------------------- merge ----
 
-// One 1024-thread workgroup per (h, b, 16-dim slice) combines the per-split
-// partials (m, l, acc) of a row whose work spanned more than one split.
-// `unit` is the rows (FAC: of min(budget, n)) or tokens (dense: of n) per
-// split.  Thread t takes dim t % 16 of the slice for splits t / 16,
-// t / 16 + 64, ..: sixteen threads read one split's 64 contiguous bytes, and
-// a thread's loads are independent.  Each thread folds its splits into an
-// (m, l, acc) state of its own and the states are merged across lanes and
-// waves, so a row of hundreds of splits costs one memory round trip.
-constexpr int kMergeThreads = 1024;
+// The merge of per-split partials (m, l, acc) of the rows whose work spanned
+// more than one split.  `unit` is the rows (FAC: of min(budget, n)) or tokens
+// (dense: of n) per split; with `fixed_splits` > 0 every split of every row
+// wrote a state (an empty one past the row) and no length is read.
+//
+// A 256-thread workgroup covers a 16-dim slice of 16 / SL rows: thread t takes
+// dim t % 16 of the slice, split lane (t / 16) % SL and row t / (16 SL), and
+// folds splits lane, lane + SL, .. (up to 8 loads in flight) into a state of
+// its own; sixteen threads read one split's 64 contiguous bytes.  The SL
+// states of a (row, dim) then merge through LDS.  SL is the launch's split
+// count rounded up to a power of two, at most 16, so a grid of many rows with
+// few splits packs several rows per workgroup and one of few rows with
+// hundreds of splits still keeps every load of a lane in flight.
+constexpr int kMergeThreads = 256;
 constexpr int kMergeDims = 16;
 
 struct MergeState {
@@ -540,86 +545,97 @@ __device__ __forceinline__ MergeState merge_states(MergeState x, MergeState y) {
   return {mn, fmaf(x.l, wx, y.l * wy), fmaf(x.a, wx, y.a * wy)};
 }
 
-__device__ __forceinline__ MergeState shfl_xor_state(MergeState x, int k) {
-  return {__shfl_xor(x.m, k), __shfl_xor(x.l, k), __shfl_xor(x.a, k)};
-}
-
-template <int D>
+template <int D, int SL>
 __global__ void __launch_bounds__(kMergeThreads)
 merge_kernel(const float* __restrict__ partial, int max_splits, const int32_t* __restrict__ nb,
-             int max_seq_len, int cap, int budget, int unit, int hq, int fixed_splits,
+             int max_seq_len, int cap, int budget, int unit, int hq, int rows, int fixed_splits,
              float* __restrict__ out) {
-  constexpr int SL = kMergeThreads / kMergeDims;  // split lanes
-  constexpr int NWV = kMergeThreads / kWave;
-  constexpr int U = 8;  // splits per thread in flight
-  __shared__ MergeState ws[NWV][kMergeDims];
-  const int h = blockIdx.x, b = blockIdx.y, d0 = blockIdx.z * kMergeDims;
-  const size_t row = (size_t)b * hq + h;
-  int nsplit = fixed_splits;  // every split wrote a state (the dense launch)
-  if (fixed_splits == 0) {
-    int n = nb[b];
-    if (n < 0 || n > max_seq_len || n > cap) n = 0;
-    const int work = (budget > 0 && budget < n) ? budget : n;
-    nsplit = (work + unit - 1) / unit;
-    if (nsplit <= 1) return;  // written directly by the split kernel
-  }
-  const float* p = partial + row * max_splits * (D + 2);
-  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
-  const int dd = t % kMergeDims;
-
-  MergeState st = {-INFINITY, 0.0f, 0.0f};
-  for (int s0 = t / kMergeDims; s0 < nsplit; s0 += U * SL) {
-    // Up to U splits at once: their loads go out together.
-    float mv[U], lv[U], av[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = s0 + u * SL;
-      const float* q = p + (size_t)(s < nsplit ? s : s0) * (D + 2);
-      mv[u] = s < nsplit ? q[0] : -INFINITY;
-      lv[u] = q[1];
-      av[u] = q[2 + d0 + dd];
+  constexpr int RPW = kMergeDims / SL;  // rows per workgroup
+  constexpr int SLICES = D / kMergeDims;
+  constexpr int U = 8;  // splits per lane in flight
+  static_assert(RPW * SL * kMergeDims == kMergeThreads, "thread layout");
+  __shared__ MergeState ws[kMergeThreads];
+  const int t = threadIdx.x;
+  const int dd = t % kMergeDims, sl = (t / kMergeDims) % SL;
+  const int row = (int)(blockIdx.x / SLICES) * RPW + t / (kMergeDims * SL);
+  const int d = (int)(blockIdx.x % SLICES) * kMergeDims + dd;
+  int nsplit = 0;
+  if (row < rows) {
+    nsplit = fixed_splits;
+    if (fixed_splits == 0) {
+      int n = nb[row / hq];
+      if (n < 0 || n > max_seq_len || n > cap) n = 0;
+      const int work = (budget > 0 && budget < n) ? budget : n;
+      nsplit = (work + unit - 1) / unit;  // <= 1: written directly by the split kernel
     }
-    float mx = st.m;
-#pragma unroll
-    for (int u = 0; u < U; ++u) mx = fmaxf(mx, mv[u]);
-    if (mx != -INFINITY) {
-      const float sc = exp2f(st.m - mx);  // -inf gives 0
-      st.l *= sc;
-      st.a *= sc;
+  }
+  MergeState st = {-INFINITY, 0.0f, 0.0f};
+  if (nsplit > 1) {
+    const float* p = partial + (size_t)row * max_splits * (D + 2);
+    for (int s0 = sl; s0 < nsplit; s0 += U * SL) {
+      float mv[U], lv[U], av[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float w = exp2f(mv[u] - mx);  // -inf gives 0
-        st.l = fmaf(lv[u], w, st.l);
-        st.a = fmaf(av[u], w, st.a);
+        const int sp = s0 + u * SL;
+        const float* q = p + (size_t)(sp < nsplit ? sp : s0) * (D + 2);
+        mv[u] = sp < nsplit ? q[0] : -INFINITY;
+        lv[u] = q[1];
+        av[u] = q[2 + d];
       }
-      st.m = mx;
+      float mx = st.m;
+#pragma unroll
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, mv[u]);
+      if (mx != -INFINITY) {
+        const float sc = exp2f(st.m - mx);  // -inf gives 0
+        st.l *= sc;
+        st.a *= sc;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float w = exp2f(mv[u] - mx);  // -inf gives 0
+          st.l = fmaf(lv[u], w, st.l);
+          st.a = fmaf(av[u], w, st.a);
+        }
+        st.m = mx;
+      }
     }
   }
-  // Lanes dd, dd + 16, dd + 32, dd + 48 of a wave, then the waves.
-  st = merge_states(st, shfl_xor_state(st, 16));
-  st = merge_states(st, shfl_xor_state(st, 32));
-  if (lane < kMergeDims) ws[wave][lane] = st;
+  ws[t] = st;
   __syncthreads();
-  if (t < kMergeDims) {
-    MergeState r = ws[0][t];
+  if (sl == 0 && nsplit > 1) {
 #pragma unroll
-    for (int w = 1; w < NWV; ++w) r = merge_states(r, ws[w][t]);
-    out[row * D + d0 + t] = (r.l > 0.0f) ? r.a / r.l : 0.0f;
+    for (int k = 1; k < SL; ++k) st = merge_states(st, ws[t + k * kMergeDims]);
+    out[(size_t)row * D + d] = (st.l > 0.0f) ? st.a / st.l : 0.0f;
   }
 }
 
 // ------------------------------------------------------------ launchers --
 
+// max_splits_used: the most splits any row of this launch can have.
 static void launch_merge(const fasa_ctx* c, const float* part, int max_splits, const int32_t* nb,
                          int max_seq_len, int budget, int unit, float* out, hipStream_t s,
                          int fixed_splits = 0) {
-  dim3 grid((unsigned)c->hq, (unsigned)c->batch, (unsigned)(c->d / kMergeDims));
-  if (c->d == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, s, part, max_splits, nb,
-                       max_seq_len, c->cap, budget, unit, c->hq, fixed_splits, out);
-  else
-    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeThreads), 0, s, part, max_splits, nb,
-                       max_seq_len, c->cap, budget, unit, c->hq, fixed_splits, out);
+  const int work_max = (budget > 0 && budget < max_seq_len) ? budget : max_seq_len;
+  const int used = fixed_splits > 0 ? fixed_splits : (work_max + unit - 1) / unit;
+  const int rows = c->batch * c->hq;
+  const int slices = c->d / kMergeDims;
+#define FASA_MERGE(DD, SLV)                                                                  \
+  hipLaunchKernelGGL((merge_kernel<DD, SLV>),                                                 \
+                     dim3((unsigned)(((rows + kMergeDims / SLV - 1) / (kMergeDims / SLV)) *   \
+                                     slices)),                                                \
+                     dim3(kMergeThreads), 0, s, part, max_splits, nb, max_seq_len, c->cap,    \
+                     budget, unit, c->hq, rows, fixed_splits, out)
+#define FASA_MERGE_D(DD)             \
+  if (used <= 2) FASA_MERGE(DD, 2);  \
+  else if (used <= 4) FASA_MERGE(DD, 4); \
+  else if (used <= 8) FASA_MERGE(DD, 8); \
+  else FASA_MERGE(DD, 16);
+  if (c->d == 128) {
+    FASA_MERGE_D(128)
+  } else {
+    FASA_MERGE_D(64)
+  }
+#undef FASA_MERGE_D
+#undef FASA_MERGE
 }
 
 hipError_t launch_fac(const fasa_ctx* c, const void* k_cache, const void* v_cache,
