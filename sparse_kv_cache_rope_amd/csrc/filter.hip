@@ -809,7 +809,9 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
         // 3. The rows FAC will read go out now; then the list's keys are
         // counted (one atomic per listed token).
         __builtin_amdgcn_wave_barrier();  // the wave reads back its own list
-        if (!ovf && cnt > 0) {
+        // A list longer than the two rounds in flight makes FAC lay T_t out
+        // flat and re-deal it (below), so its rows would be issued for nothing.
+        if (!ovf && cnt > 0 && cnt <= 2 * F::RR) {
           fac_issue(fac0, 0, cnt, wpos, K, V, kvbase, part);
           issued = 1;
           if (cnt > F::RR) {
