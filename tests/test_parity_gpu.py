@@ -301,6 +301,31 @@ def test_dense_attn(gpu, name):
             check_out(got[b, h], want, w.dtype, f"b{b} h{h}")
 
 
+def test_dense_empty_and_invalid_rows_in_chunk_walking_grid(gpu):
+    """A grid whose workgroups walk several chunks (every split then writes a
+    state and the merge reads no lengths): an empty sequence gives zeros
+    without a flag, a length past max_seq_len gives zeros and the flag, and
+    the other rows still match the oracle."""
+    w, x, g, o = _prefilled(gpu, "dm4")
+    lens = (x["ctx"] - 1).astype(np.int32)
+    msl = int(lens.max())
+    lens[0] = 0
+    lens[1] = msl + 5
+    n = torch.from_numpy(lens).cuda()
+    out = torch.full((w.batch, w.n_q_heads, w.head_dim), np.nan, dtype=torch.float32,
+                     device="cuda")
+    g.ctx.dense_attn(g.k, g.v, to_dev(x["q"][0], g.td), n, msl, out, g.ws)
+    got = out.cpu().numpy()
+    assert g.ctx.check(g.ws) & gpu.DEVFLAG_SEQ_LEN
+    assert np.all(got[0] == 0) and np.all(got[1] == 0)
+    for b in range(2, w.batch):
+        nb = int(lens[b])
+        o.lens[b] = nb
+        qr = oracle.rope.rope_rotate(x["q"][0][b], nb - 1, w.rope_theta)
+        for h in range(0, w.n_q_heads, 5):
+            check_out(got[b, h], o.attend(b, h, qr[h], np.arange(nb)), w.dtype, f"b{b} h{h}")
+
+
 # -------------------------------------------------------- decode step ----
 
 def _decode_parity(gpu, w, x, steps=None, heads=None, check_steps=None):
