@@ -351,7 +351,8 @@ dense_mfma_kernel(const void* __restrict__ k_cache, const void* __restrict__ v_c
   issue_v(0);
 
   // The queries, rotated to position n - 1 while the loads fly: one FC pair
-  // per thread (angle reduced in fp64, sine and cosine in fp32, as TIP does).
+  // per thread (angle reduced in fp64, sine and cosine in fp32; the logits
+  // then go through bf16 halves on the matrix cores anyway).
   if (threadIdx.x < HPW * (D / 2)) {
     const int hh = threadIdx.x / (D / 2), cf = threadIdx.x % (D / 2);
     const int lo = fc_lo(cf, R), hi = fc_hi(cf, R, D / 2);

@@ -21,8 +21,8 @@
 // plane, and every wave keeps all its loads in flight at once.
 //
 // The step's other per-token work is fused here and runs while those loads
-// are in flight: every workgroup rotates its group's queries (angle reduced
-// in fp64, sine and cosine in fp32, kept in fp32) into LDS weights (q~_c, q~_{c+C}) per plane and head, zero where
+// are in flight: every workgroup rotates its group's queries (in fp64, kept
+// in fp32) into LDS weights (q~_c, q~_{c+C}) per plane and head, zero where
 // the FC is not dominant for the head; in decode mode the workgroup whose tile
 // holds the new position n - 1 also rotates the step's key.
 //
@@ -188,16 +188,12 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
     const bool dom = (dmask[r] >> c) & 1ull;
     const bool pass = om[r] == 0.0;  // pass-through FC
     const double qx0 = to_f64(qr0[r]), qx1 = to_f64(qr1[r]);
-    // The query's angle, reduced to [-pi, pi] in fp64 (pos < 2^24, so the
-    // reduction keeps about 1e-8 rad), then its sine and cosine in fp32:
-    // q~ is kept in fp32 anyway.
+    // The query's rotation in fp64, kept in fp32.
     const double ang = (double)pos * om[r];
-    const double rev = ang * 0.15915494309189533577;  // 1 / (2 pi)
-    const float red = (float)((rev - rint(rev)) * 6.28318530717958647693);
-    float sf, cf;
-    sincosf(red, &sf, &cf);
-    qy0[r] = (float)(pass ? qx0 : qx0 * (double)cf - qx1 * (double)sf);
-    qy1[r] = (float)(pass ? qx1 : qx1 * (double)cf + qx0 * (double)sf);
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    qy0[r] = (float)(pass ? qx0 : qx0 * cs - qx1 * sn);
+    qy1[r] = (float)(pass ? qx1 : qx1 * cs + qx0 * sn);
     if (tid + r * kTipThreads < G * C && slot[r] >= 0)
       wts[slot[r]][hh] = dom ? make_float2(qy0[r], qy1[r]) : make_float2(0.0f, 0.0f);
     if (r == 0 && owner) {
@@ -205,8 +201,6 @@ tip_kernel(const int32_t* __restrict__ seq_lens, void* sidecar, int mode, int ma
       // fp64 like the bulk append (the cache keeps its bf16 rounding of the
       // exact rotation).  Thread tid < C holds FC tid here (head 0), the FC
       // of its key pair.
-      double sn, cs;
-      sincos(ang, &sn, &cs);
       own_bits = rotate_pair<BF16>(to_f64(kr0), to_f64(kr1), sn, cs, pass);
       if (tid < C && slot[0] >= 0) patch[slot[0]] = own_bits;
     }
@@ -455,22 +449,20 @@ tip_head_kernel(const int32_t* __restrict__ seq_lens, void* sidecar,
 
   __builtin_amdgcn_sched_barrier(0);
 
-  // Rotation of FC c at position n - 1 (angle reduced in fp64, sine and
-  // cosine in fp32, as in tip_kernel).
+  // Rotation of FC c at position n - 1 in fp64 (q~ kept in fp32: each
+  // component within half an fp32 ulp of its own value, which a sine and
+  // cosine taken in fp32 would not keep for a component that the rotation
+  // nearly cancels).
   const bool pass = om == 0.0;
   const double qx0 = to_f64(qr0), qx1 = to_f64(qr1);
   const double ang = (double)pos * om;
-  const double rev = ang * 0.15915494309189533577;  // 1 / (2 pi)
-  const float red = (float)((rev - rint(rev)) * 6.28318530717958647693);
-  float sf, cf;
-  sincosf(red, &sf, &cf);
-  const float qy0 = (float)(pass ? qx0 : qx0 * (double)cf - qx1 * (double)sf);
-  const float qy1 = (float)(pass ? qx1 : qx1 * (double)cf + qx0 * (double)sf);
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  const float qy0 = (float)(pass ? qx0 : qx0 * cs - qx1 * sn);
+  const float qy1 = (float)(pass ? qx1 : qx1 * cs + qx0 * sn);
   uint2 own_bits = make_uint2(0u, 0u);
   if (owner && wave == 0 && lane < C) {
-    // The tile holding the step's position rotates the step's key in fp64.
-    double sn, cs;
-    sincos(ang, &sn, &cs);
+    // The tile holding the step's position rotates the step's key too.
     own_bits = rotate_pair<BF16>(to_f64(kr0), to_f64(kr1), sn, cs, pass);
     if (slot_c >= 0) patch[slot_c] = own_bits;
   }

@@ -49,6 +49,12 @@ SMALL = {
     # B past the fused limit on rows chunks would barely cut: each row held
     # whole in 1024 threads (32 per thread), then the split FAC.
     "c4w": small("c4", batch=1, context=20000, budget=5000, steps=2),
+    # TIP's per-head kernel at its edges: one dominant FC per head (3 of a
+    # wave's 4 plane slots empty), and 8 query heads per KV head with 13
+    # dominant FCs (16 slots, 3 empty).  (Partial RoPE: its own test file.)
+    "t1": small("c2", n_dom=1, context=3001),
+    "t8": small("c3", batch=2, n_q_heads=16, n_kv_heads=2, context=3001, context_min=2000,
+                n_dom=13),
     # Dense grids past two workgroups per CU, so each workgroup walks several
     # 256-token chunks: 1, 2, 4 (ragged) and 8 query heads per KV head.
     "dm1": small("c3", batch=4, n_q_heads=8, n_kv_heads=8, context=6001, context_min=3000),
@@ -109,7 +115,8 @@ def test_append_past_capacity_raises_flag(gpu):
 
 # ---------------------------------------------------------------- TIP ----
 
-@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "h64s", "f128s", "g1s", "g2s", "g8s"])
+@pytest.mark.parametrize("name", ["c1", "c2s", "c3s", "h64s", "f128s", "g1s", "g2s", "g8s",
+                                  "t1", "t8"])
 def test_tip_scores(gpu, name):
     w, x, g, o = _prefilled(gpu, name)
     # Score the prefilled tokens with the step-0 query at position n0 - 1.
