@@ -64,6 +64,20 @@ constexpr int kTipTokens = kWave * 4;  // tokens per workgroup
 constexpr int kMaxPlanes = 64;         // d/2 FCs at d = 128
 static_assert(kGroupTokens == 16, "a group is the 4 tokens of each lane of a quad");
 
+typedef __bf16 tip_bf16x2 __attribute__((ext_vector_type(2)));
+
+// a.lo * b.lo + a.hi * b.hi + c over bf16 pairs, accumulated in fp32.
+__device__ __forceinline__ float tip_dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(tip_bf16x2, a),
+                                         __builtin_bit_cast(tip_bf16x2, b), c, false);
+}
+
+// bf16 bits of a finite float, rounded to nearest even.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
 // The arguments needed first lead the list: the build preloads the first 16
 // dwords of kernel arguments into registers, which saves a dependent load
 // before the stream starts.  PW: sidecar loads per wave, enough for the
@@ -476,7 +490,18 @@ tip_head_kernel(const int32_t* __restrict__ seq_lens, void* sidecar,
   if (owner) __syncthreads();  // the patch is written (owner is uniform per workgroup)
 
   // The head's weights: the rotated pair of its k-th dominant FC, read from
-  // that FC's lane.
+  // that FC's lane.  For bf16 pairs each weight is split into a high and a
+  // low bf16 (w = hi + lo within 2^-18 of w), packed per FC like the pair's
+  // (lo, hi) dims, so a token's pair takes two v_dot2_f32_bf16 and no
+  // unpacking.
+  uint32_t wph = 0u, wpl = 0u;
+  if constexpr (BF16) {
+    const uint32_t h0 = f32_to_bf16_rne_bits(qy0), h1 = f32_to_bf16_rne_bits(qy1);
+    const uint32_t l0 = f32_to_bf16_rne_bits(qy0 - __uint_as_float(h0 << 16));
+    const uint32_t l1 = f32_to_bf16_rne_bits(qy1 - __uint_as_float(h1 << 16));
+    wph = h0 | (h1 << 16);
+    wpl = l0 | (l1 << 16);
+  }
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   const bool pos_lane = lane == (int)((pos - tile0) >> 2);
   const int pos_t = (int)(pos & 3);
@@ -486,8 +511,6 @@ tip_head_kernel(const int32_t* __restrict__ seq_lens, void* sidecar,
     for (int k = 0; k < PW; ++k) {
       const int fc = hf[k].x, sl = hf[k].y;
       if (sl < 0) break;
-      const float wx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qy0), fc));
-      const float wy = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qy1), fc));
       uint4 da = xa[k], db = xb[k];
       if constexpr (OWN) {
         const uint2 p = patch[sl];
@@ -507,26 +530,22 @@ tip_head_kernel(const int32_t* __restrict__ seq_lens, void* sidecar,
           db.w = (pos_lane && pos_t == 3) ? p.y : db.w;
         }
       }
-      float lo[4], hi[4];
       if constexpr (BF16) {
+        const uint32_t wh = (uint32_t)__builtin_amdgcn_readlane((int)wph, fc);
+        const uint32_t wl = (uint32_t)__builtin_amdgcn_readlane((int)wpl, fc);
         const uint32_t wd[4] = {da.x, da.y, da.z, da.w};
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          lo[t] = bf16_lo(wd[t]);
-          hi[t] = bf16_hi(wd[t]);
-        }
+        for (int t = 0; t < 4; ++t) acc[t] = tip_dot2(wh, wd[t], tip_dot2(wl, wd[t], acc[t]));
       } else {
-        lo[0] = __uint_as_float(da.x);
-        hi[0] = __uint_as_float(da.y);
-        lo[1] = __uint_as_float(da.z);
-        hi[1] = __uint_as_float(da.w);
-        lo[2] = __uint_as_float(db.x);
-        hi[2] = __uint_as_float(db.y);
-        lo[3] = __uint_as_float(db.z);
-        hi[3] = __uint_as_float(db.w);
-      }
+        const float wx = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qy0), fc));
+        const float wy = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qy1), fc));
+        const float lo[4] = {__uint_as_float(da.x), __uint_as_float(da.z), __uint_as_float(db.x),
+                             __uint_as_float(db.z)};
+        const float hi[4] = {__uint_as_float(da.y), __uint_as_float(da.w), __uint_as_float(db.y),
+                             __uint_as_float(db.w)};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[t] = fmaf(wy, hi[t], fmaf(wx, lo[t], acc[t]));
+        for (int t = 0; t < 4; ++t) acc[t] = fmaf(wy, hi[t], fmaf(wx, lo[t], acc[t]));
+      }
     }
   };
   if (owner)

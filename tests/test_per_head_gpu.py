@@ -171,7 +171,8 @@ def test_decode_step_per_head_all_equal_is_uniform(gpu):
 
 def test_per_layer_budgets_in_one_graph(gpu):
     """Layer-wise allocation: L layers, each with its own budget and per-head
-    budgets, captured in one HIP graph; every replay matches eager."""
+    budgets, captured in one HIP graph; every replay matches eager, and each
+    layer's eager step meets the oracle's step with its budgets."""
     w = W.shrink(W.get("c2"), context=3000, budget=512)
     x = W.generate(w)
     L = 4
@@ -212,10 +213,26 @@ def test_per_layer_budgets_in_one_graph(gpu):
         torch.cuda.synchronize()
         for i in range(L):
             assert torch.equal(outs[i], eager[i][0]) and torch.equal(idxs[i], eager[i][1]), (rep, i)
-    # Each layer's per-head sets have min(B_h, n) entries.
-    n = msl
+    # Each layer's eager step against the oracle's step with that layer's
+    # budgets: the per-head index sets (tau band) and the outputs recomputed
+    # on the GPU's sets.
     for i in range(L):
         hb = hbs[i].cpu().numpy()
-        got = idxs[i].cpu().numpy()[0]
+        got_idx, got_out = eager[i][1].cpu().numpy(), eager[i][0].cpu().numpy()
+        o = oracle_setup(w, x)
+        res = o.step(x["q"][0], x["k_new"][0], x["v_new"][0], layer_budget[i], head_budgets=hb)
+        n = int(o.lens[0])
+        qr = o.query_rot(0, x["q"][0][0])
         for h in range(w.n_q_heads):
-            assert (got[h] >= 0).sum() == min(int(hb[h]), n), (i, h)
+            where = f"layer {i} h{h} B_h={hb[h]}"
+            bh = int(hb[h])
+            row = got_idx[0, h]
+            take = min(bh, n)
+            assert np.all(row[take:] == -1), where
+            sel = row[:take]
+            assert np.all(np.diff(sel) > 0) and np.all((sel >= 0) & (sel < n)), where
+            if bh:
+                diff = np.setxor1d(sel, res["idx"][0, h][:take])
+                s, tau = res["scores"][(0, h)], res["tau"][0, h]
+                assert np.all(np.abs(s[diff] - tau) <= 1e-3 * abs(tau)), where
+            check_out(got_out[0, h], o.attend(0, h, qr[h], row), w.dtype, where)
