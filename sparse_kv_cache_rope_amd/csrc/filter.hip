@@ -1010,7 +1010,7 @@ int filter_group_slots(int max_seq_len) {
 int filter_survivor_slots(int budget) { return budget <= 320 ? 16 : 40; }
 
 // Column parts of the fused FAC when the rows are few (as in select2.hip).
-constexpr int kFilterColumnParts = 4;
+constexpr int kFilterColumnParts = 8;
 
 template <bool BF16, int D, int E1, int E2>
 static void launch_filter_t(const fasa_ctx* c, hipStream_t s, const uint32_t* gm,
