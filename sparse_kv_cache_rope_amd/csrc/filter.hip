@@ -332,8 +332,11 @@ struct WaveFac {
   uint4 k[KST], v[VST];
 };
 
-// Issues round r0's K and V loads (cnt >= 1).
-template <class F>
+// Issues round r0's K and V loads (cnt >= 1).  TRIM: a step whose rows all
+// lie past cnt loads nothing (fac_round<.., true> skips it); only for rounds
+// after which no further loads are issued, since the guards cost the
+// compiler its exact load counts.
+template <bool TRIM, class F>
 __device__ __forceinline__ void fac_issue(F& f, int r0, int cnt, const int32_t* pos,
                                           const uint4* __restrict__ K, const uint4* __restrict__ V,
                                           size_t kvbase, int part) {
@@ -341,12 +344,14 @@ __device__ __forceinline__ void fac_issue(F& f, int r0, int cnt, const int32_t* 
   const int last = cnt - 1;
 #pragma unroll
   for (int s = 0; s < F::KST; ++s) {
+    if (TRIM && r0 + s * F::RS >= cnt) continue;
     const int r = r0 + s * F::RS + lane / F::LPR;
     const int j = pos[r < cnt ? r : last];
     f.k[s] = K[(kvbase + (size_t)j) * F::LPR + lane % F::LPR];
   }
 #pragma unroll
   for (int s = 0; s < F::VST; ++s) {
+    if (TRIM && r0 + s * F::RV >= cnt) continue;
     const int r = r0 + s * F::RV + lane / F::VL;
     const int j = pos[r < cnt ? r : last];
     f.v[s] = V[(kvbase + (size_t)j) * F::LPR + part * F::VL + lane % F::VL];
@@ -436,7 +441,7 @@ struct WaveSoft {
 // dot products are independent chains (so they interleave), their group sums
 // likewise; lane i then masks entry r0 + i (past cnt, or below tau) and the
 // masked logits go back through the wave's LDS slot.
-template <int NSETS, class F, class Q>
+template <int NSETS, bool TRIM, class F, class Q>
 __device__ __forceinline__ void fac_round(const F& f0, const F& f1, const Q& qq, int r0, int cnt,
                                           const int32_t* pos, const uint32_t* key, uint64_t tau,
                                           float* zw, WaveSoft<F::EPL>& st) {
@@ -444,9 +449,15 @@ __device__ __forceinline__ void fac_round(const F& f0, const F& f1, const Q& qq,
   constexpr int KS = F::KST * NSETS, VS = F::VST * NSETS, RN = F::RR * NSETS;
   static_assert(RN <= kWave, "a round's logits fit the wave's LDS slot");
   const int lane = threadIdx.x & (kWave - 1);
+  // Step s's first entry; with TRIM a step whose entries all lie past cnt
+  // (its rows were never loaded) is skipped: they are masked below anyway.
+  auto kfirst = [&](int s) { return r0 + (s / F::KST) * F::RR + (s % F::KST) * F::RS; };
+  auto vfirst = [&](int s) { return r0 + (s / F::VST) * F::RR + (s % F::VST) * F::RV; };
   float d[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
+    d[s] = 0.0f;
+    if (TRIM && kfirst(s) >= cnt) continue;
     const uint4 x = s < F::KST ? f0.k[s % F::KST] : f1.k[s % F::KST];
     if constexpr (F::Geo::ES == 2) {
       const uint32_t w[4] = {x.x, x.y, x.z, x.w};
@@ -463,12 +474,14 @@ __device__ __forceinline__ void fac_round(const F& f0, const F& f1, const Q& qq,
     }
   }
 #pragma unroll
-  for (int s = 0; s < KS; ++s) d[s] = group_sum<LPR>(d[s]);
+  for (int s = 0; s < KS; ++s)
+    if (!TRIM || kfirst(s) < cnt) d[s] = group_sum<LPR>(d[s]);
   if (lane % LPR == 0) {
     // Set k's step s covers round entries k RR + s RS + lane / LPR.
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      zw[(s / F::KST) * F::RR + (s % F::KST) * F::RS + lane / LPR] = d[s];
+      if (!TRIM || kfirst(s) < cnt)
+        zw[(s / F::KST) * F::RR + (s % F::KST) * F::RS + lane / LPR] = d[s];
   }
   // The wave reads back what its own lanes wrote (LDS keeps a wave's
   // accesses in order); the barrier only stops the compiler moving them.
@@ -491,6 +504,7 @@ __device__ __forceinline__ void fac_round(const F& f0, const F& f1, const Q& qq,
   st.m = mn;
 #pragma unroll
   for (int s = 0; s < VS; ++s) {
+    if (TRIM && vfirst(s) >= cnt) continue;
     const int rr = (s / F::VST) * F::RR + (s % F::VST) * F::RV + lane / VL;
     const bool in_set = (s % F::VST) * F::RV + lane / VL < F::RR;
     const float z = in_set ? zw[in_set ? rr : 0] : -INFINITY;
@@ -525,20 +539,22 @@ __device__ __forceinline__ void fac_wave(WaveFac<BF16, D, S>& f0, WaveFac<BF16, 
   for (int e = 0; e < EPL; ++e) st.acc[e] = 0.0f;
   float* zw = L.zw[wave];
   const int nr = (cnt + F::RR - 1) / F::RR;
-  if (nr > 0 && issued < 1) fac_issue(f0, 0, cnt, pos, K, V, kvbase, part);
-  if (nr > 1 && issued < 2) fac_issue(f1, F::RR, cnt, pos, K, V, kvbase, part);
   if (nr <= 2) {
     // Both sets as one round: one max, one rescale.
-    if (nr == 2) fac_round<2>(f0, f1, qq, 0, cnt, pos, key, tau, zw, st);
-    else if (nr == 1) fac_round<1>(f0, f1, qq, 0, cnt, pos, key, tau, zw, st);
+    if (nr > 0 && issued < 1) fac_issue<true>(f0, 0, cnt, pos, K, V, kvbase, part);
+    if (nr > 1 && issued < 2) fac_issue<true>(f1, F::RR, cnt, pos, K, V, kvbase, part);
+    if (nr == 2) fac_round<2, true>(f0, f1, qq, 0, cnt, pos, key, tau, zw, st);
+    else if (nr == 1) fac_round<1, true>(f0, f1, qq, 0, cnt, pos, key, tau, zw, st);
   } else {
     // Longer lists: round r computed while round r + 1 flies.
+    if (issued < 1) fac_issue<false>(f0, 0, cnt, pos, K, V, kvbase, part);
+    if (issued < 2) fac_issue<false>(f1, F::RR, cnt, pos, K, V, kvbase, part);
     for (int r = 0; r < nr; r += 2) {
-      fac_round<1>(f0, f0, qq, r * F::RR, cnt, pos, key, tau, zw, st);
-      if (r + 2 < nr) fac_issue(f0, (r + 2) * F::RR, cnt, pos, K, V, kvbase, part);
+      fac_round<1, false>(f0, f0, qq, r * F::RR, cnt, pos, key, tau, zw, st);
+      if (r + 2 < nr) fac_issue<false>(f0, (r + 2) * F::RR, cnt, pos, K, V, kvbase, part);
       if (r + 1 < nr) {
-        fac_round<1>(f1, f1, qq, (r + 1) * F::RR, cnt, pos, key, tau, zw, st);
-        if (r + 3 < nr) fac_issue(f1, (r + 3) * F::RR, cnt, pos, K, V, kvbase, part);
+        fac_round<1, false>(f1, f1, qq, (r + 1) * F::RR, cnt, pos, key, tau, zw, st);
+        if (r + 3 < nr) fac_issue<false>(f1, (r + 3) * F::RR, cnt, pos, K, V, kvbase, part);
       }
     }
   }
@@ -812,10 +828,10 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
         // A list longer than the two rounds in flight makes FAC lay T_t out
         // flat and re-deal it (below), so its rows would be issued for nothing.
         if (!ovf && cnt > 0 && cnt <= 2 * F::RR) {
-          fac_issue(fac0, 0, cnt, wpos, K, V, kvbase, part);
+          fac_issue<true>(fac0, 0, cnt, wpos, K, V, kvbase, part);
           issued = 1;
           if (cnt > F::RR) {
-            fac_issue(fac1, F::RR, cnt, wpos, K, V, kvbase, part);
+            fac_issue<true>(fac1, F::RR, cnt, wpos, K, V, kvbase, part);
             issued = 2;
           }
         }
