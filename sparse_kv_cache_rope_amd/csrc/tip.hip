@@ -385,7 +385,6 @@ tip_head_kernel(const int32_t* __restrict__ seq_lens, void* sidecar,
   constexpr int kPairBytes = BF16 ? 4 : 8;
   static_assert(PW <= kHeadPlanes && C <= kWave, "planes per head, FCs per lane");
   const int hq = hkv * G;
-  __shared__ uint2 patch[kMaxPlanes];
 
   const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -474,12 +473,11 @@ tip_head_kernel(const int32_t* __restrict__ seq_lens, void* sidecar,
   sincos(ang, &sn, &cs);
   const float qy0 = (float)(pass ? qx0 : qx0 * cs - qx1 * sn);
   const float qy1 = (float)(pass ? qx1 : qx1 * cs + qx0 * sn);
+  // The tile holding the step's position rotates the step's key too, in
+  // every wave: lane c holds FC c's rotated pair, which the sums below read
+  // by readlane (no LDS, no barrier).
   uint2 own_bits = make_uint2(0u, 0u);
-  if (owner && wave == 0 && lane < C) {
-    // The tile holding the step's position rotates the step's key too.
-    own_bits = rotate_pair<BF16>(to_f64(kr0), to_f64(kr1), sn, cs, pass);
-    if (slot_c >= 0) patch[slot_c] = own_bits;
-  }
+  if (owner && lane < C) own_bits = rotate_pair<BF16>(to_f64(kr0), to_f64(kr1), sn, cs, pass);
   if (!live) {
     if (lead) {
       nb_out[b] = ok ? n : 0;
@@ -487,7 +485,6 @@ tip_head_kernel(const int32_t* __restrict__ seq_lens, void* sidecar,
     }
     return;
   }
-  if (owner) __syncthreads();  // the patch is written (owner is uniform per workgroup)
 
   // The head's weights: the rotated pair of its k-th dominant FC, read from
   // that FC's lane.  For bf16 pairs each weight is split into a high and a
@@ -513,7 +510,8 @@ tip_head_kernel(const int32_t* __restrict__ seq_lens, void* sidecar,
       if (sl < 0) break;
       uint4 da = xa[k], db = xb[k];
       if constexpr (OWN) {
-        const uint2 p = patch[sl];
+        const uint2 p = make_uint2((uint32_t)__builtin_amdgcn_readlane((int)own_bits.x, fc),
+                                   (uint32_t)__builtin_amdgcn_readlane((int)own_bits.y, fc));
         if constexpr (BF16) {
           da.x = (pos_lane && pos_t == 0) ? p.x : da.x;
           da.y = (pos_lane && pos_t == 1) ? p.x : da.y;
