@@ -85,6 +85,9 @@ struct FilterLds {
   int32_t pos[kFilterWaves * kWavePlayCap];
   uint32_t key[kFilterWaves * kWavePlayCap];
   float red[kFacRedFloats];  // FAC: the waves' partial sums
+  // FAC on the matrix cores (bf16, d = 128): the scaled query's high and low
+  // bf16 halves, staged once per workgroup.
+  alignas(16) uint16_t qhi[128], qlo[128];
   float zw[kFilterWaves][64];  // FAC: a wave's logits of one round
   float mw[kFilterWaves], lw[kFilterWaves];
   uint64_t pivot[kPivotCap];
@@ -328,6 +331,13 @@ struct WaveFac {
   static_assert(2 * RR <= 64, "two rounds' logits fit the wave's LDS slot");
   // Floats of a wave's state (this part's columns).
   static constexpr int W = D / S;
+  // bf16 at d = 128, lists whose rounds are all in flight at once (the TRIM
+  // issue and round): logits on the matrix cores.  k[4 t + kk] then holds,
+  // for 16-row tile t of the round, row 16 t + lane % 16's 16-byte chunk
+  // lane / 16 + 4 kk (dims 32 kk + 8 (lane / 16) ..): the A operand of
+  // v_mfma_f32_16x16x32_bf16 step kk.
+  static constexpr bool MF = BF16 && D == 128;
+  static_assert(!MF || (KST == 8 && RR == 32), "two 16-row tiles of 4 steps");
   static_assert(VL <= 32 && kFilterWaves * W <= kFacRedFloats, "partial sums");
   uint4 k[KST], v[VST];
 };
@@ -342,12 +352,23 @@ __device__ __forceinline__ void fac_issue(F& f, int r0, int cnt, const int32_t* 
                                           size_t kvbase, int part) {
   const int lane = threadIdx.x & (kWave - 1);
   const int last = cnt - 1;
+  if constexpr (F::MF && TRIM) {
 #pragma unroll
-  for (int s = 0; s < F::KST; ++s) {
-    if (TRIM && r0 + s * F::RS >= cnt) continue;
-    const int r = r0 + s * F::RS + lane / F::LPR;
-    const int j = pos[r < cnt ? r : last];
-    f.k[s] = K[(kvbase + (size_t)j) * F::LPR + lane % F::LPR];
+    for (int s = 0; s < F::KST; ++s) {
+      const int t = s / 4, kk = s % 4;
+      if (TRIM && r0 + 16 * t >= cnt) continue;
+      const int r = r0 + 16 * t + lane % 16;
+      const int j = pos[r < cnt ? r : last];
+      f.k[s] = K[(kvbase + (size_t)j) * F::LPR + lane / 16 + 4 * kk];
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < F::KST; ++s) {
+      if (TRIM && r0 + s * F::RS >= cnt) continue;
+      const int r = r0 + s * F::RS + lane / F::LPR;
+      const int j = pos[r < cnt ? r : last];
+      f.k[s] = K[(kvbase + (size_t)j) * F::LPR + lane % F::LPR];
+    }
   }
 #pragma unroll
   for (int s = 0; s < F::VST; ++s) {
@@ -430,6 +451,30 @@ __device__ __forceinline__ FacQuery<RowGeom<BF16, D>::EPL> fac_query(const Query
   return qq;
 }
 
+// The B operand of the matrix-core logits: column 0 holds the scaled query's
+// high bf16 half, column 1 its low half (so a logit is column 0 plus column
+// 1, within about 2^-16 of q~ . k), the other columns zero.  Lane l holds
+// column l % 16, dims 32 kk + 8 (l / 16) .. + 7 for step kk.
+typedef __bf16 fasa_fbf16x8 __attribute__((ext_vector_type(8)));
+typedef float fasa_ff32x4 __attribute__((ext_vector_type(4)));
+
+struct FacQueryM {
+  fasa_fbf16x8 b[4];
+};
+
+__device__ __forceinline__ FacQueryM fac_query_mfma(const FilterLds& L) {
+  const int lane = threadIdx.x & (kWave - 1), c = lane % 16;
+  FacQueryM qm;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int d0 = 32 * kk + 8 * (lane / 16);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (c < 2) v = *reinterpret_cast<const uint4*>(c == 0 ? &L.qhi[d0] : &L.qlo[d0]);
+    qm.b[kk] = __builtin_bit_cast(fasa_fbf16x8, v);
+  }
+  return qm;
+}
+
 // The wave's online-softmax state over its list.
 template <int EPL>
 struct WaveSoft {
@@ -453,6 +498,28 @@ __device__ __forceinline__ void fac_round(const F& f0, const F& f1, const Q& qq,
   // (its rows were never loaded) is skipped: they are masked below anyway.
   auto kfirst = [&](int s) { return r0 + (s / F::KST) * F::RR + (s % F::KST) * F::RS; };
   auto vfirst = [&](int s) { return r0 + (s / F::VST) * F::RR + (s % F::VST) * F::RV; };
+  if constexpr (F::MF && TRIM) {
+    // Per 16-row tile, 4 matrix-core steps; the D fragment's lane l holds
+    // rows 4 (l / 16) + i of column l % 16, and a row's logit is column 0
+    // plus column 1 (lane l + 1).
+#pragma unroll
+    for (int t = 0; t < 2 * NSETS; ++t) {
+      if (TRIM && r0 + 16 * t >= cnt) continue;
+      fasa_ff32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint4 x = t < 2 ? f0.k[4 * (t % 2) + kk] : f1.k[4 * (t % 2) + kk];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(fasa_fbf16x8, x),
+                                                      qq.b[kk], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = acc[i] + __int_as_float(__builtin_amdgcn_update_dpp(
+                                     0, __float_as_int(acc[i]), 0x101, 0xf, 0xf, true));
+        if (lane % 16 == 0) zw[16 * t + 4 * (lane / 16) + i] = v;
+      }
+    }
+  } else {
   float d[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
@@ -482,6 +549,7 @@ __device__ __forceinline__ void fac_round(const F& f0, const F& f1, const Q& qq,
     for (int s = 0; s < KS; ++s)
       if (!TRIM || kfirst(s) < cnt)
         zw[(s / F::KST) * F::RR + (s % F::KST) * F::RS + lane / LPR] = d[s];
+  }
   }
   // The wave reads back what its own lanes wrote (LDS keeps a wave's
   // accesses in order); the barrier only stops the compiler moving them.
@@ -531,7 +599,7 @@ __device__ __forceinline__ void fac_wave(WaveFac<BF16, D, S>& f0, WaveFac<BF16, 
   using F = WaveFac<BF16, D, S>;
   constexpr int EPL = F::EPL, VL = F::VL;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const auto qq = fac_query<BF16, D>(qraw);
+
   WaveSoft<EPL> st;
   st.m = -INFINITY;
   st.l = 0.0f;
@@ -540,12 +608,18 @@ __device__ __forceinline__ void fac_wave(WaveFac<BF16, D, S>& f0, WaveFac<BF16, 
   float* zw = L.zw[wave];
   const int nr = (cnt + F::RR - 1) / F::RR;
   if (nr <= 2) {
-    // Both sets as one round: one max, one rescale.
+    // Both sets as one round: one max, one rescale.  The whole list is in
+    // flight, so its logits may take the matrix cores (bf16, d = 128).
+    const auto qq = [&]() {
+      if constexpr (F::MF) return fac_query_mfma(L);
+      else return fac_query<BF16, D>(qraw);
+    }();
     if (nr > 0 && issued < 1) fac_issue<true>(f0, 0, cnt, pos, K, V, kvbase, part);
     if (nr > 1 && issued < 2) fac_issue<true>(f1, F::RR, cnt, pos, K, V, kvbase, part);
     if (nr == 2) fac_round<2, true>(f0, f1, qq, 0, cnt, pos, key, tau, zw, st);
     else if (nr == 1) fac_round<1, true>(f0, f1, qq, 0, cnt, pos, key, tau, zw, st);
   } else {
+    const auto qq = fac_query<BF16, D>(qraw);
     // Longer lists: round r computed while round r + 1 flies.
     if (issued < 1) fac_issue<false>(f0, 0, cnt, pos, K, V, kvbase, part);
     if (issued < 2) fac_issue<false>(f1, F::RR, cnt, pos, K, V, kvbase, part);
@@ -684,6 +758,22 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
     }
     for (int i = t; i < kFilterMaxGroups / kFilterThreads * kFilterWaves; i += NT)
       (&L.emit_cnt[0][0])[i] = 0u;
+  }
+  if constexpr (WaveFac<BF16, D, S>::MF) {
+    // The scaled query's bf16 halves for the matrix-core logits (read after
+    // the barriers every route passes before FAC).
+    if (t < 16) {
+      const float scale = logit_scale<D>();
+      const float qv[8] = {qraw.v[0].x, qraw.v[0].y, qraw.v[0].z, qraw.v[0].w,
+                           qraw.v[1].x, qraw.v[1].y, qraw.v[1].z, qraw.v[1].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = qv[i] * scale;
+        const uint32_t hb = f32_to_bf16_bits(x);
+        L.qhi[8 * t + i] = (uint16_t)hb;
+        L.qlo[8 * t + i] = (uint16_t)f32_to_bf16_bits(x - __uint_as_float(hb << 16));
+      }
+    }
   }
   const int n = checked_len(nb, b, max_seq_len, cap, err, lead && h == 0 && t == 0);
   if (advance != nullptr && lead && h == 0 && t == 0 && n > 0) advance[b] = n;
