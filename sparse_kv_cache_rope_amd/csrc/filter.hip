@@ -318,7 +318,7 @@ __device__ __forceinline__ void stream_emit(const float* row, int n, uint64_t ta
 // consecutive rounds, so round r + 1's rows fly while round r is computed.
 // Entries past cnt load the list's last row (fetched anyway) and count as
 // absent.
-template <bool BF16, int D, int S>
+template <bool BF16, int D, int S, bool MFOK>
 struct WaveFac {
   using Geo = RowGeom<BF16, D>;
   static constexpr int LPR = Geo::LPR, EPL = Geo::EPL, RS = Geo::RS;
@@ -336,7 +336,7 @@ struct WaveFac {
   // for 16-row tile t of the round, row 16 t + lane % 16's 16-byte chunk
   // lane / 16 + 4 kk (dims 32 kk + 8 (lane / 16) ..): the A operand of
   // v_mfma_f32_16x16x32_bf16 step kk.
-  static constexpr bool MF = BF16 && D == 128;
+  static constexpr bool MF = MFOK && BF16 && D == 128;
   static_assert(!MF || (KST == 8 && RR == 32), "two 16-row tiles of 4 steps");
   static_assert(VL <= 32 && kFilterWaves * W <= kFacRedFloats, "partial sums");
   uint4 k[KST], v[VST];
@@ -589,14 +589,15 @@ __device__ __forceinline__ void fac_round(const F& f0, const F& f1, const Q& qq,
 // FAC of a wave over its list (rounds 0 and 1 already in flight in f0 / f1
 // when `issued` says so), its state left in L.red / L.mw / L.lw for
 // fac_merge.
-template <bool BF16, int D, int S>
-__device__ __forceinline__ void fac_wave(WaveFac<BF16, D, S>& f0, WaveFac<BF16, D, S>& f1,
+template <bool BF16, int D, int S, bool MFOK>
+__device__ __forceinline__ void fac_wave(WaveFac<BF16, D, S, MFOK>& f0,
+                                         WaveFac<BF16, D, S, MFOK>& f1,
                                          int issued, int cnt, const int32_t* pos,
                                          const uint32_t* key, uint64_t tau,
                                          const uint4* __restrict__ K, const uint4* __restrict__ V,
                                          size_t kvbase, int part,
                                          const QueryRaw<BF16, D>& qraw, FilterLds& L) {
-  using F = WaveFac<BF16, D, S>;
+  using F = WaveFac<BF16, D, S, MFOK>;
   constexpr int EPL = F::EPL, VL = F::VL;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
 
@@ -667,7 +668,7 @@ __device__ __forceinline__ void fac_wave(WaveFac<BF16, D, S>& f0, WaveFac<BF16, 
 // 64 apart), and the 8 lanes holding one column's terms sum them.
 template <bool BF16, int D, int S>
 __device__ __forceinline__ void fac_merge(float* __restrict__ out_row, int part, FilterLds& L) {
-  using F = WaveFac<BF16, D, S>;
+  using F = WaveFac<BF16, D, S, false>;
   constexpr int NW = kFilterWaves;
   static_assert(NW == 8, "a column's terms are 8 consecutive lanes");
   const int t = threadIdx.x, w = t % NW;
@@ -722,7 +723,11 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
   constexpr int NW = kFilterWaves;
   constexpr int kCapW = E2 * kWave / kGroupTokens;  // surviving groups a wave holds
   static_assert(kCapW <= kWaveMaxSurvivors && E2 % 4 == 0, "survivor slots");
-  using F = WaveFac<BF16, D, S>;
+  // Matrix-core logits for the small survivor slots (B <= 320): those lists
+  // stay within the two rounds in flight.  Larger budgets run their long
+  // lists' pipelined rounds on VALU, and their instances carry no
+  // matrix-core code at all.
+  using F = WaveFac<BF16, D, S, (E2 <= 16)>;
   __shared__ FilterLds L;
   const int part = S > 1 ? (int)blockIdx.x / hq : 0;
   const int h = S > 1 ? (int)blockIdx.x % hq : (int)blockIdx.x, b = blockIdx.y;
@@ -759,7 +764,7 @@ filter_select_kernel(const uint32_t* __restrict__ gmax, int gstride,
     for (int i = t; i < kFilterMaxGroups / kFilterThreads * kFilterWaves; i += NT)
       (&L.emit_cnt[0][0])[i] = 0u;
   }
-  if constexpr (WaveFac<BF16, D, S>::MF) {
+  if constexpr (F::MF) {
     // The scaled query's bf16 halves for the matrix-core logits (read after
     // the barriers every route passes before FAC).
     if (t < 16) {
