@@ -25,9 +25,10 @@
 //      keys in a shared histogram (bins of keys from kp): the bin of the
 //      B-th largest in-play key gives tau at once when the whole bin is
 //      taken, else its few elements are ranked;
-//   4. FAC, each wave over its own list (entries below tau masked): logits,
-//      the wave's softmax max and sum, its weighted V sum, then one merge of
-//      the waves' states through LDS; when some wave's list is long (tokens
+//   4. FAC, each wave over its own list (entries below tau masked): logits
+//      (on the matrix cores for bf16 at d = 128 when the list's rows are all
+//      in flight at once), the wave's softmax max and sum, its weighted V
+//      sum, then one merge of the waves' states through LDS; when some wave's list is long (tokens
 //      clustered in few waves' groups), T_t is first laid out flat and split
 //      evenly over the waves;
 //   5. rows this does not fit (fewer groups than B, one score value, more
