@@ -125,23 +125,39 @@ __device__ __forceinline__ WavePick wave_pick(const uint32_t* hist, uint32_t nee
     c[13 - 4 * i] = x.z;
     c[12 - 4 * i] = x.w;
   }
-  uint32_t local = 0;
+  uint32_t q4[4];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) local += c[r];
+  for (int q = 0; q < 4; ++q) q4[q] = c[4 * q] + c[4 * q + 1] + c[4 * q + 2] + c[4 * q + 3];
+  const uint32_t local = q4[0] + q4[1] + q4[2] + q4[3];
   const uint32_t incl = wave_scan_incl(local);
   const uint32_t before = incl - local;
   const uint64_t bal = __ballot(before < need && need <= incl);
   WavePick p{0u, 0u, 0u, bal != 0ull};
   if (!p.ok) return p;
-  uint32_t bin = 0, above = 0, count = 0, acc = before;
+  // The target lane's bin: first the run of 4 (ranks 4 q ..) holding it,
+  // then the bin within that run.
+  uint32_t qsel = 0, acc = before, qacc = before;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    if (acc < need && need <= acc + c[r]) {
-      bin = (uint32_t)(kSelBins - 1 - 16 * l - r);
+  for (int q = 0; q < 4; ++q) {
+    const bool hit = acc < need && need <= acc + q4[q];
+    qsel = hit ? (uint32_t)q : qsel;
+    qacc = hit ? acc : qacc;
+    acc += q4[q];
+  }
+  uint32_t cq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    cq[i] = qsel == 0 ? c[i] : qsel == 1 ? c[4 + i] : qsel == 2 ? c[8 + i] : c[12 + i];
+  uint32_t bin = 0, above = 0, count = 0;
+  acc = qacc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (acc < need && need <= acc + cq[i]) {
+      bin = (uint32_t)(kSelBins - 1 - 16 * l) - (4u * qsel + (uint32_t)i);
       above = acc;
-      count = c[r];
+      count = cq[i];
     }
-    acc += c[r];
+    acc += cq[i];
   }
   const int src = (int)__builtin_ctzll(bal);
   p.bin = (uint32_t)__builtin_amdgcn_readlane((int)bin, src);
